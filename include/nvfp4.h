@@ -1,0 +1,191 @@
+/*
+ * nvfp4.h - C ABI of the MI355X (gfx950) W4A16 NVFP4 routed-expert MLP.
+ *
+ * The library runs the expert weights of a ModelOpt NVFP4 checkpoint as
+ * stored, with bf16 activations (W4A16). It follows the TensorFold issue #308,
+ * "GLM-5.3-Flash on CUDA: read nvidia/GLM-5.3-Flash-NVFP4 (ModelOpt NVFP4) as
+ * stored, W4A16":
+ *   - section "The checkpoint": weights are e2m1 codes with one e4m3 scale per
+ *     16 inputs and one fp32 weight_scale_2 per tensor;
+ *   - section "What the branch does": routed experts run in a grouped NVFP4
+ *     kernel with weight_scale_2 as the per-expert multiplier; the dense MLP
+ *     runs on Fp4Linear with gate and up apart (their tensor scales differ);
+ *     activations stay bf16 and the grouped kernel takes bf16 rows only; the
+ *     MTP layer's BF16 experts are packed to NVFP4 at load, a projection at a
+ *     time.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Memory.   Every tensor argument is a DEVICE pointer to contiguous row-major
+ *           memory owned by the caller. The library never allocates, frees,
+ *           copies to the host or synchronizes; all work is enqueued on
+ *           `stream` (a hipStream_t; NULL is the default stream). It keeps no
+ *           mutable global state and does not change the current device.
+ * bf16.     bf16 tensors are passed as uint16_t bit patterns.
+ * Weights.  A weight [n, k] (out x in) is described by nvfp4_weight_t:
+ *             codes   [groups, n, k/2]  uint8: element 2j of a row in the LOW
+ *                                       nibble of byte j, 2j+1 in the high;
+ *             scales  [groups, n, k/16] uint8: e4m3fn bits, one per 16
+ *                                       consecutive inputs of a row;
+ *             scale_2 [groups]          fp32 in device memory.
+ *           A weight is W[n,k] = e2m1(code) * e4m3(scale[n, k/16]) * scale_2.
+ * Shapes.   k must be a positive multiple of 32 (whole 16-input groups, in
+ *           32-wide tiles); n >= 1; row counts >= 0 (0 is a no-op).
+ * Alignment. codes, scales, activations and outputs must be 16-byte aligned.
+ * Errors.   Argument errors are detected on the host before anything is
+ *           enqueued; on error nothing is written. A failed launch returns
+ *           NVFP4_ERR_HIP. No C++ exception crosses this interface.
+ * Numerics. Products use bf16 matrix cores with fp32 accumulation over exactly
+ *           dequantized weights; scale_2 multiplies the fp32 accumulator. For a
+ *           given output element the summation order is fixed and does not
+ *           depend on the batch, the tile it lands in, or the other rows, so
+ *           results are bitwise reproducible.
+ */
+#ifndef NVFP4_MOE_EXPERT_AMD_NVFP4_H
+#define NVFP4_MOE_EXPERT_AMD_NVFP4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define NVFP4_ABI_VERSION 1
+
+typedef enum nvfp4_status {
+  NVFP4_OK = 0,
+  NVFP4_ERR_NULL = 1,        /* a required pointer is NULL */
+  NVFP4_ERR_SHAPE = 2,       /* inconsistent or unsupported sizes (k % 32 != 0, n < 1, ...) */
+  NVFP4_ERR_ALIGN = 3,       /* a pointer is not 16-byte aligned */
+  NVFP4_ERR_WORKSPACE = 4,   /* workspace missing or smaller than the *_workspace_size() figure */
+  NVFP4_ERR_UNSUPPORTED = 5, /* a request outside W4A16 (e.g. FP4 activations) */
+  NVFP4_ERR_HIP = 6          /* the HIP runtime reported an error when enqueueing */
+} nvfp4_status;
+
+typedef struct nvfp4_weight_t {
+  const uint8_t* codes;   /* [groups, n, k/2] */
+  const uint8_t* scales;  /* [groups, n, k/16] */
+  const float* scale_2;   /* [groups] */
+  int64_t n;              /* output features (rows) */
+  int64_t k;              /* input features, multiple of 32 */
+  int32_t groups;         /* number of tensors (experts); 1 for a dense weight */
+} nvfp4_weight_t;
+
+/* Version of this interface (NVFP4_ABI_VERSION). */
+int nvfp4_abi_version(void);
+
+/* Static, NUL-terminated description of a status code. */
+const char* nvfp4_status_string(int status);
+
+/*
+ * nvfp4_pack - load-time BF16 -> NVFP4 pack of `batch` independent tensors.
+ * Passage: issue #308 "What the branch does" (the MTP layer's BF16 experts are
+ * packed to NVFP4 by ModelOpt's recipe at load, a projection at a time).
+ * Recipe, per tensor, in fp32 with correctly rounded division:
+ *   scale_2 = amax / 2688  (6 * 448);
+ *   per 16-block along k: byte = e4m3(block_amax / 6 / scale_2), nearest-even,
+ *   saturating at 448;  s_eff = e4m3(byte) * scale_2;
+ *   per element: code = e2m1(w / s_eff), nearest-even, clamped at 6, sign bit
+ *   of the quotient (so -0.0 encodes as 0x8).
+ *   An all-zero tensor packs to scale_2 = 0, bytes 0, codes 0; a block whose
+ *   s_eff is 0 packs to codes 0. Non-finite inputs are outside the contract.
+ * w       [batch, n, k] bf16 (device).
+ * codes   [batch, n, k/2] out;  scales [batch, n, k/16] out;  scale_2 [batch] out.
+ * ws      device workspace of at least nvfp4_pack_workspace_size(batch, n, k)
+ *         bytes (per-tensor partial maxima); contents need not be initialised.
+ */
+size_t nvfp4_pack_workspace_size(int32_t batch, int64_t n, int64_t k);
+nvfp4_status nvfp4_pack(const uint16_t* w, int32_t batch, int64_t n, int64_t k,
+                        uint8_t* codes, uint8_t* scales, float* scale_2,
+                        void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * nvfp4_dequant - debug export of the dequantized weights (bit-exact checks).
+ * Passage: issue #308 "The checkpoint" (code, block scale and tensor scale).
+ * wq_unscaled [groups, n, k] bf16 out: e2m1(code) * e4m3(scale), exact in bf16.
+ * wq_scaled   [groups, n, k] fp32 out: fp32(unscaled * scale_2), one rounding.
+ * Either output may be NULL (not written); not both.
+ */
+nvfp4_status nvfp4_dequant(const nvfp4_weight_t* w, uint16_t* wq_unscaled, float* wq_scaled,
+                           void* stream);
+
+/*
+ * nvfp4_linear - dense Fp4Linear: y[m, n] = bf16(scale_2 * sum_k x[m,k] * W[n,k]).
+ * Passage: issue #308 "What the branch does" (the dense MLP runs on Fp4Linear).
+ * x [m, k] bf16; w: groups == 1, w->k == k of x; y [m, n] bf16 out (round to
+ * nearest even). m may be 0.
+ */
+nvfp4_status nvfp4_linear(const uint16_t* x, int64_t m, const nvfp4_weight_t* w, uint16_t* y,
+                          void* stream);
+
+/*
+ * nvfp4_linear_gated - the dense MLP's gate and up projections, kept apart
+ * because their tensor scales differ (issue #308, "What the branch does"), and
+ * combined as h[m, n] = bf16(SiLU(g) * u) with g, u the fp32 outputs of
+ * nvfp4_linear on w_gate and w_up, SiLU(z) = z / (1 + exp(-z)).
+ * w_gate and w_up: same n and k, groups == 1, each its own scale_2.
+ * h [m, n] bf16 out.
+ */
+nvfp4_status nvfp4_linear_gated(const uint16_t* x, int64_t m, const nvfp4_weight_t* w_gate,
+                                const nvfp4_weight_t* w_up, uint16_t* h, void* stream);
+
+/*
+ * nvfp4_moe_route - debug export of the token permutation by expert (bit-exact checks).
+ * Slot s = t*k + j holds topk_ids[t, j]; it is local iff
+ * expert_begin <= id < expert_begin + n_experts. Outputs:
+ *   offsets [n_experts + 1] int32: exclusive prefix sums of the per-expert counts;
+ *   perm    [T*k] int32: the local slots ordered by (expert, slot) - stable;
+ *           entries past offsets[n_experts] are left unspecified;
+ *   inv     [T*k] int32: the position of each slot in perm, -1 if skipped.
+ * The counts are a histogram; the offsets come from a wavefront prefix scan.
+ * ws: at least nvfp4_moe_route_workspace_size(T, k, n_experts) bytes.
+ * Limits: 1 <= n_experts <= 4096, 1 <= k <= 64.
+ */
+size_t nvfp4_moe_route_workspace_size(int64_t T, int32_t k, int32_t n_experts);
+nvfp4_status nvfp4_moe_route(const int32_t* topk_ids, int64_t T, int32_t k, int32_t n_experts,
+                             int32_t expert_begin, int32_t* offsets, int32_t* perm, int32_t* inv,
+                             void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * nvfp4_moe_grouped - the routed expert MLP of one MoE layer.
+ * Passage: issue #308 "What the branch does" (routed experts in the grouped
+ * NVFP4 kernel, weight_scale_2 as the per-expert multiplier, bf16 rows only).
+ * For every local slot (t, j) with expert e = topk_ids[t, j] - expert_begin:
+ *   g = s2g[e] * x_t . Wg_e^T,  u = s2u[e] * x_t . Wu_e^T   (fp32 accumulators)
+ *   h = bf16(SiLU(g) * u)                                     [I]
+ *   d = s2d[e] * h . Wd_e^T                                   (fp32)
+ *   y_t = bf16( sum over j = 0..k-1, in that order, of topk_w[t, j] * d )
+ * Slots whose id is not local contribute 0 (the expert-parallel hook:
+ * expert_begin = 0 on one GPU). Duplicate ids in a token count separately.
+ * y is overwritten. The sum over j is a fixed-order gather, not atomics.
+ * x        [T, H] bf16;  topk_ids [T, k] int32;  topk_w [T, k] fp32.
+ * gate, up: groups = E, n = I, k = H.   down: groups = E, n = H, k = I.
+ * ws       at least nvfp4_moe_workspace_size(T, k, E, H, I) bytes.
+ * y        [T, H] bf16 out.
+ * Limits: 1 <= E <= 4096, 1 <= k <= 64, H and I multiples of 32.
+ */
+size_t nvfp4_moe_workspace_size(int64_t T, int32_t k, int32_t n_experts, int64_t H, int64_t I);
+nvfp4_status nvfp4_moe_grouped(const uint16_t* x, int64_t T, int64_t H, const int32_t* topk_ids,
+                               const float* topk_w, int32_t k, int32_t expert_begin,
+                               const nvfp4_weight_t* gate, const nvfp4_weight_t* up,
+                               const nvfp4_weight_t* down, void* ws, size_t ws_bytes,
+                               uint16_t* y, void* stream);
+
+/*
+ * nvfp4_moe_grouped_timed - nvfp4_moe_grouped with a hipEvent_t recorded on
+ * `stream` before the first kernel and after each of its stages (route,
+ * gate/up, down, combine): events[0..4]. Same results; for per-stage timing.
+ */
+nvfp4_status nvfp4_moe_grouped_timed(const uint16_t* x, int64_t T, int64_t H,
+                                     const int32_t* topk_ids, const float* topk_w, int32_t k,
+                                     int32_t expert_begin, const nvfp4_weight_t* gate,
+                                     const nvfp4_weight_t* up, const nvfp4_weight_t* down,
+                                     void* ws, size_t ws_bytes, uint16_t* y, void* stream,
+                                     void* const* events);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NVFP4_MOE_EXPERT_AMD_NVFP4_H */

@@ -1,0 +1,279 @@
+"""MI355X-native W4A16 NVFP4 routed-expert MLP.
+
+Thin ctypes binding over ``libnvfp4.so`` (C ABI in ``include/nvfp4.h``). This
+module only marshals arguments: it checks dtypes, shapes and contiguity,
+passes device pointers and the current HIP stream, and allocates outputs and
+workspaces with torch. Every step of the computation runs in the library's
+HIP kernels; there is no fallback. If the library is missing, every call
+raises.
+
+The weight layout is the ModelOpt NVFP4 one read "as stored" (TensorFold issue
+#308, section "The checkpoint"): codes [G, N, K/2] uint8 (even k in the low
+nibble), scales [G, N, K/16] e4m3fn bytes, scale_2 [G] float32.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+__all__ = [
+    "Nvfp4Error", "NVFP4Weight", "load_library", "library_path", "abi_version",
+    "pack", "dequant", "linear", "linear_gated", "moe_route", "moe_grouped",
+    "moe_workspace_size", "pack_workspace_size",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libnvfp4.so")
+_lib = None
+
+
+class Nvfp4Error(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = load_library().nvfp4_status_string(status).decode()
+        super().__init__(f"{where}: nvfp4 status {status} ({msg})")
+
+
+class _Weight(ctypes.Structure):
+    _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("scale_2", ctypes.c_void_p),
+                ("n", ctypes.c_int64), ("k", ctypes.c_int64), ("groups", ctypes.c_int32)]
+
+
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_I32 = ctypes.c_int32
+_SZ = ctypes.c_size_t
+_WP = ctypes.POINTER(_Weight)
+
+_SIGNATURES = {
+    "nvfp4_abi_version": (ctypes.c_int, []),
+    "nvfp4_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "nvfp4_pack_workspace_size": (_SZ, [_I32, _I64, _I64]),
+    "nvfp4_pack": (ctypes.c_int, [_P, _I32, _I64, _I64, _P, _P, _P, _P, _SZ, _P]),
+    "nvfp4_dequant": (ctypes.c_int, [_WP, _P, _P, _P]),
+    "nvfp4_linear": (ctypes.c_int, [_P, _I64, _WP, _P, _P]),
+    "nvfp4_linear_gated": (ctypes.c_int, [_P, _I64, _WP, _WP, _P, _P]),
+    "nvfp4_moe_route_workspace_size": (_SZ, [_I64, _I32, _I32]),
+    "nvfp4_moe_route": (ctypes.c_int, [_P, _I64, _I32, _I32, _I32, _P, _P, _P, _P, _SZ, _P]),
+    "nvfp4_moe_workspace_size": (_SZ, [_I64, _I32, _I32, _I64, _I64]),
+    "nvfp4_moe_grouped": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _I32, _I32, _WP, _WP, _WP, _P, _SZ, _P, _P]),
+    "nvfp4_moe_grouped_timed": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _I32, _I32, _WP, _WP, _WP, _P, _SZ, _P,
+                                               _P, ctypes.POINTER(_P)]),
+}
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load libnvfp4.so (built in-tree by ``python -m nvfp4_moe_expert_amd.build``)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(f"{_LIB_PATH} is missing: build it with `python -m nvfp4_moe_expert_amd.build`")
+        lib = ctypes.CDLL(_LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def abi_version() -> int:
+    return load_library().nvfp4_abi_version()
+
+
+# ---------------------------------------------------------------- helpers
+def _stream() -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ptr(t: torch.Tensor | None) -> ctypes.c_void_p:
+    return ctypes.c_void_p(0 if t is None else t.data_ptr())
+
+
+def _need(t: torch.Tensor, dtype: torch.dtype, name: str, ndim: int | None = None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (W4A16: activations are bf16 rows), got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on a GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous row-major")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise Nvfp4Error(status, where)
+
+
+@dataclass
+class NVFP4Weight:
+    """Device tensors of one NVFP4 weight or a group of them (experts)."""
+    codes: torch.Tensor    # uint8 [G, N, K/2]
+    scales: torch.Tensor   # uint8 [G, N, K/16]
+    scale_2: torch.Tensor  # float32 [G]
+
+    def __post_init__(self):
+        if self.codes.dim() == 2:
+            self.codes = self.codes.unsqueeze(0)
+        if self.scales.dim() == 2:
+            self.scales = self.scales.unsqueeze(0)
+        if self.scale_2.dim() == 0:
+            self.scale_2 = self.scale_2.reshape(1)
+        _need(self.codes, torch.uint8, "codes", 3)
+        _need(self.scales, torch.uint8, "scales", 3)
+        _need(self.scale_2, torch.float32, "scale_2", 1)
+        g, n, k2 = self.codes.shape
+        if self.scales.shape != (g, n, k2 * 2 // 16) or self.scale_2.shape != (g,):
+            raise ValueError("inconsistent NVFP4 weight shapes")
+
+    @property
+    def groups(self) -> int:
+        return self.codes.shape[0]
+
+    @property
+    def n(self) -> int:
+        return self.codes.shape[1]
+
+    @property
+    def k(self) -> int:
+        return self.codes.shape[2] * 2
+
+    def _struct(self) -> _Weight:
+        return _Weight(self.codes.data_ptr(), self.scales.data_ptr(), self.scale_2.data_ptr(),
+                       self.n, self.k, self.groups)
+
+    def expert(self, e: int) -> "NVFP4Weight":
+        return NVFP4Weight(self.codes[e:e + 1], self.scales[e:e + 1], self.scale_2[e:e + 1])
+
+
+# ---------------------------------------------------------------- entry points
+def pack_workspace_size(batch: int, n: int, k: int) -> int:
+    return load_library().nvfp4_pack_workspace_size(batch, n, k)
+
+
+def pack(w: torch.Tensor) -> NVFP4Weight:
+    """BF16 [N, K] or [G, N, K] -> NVFP4 (one scale_2 per tensor)."""
+    lib = load_library()
+    if w.dim() == 2:
+        w = w.unsqueeze(0)
+    _need(w, torch.bfloat16, "w", 3)
+    g, n, k = w.shape
+    dev = w.device
+    codes = torch.empty((g, n, k // 2), dtype=torch.uint8, device=dev)
+    scales = torch.empty((g, n, k // 16), dtype=torch.uint8, device=dev)
+    s2 = torch.empty((g,), dtype=torch.float32, device=dev)
+    wsb = max(lib.nvfp4_pack_workspace_size(g, n, k), 16)
+    ws = torch.empty((wsb,), dtype=torch.uint8, device=dev)
+    _check(lib.nvfp4_pack(_ptr(w), g, n, k, _ptr(codes), _ptr(scales), _ptr(s2), _ptr(ws), wsb, _stream()),
+           "nvfp4_pack")
+    return NVFP4Weight(codes, scales, s2)
+
+
+def dequant(w: NVFP4Weight, unscaled: bool = True, scaled: bool = True):
+    """(bf16 [G,N,K] code*scale, fp32 [G,N,K] code*scale*scale_2); either may be None."""
+    lib = load_library()
+    dev = w.codes.device
+    u = torch.empty((w.groups, w.n, w.k), dtype=torch.bfloat16, device=dev) if unscaled else None
+    s = torch.empty((w.groups, w.n, w.k), dtype=torch.float32, device=dev) if scaled else None
+    ws = w._struct()
+    _check(lib.nvfp4_dequant(ctypes.byref(ws), _ptr(u), _ptr(s), _stream()), "nvfp4_dequant")
+    return u, s
+
+
+def linear(x: torch.Tensor, w: NVFP4Weight, out: torch.Tensor | None = None) -> torch.Tensor:
+    """y[m, n] = bf16(scale_2 * x . W^T)."""
+    lib = load_library()
+    _need(x, torch.bfloat16, "x", 2)
+    if out is None:
+        out = torch.empty((x.shape[0], w.n), dtype=torch.bfloat16, device=x.device)
+    _need(out, torch.bfloat16, "out", 2)
+    if x.shape[1] != w.k or out.shape != (x.shape[0], w.n):
+        raise ValueError("shape mismatch in linear")
+    ws = w._struct()
+    _check(lib.nvfp4_linear(_ptr(x), x.shape[0], ctypes.byref(ws), _ptr(out), _stream()), "nvfp4_linear")
+    return out
+
+
+def linear_gated(x: torch.Tensor, w_gate: NVFP4Weight, w_up: NVFP4Weight,
+                 out: torch.Tensor | None = None) -> torch.Tensor:
+    """h[m, n] = bf16(SiLU(gate) * up), gate and up each with their own scale_2."""
+    lib = load_library()
+    _need(x, torch.bfloat16, "x", 2)
+    if out is None:
+        out = torch.empty((x.shape[0], w_gate.n), dtype=torch.bfloat16, device=x.device)
+    _need(out, torch.bfloat16, "out", 2)
+    if x.shape[1] != w_gate.k or out.shape != (x.shape[0], w_gate.n):
+        raise ValueError("shape mismatch in linear_gated")
+    g, u = w_gate._struct(), w_up._struct()
+    _check(lib.nvfp4_linear_gated(_ptr(x), x.shape[0], ctypes.byref(g), ctypes.byref(u), _ptr(out), _stream()),
+           "nvfp4_linear_gated")
+    return out
+
+
+def moe_route(topk_ids: torch.Tensor, n_experts: int, expert_begin: int = 0):
+    """(offsets [E+1], perm [T*k] (valid prefix), inv [T*k]) - the stable permutation by expert."""
+    lib = load_library()
+    _need(topk_ids, torch.int32, "topk_ids", 2)
+    T, k = topk_ids.shape
+    dev = topk_ids.device
+    offsets = torch.empty((n_experts + 1,), dtype=torch.int32, device=dev)
+    perm = torch.empty((max(T * k, 1),), dtype=torch.int32, device=dev)
+    inv = torch.empty((max(T * k, 1),), dtype=torch.int32, device=dev)
+    _check(lib.nvfp4_moe_route(_ptr(topk_ids), T, k, n_experts, expert_begin, _ptr(offsets), _ptr(perm),
+                               _ptr(inv), None, 0, _stream()), "nvfp4_moe_route")
+    return offsets, perm[: T * k], inv[: T * k]
+
+
+def moe_workspace_size(T: int, k: int, n_experts: int, H: int, I: int) -> int:
+    return load_library().nvfp4_moe_workspace_size(T, k, n_experts, H, I)
+
+
+def moe_grouped(x: torch.Tensor, topk_ids: torch.Tensor, topk_w: torch.Tensor, gate: NVFP4Weight,
+                up: NVFP4Weight, down: NVFP4Weight, expert_begin: int = 0, workspace: torch.Tensor | None = None,
+                out: torch.Tensor | None = None, events=None) -> torch.Tensor:
+    """Routed expert MLP of one MoE layer: y[T, H] bf16.
+
+    events: optional sequence of 5 torch.cuda.Event; the library records them on the
+    current stream before the first kernel and after the route, gate/up, down and
+    combine stages."""
+    lib = load_library()
+    _need(x, torch.bfloat16, "x", 2)
+    _need(topk_ids, torch.int32, "topk_ids", 2)
+    _need(topk_w, torch.float32, "topk_w", 2)
+    T, H = x.shape
+    k = topk_ids.shape[1]
+    if topk_ids.shape != (T, k) or topk_w.shape != (T, k):
+        raise ValueError("topk_ids / topk_w must be [T, k]")
+    E, I = gate.groups, gate.n
+    need = lib.nvfp4_moe_workspace_size(T, k, E, H, I)
+    if workspace is None:
+        workspace = torch.empty((max(need, 256),), dtype=torch.uint8, device=x.device)
+    _need(workspace, torch.uint8, "workspace", 1)
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
+    _need(out, torch.bfloat16, "out", 2)
+    g, u, d = gate._struct(), up._struct(), down._struct()
+    args = (_ptr(x), T, H, _ptr(topk_ids), _ptr(topk_w), k, expert_begin, ctypes.byref(g), ctypes.byref(u),
+            ctypes.byref(d), _ptr(workspace), workspace.numel(), _ptr(out), _stream())
+    if events is None:
+        st = lib.nvfp4_moe_grouped(*args)
+    else:
+        if len(events) != 5:
+            raise ValueError("events must hold 5 torch.cuda.Event")
+        for ev in events:          # make sure each event object exists on the device
+            if ev.cuda_event == 0:
+                ev.record()
+        arr = (_P * 5)(*[ctypes.c_void_p(ev.cuda_event) for ev in events])
+        st = lib.nvfp4_moe_grouped_timed(*args, arr)
+    _check(st, "nvfp4_moe_grouped")
+    return out

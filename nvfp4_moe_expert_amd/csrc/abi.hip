@@ -1,0 +1,272 @@
+// C ABI of the NVFP4 expert library: host-side validation, workspace layout and
+// launch orchestration. The declarations and the contract are in include/nvfp4.h.
+//
+// No entry point allocates, frees, synchronizes, copies to the host, or changes
+// the current device; everything is enqueued on the caller's stream. Every
+// argument check runs before the first launch, so an error writes nothing.
+#include <hip/hip_runtime.h>
+
+#include "../../include/nvfp4.h"
+#include "launch.hpp"
+
+using namespace nvfp4;
+
+namespace {
+
+constexpr int64_t kMaxExperts = 4096;
+constexpr int kMaxTopk = 64;
+constexpr int64_t kMaxSlots = (int64_t)1 << 30;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t round_up(size_t v) { return (v + 255) & ~(size_t)255; }
+
+nvfp4_status check_weight(const nvfp4_weight_t* w) {
+  if (!w || !w->codes || !w->scales || !w->scale_2) return NVFP4_ERR_NULL;
+  if (w->n < 1 || w->k < 32 || (w->k % 32) != 0 || w->groups < 1) return NVFP4_ERR_SHAPE;
+  // grid.y of the GEMM counts 64-row blocks of n (<= 65535); dequant grid < 2^31 blocks
+  if (w->n > (int64_t)64 * 65535 || w->k > ((int64_t)1 << 31)) return NVFP4_ERR_SHAPE;
+  if ((int64_t)w->groups * w->n * (w->k / 8) / 256 >= ((int64_t)1 << 31)) return NVFP4_ERR_SHAPE;
+  if (!aligned16(w->codes) || !aligned16(w->scales)) return NVFP4_ERR_ALIGN;
+  return NVFP4_OK;
+}
+
+nvfp4_status from_hip(hipError_t e) { return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP; }
+
+// Workspace of nvfp4_moe_grouped, in order: offsets[E+1], perm[S], tiles[max_tiles][4],
+// n_tiles, H[S][I] bf16, Ypart[S][H] fp32. Each region starts on a 256-byte boundary.
+struct MoeLayout {
+  size_t offsets, perm, tiles, n_tiles, h, ypart, total;
+  int64_t max_tiles;
+};
+
+// Decode tiles (16 rows) when the average local expert gets at most 16 rows, else prefill tiles.
+GemmVariant moe_variant(int64_t S, int64_t E) {
+  const int64_t busy = S < E ? S : E;
+  return (busy > 0 && S <= 16 * busy) ? kDecode : kPrefill;
+}
+
+MoeLayout moe_layout(int64_t T, int k, int64_t E, int64_t H, int64_t I) {
+  MoeLayout L{};
+  const int64_t S = T * k;
+  const int64_t tr = variant_tile_rows(moe_variant(S, E));
+  // sum over experts of ceil(rows/tr) <= floor(S/tr) + (number of non-empty experts)
+  L.max_tiles = S / tr + (S < E ? S : E);
+  size_t off = 0;
+  L.offsets = off; off += round_up(sizeof(int32_t) * (size_t)(E + 1));
+  L.perm = off;    off += round_up(sizeof(int32_t) * (size_t)(S > 0 ? S : 1));
+  L.tiles = off;   off += round_up(sizeof(int32_t) * 4 * (size_t)(L.max_tiles > 0 ? L.max_tiles : 1));
+  L.n_tiles = off; off += 256;
+  L.h = off;       off += round_up(sizeof(uint16_t) * (size_t)S * (size_t)I);
+  L.ypart = off;   off += round_up(sizeof(float) * (size_t)S * (size_t)H);
+  L.total = off;
+  return L;
+}
+
+template <typename T>
+T* at(void* base, size_t off) {
+  return reinterpret_cast<T*>(reinterpret_cast<char*>(base) + off);
+}
+
+nvfp4_status moe_impl(const uint16_t* x, int64_t T, int64_t H, const int32_t* ids, const float* tw,
+                      int32_t k, int32_t eb, const nvfp4_weight_t* gate, const nvfp4_weight_t* up,
+                      const nvfp4_weight_t* down, void* ws, size_t ws_bytes, uint16_t* y,
+                      hipStream_t s, void* const* events) {
+  nvfp4_status st;
+  if ((st = check_weight(gate)) != NVFP4_OK) return st;
+  if ((st = check_weight(up)) != NVFP4_OK) return st;
+  if ((st = check_weight(down)) != NVFP4_OK) return st;
+  if (T < 0 || k < 1 || k > kMaxTopk) return NVFP4_ERR_SHAPE;
+  const int64_t E = gate->groups, I = gate->n;
+  if (E > kMaxExperts) return NVFP4_ERR_SHAPE;
+  if (gate->k != H || up->k != H || up->n != I || up->groups != E) return NVFP4_ERR_SHAPE;
+  if (down->groups != E || down->n != H || down->k != I) return NVFP4_ERR_SHAPE;
+  if (T * (int64_t)k > kMaxSlots) return NVFP4_ERR_SHAPE;
+  if (T > 0 && (!x || !ids || !tw || !y)) return NVFP4_ERR_NULL;
+  if (T > 0 && (!aligned16(x) || !aligned16(y))) return NVFP4_ERR_ALIGN;
+  const MoeLayout L = moe_layout(T, k, E, H, I);
+  if (T > 0) {
+    if (!ws) return NVFP4_ERR_WORKSPACE;
+    if (!aligned16(ws)) return NVFP4_ERR_ALIGN;
+    if (ws_bytes < L.total) return NVFP4_ERR_WORKSPACE;
+  }
+  hipEvent_t ev[5] = {};
+  if (events)
+    for (int i = 0; i < 5; ++i) {
+      if (!events[i]) return NVFP4_ERR_NULL;
+      ev[i] = reinterpret_cast<hipEvent_t>(events[i]);
+    }
+  auto mark = [&](int i) -> hipError_t { return events ? hipEventRecord(ev[i], s) : hipSuccess; };
+  hipError_t e = mark(0);
+  if (T == 0) {
+    for (int i = 1; i < 5 && e == hipSuccess; ++i) e = mark(i);
+    return from_hip(e);
+  }
+  const int64_t S = T * k;
+  const GemmVariant v = moe_variant(S, E);
+  int32_t* offsets = at<int32_t>(ws, L.offsets);
+  int32_t* perm = at<int32_t>(ws, L.perm);
+  int32_t* tiles = at<int32_t>(ws, L.tiles);
+  int32_t* n_tiles = at<int32_t>(ws, L.n_tiles);
+  uint16_t* hbuf = at<uint16_t>(ws, L.h);
+  float* ypart = at<float>(ws, L.ypart);
+
+  if (e == hipSuccess)
+    e = launch_route(ids, S, (int)E, eb, variant_tile_rows(v), offsets, perm, nullptr, tiles, n_tiles, s);
+  if (e == hipSuccess) e = mark(1);
+
+  GemmArgs g{};
+  g.perm = perm;
+  g.topk = k;
+  g.tiles = tiles;
+  g.n_tiles = n_tiles;
+  if (e == hipSuccess) {
+    g.x = x;
+    g.w0 = {gate->codes, gate->scales, gate->scale_2};
+    g.w1 = {up->codes, up->scales, up->scale_2};
+    g.N = I;
+    g.K = H;
+    g.out = hbuf;
+    e = launch_gemm(kGateUp, v, g, L.max_tiles, s);
+  }
+  if (e == hipSuccess) e = mark(2);
+  if (e == hipSuccess) {
+    g.x = hbuf;
+    g.w0 = {down->codes, down->scales, down->scale_2};
+    g.w1 = {nullptr, nullptr, nullptr};
+    g.N = H;
+    g.K = I;
+    g.out = ypart;
+    e = launch_gemm(kDown, v, g, L.max_tiles, s);
+  }
+  if (e == hipSuccess) e = mark(3);
+  if (e == hipSuccess) e = launch_combine(ids, tw, ypart, T, k, H, (int)E, eb, y, s);
+  if (e == hipSuccess) e = mark(4);
+  return from_hip(e);
+}
+
+nvfp4_status linear_impl(const uint16_t* x, int64_t m, const nvfp4_weight_t* w0,
+                         const nvfp4_weight_t* w1, uint16_t* out, hipStream_t s) {
+  nvfp4_status st;
+  if ((st = check_weight(w0)) != NVFP4_OK) return st;
+  if (w1) {
+    if ((st = check_weight(w1)) != NVFP4_OK) return st;
+    if (w1->n != w0->n || w1->k != w0->k || w1->groups != 1) return NVFP4_ERR_SHAPE;
+  }
+  if (w0->groups != 1 || m < 0 || m > kMaxSlots) return NVFP4_ERR_SHAPE;
+  if (m == 0) return NVFP4_OK;
+  if (!x || !out) return NVFP4_ERR_NULL;
+  if (!aligned16(x) || !aligned16(out)) return NVFP4_ERR_ALIGN;
+  const GemmVariant v = m <= 16 ? kDecode : kPrefill;
+  const int64_t tr = variant_tile_rows(v);
+  GemmArgs g{};
+  g.x = x;
+  g.M = m;
+  g.w0 = {w0->codes, w0->scales, w0->scale_2};
+  if (w1) g.w1 = {w1->codes, w1->scales, w1->scale_2};
+  g.N = w0->n;
+  g.K = w0->k;
+  g.out = out;
+  return from_hip(launch_gemm(w1 ? kGated : kLinear, v, g, (m + tr - 1) / tr, s));
+}
+
+}  // namespace
+
+extern "C" {
+
+int nvfp4_abi_version(void) { return NVFP4_ABI_VERSION; }
+
+const char* nvfp4_status_string(int status) {
+  switch (status) {
+    case NVFP4_OK: return "ok";
+    case NVFP4_ERR_NULL: return "a required pointer is NULL";
+    case NVFP4_ERR_SHAPE: return "inconsistent or unsupported sizes";
+    case NVFP4_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+    case NVFP4_ERR_WORKSPACE: return "workspace missing or too small";
+    case NVFP4_ERR_UNSUPPORTED: return "unsupported request (the library is W4A16: bf16 activations only)";
+    case NVFP4_ERR_HIP: return "HIP runtime error while enqueueing";
+  }
+  return "unknown status";
+}
+
+size_t nvfp4_pack_workspace_size(int32_t batch, int64_t n, int64_t k) {
+  if (batch < 1 || n < 1 || k < 32) return 0;
+  return sizeof(uint32_t) * (size_t)batch * (size_t)pack_nblk(n * k);
+}
+
+nvfp4_status nvfp4_pack(const uint16_t* w, int32_t batch, int64_t n, int64_t k, uint8_t* codes,
+                        uint8_t* scales, float* scale_2, void* ws, size_t ws_bytes, void* stream) {
+  if (batch < 1 || batch > 65535 || n < 1 || k < 32 || (k % 32) != 0) return NVFP4_ERR_SHAPE;
+  if (n * k / 32 > ((int64_t)1 << 38)) return NVFP4_ERR_SHAPE;
+  if (!w || !codes || !scales || !scale_2) return NVFP4_ERR_NULL;
+  if (!aligned16(w) || !aligned16(codes) || !aligned16(scales)) return NVFP4_ERR_ALIGN;
+  if (!ws || ws_bytes < nvfp4_pack_workspace_size(batch, n, k)) return NVFP4_ERR_WORKSPACE;
+  if (!aligned16(ws)) return NVFP4_ERR_ALIGN;
+  return from_hip(launch_pack(w, batch, n, k, codes, scales, scale_2, static_cast<uint32_t*>(ws),
+                              static_cast<hipStream_t>(stream)));
+}
+
+nvfp4_status nvfp4_dequant(const nvfp4_weight_t* w, uint16_t* wq_unscaled, float* wq_scaled,
+                           void* stream) {
+  nvfp4_status st = check_weight(w);
+  if (st != NVFP4_OK) return st;
+  if (!wq_unscaled && !wq_scaled) return NVFP4_ERR_NULL;
+  if ((wq_unscaled && !aligned16(wq_unscaled)) || (wq_scaled && !aligned16(wq_scaled)))
+    return NVFP4_ERR_ALIGN;
+  return from_hip(launch_dequant(w->codes, w->scales, w->scale_2, w->groups, w->n, w->k, wq_unscaled,
+                                 wq_scaled, static_cast<hipStream_t>(stream)));
+}
+
+nvfp4_status nvfp4_linear(const uint16_t* x, int64_t m, const nvfp4_weight_t* w, uint16_t* y,
+                          void* stream) {
+  return linear_impl(x, m, w, nullptr, y, static_cast<hipStream_t>(stream));
+}
+
+nvfp4_status nvfp4_linear_gated(const uint16_t* x, int64_t m, const nvfp4_weight_t* w_gate,
+                                const nvfp4_weight_t* w_up, uint16_t* h, void* stream) {
+  if (!w_up) return NVFP4_ERR_NULL;
+  return linear_impl(x, m, w_gate, w_up, h, static_cast<hipStream_t>(stream));
+}
+
+size_t nvfp4_moe_route_workspace_size(int64_t T, int32_t k, int32_t n_experts) {
+  (void)T; (void)k; (void)n_experts;
+  return 0;
+}
+
+nvfp4_status nvfp4_moe_route(const int32_t* topk_ids, int64_t T, int32_t k, int32_t n_experts,
+                             int32_t expert_begin, int32_t* offsets, int32_t* perm, int32_t* inv,
+                             void* ws, size_t ws_bytes, void* stream) {
+  (void)ws; (void)ws_bytes;
+  if (T < 0 || k < 1 || k > kMaxTopk || n_experts < 1 || n_experts > kMaxExperts) return NVFP4_ERR_SHAPE;
+  if (T * (int64_t)k > kMaxSlots) return NVFP4_ERR_SHAPE;
+  if (!offsets || !perm || !inv || (T > 0 && !topk_ids)) return NVFP4_ERR_NULL;
+  return from_hip(launch_route(topk_ids, T * k, n_experts, expert_begin, 16, offsets, perm, inv, nullptr,
+                               nullptr, static_cast<hipStream_t>(stream)));
+}
+
+size_t nvfp4_moe_workspace_size(int64_t T, int32_t k, int32_t n_experts, int64_t H, int64_t I) {
+  if (T < 0 || k < 1 || n_experts < 1 || H < 1 || I < 1) return 0;
+  return moe_layout(T, k, n_experts, H, I).total;
+}
+
+nvfp4_status nvfp4_moe_grouped(const uint16_t* x, int64_t T, int64_t H, const int32_t* topk_ids,
+                               const float* topk_w, int32_t k, int32_t expert_begin,
+                               const nvfp4_weight_t* gate, const nvfp4_weight_t* up,
+                               const nvfp4_weight_t* down, void* ws, size_t ws_bytes, uint16_t* y,
+                               void* stream) {
+  return moe_impl(x, T, H, topk_ids, topk_w, k, expert_begin, gate, up, down, ws, ws_bytes, y,
+                  static_cast<hipStream_t>(stream), nullptr);
+}
+
+nvfp4_status nvfp4_moe_grouped_timed(const uint16_t* x, int64_t T, int64_t H,
+                                     const int32_t* topk_ids, const float* topk_w, int32_t k,
+                                     int32_t expert_begin, const nvfp4_weight_t* gate,
+                                     const nvfp4_weight_t* up, const nvfp4_weight_t* down,
+                                     void* ws, size_t ws_bytes, uint16_t* y, void* stream,
+                                     void* const* events) {
+  if (!events) return NVFP4_ERR_NULL;
+  return moe_impl(x, T, H, topk_ids, topk_w, k, expert_begin, gate, up, down, ws, ws_bytes, y,
+                  static_cast<hipStream_t>(stream), events);
+}
+
+}  // extern "C"

@@ -1,0 +1,73 @@
+// Device-side helpers shared by the gfx950 kernels of the NVFP4 expert library.
+//
+// Formats (TensorFold issue #308, section "The checkpoint"): e2m1 codes, two
+// per byte with the even element in the low nibble; one e4m3fn scale byte per
+// 16 consecutive inputs; one fp32 scale_2 per tensor.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nvfp4 {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// ---------------------------------------------------------------- conversions
+// e4m3fn byte (in the low 8 bits) -> fp32. gfx950's fp8 convert uses the OCP
+// E4M3 encoding; it is exact for all 254 finite bytes (checked exhaustively on
+// the device against the closed form).
+__device__ __forceinline__ float e4m3_to_f32(uint32_t byte) {
+  return __builtin_amdgcn_cvt_f32_fp8(byte, 0);
+}
+
+// Two e2m1 codes of byte `sel` of `w` -> two fp32 values (low nibble first).
+// The scale operand of the gfx950 scaled convert contributes only its exponent,
+// so 1.0f gives the plain e2m1 values.
+template <int SEL>
+__device__ __forceinline__ f32x2 e2m1x2_to_f32(uint32_t w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, SEL);
+}
+
+// Round two fp32 to bf16 (nearest even) and pack: lo in bits 0..15.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2 v;
+  v[0] = (__bf16)lo;
+  v[1] = (__bf16)hi;
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xFFFF0000u); }
+
+// Eight e2m1 codes (one dword, k..k+7, even k in the low nibble of each byte)
+// times one block scale -> eight bf16 values in k order. Each product is exact
+// in bf16 (<= 6 significant bits, magnitude 2^-10 .. 2688), so the fp32
+// multiply and the bf16 packing introduce no rounding.
+__device__ __forceinline__ bf16x8 dequant8(uint32_t w, float scale) {
+  f32x2 p0 = e2m1x2_to_f32<0>(w);
+  f32x2 p1 = e2m1x2_to_f32<1>(w);
+  f32x2 p2 = e2m1x2_to_f32<2>(w);
+  f32x2 p3 = e2m1x2_to_f32<3>(w);
+  u32x4 r;
+  r[0] = pack_bf16x2(p0[0] * scale, p0[1] * scale);
+  r[1] = pack_bf16x2(p1[0] * scale, p1[1] * scale);
+  r[2] = pack_bf16x2(p2[0] * scale, p2[1] * scale);
+  r[3] = pack_bf16x2(p3[0] * scale, p3[1] * scale);
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+__device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
+
+// ------------------------------------------------------------------- loads
+__device__ __forceinline__ u32x4 ld16(const void* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+__device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+
+}  // namespace nvfp4

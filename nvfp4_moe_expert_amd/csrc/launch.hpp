@@ -1,0 +1,60 @@
+// Internal launcher interface between the C ABI (abi.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nvfp4 {
+
+// Grouped GEMM epilogues.
+enum GemmMode : int {
+  kGateUp = 0,  // MoE: H[p] = bf16(SiLU(s2g*g) * s2u*u), rows gathered through perm
+  kDown = 1,    // MoE: Ypart[perm[p]] = s2d * acc (fp32), scattered to slot order
+  kLinear = 2,  // dense: Y[m] = bf16(s2 * acc)
+  kGated = 3,   // dense: H[m] = bf16(SiLU(s2g*g) * s2u*u)
+};
+
+struct WeightDev {
+  const uint8_t* codes;
+  const uint8_t* scales;
+  const float* scale_2;
+};
+
+struct GemmArgs {
+  const uint16_t* x;       // activation rows (bf16 bits), row stride K
+  const int32_t* perm;     // MoE only: perm order -> slot
+  int32_t topk;            // MoE gate/up: token = slot / topk
+  const int32_t* tiles;    // MoE only: [max_tiles][4] = (expert, row_begin, rows, 0)
+  const int32_t* n_tiles;  // MoE only: device count of valid tiles
+  int64_t M;               // dense only: number of rows
+  WeightDev w0, w1;        // w1 only for the two-weight modes
+  int64_t N, K;            // weight rows / inputs
+  void* out;               // H / Ypart / Y
+};
+
+// Tile-shape variants of the grouped GEMM.
+//   decode : 16-row tiles, activations read straight into MFMA registers;
+//   prefill: 128-row tiles, activations staged through LDS and shared by 4 waves.
+enum GemmVariant : int { kDecode = 0, kPrefill = 1 };
+int variant_tile_rows(GemmVariant v);
+
+hipError_t launch_gemm(GemmMode mode, GemmVariant v, const GemmArgs& a, int64_t grid_tiles,
+                       hipStream_t s);
+
+hipError_t launch_pack(const uint16_t* w, int batch, int64_t n, int64_t k, uint8_t* codes,
+                       uint8_t* scales, float* scale_2, uint32_t* partial, hipStream_t s);
+int pack_nblk(int64_t per_tensor);
+
+hipError_t launch_dequant(const uint8_t* codes, const uint8_t* scales, const float* scale_2,
+                          int groups, int64_t n, int64_t k, uint16_t* unscaled, float* scaled,
+                          hipStream_t s);
+
+// Permutation by expert; also writes the tile list (tile_rows rows per tile) when tiles != null.
+hipError_t launch_route(const int32_t* ids, int64_t S, int E, int expert_begin, int tile_rows,
+                        int32_t* offsets, int32_t* perm, int32_t* inv, int32_t* tiles,
+                        int32_t* n_tiles, hipStream_t s);
+
+hipError_t launch_combine(const int32_t* ids, const float* w, const float* ypart, int64_t T, int k,
+                          int64_t H, int E, int expert_begin, uint16_t* y, hipStream_t s);
+
+}  // namespace nvfp4

@@ -1,0 +1,206 @@
+// Load-time BF16 -> NVFP4 pack, and the dequant debug export.
+//
+// Pack recipe (ModelOpt's, which TensorFold issue #308 applies at load to the
+// MTP layer's BF16 experts, "What the branch does"): per tensor
+//   scale_2 = amax / 2688;  per 16-block: byte = e4m3_rne(block_amax / 6 / scale_2);
+//   s_eff = e4m3(byte) * scale_2;  code = e2m1_rne(w / s_eff), sign of the quotient.
+// Every step is fp32 with correctly rounded division and no contraction (the
+// library is compiled with -ffp-contract=off), so the bytes are reproducible.
+//
+// Two kernels per call: (1) per-tensor partial maxima of |w| (no atomics, so no
+// workspace clearing is needed), (2) the quantization, whose workgroups each
+// finish the max reduction of their tensor from the partials.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace nvfp4 {
+
+constexpr int kPackThreads = 256;
+
+// |bf16| ordered as an unsigned integer: for non-NaN values the magnitude bits
+// (sign cleared) compare exactly like the magnitudes.
+__device__ __forceinline__ uint32_t absmax8(u32x4 v) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint32_t a = v[i] & 0x7FFFu, b = (v[i] >> 16) & 0x7FFFu;
+    m = max(m, max(a, b));
+  }
+  return m;
+}
+
+__global__ __launch_bounds__(kPackThreads) void pack_amax_kernel(const uint16_t* __restrict__ w,
+                                                                 int64_t per_tensor, int nblk,
+                                                                 uint32_t* __restrict__ partial) {
+  const int g = blockIdx.y;
+  const uint16_t* base = w + (int64_t)g * per_tensor;
+  uint32_t m = 0;
+  const int64_t stride = (int64_t)nblk * kPackThreads * 8;
+  for (int64_t i = ((int64_t)blockIdx.x * kPackThreads + threadIdx.x) * 8; i < per_tensor; i += stride)
+    m = max(m, absmax8(ld16(base + i)));
+  // wave reduction then across the 4 waves
+  for (int off = 32; off >= 1; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
+  __shared__ uint32_t red[kPackThreads / 64];
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t r = red[0];
+    for (int i = 1; i < kPackThreads / 64; ++i) r = max(r, red[i]);
+    partial[(int64_t)g * nblk + blockIdx.x] = r;
+  }
+}
+
+// e4m3fn byte of a finite v >= 0, round to nearest even, saturating at 448 (0x7E).
+__device__ __forceinline__ uint32_t e4m3_rne(float v) {
+  if (v >= 448.0f) return 0x7Eu;
+  if (v < 0.015625f) {                       // below 2^-6: subnormal grid of 2^-9
+    float m = __builtin_rintf(v * 512.0f);  // exact scaling, ties to even; 8 -> 0x08 (min normal)
+    return (uint32_t)m;
+  }
+  uint32_t b = __builtin_bit_cast(uint32_t, v);
+  int e = (int)(b >> 23) - 127;              // v = 2^e * 1.f, -6 <= e <= 8
+  uint32_t m3 = (b >> 20) & 7u, rem = b & 0xFFFFFu;
+  if (rem > 0x80000u || (rem == 0x80000u && (m3 & 1u))) ++m3;
+  if (m3 == 8u) { m3 = 0; ++e; }
+  uint32_t code = ((uint32_t)(e + 7) << 3) | m3;
+  return code > 0x7Eu ? 0x7Eu : code;
+}
+
+// e2m1 code of q: nearest even, clamped at 6, sign bit of q. Midpoints
+// 0.25 .. 5.0 are passed when above them, or when on them and the upper code is even.
+__device__ __forceinline__ uint32_t e2m1_rne(float q) {
+  float a = fabsf(q);
+  uint32_t idx = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
+                 (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +
+                 (uint32_t)(a > 5.0f);
+  return idx | ((__builtin_bit_cast(uint32_t, q) >> 31) << 3);
+}
+
+// One thread packs 32 consecutive elements of a row (two 16-blocks).
+__global__ __launch_bounds__(kPackThreads) void pack_quant_kernel(
+    const uint16_t* __restrict__ w, int64_t n, int64_t k, int nblk, const uint32_t* __restrict__ partial,
+    uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, float* __restrict__ scale_2) {
+  const int g = blockIdx.y;
+  __shared__ float s_scale2;
+  if (threadIdx.x < 64) {
+    uint32_t m = 0;
+    for (int i = threadIdx.x; i < nblk; i += 64) m = max(m, partial[(int64_t)g * nblk + i]);
+    for (int off = 32; off >= 1; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
+    if (threadIdx.x == 0) {
+      float amax = __builtin_bit_cast(float, m << 16);
+      float s2 = amax / 2688.0f;
+      s_scale2 = s2;
+      if (blockIdx.x == 0) scale_2[g] = s2;
+    }
+  }
+  __syncthreads();
+  const float s2 = s_scale2;
+  const int64_t units_per_row = k / 32;
+  const int64_t u = (int64_t)blockIdx.x * kPackThreads + threadIdx.x;
+  if (u >= n * units_per_row) return;
+  const int64_t row = u / units_per_row, c32 = u % units_per_row;
+  const uint16_t* src = w + (int64_t)g * n * k + row * k + c32 * 32;
+  u32x4 v[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) v[i] = ld16(src + 8 * i);
+  uint32_t sbytes = 0;
+  u32x4 out = {0, 0, 0, 0};
+#pragma unroll
+  for (int blk = 0; blk < 2; ++blk) {
+    const u32x4 a = v[2 * blk], b = v[2 * blk + 1];
+    uint32_t byte = 0;
+    float s_eff = 0.0f;
+    if (s2 != 0.0f) {
+      float bamax = __builtin_bit_cast(float, max(absmax8(a), absmax8(b)) << 16);
+      float vv = (bamax / 6.0f) / s2;
+      byte = e4m3_rne(vv);
+      s_eff = e4m3_to_f32(byte) * s2;
+    }
+    uint32_t c[16];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      uint32_t wa = (i < 4) ? a[i] : b[i - 4];
+      float lo = bf16_lo(wa), hi = bf16_hi(wa);
+      c[2 * i] = (s_eff != 0.0f) ? e2m1_rne(lo / s_eff) : 0u;
+      c[2 * i + 1] = (s_eff != 0.0f) ? e2m1_rne(hi / s_eff) : 0u;
+    }
+#pragma unroll
+    for (int d = 0; d < 2; ++d) {
+      uint32_t word = 0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) word |= c[8 * d + j] << (4 * j);
+      out[2 * blk + d] = word;
+    }
+    sbytes |= byte << (8 * blk);
+  }
+  st16(codes + (int64_t)g * n * (k / 2) + row * (k / 2) + c32 * 16, out);
+  *reinterpret_cast<uint16_t*>(scales + (int64_t)g * n * (k / 16) + row * (k / 16) + c32 * 2) =
+      (uint16_t)sbytes;
+}
+
+// One thread dequantizes 8 elements (one dword of codes).
+__global__ __launch_bounds__(kPackThreads) void dequant_kernel(
+    const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
+    const float* __restrict__ scale_2, int64_t n, int64_t k, int64_t total8,
+    uint16_t* __restrict__ unscaled, float* __restrict__ scaled) {
+  const int64_t u = (int64_t)blockIdx.x * kPackThreads + threadIdx.x;
+  if (u >= total8) return;
+  const int64_t per_group8 = n * k / 8;
+  const int64_t g = u / per_group8, r = u % per_group8;
+  const int64_t row = r / (k / 8), c8 = r % (k / 8);
+  const uint32_t w = *reinterpret_cast<const uint32_t*>(codes + g * n * (k / 2) + row * (k / 2) + c8 * 4);
+  const float s = e4m3_to_f32(scales[g * n * (k / 16) + row * (k / 16) + c8 / 2]);
+  const bf16x8 d = dequant8(w, s);
+  const int64_t o = g * n * k + row * k + c8 * 8;
+  if (unscaled) st16(unscaled + o, __builtin_bit_cast(u32x4, d));
+  if (scaled) {
+    const float s2 = scale_2[g];
+    const u32x4 dw = __builtin_bit_cast(u32x4, d);
+    f32x4 lo, hi;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      lo[2 * i] = bf16_lo(dw[i]) * s2;
+      lo[2 * i + 1] = bf16_hi(dw[i]) * s2;
+      hi[2 * i] = bf16_lo(dw[i + 2]) * s2;
+      hi[2 * i + 1] = bf16_hi(dw[i + 2]) * s2;
+    }
+    *reinterpret_cast<f32x4*>(scaled + o) = lo;
+    *reinterpret_cast<f32x4*>(scaled + o + 4) = hi;
+  }
+}
+
+// ------------------------------------------------------------------ launchers
+int pack_nblk(int64_t per_tensor) {
+  int64_t per_block = (int64_t)kPackThreads * 8 * 16;   // 16 loads per thread per block
+  int64_t nb = (per_tensor + per_block - 1) / per_block;
+  if (nb < 1) nb = 1;
+  if (nb > 512) nb = 512;
+  return (int)nb;
+}
+
+hipError_t launch_pack(const uint16_t* w, int batch, int64_t n, int64_t k, uint8_t* codes,
+                       uint8_t* scales, float* scale_2, uint32_t* partial, hipStream_t s) {
+  const int64_t per_tensor = n * k;
+  const int nblk = pack_nblk(per_tensor);
+  hipLaunchKernelGGL(pack_amax_kernel, dim3(nblk, batch), dim3(kPackThreads), 0, s, w, per_tensor,
+                     nblk, partial);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t units = n * (k / 32);
+  const int64_t gx = (units + kPackThreads - 1) / kPackThreads;
+  hipLaunchKernelGGL(pack_quant_kernel, dim3((unsigned)gx, batch), dim3(kPackThreads), 0, s, w, n, k,
+                     nblk, partial, codes, scales, scale_2);
+  return hipGetLastError();
+}
+
+hipError_t launch_dequant(const uint8_t* codes, const uint8_t* scales, const float* scale_2,
+                          int groups, int64_t n, int64_t k, uint16_t* unscaled, float* scaled,
+                          hipStream_t s) {
+  const int64_t total8 = (int64_t)groups * n * k / 8;
+  const int64_t gx = (total8 + kPackThreads - 1) / kPackThreads;
+  hipLaunchKernelGGL(dequant_kernel, dim3((unsigned)gx), dim3(kPackThreads), 0, s, codes, scales,
+                     scale_2, n, k, total8, unscaled, scaled);
+  return hipGetLastError();
+}
+
+}  // namespace nvfp4

@@ -1,0 +1,175 @@
+// Token permutation by expert, and the routing-weighted combine.
+//
+// route: one workgroup of 16 waves.
+//   1. histogram of local expert ids, split into P slot ranges (LDS atomics:
+//      counting is order-free);
+//   2. one wavefront turns the per-range counts into exclusive offsets with a
+//      wavefront prefix scan (each lane owns a run of experts, the runs' totals
+//      are scanned across lanes), then into a cursor per (range, expert);
+//      the same wave writes the tile list (expert, first row, rows);
+//   3. each range's wave walks its slots in order, 64 at a time: a slot's
+//      rank among earlier lanes with the same expert plus that expert's cursor
+//      is its position, so the order within an expert is slot order (stable).
+// combine: y[t] = bf16(sum_j w[t,j] * Ypart[t*k+j]) over local slots, j in
+// order - a fixed-order gather instead of a scatter-add, so results are
+// bitwise reproducible (deterministic batch execution, as on the model card
+// "GLM-5.3-Flash-NVFP4-W4A4-Experts", opening section).
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace nvfp4 {
+
+constexpr int kRouteThreads = 1024;
+constexpr int kRouteWaves = kRouteThreads / 64;
+constexpr int kRouteLdsInts = 16384;   // per-(range, expert) counters: 64 KB
+
+__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    int t = __shfl_up(v, off);
+    if (lane >= off) v += t;
+  }
+  return v;
+}
+
+__global__ __launch_bounds__(kRouteThreads) void route_kernel(
+    const int32_t* __restrict__ ids, int S, int E, int eb, int P, int chunk, int tile_rows,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ perm, int32_t* __restrict__ inv,
+    int32_t* __restrict__ tiles, int32_t* __restrict__ n_tiles) {
+  extern __shared__ int32_t cnt[];      // [P][E]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int i = tid; i < P * E; i += kRouteThreads) cnt[i] = 0;
+  __syncthreads();
+  // 1. histogram per slot range
+  for (int s = tid; s < S; s += kRouteThreads) {
+    int e = ids[s] - eb;
+    if (e >= 0 && e < E) atomicAdd(&cnt[(s / chunk) * E + e], 1);
+  }
+  __syncthreads();
+  // 2. wavefront scan (wave 0)
+  if (wave == 0) {
+    const int run = (E + 63) / 64;
+    const int e0 = min(lane * run, E), e1 = min(e0 + run, E);
+    int rows = 0, ntl = 0;
+    for (int e = e0; e < e1; ++e) {
+      int tot = 0;
+      for (int p = 0; p < P; ++p) tot += cnt[p * E + e];
+      rows += tot;
+      ntl += (tot + tile_rows - 1) / tile_rows;
+    }
+    const int rows_incl = wave_incl_scan(rows, lane);
+    const int tl_incl = wave_incl_scan(ntl, lane);
+    int off = rows_incl - rows, toff = tl_incl - ntl;
+    for (int e = e0; e < e1; ++e) {
+      offsets[e] = off;
+      int cur = off;
+      for (int p = 0; p < P; ++p) {   // counts -> cursors, range by range
+        int c = cnt[p * E + e];
+        cnt[p * E + e] = cur;
+        cur += c;
+      }
+      const int tot = cur - off;
+      if (tiles) {
+        for (int r = 0; r < tot; r += tile_rows, ++toff) {
+          tiles[4 * toff + 0] = e;
+          tiles[4 * toff + 1] = off + r;
+          tiles[4 * toff + 2] = min(tile_rows, tot - r);
+          tiles[4 * toff + 3] = 0;
+        }
+      }
+      off = cur;
+    }
+    if (lane == 63) {
+      offsets[E] = rows_incl;
+      if (n_tiles) *n_tiles = tl_incl;
+    }
+  }
+  __syncthreads();
+  // 3. stable scatter, one wave per slot range
+  if (wave < P) {
+    const int s_begin = wave * chunk, s_end = min(S, s_begin + chunk);
+    for (int base = s_begin; base < s_end; base += 64) {
+      const int s = base + lane;
+      int e = -1;
+      if (s < s_end) {
+        e = ids[s] - eb;
+        if (e < 0 || e >= E) e = -1;
+      }
+      int rank = 0, tot = 0;
+      for (int j = 0; j < 64; ++j) {
+        const int ej = __builtin_amdgcn_readlane(e, j);
+        const int same = (ej == e) ? 1 : 0;
+        tot += same;
+        rank += (j < lane) ? same : 0;
+      }
+      if (e >= 0) {
+        const int pos = cnt[wave * E + e] + rank;
+        perm[pos] = s;
+        if (inv) inv[s] = pos;
+      } else if (s < s_end && inv) {
+        inv[s] = -1;
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      if (e >= 0 && rank == tot - 1) cnt[wave * E + e] += tot;
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+    }
+  }
+}
+
+hipError_t launch_route(const int32_t* ids, int64_t S, int E, int eb, int tile_rows, int32_t* offsets,
+                        int32_t* perm, int32_t* inv, int32_t* tiles, int32_t* n_tiles,
+                        hipStream_t s) {
+  int P = kRouteLdsInts / E;
+  if (P > kRouteWaves) P = kRouteWaves;
+  if (P < 1) P = 1;
+  int64_t chunk = (S + P - 1) / P;
+  chunk = ((chunk + 63) / 64) * 64;
+  if (chunk < 64) chunk = 64;
+  const size_t lds = (size_t)P * E * sizeof(int32_t);
+  hipLaunchKernelGGL(route_kernel, dim3(1), dim3(kRouteThreads), lds, s, ids, (int)S, E, eb, P,
+                     (int)chunk, tile_rows, offsets, perm, inv, tiles, n_tiles);
+  return hipGetLastError();
+}
+
+// One thread: 8 consecutive outputs of one token.
+__global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict__ ids,
+                                                      const float* __restrict__ w,
+                                                      const float* __restrict__ ypart, int64_t T, int k,
+                                                      int64_t H, int E, int eb,
+                                                      uint16_t* __restrict__ y) {
+  const int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t per_tok = H / 8;
+  if (u >= T * per_tok) return;
+  const int64_t t = u / per_tok, c8 = u % per_tok;
+  float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (int j = 0; j < k; ++j) {
+    const int64_t slot = t * k + j;
+    const int e = ids[slot] - eb;
+    if (e < 0 || e >= E) continue;
+    const float wt = w[slot];
+    const f32x4* src = reinterpret_cast<const f32x4*>(ypart + slot * H + c8 * 8);
+    const f32x4 a = src[0], b = src[1];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      acc[i] += wt * a[i];
+      acc[4 + i] += wt * b[i];
+    }
+  }
+  u32x4 o;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(acc[2 * i], acc[2 * i + 1]);
+  st16(y + t * H + c8 * 8, o);
+}
+
+hipError_t launch_combine(const int32_t* ids, const float* w, const float* ypart, int64_t T, int k,
+                          int64_t H, int E, int eb, uint16_t* y, hipStream_t s) {
+  const int64_t n = T * (H / 8);
+  const int64_t gx = (n + 255) / 256;
+  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)gx), dim3(256), 0, s, ids, w, ypart, T, k, H, E,
+                     eb, y);
+  return hipGetLastError();
+}
+
+}  // namespace nvfp4

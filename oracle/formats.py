@@ -90,9 +90,9 @@ def e2m1_encode(q) -> np.ndarray:
     and index i+1 is even (mantissa bit 0). |q| >= 6 lands on index 7 (6.0)
     because every midpoint is passed. The sign bit is the sign bit of q."""
     q = np.asarray(q, dtype=np.float32)
-    a = np.abs(q).astype(np.float64)
+    a = np.abs(q)                       # the midpoints are exact in float32
     idx = np.zeros(q.shape, dtype=np.uint8)
-    for i, mid in enumerate(_E2M1_MIDS):
+    for i, mid in enumerate(_E2M1_MIDS.astype(np.float32)):
         up_even = ((i + 1) % 2) == 0
         passed = (a > mid) | ((a == mid) & up_even)
         idx = idx + passed.astype(np.uint8)

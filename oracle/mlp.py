@@ -55,6 +55,14 @@ def linear_gated(x_bits: np.ndarray, w_gate, w_up) -> np.ndarray:
     return silu(linear(x_bits, w_gate)) * linear(x_bits, w_up)
 
 
+def dense_mlp(x_bits: np.ndarray, w_gate, w_up, w_down) -> np.ndarray:
+    """Dense MLP on Fp4Linear: Y = s2d * (SiLU(Y_gate) * Y_up) . Wd^T, all float64
+    (the intermediate is not rounded)."""
+    h = linear_gated(x_bits, w_gate, w_up)
+    wd, s2d = _w64(w_down)
+    return s2d * (h @ wd.T)
+
+
 def route(ids: np.ndarray, n_experts: int, expert_begin: int = 0):
     """Group the T*k slots by expert.
 

@@ -73,12 +73,17 @@ def unpack_codes(codes: np.ndarray) -> np.ndarray:
     return out
 
 
+# Value of every code and every scale byte, from the closed forms (decoded once).
+_E2M1_VALUE = e2m1_decode(np.arange(16))
+_E4M3_VALUE = e4m3_decode(np.arange(256))
+
+
 def dequant_unscaled(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
     """e2m1(code) * e4m3(scale) per element, float64 [..., K]. The product of a
     1-bit-mantissa and a 3-bit-mantissa value has at most 6 significant bits and
     lies in [2^-10, 2688], so it is exact in bf16 and in float32."""
-    vals = e2m1_decode(unpack_codes(codes))
-    sc = np.repeat(e4m3_decode(scales), GROUP, axis=-1)
+    vals = _E2M1_VALUE[unpack_codes(codes)]
+    sc = np.repeat(_E4M3_VALUE[np.asarray(scales, np.uint8)], GROUP, axis=-1)
     return vals * sc
 
 

@@ -1,0 +1,167 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports every
+symbol the header declares, reports its version and status strings, sizes its
+workspaces, and rejects bad arguments before anything is enqueued.
+
+Only argument errors are exercised here: every call below fails validation on
+the host, so no kernel is launched and no device memory is touched (the
+pointers are dummies)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import nvfp4_moe_expert_amd as nv
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "nvfp4.h")
+A = 0x100000          # 16-byte aligned dummy device address
+B = 0x200000
+OK, ENULL, ESHAPE, EALIGN, EWS = 0, 1, 2, 3, 4
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(nvfp4_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_is_built_and_loads():
+    assert os.path.exists(nv.library_path())
+    nv.load_library()
+
+
+def test_every_declared_symbol_is_exported():
+    lib = nv.load_library()
+    syms = declared_symbols()
+    assert len(syms) >= 12
+    for s in syms:
+        assert hasattr(lib, s), f"{s} declared in nvfp4.h but not exported"
+
+
+def test_binding_covers_every_symbol():
+    assert set(declared_symbols()) == set(nv._SIGNATURES)
+
+
+def test_version_and_status_strings():
+    lib = nv.load_library()
+    assert nv.abi_version() == 1
+    for code in range(7):
+        assert lib.nvfp4_status_string(code)
+    assert b"unknown" in lib.nvfp4_status_string(99)
+
+
+def _w(n=64, k=128, groups=1, codes=A, scales=A, s2=A):
+    return nv._Weight(codes, scales, s2, n, k, groups)
+
+
+def P(v):
+    return ctypes.c_void_p(v)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(k=48), ESHAPE), (dict(k=16), ESHAPE), (dict(k=0), ESHAPE), (dict(n=0), ESHAPE),
+    (dict(groups=0), ESHAPE), (dict(codes=0), ENULL), (dict(scales=0), ENULL), (dict(s2=0), ENULL),
+    (dict(codes=A + 4), EALIGN), (dict(scales=A + 8), EALIGN), (dict(groups=2), ESHAPE),
+])
+def test_linear_rejects_bad_weight(kw, status):
+    lib = nv.load_library()
+    w = _w(**kw)
+    assert lib.nvfp4_linear(P(A), 4, ctypes.byref(w), P(B), None) == status
+
+
+def test_linear_rejects_bad_activations():
+    lib = nv.load_library()
+    w = _w()
+    assert lib.nvfp4_linear(P(0), 4, ctypes.byref(w), P(B), None) == ENULL
+    assert lib.nvfp4_linear(P(A), 4, ctypes.byref(w), P(0), None) == ENULL
+    assert lib.nvfp4_linear(P(A + 2), 4, ctypes.byref(w), P(B), None) == EALIGN
+    assert lib.nvfp4_linear(P(A), -1, ctypes.byref(w), P(B), None) == ESHAPE
+    assert lib.nvfp4_linear(P(A), 4, None, P(B), None) == ENULL
+    # m == 0 is a successful no-op (nothing enqueued)
+    assert lib.nvfp4_linear(P(0), 0, ctypes.byref(w), P(0), None) == OK
+
+
+def test_linear_gated_rejects_mismatched_up():
+    lib = nv.load_library()
+    g, u = _w(n=64), _w(n=32)
+    assert lib.nvfp4_linear_gated(P(A), 4, ctypes.byref(g), ctypes.byref(u), P(B), None) == ESHAPE
+    assert lib.nvfp4_linear_gated(P(A), 4, ctypes.byref(g), None, P(B), None) == ENULL
+
+
+def test_pack_validation():
+    lib = nv.load_library()
+    ws = lib.nvfp4_pack_workspace_size(3, 64, 128)
+    assert ws > 0
+    args = lambda **o: [P(o.get("w", A)), o.get("batch", 3), o.get("n", 64), o.get("k", 128), P(o.get("codes", A)),
+                        P(o.get("scales", A)), P(o.get("s2", A)), P(o.get("ws", B)), o.get("wsb", ws), None]
+    assert lib.nvfp4_pack(*args(k=40)) == ESHAPE
+    assert lib.nvfp4_pack(*args(batch=0)) == ESHAPE
+    assert lib.nvfp4_pack(*args(w=0)) == ENULL
+    assert lib.nvfp4_pack(*args(codes=A + 1)) == EALIGN
+    assert lib.nvfp4_pack(*args(wsb=ws - 1)) == EWS
+    assert lib.nvfp4_pack(*args(ws=0)) == EWS
+
+
+def test_dequant_validation():
+    lib = nv.load_library()
+    w = _w()
+    assert lib.nvfp4_dequant(ctypes.byref(w), P(0), P(0), None) == ENULL
+    assert lib.nvfp4_dequant(ctypes.byref(w), P(A + 2), P(0), None) == EALIGN
+    bad = _w(k=40)
+    assert lib.nvfp4_dequant(ctypes.byref(bad), P(A), P(0), None) == ESHAPE
+
+
+def test_route_validation():
+    lib = nv.load_library()
+    assert lib.nvfp4_moe_route(P(A), 4, 0, 16, 0, P(A), P(A), P(A), P(0), 0, None) == ESHAPE
+    assert lib.nvfp4_moe_route(P(A), 4, 65, 16, 0, P(A), P(A), P(A), P(0), 0, None) == ESHAPE
+    assert lib.nvfp4_moe_route(P(A), 4, 8, 0, 0, P(A), P(A), P(A), P(0), 0, None) == ESHAPE
+    assert lib.nvfp4_moe_route(P(A), 4, 8, 4097, 0, P(A), P(A), P(A), P(0), 0, None) == ESHAPE
+    assert lib.nvfp4_moe_route(P(A), 4, 8, 16, 0, P(0), P(A), P(A), P(0), 0, None) == ENULL
+    assert lib.nvfp4_moe_route(P(0), 4, 8, 16, 0, P(A), P(A), P(A), P(0), 0, None) == ENULL
+
+
+def _moe(lib, T=8, H=256, k=4, E=16, I=128, eb=0, x=A, ids=A, tw=A, y=B, ws=B, wsb=None, **wo):
+    g = _w(n=wo.get("gn", I), k=wo.get("gk", H), groups=wo.get("gg", E))
+    u = _w(n=wo.get("un", I), k=wo.get("uk", H), groups=wo.get("ug", E))
+    d = _w(n=wo.get("dn", H), k=wo.get("dk", I), groups=wo.get("dg", E))
+    if wsb is None:
+        wsb = lib.nvfp4_moe_workspace_size(T, k, E, H, I)
+    return lib.nvfp4_moe_grouped(P(x), T, H, P(ids), P(tw), k, eb, ctypes.byref(g), ctypes.byref(u),
+                                 ctypes.byref(d), P(ws), wsb, P(y), None)
+
+
+def test_moe_validation():
+    lib = nv.load_library()
+    assert _moe(lib, gk=128) == ESHAPE            # gate k != H
+    assert _moe(lib, un=64) == ESHAPE             # up n != I
+    assert _moe(lib, dn=128) == ESHAPE            # down n != H
+    assert _moe(lib, dk=64) == ESHAPE             # down k != I
+    assert _moe(lib, ug=8) == ESHAPE              # expert counts differ
+    assert _moe(lib, k=0) == ESHAPE
+    assert _moe(lib, k=65) == ESHAPE
+    assert _moe(lib, T=-1) == ESHAPE
+    assert _moe(lib, H=48, gk=48, uk=48, dn=48) == ESHAPE   # H % 32 != 0
+    assert _moe(lib, x=0) == ENULL
+    assert _moe(lib, ids=0) == ENULL
+    assert _moe(lib, tw=0) == ENULL
+    assert _moe(lib, x=A + 2) == EALIGN
+    assert _moe(lib, ws=0) == EWS
+    assert _moe(lib, wsb=lib.nvfp4_moe_workspace_size(8, 4, 16, 256, 128) - 1) == EWS
+    assert _moe(lib, E=4097) == ESHAPE
+
+
+def test_moe_empty_batch_is_noop():
+    lib = nv.load_library()
+    assert _moe(lib, T=0, x=0, ids=0, tw=0, y=0, ws=0, wsb=0) == OK
+
+
+def test_workspace_sizes_monotone_and_cover_buffers():
+    lib = nv.load_library()
+    a = lib.nvfp4_moe_workspace_size(64, 8, 288, 4096, 1536)
+    b = lib.nvfp4_moe_workspace_size(4096, 8, 288, 4096, 1536)
+    S = 4096 * 8
+    assert b > a > 0
+    assert b >= S * 1536 * 2 + S * 4096 * 4          # H (bf16) and Ypart (fp32)
+    assert lib.nvfp4_moe_workspace_size(0, 8, 288, 4096, 1536) > 0
+    assert lib.nvfp4_moe_workspace_size(4, 0, 288, 4096, 1536) == 0

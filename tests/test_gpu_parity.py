@@ -1,0 +1,307 @@
+"""GPU parity of every entry point against the CPU oracle, at sizes the oracle
+finishes in seconds (several tiles and ragged tails), plus the edge cases.
+
+Bit-exact: dequantized weights, packed codes/scales/scale_2, the permutation,
+and the integer-exact linear. Within max|diff| <= 1e-2*max|ref| and cosine >=
+0.9999: every bf16 output of a contraction."""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import nvfp4_moe_expert_amd as nv
+import synth
+from gpu_util import DEV, assert_close, bf16_dev, bf16_host_bits, bf16_host_f64, note, weight_dev
+from oracle import formats as F
+from oracle import mlp as OM
+from oracle import nvfp4 as ONV
+
+pytestmark = pytest.mark.gpu
+
+
+# ------------------------------------------------------------------ dequant
+def _all_pairs():
+    """Row r uses scale byte r in every block; every block holds the 16 codes in order."""
+    n, k = 256, 64
+    codes4 = np.tile(np.arange(16, dtype=np.uint8), (n, k // 16))
+    codes = (codes4[:, 0::2] | (codes4[:, 1::2] << 4)).astype(np.uint8)
+    scales = np.repeat(np.arange(256, dtype=np.uint8)[:, None], k // 16, axis=1)
+    return codes, scales
+
+
+@pytest.mark.parametrize("s2", [1.0, float(np.float32(1.0) / np.float32(2688.0)), 3.7e-5, 0.0])
+def test_dequant_all_code_scale_pairs_bit_exact(s2):
+    note(f"dequant all pairs s2={s2}")
+    codes, scales = _all_pairs()
+    w = weight_dev((codes[None], scales[None], np.float32(s2)))
+    u, s = nv.dequant(w)
+    torch.cuda.synchronize()
+    ref_u, ref_s = ONV.dequant(codes, scales, np.float32(s2))
+    gu = F.bf16_to_f32(bf16_host_bits(u[0]))
+    gs = s[0].cpu().numpy()
+    finite = np.isfinite(ref_u)
+    assert np.array_equal(np.isnan(gu), ~finite) and np.array_equal(np.isnan(gs), ~np.isfinite(ref_s))
+    assert np.array_equal(gu[finite].view(np.uint32), ref_u[finite].view(np.uint32))
+    fs = np.isfinite(ref_s)
+    assert np.array_equal(gs[fs].view(np.uint32), ref_s[fs].view(np.uint32))
+
+
+def test_dequant_only_one_output():
+    codes, scales = _all_pairs()
+    w = weight_dev((codes[None], scales[None], np.float32(2.0)))
+    u, s = nv.dequant(w, unscaled=True, scaled=False)
+    assert s is None and u is not None
+    u2, s2 = nv.dequant(w, unscaled=False, scaled=True)
+    assert u2 is None
+    ref_u, ref_s = ONV.dequant(codes, scales, np.float32(2.0))
+    f = np.isfinite(ref_s)
+    assert np.array_equal(s2[0].cpu().numpy()[f].view(np.uint32), ref_s[f].view(np.uint32))
+
+
+# ------------------------------------------------------------------ pack
+def _golden():
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "pack_small.json")))
+    w = np.zeros(g["w_bf16"]["shape"], np.uint16)
+    for r, c, h in g["w_bf16"]["nonzero"]:
+        w[r, c] = int(h, 16)
+    return w[None]
+
+
+def _pack_cases():
+    rng = np.random.default_rng(77)
+    cases = {
+        "golden": _golden(),
+        "normal_0.02": np.stack([synth.bf16_normal((64, 256), 0.02, 30, i) for i in range(3)]),
+        "normal_1_ragged_rows": np.stack([synth.bf16_normal((33, 512), 1.0, 31, i) for i in range(2)]),
+        "single_block": synth.bf16_normal((1, 32), 0.5, 32)[None],
+        "mixed_magnitude": synth.f32_to_bf16_bits(
+            (rng.standard_normal((24, 256)) * np.exp2(rng.integers(-20, 6, (24, 1)))).astype(np.float32))[None],
+        "cauchy": synth.f32_to_bf16_bits((rng.standard_cauchy((24, 256)) * 0.01).astype(np.float32))[None],
+        "expert_sized": np.stack([synth.bf16_normal((1536, 4096), 0.02, 33, i) for i in range(2)]),
+    }
+    z = np.zeros((3, 8, 64), np.uint16)
+    z[1] = synth.bf16_normal((8, 64), 0.02, 34)
+    z[1, :, 16:32] = 0
+    z[1, 3, :] = 0x8000
+    z[2] = synth.bf16_normal((8, 64), 0.02, 35)
+    z[2, 0, 1] = 0x8000
+    cases["zeros_and_negzeros"] = z
+    t = np.zeros((2, 2, 32), np.uint16)
+    t[0, 0, 0] = 0x0001
+    t[1, 1, 0] = 0x3F80
+    t[1, 1, 16] = 0x3780
+    cases["subnormal"] = t
+    return cases
+
+
+@pytest.mark.parametrize("name", list(_pack_cases()))
+def test_pack_bit_exact(name):
+    w = _pack_cases()[name]
+    note(f"pack {name} {w.shape}")
+    g = nv.pack(bf16_dev(w))
+    torch.cuda.synchronize()
+    c, s, s2 = ONV.pack_batch(w)
+    assert np.array_equal(g.codes.cpu().numpy(), c)
+    assert np.array_equal(g.scales.cpu().numpy(), s)
+    assert np.array_equal(g.scale_2.cpu().numpy().view(np.uint32), s2.view(np.uint32))
+
+
+def test_pack_2d_input_and_repeat_determinism():
+    w = synth.bf16_normal((48, 128), 0.02, 36)
+    a = nv.pack(bf16_dev(w))
+    b = nv.pack(bf16_dev(w))
+    assert torch.equal(a.codes, b.codes) and torch.equal(a.scales, b.scales)
+    assert a.codes.shape == (1, 48, 64)
+
+
+# ------------------------------------------------------------------ route
+def _route_cases():
+    r = np.random.default_rng(5)
+    cases = []
+    ids, _ = synth.topk_softmax_routing(8, 16, 4, 2, synth.S_ROUTE)
+    cases.append(("cfg2", ids, 16, 0))
+    for T in (1, 16, 64):
+        ids, _ = synth.topk_softmax_routing(T, 288, 8, 3, synth.S_ROUTE, T)
+        cases.append((f"decode_T{T}", ids, 288, 0))
+    ids, _ = synth.zipf_routing(4096, 288, 8, 1.1, 4, synth.S_ROUTE)
+    cases.append(("prefill_zipf", ids, 288, 0))
+    cases.append(("skipped_ep", r.integers(0, 30, (37, 3)).astype(np.int32), 5, 10))
+    cases.append(("one_expert", np.zeros((100, 2), np.int32), 1, 0))
+    cases.append(("many_experts", r.integers(0, 4096, (50, 8)).astype(np.int32), 4096, 0))
+    dup = r.integers(0, 6, (70, 4)).astype(np.int32)
+    dup[:, 1] = dup[:, 0]
+    cases.append(("duplicates", dup, 6, 0))
+    cases.append(("all_skipped", r.integers(0, 16, (9, 4)).astype(np.int32), 16, 1000))
+    cases.append(("ragged_S", r.integers(0, 3, (67, 1)).astype(np.int32), 3, 0))
+    cases.append(("negative_ids", r.integers(-5, 5, (20, 2)).astype(np.int32), 5, 0))
+    return cases
+
+
+@pytest.mark.parametrize("ci", range(len(_route_cases())))
+def test_route_bit_exact(ci):
+    name, ids, E, eb = _route_cases()[ci]
+    note(f"route {name} ids{ids.shape} E={E} eb={eb}")
+    off, perm, inv = nv.moe_route(torch.from_numpy(ids).to(DEV), E, eb)
+    torch.cuda.synchronize()
+    counts, roff, rperm, rinv = OM.route(ids, E, eb)
+    assert np.array_equal(off.cpu().numpy(), roff)
+    V = int(roff[-1])
+    assert np.array_equal(perm.cpu().numpy()[:V], rperm)
+    assert np.array_equal(inv.cpu().numpy(), rinv)
+
+
+def test_route_empty_batch():
+    ids = torch.zeros((0, 8), dtype=torch.int32, device=DEV)
+    off, perm, inv = nv.moe_route(ids, 16, 0)
+    torch.cuda.synchronize()
+    assert np.all(off.cpu().numpy() == 0)
+
+
+# ------------------------------------------------------------------ linear
+@pytest.mark.parametrize("M,N,K,seed", [
+    (4, 256, 512, 1),        # single NVFP4 linear workload: X[4,512], W[256,512]
+    (1, 64, 32, 40), (16, 128, 256, 41), (17, 100, 96, 42), (130, 48, 160, 43),
+    (300, 256, 1024, 44), (129, 200, 544, 45),
+])
+def test_linear_vs_oracle(M, N, K, seed):
+    note(f"linear M={M} N={N} K={K}")
+    x = synth.bf16_normal((M, K), 1.0, seed, synth.S_X)
+    wp = ONV.pack(synth.bf16_normal((N, K), 0.02, seed, synth.S_W))
+    y = nv.linear(bf16_dev(x), weight_dev(wp))
+    torch.cuda.synchronize()
+    assert_close(bf16_host_f64(y), OM.linear(x, wp), f"linear {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("M", [4, 40])
+def test_linear_integer_exact(M):
+    # scale bytes 1.0, scale_2 1.0, integer activations: every partial sum is exact in
+    # fp32, so the bf16 output must be the nearest-even rounding of the exact result
+    N, K = 64, 512
+    g = np.random.default_rng(M)
+    x = synth.bf16_integers((M, K), -8, 8, 46, M)
+    codes4 = g.integers(0, 16, (N, K)).astype(np.uint8)
+    codes = (codes4[:, 0::2] | (codes4[:, 1::2] << 4)).astype(np.uint8)
+    scales = np.full((N, K // 16), 0x38, np.uint8)
+    wp = (codes, scales, np.float32(1.0))
+    y = nv.linear(bf16_dev(x), weight_dev(wp))
+    exact = OM.linear(x, wp)
+    assert np.array_equal(bf16_host_bits(y), F.f32_to_bf16(exact.astype(np.float32)))
+
+
+def test_linear_empty_rows():
+    x = torch.zeros((0, 64), dtype=torch.bfloat16, device=DEV)
+    wp = ONV.pack(synth.bf16_normal((32, 64), 0.02, 47))
+    y = nv.linear(x, weight_dev(wp))
+    assert y.shape == (0, 32)
+
+
+@pytest.mark.parametrize("M,N,K", [(4, 128, 512), (33, 96, 256), (200, 64, 128)])
+def test_linear_gated_vs_oracle(M, N, K):
+    note(f"linear_gated M={M} N={N} K={K}")
+    x = synth.bf16_normal((M, K), 1.0, 48, M)
+    wg = ONV.pack(synth.bf16_normal((N, K), 0.05, 48, synth.S_GATE, M))
+    wu = ONV.pack(synth.bf16_normal((N, K), 0.05, 48, synth.S_UP, M))
+    h = nv.linear_gated(bf16_dev(x), weight_dev(wg), weight_dev(wu))
+    torch.cuda.synchronize()
+    assert_close(bf16_host_f64(h), OM.linear_gated(x, wg, wu), "linear_gated")
+
+
+# ------------------------------------------------------------------ moe
+def _moe_problem(T, k, E, H, I, seed, sigma=0.02, ids=None, weights=None):
+    x = synth.bf16_normal((T, H), 1.0, seed, synth.S_X)
+    if ids is None:
+        ids, weights = synth.topk_softmax_routing(T, E, k, seed, synth.S_ROUTE)
+    gate = ONV.pack_batch(synth.expert_weights(E, I, H, sigma, seed, synth.S_GATE))
+    up = ONV.pack_batch(synth.expert_weights(E, I, H, sigma, seed, synth.S_UP))
+    down = ONV.pack_batch(synth.expert_weights(E, H, I, sigma, seed, synth.S_DOWN))
+    return x, ids.astype(np.int32), weights.astype(np.float32), gate, up, down
+
+
+def _run_moe(x, ids, w, gate, up, down, eb=0):
+    return nv.moe_grouped(bf16_dev(x), torch.from_numpy(ids).to(DEV), torch.from_numpy(w).to(DEV),
+                          weight_dev(gate), weight_dev(up), weight_dev(down), expert_begin=eb)
+
+
+@pytest.mark.parametrize("T,k,E,H,I,seed", [
+    (8, 4, 16, 2048, 512, 2),      # grouped decode MoE workload: 16 experts, top-4, 8 tokens
+    (5, 2, 3, 64, 32, 60),
+    (1, 8, 12, 256, 96, 61),
+    (200, 2, 4, 128, 64, 62),      # 100 rows per expert: prefill tiles
+    (64, 8, 20, 256, 160, 63),
+])
+def test_moe_vs_oracle(T, k, E, H, I, seed):
+    note(f"moe T={T} k={k} E={E} H={H} I={I}")
+    x, ids, w, gate, up, down = _moe_problem(T, k, E, H, I, seed, sigma=0.05)
+    y = _run_moe(x, ids, w, gate, up, down)
+    torch.cuda.synchronize()
+    assert_close(bf16_host_f64(y), OM.moe(x, ids, w, gate, up, down), "moe")
+
+
+def test_moe_expert_parallel_slice_and_duplicates():
+    T, k, E, H, I = 30, 4, 4, 128, 64
+    g = np.random.default_rng(3)
+    ids = g.integers(0, 12, (T, k)).astype(np.int32)
+    ids[:, 1] = ids[:, 0]                          # duplicate ids count twice
+    w = g.uniform(0.1, 1.0, (T, k)).astype(np.float32)
+    x, _, _, gate, up, down = _moe_problem(T, k, E, H, I, 64, sigma=0.05, ids=ids, weights=w)
+    y = _run_moe(x, ids, w, gate, up, down, eb=4)
+    torch.cuda.synchronize()
+    ref = OM.moe(x, ids, w, gate, up, down, expert_begin=4)
+    assert_close(bf16_host_f64(y), ref, "moe ep slice")
+    none_local = ~np.any((ids >= 4) & (ids < 8), axis=1)
+    assert np.all(bf16_host_f64(y)[none_local] == 0)
+
+
+def test_moe_all_slots_skipped_gives_zero():
+    x, ids, w, gate, up, down = _moe_problem(9, 4, 4, 64, 32, 65)
+    y = _run_moe(x, ids, w, gate, up, down, eb=100)
+    torch.cuda.synchronize()
+    assert np.all(bf16_host_bits(y) == 0)
+
+
+def test_moe_empty_batch():
+    _, _, _, gate, up, down = _moe_problem(1, 2, 3, 64, 32, 66)
+    y = nv.moe_grouped(torch.zeros((0, 64), dtype=torch.bfloat16, device=DEV),
+                       torch.zeros((0, 2), dtype=torch.int32, device=DEV),
+                       torch.zeros((0, 2), dtype=torch.float32, device=DEV),
+                       weight_dev(gate), weight_dev(up), weight_dev(down))
+    assert y.shape == (0, 64)
+
+
+@pytest.mark.parametrize("T,k,E,H,I", [(8, 4, 16, 2048, 512), (200, 2, 4, 128, 64)])
+def test_moe_token_permutation_and_repeat_bitwise(T, k, E, H, I):
+    x, ids, w, gate, up, down = _moe_problem(T, k, E, H, I, 67, sigma=0.05)
+    y1 = bf16_host_bits(_run_moe(x, ids, w, gate, up, down))
+    y2 = bf16_host_bits(_run_moe(x, ids, w, gate, up, down))
+    assert np.array_equal(y1, y2)
+    p = np.random.default_rng(1).permutation(T)
+    yp = bf16_host_bits(_run_moe(x[p], ids[p], w[p], gate, up, down))
+    assert np.array_equal(yp, y1[p])
+
+
+def test_moe_k1_matches_dense_mlp_path():
+    # one expert per token with weight 1: the grouped path equals linear_gated then linear
+    T, E, H, I = 24, 3, 256, 128
+    ids = np.full((T, 1), 1, np.int32)
+    w = np.ones((T, 1), np.float32)
+    x, _, _, gate, up, down = _moe_problem(T, 1, E, H, I, 68, sigma=0.05, ids=ids, weights=w)
+    y = _run_moe(x, ids, w, gate, up, down)
+    gd, ud, dd = weight_dev(gate).expert(1), weight_dev(up).expert(1), weight_dev(down).expert(1)
+    h = nv.linear_gated(bf16_dev(x), gd, ud)
+    y2 = nv.linear(h, dd)
+    torch.cuda.synchronize()
+    assert np.array_equal(bf16_host_bits(y), bf16_host_bits(y2))
+
+
+def test_moe_timed_events_same_result():
+    x, ids, w, gate, up, down = _moe_problem(8, 4, 16, 256, 128, 69, sigma=0.05)
+    y1 = bf16_host_bits(_run_moe(x, ids, w, gate, up, down))
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+    y2 = nv.moe_grouped(bf16_dev(x), torch.from_numpy(ids).to(DEV), torch.from_numpy(w).to(DEV),
+                        weight_dev(gate), weight_dev(up), weight_dev(down), events=ev)
+    torch.cuda.synchronize()
+    assert np.array_equal(bf16_host_bits(y2), y1)
+    times = [ev[i].elapsed_time(ev[i + 1]) for i in range(4)]
+    assert all(t >= 0 for t in times)

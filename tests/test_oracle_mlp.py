@@ -154,3 +154,17 @@ def test_moe_token_permutation_equivariant():
     y = mlp.moe(x, ids, w, gate, up, down)
     yp = mlp.moe(x[p], ids[p], w[p], gate, up, down)
     assert np.allclose(yp, y[p], rtol=1e-12, atol=1e-14)
+
+
+def test_dense_mlp_vs_brute():
+    M, H = 2, 32
+    x = synth.bf16_normal((M, H), 1.0, 926)
+    wd = _packed(H, 32, 0.5, 929)
+    wg, wu = _packed(32, H, 0.5, 927), _packed(32, H, 0.5, 928)
+    y = mlp.dense_mlp(x, wg, wu, wd)
+    g = brute.linear(x.tolist(), wg[0].tolist(), wg[1].tolist(), wg[2], M, 32, H)
+    u = brute.linear(x.tolist(), wu[0].tolist(), wu[1].tolist(), wu[2], M, 32, H)
+    h = [[brute.silu(g[m][i]) * u[m][i] for i in range(32)] for m in range(M)]
+    yb = [[sum(h[m][i] * brute.weight(wd[0], wd[1], wd[2], n, i) for i in range(32)) for n in range(H)]
+          for m in range(M)]
+    assert np.allclose(y, np.array(yb), rtol=1e-12, atol=1e-14)

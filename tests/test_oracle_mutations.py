@@ -53,8 +53,8 @@ MUTANTS = [
      [TF.test_e2m1_encode_vs_nearest_search, TP.test_pack_negative_zero_inside_nonzero_block]),
     (oracle.formats, "minifloat_decode", "frac * 2.0 ** (1 - bias)", "frac * 2.0 ** (-bias)",
      [TF.test_generic_minifloat_matches_torch_e4m3fn_all_bytes, TF.test_e2m1_value_table]),
-    (oracle.nvfp4, "dequant_unscaled", "np.repeat(e4m3_decode(scales), GROUP, axis=-1)",
-     "np.tile(e4m3_decode(scales), GROUP)",
+    (oracle.nvfp4, "dequant_unscaled", "np.repeat(_E4M3_VALUE[np.asarray(scales, np.uint8)], GROUP, axis=-1)",
+     "np.tile(_E4M3_VALUE[np.asarray(scales, np.uint8)], GROUP)",
      [TP.test_nibble_order_against_brute_weight]),
     (oracle.mlp, "linear", "s2 * (x @ wu.T)", "s2 * (x @ wu[::-1].T)",
      [lambda: TM.test_linear_vs_brute(2, 3, 32), TM.test_linear_integer_exact]),
