@@ -1,0 +1,319 @@
+#!/usr/bin/env python3
+"""Benchmark of the W4A16 NVFP4 routed-expert MLP on one MI355X.
+
+One step = one routed-expert MLP of the decode-shaped MoE layer (288 experts,
+top-8, hidden 4096, intermediate 1536, 64 tokens): route, grouped gate/up with
+SiLU(gate)*up, grouped down, routing-weighted combine, through the C ABI.
+Consecutive steps cycle through 32 independently seeded routings and inputs,
+so the 256 MB Infinity Cache cannot keep serving the same experts.
+
+value = algorithmic bytes / time, where algorithmic bytes per call = touched
+experts x 10,616,832 B (gate, up, down: 0.5625 B per weight, codes plus e4m3
+scales) + their scale_2 + x + y + ids + routing weights. Inputs are resident in
+HBM before the timed region starts.
+
+Also reported in the same line: the T = 1 and 16 decode batches, the
+prefill-shaped layer (4096 tokens, Zipf(1.1) routing) in TFLOP/s, the dense
+Fp4Linear MLP (2048 x 4096 -> 12288 -> 4096) in TFLOP/s, and the load-time
+pack of the 288 experts x 3 projections in GB/s; the roofline of the dominant
+kernel (from HIP events recorded between the library's stages on the stream
+it runs on); and the CPU oracle timed on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "NVFP4 W4A16 grouped-expert GB/s (decode) & TFLOP/s (prefill), % roofline"
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
+E, K_TOP, H, I = 288, 8, 4096, 1536
+W_BYTES = 9 / 16                 # bytes per weight: 4-bit code + one e4m3 byte per 16
+EXPERT_BYTES = int(3 * I * H * W_BYTES)          # 10,616,832
+GATEUP_BYTES = int(2 * I * H * W_BYTES)          # 7,077,888
+DOWN_BYTES = int(I * H * W_BYTES)                # 3,538,944
+ROTATE = 32
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--tokens", type=int, default=64, help="decode batch of the headline step")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-extras", action="store_true", help="only the headline decode step")
+    p.add_argument("--calibrate-copy-mib", type=int, default=256,
+                   help="size of the plain device copy run once (counter calibration)")
+    return p.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on one GPU; multi-GPU sharding is not part of "
+                                   "this build (see DESIGN.md for how the path would shard)",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+    import torch
+
+    import nvfp4_moe_expert_amd as nv
+    import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    nv.load_library()
+
+    # ---------------------------------------------------------------- weights
+    log("drawing the 288-expert layer (bf16 ~ N(0, 0.02)) and packing it on the device")
+    raw = {
+        "gate": synth.torch_bf16_normal((E, I, H), 0.02, 51, dev),
+        "up": synth.torch_bf16_normal((E, I, H), 0.02, 52, dev),
+        "down": synth.torch_bf16_normal((E, H, I), 0.02, 53, dev),
+    }
+    layer = {k: nv.pack(v) for k, v in raw.items()}
+    torch.cuda.synchronize()
+
+    def decode_inputs(T, seed):
+        xs, ids, ws = [], [], []
+        for r in range(ROTATE):
+            xs.append(synth.bf16_normal((T, H), 1.0, seed, synth.S_X, T, r))
+            i_, w_ = synth.topk_softmax_routing(T, E, K_TOP, seed, synth.S_ROUTE, T, r)
+            ids.append(i_)
+            ws.append(w_)
+        x = torch.from_numpy(np.stack(xs).view(np.int16)).view(torch.bfloat16).to(dev)
+        idt = torch.from_numpy(np.stack(ids)).to(dev)
+        wt = torch.from_numpy(np.stack(ws)).to(dev)
+        touched = [len(np.unique(i_)) for i_ in ids]
+        return x, idt, wt, touched
+
+    def alg_bytes(T, U):
+        return U * (EXPERT_BYTES + 3 * 4) + 2 * T * H * 2 + 2 * T * K_TOP * 4
+
+    def run_decode(T, steps, warmup, seed=3):
+        x, ids, w, touched = decode_inputs(T, seed)
+        ws = torch.empty((nv.moe_workspace_size(T, K_TOP, E, H, I),), dtype=torch.uint8, device=dev)
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+        nev = 5
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(steps)]
+        for i in range(warmup):
+            r = i % ROTATE
+            nv.moe_grouped(x[r], ids[r], w[r], layer["gate"], layer["up"], layer["down"], workspace=ws, out=out)
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for i in range(steps):
+            r = (warmup + i) % ROTATE
+            nv.moe_grouped(x[r], ids[r], w[r], layer["gate"], layer["up"], layer["down"], workspace=ws, out=out,
+                           events=evs[i])
+        t1.record()
+        torch.cuda.synchronize()
+        ms = t0.elapsed_time(t1)
+        us = [touched[(warmup + i) % ROTATE] for i in range(steps)]
+        stage = np.array([[evs[i][j].elapsed_time(evs[i][j + 1]) for j in range(nev - 1)] for i in range(steps)])
+        total_bytes = sum(alg_bytes(T, u) for u in us)
+        gateup_bytes = sum(u * (GATEUP_BYTES + 2 * 4) + T * H * 2 for u in us)
+        down_bytes = sum(u * (DOWN_BYTES + 4) for u in us)
+        return {
+            "T": T, "ms_total": ms, "ms_per_step": ms / steps, "gbs": total_bytes / (ms * 1e-3) / 1e9,
+            "experts_touched_mean": float(np.mean(us)),
+            "stage_ms_mean": {n: float(stage[:, j].mean()) for j, n in enumerate(["route", "gate_up", "down", "combine"])},
+            "gateup_gbs": gateup_bytes / (stage[:, 1].sum() * 1e-3) / 1e9,
+            "down_gbs": down_bytes / (stage[:, 2].sum() * 1e-3) / 1e9,
+            "gateup_bytes_per_launch": gateup_bytes / steps,
+        }
+
+    # ------------------------------------------------------- headline: decode
+    log(f"decode T={args.tokens}: warmup {args.warmup}, timed {args.steps}")
+    head = run_decode(args.tokens, args.steps, args.warmup)
+    result = {
+        "metric": METRIC,
+        "value": round(head["gbs"], 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(head["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"decode-shaped MoE layer, {args.tokens} tokens", "experts": E, "top_k": K_TOP,
+                   "hidden": H, "intermediate": I, "tokens": args.tokens, "weights": "NVFP4 (e2m1, e4m3/16, fp32 scale_2)",
+                   "activations": "bf16", "routing": "top-8 softmax over N(0,1) logits, 32 rotating draws"},
+        "roofline": {"bound": "hbm", "kernel": "gemm_kernel<gate_up, decode tile>",
+                     "achieved": round(head["gateup_gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(head["gateup_gbs"] / HBM_PEAK_GBS, 4), "traffic": None,
+                     "algorithmic_bytes_per_launch": round(head["gateup_bytes_per_launch"]),
+                     "avg_launch_ms": round(head["stage_ms_mean"]["gate_up"], 5)},
+        "stages_ms": {k: round(v, 5) for k, v in head["stage_ms_mean"].items()},
+        "experts_touched_mean": head["experts_touched_mean"],
+        "down_kernel_gbs": round(head["down_gbs"], 1),
+    }
+
+    if not args.no_extras:
+        sweep = {}
+        for T in (1, 16, 64):
+            if T == args.tokens:
+                continue
+            log(f"decode T={T}")
+            r = run_decode(T, args.steps, args.warmup)
+            sweep[str(T)] = {"GB/s": round(r["gbs"], 1), "ms_per_step": round(r["ms_per_step"], 5),
+                             "frac_hbm": round(r["gbs"] / HBM_PEAK_GBS, 4),
+                             "experts_touched_mean": r["experts_touched_mean"],
+                             "stages_ms": {k: round(v, 5) for k, v in r["stage_ms_mean"].items()}}
+        result["decode_sweep"] = sweep
+
+        # ------------------------------------------------------- prefill layer
+        log("prefill T=4096 Zipf(1.1)")
+        Tp = 4096
+        ids_np, w_np = synth.zipf_routing(Tp, E, K_TOP, 1.1, 4, synth.S_ROUTE)
+        xp = torch.from_numpy(synth.bf16_normal((Tp, H), 1.0, 4, synth.S_X).view(np.int16)).view(torch.bfloat16).to(dev)
+        idp, wp = torch.from_numpy(ids_np).to(dev), torch.from_numpy(w_np).to(dev)
+        wsp = torch.empty((nv.moe_workspace_size(Tp, K_TOP, E, H, I),), dtype=torch.uint8, device=dev)
+        outp = torch.empty((Tp, H), dtype=torch.bfloat16, device=dev)
+        psteps = max(3, min(args.steps, 20))
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(psteps)]
+        for _ in range(3):
+            nv.moe_grouped(xp, idp, wp, layer["gate"], layer["up"], layer["down"], workspace=wsp, out=outp)
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for i in range(psteps):
+            nv.moe_grouped(xp, idp, wp, layer["gate"], layer["up"], layer["down"], workspace=wsp, out=outp,
+                           events=evs[i])
+        t1.record()
+        torch.cuda.synchronize()
+        ms = t0.elapsed_time(t1) / psteps
+        flops = 6.0 * Tp * K_TOP * H * I
+        st = np.array([[evs[i][j].elapsed_time(evs[i][j + 1]) for j in range(4)] for i in range(psteps)]).mean(0)
+        result["prefill"] = {
+            "workload": "prefill-shaped MoE layer, 4096 tokens, Zipf(1.1) routing", "TFLOP/s": round(flops / ms / 1e9, 2),
+            "ms_per_call": round(ms, 4), "frac_mfma_bf16": round(flops / ms / 1e9 / MFMA_BF16_PEAK_TFLOPS, 4),
+            "stages_ms": dict(zip(["route", "gate_up", "down", "combine"], [round(v, 4) for v in st])),
+            "rows_max_expert": int(np.bincount(ids_np.ravel(), minlength=E).max())}
+        del wsp, outp
+
+        # --------------------------------------------------------- dense MLP
+        log("dense MLP 2048 x 4096 -> 12288 -> 4096")
+        M, F = 2048, 12288
+        dg = nv.pack(synth.torch_bf16_normal((F, H), 0.02, 61, dev))
+        du = nv.pack(synth.torch_bf16_normal((F, H), 0.025, 62, dev))
+        dd = nv.pack(synth.torch_bf16_normal((H, F), 0.02, 63, dev))
+        xm = torch.from_numpy(synth.bf16_normal((M, H), 1.0, 5, synth.S_X).view(np.int16)).view(torch.bfloat16).to(dev)
+        hm = torch.empty((M, F), dtype=torch.bfloat16, device=dev)
+        ym = torch.empty((M, H), dtype=torch.bfloat16, device=dev)
+        for _ in range(2):
+            nv.linear_gated(xm, dg, du, out=hm)
+            nv.linear(hm, dd, out=ym)
+        torch.cuda.synchronize()
+        dsteps = max(3, min(args.steps, 10))
+        e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+        tg = td = 0.0
+        for _ in range(dsteps):
+            e0.record()
+            nv.linear_gated(xm, dg, du, out=hm)
+            e1.record()
+            nv.linear(hm, dd, out=ym)
+            e2.record()
+            torch.cuda.synchronize()
+            tg += e0.elapsed_time(e1)
+            td += e1.elapsed_time(e2)
+        tg, td = tg / dsteps, td / dsteps
+        fg, fd = 2.0 * M * H * F * 2, 2.0 * M * F * H
+        result["dense_mlp"] = {
+            "workload": "dense Fp4Linear MLP 2048 x 4096 -> 12288 -> 4096", "TFLOP/s": round((fg + fd) / (tg + td) / 1e9, 2),
+            "ms_per_call": round(tg + td, 4), "frac_mfma_bf16": round((fg + fd) / (tg + td) / 1e9 / MFMA_BF16_PEAK_TFLOPS, 4),
+            "gated_ms": round(tg, 4), "down_ms": round(td, 4)}
+        del dg, du, dd, xm, hm, ym
+
+        # ---------------------------------------------------------------- pack
+        log("pack of 288 experts x 3 projections")
+        pk_steps = 3
+        for k_ in raw:
+            nv.pack(raw[k_])
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(pk_steps):
+            for k_ in raw:
+                nv.pack(raw[k_])
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / pk_steps
+        nw = 3 * E * I * H
+        pbytes = nw * 2 + nw * W_BYTES + 3 * E * 4
+        result["pack"] = {"workload": "pack of 288 experts x 3 projections (4096 x 1536 each)",
+                          "GB/s": round(pbytes / (ms * 1e-3) / 1e9, 1), "ms_per_call": round(ms, 3),
+                          "frac_hbm": round(pbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+
+    # --------------------------------------------- counter calibration copy
+    if args.calibrate_copy_mib > 0:
+        n = args.calibrate_copy_mib * (1 << 20) // 4
+        a = torch.ones(n, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        result["calibration_copy_bytes"] = {"read": n * 4, "write": n * 4}
+        del a, b
+
+    # ------------------------------------------------------------ CPU oracle
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(raw, torch, synth)
+
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(raw, torch, synth):
+    """The CPU oracle (float64 numpy) on a bounded sample of the same workload: one
+    decode token, its 8 experts. The oracle packs those experts first (not timed),
+    then its routed MLP is timed; GB/s uses the same algorithmic bytes."""
+    from oracle import mlp as OM
+    from oracle import nvfp4 as ONV
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        blas_threads = 1
+    T = 1
+    x = synth.bf16_normal((T, H), 1.0, 3, synth.S_X, T, 0)
+    ids, w = synth.topk_softmax_routing(T, E, K_TOP, 3, synth.S_ROUTE, T, 0)
+    experts = sorted(set(ids.ravel().tolist()))
+    host = lambda t: t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    packs = {p: [ONV.pack(host(raw[p][e])) for e in experts] for p in raw}
+    stack = lambda p: (np.stack([c for c, _, _ in packs[p]]), np.stack([s for _, s, _ in packs[p]]),
+                       np.array([s2 for _, _, s2 in packs[p]], np.float32))
+    loc = {e: i for i, e in enumerate(experts)}
+    lids = np.vectorize(lambda v: loc[int(v)])(ids).astype(np.int32)
+    g, u, d = stack("gate"), stack("up"), stack("down")
+    t0 = time.perf_counter()
+    reps = 0
+    while True:
+        OM.moe(x, lids, w, g, u, d)
+        reps += 1
+        if time.perf_counter() - t0 > 10.0:
+            break
+    sec = (time.perf_counter() - t0) / reps
+    nbytes = len(experts) * (EXPERT_BYTES + 12) + 2 * T * H * 2 + 2 * T * K_TOP * 4
+    return {"value": round(nbytes / sec / 1e9, 4), "unit": "GB/s", "cores": int(blas_threads), "kind": "oracle",
+            "sample": f"1 token of the decode-shaped layer ({len(experts)} experts x 3 projections), "
+                      f"float64 numpy routed MLP, {reps} repetitions, {sec:.2f} s each",
+            "host_cpus": len(os.sched_getaffinity(0))}
+
+
+if __name__ == "__main__":
+    main()
