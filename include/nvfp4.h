@@ -36,10 +36,13 @@
  *           enqueued; on error nothing is written. A failed launch returns
  *           NVFP4_ERR_HIP. No C++ exception crosses this interface.
  * Numerics. Products use bf16 matrix cores with fp32 accumulation over exactly
- *           dequantized weights; scale_2 multiplies the fp32 accumulator. For a
- *           given output element the summation order is fixed and does not
- *           depend on the batch, the tile it lands in, or the other rows, so
- *           results are bitwise reproducible.
+ *           dequantized weights; scale_2 multiplies the fp32 accumulator. The
+ *           summation order of an output element is fixed by the shapes and by
+ *           the call's class (decode-shaped: at most 16 rows per local expert on
+ *           average, or at most 16 rows for the dense entry points; otherwise
+ *           prefill-shaped). It never depends on the values, on the other rows or
+ *           on the tile a row lands in, so results are bitwise reproducible and
+ *           permuting the tokens permutes the outputs bit for bit.
  */
 #ifndef NVFP4_MOE_EXPERT_AMD_NVFP4_H
 #define NVFP4_MOE_EXPERT_AMD_NVFP4_H

@@ -34,9 +34,10 @@ nvfp4_status check_weight(const nvfp4_weight_t* w) {
 nvfp4_status from_hip(hipError_t e) { return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP; }
 
 // Workspace of nvfp4_moe_grouped, in order: offsets[E+1], perm[S], tiles[max_tiles][4],
-// n_tiles, H[S][I] bf16, Ypart[S][H] fp32. Each region starts on a 256-byte boundary.
+// n_tiles, H[S][I] bf16, Ypart[S][H] fp32, x16[T][H] fp16, xexp[T], hmax[S].
+// Each region starts on a 256-byte boundary.
 struct MoeLayout {
-  size_t offsets, perm, tiles, n_tiles, h, ypart, total;
+  size_t offsets, perm, tiles, n_tiles, h, ypart, x16, xexp, hmax, total;
   int64_t max_tiles;
 };
 
@@ -59,6 +60,9 @@ MoeLayout moe_layout(int64_t T, int k, int64_t E, int64_t H, int64_t I) {
   L.n_tiles = off; off += 256;
   L.h = off;       off += round_up(sizeof(uint16_t) * (size_t)S * (size_t)I);
   L.ypart = off;   off += round_up(sizeof(float) * (size_t)S * (size_t)H);
+  L.x16 = off;     off += round_up(sizeof(uint16_t) * (size_t)T * (size_t)H);
+  L.xexp = off;    off += round_up(sizeof(int32_t) * (size_t)(T > 0 ? T : 1));
+  L.hmax = off;    off += round_up(sizeof(uint32_t) * (size_t)(S > 0 ? S : 1));
   L.total = off;
   return L;
 }
@@ -110,9 +114,14 @@ nvfp4_status moe_impl(const uint16_t* x, int64_t T, int64_t H, const int32_t* id
   int32_t* n_tiles = at<int32_t>(ws, L.n_tiles);
   uint16_t* hbuf = at<uint16_t>(ws, L.h);
   float* ypart = at<float>(ws, L.ypart);
+  // decode tiles on shapes the weight-stream kernel covers: fp16 form, with prep
+  const bool dec = v == kDecode && decode_supported(kGateUp, H, I) && decode_supported(kDown, I, H);
+  DecodeExtra dx{at<uint16_t>(ws, L.x16), at<int32_t>(ws, L.xexp), at<uint32_t>(ws, L.hmax)};
+  RoutePrep prep{};
+  if (dec) prep = RoutePrep{x, T, H, k, at<uint16_t>(ws, L.x16), at<int32_t>(ws, L.xexp), at<uint32_t>(ws, L.hmax)};
 
   if (e == hipSuccess)
-    e = launch_route(ids, S, (int)E, eb, variant_tile_rows(v), offsets, perm, nullptr, tiles, n_tiles, s);
+    e = launch_route(ids, S, (int)E, eb, variant_tile_rows(v), offsets, perm, nullptr, tiles, n_tiles, prep, s);
   if (e == hipSuccess) e = mark(1);
 
   GemmArgs g{};
@@ -127,7 +136,7 @@ nvfp4_status moe_impl(const uint16_t* x, int64_t T, int64_t H, const int32_t* id
     g.N = I;
     g.K = H;
     g.out = hbuf;
-    e = launch_gemm(kGateUp, v, g, L.max_tiles, s);
+    e = dec ? launch_decode(kGateUp, true, g, dx, L.max_tiles, s) : launch_gemm(kGateUp, v, g, L.max_tiles, s);
   }
   if (e == hipSuccess) e = mark(2);
   if (e == hipSuccess) {
@@ -137,7 +146,7 @@ nvfp4_status moe_impl(const uint16_t* x, int64_t T, int64_t H, const int32_t* id
     g.N = H;
     g.K = I;
     g.out = ypart;
-    e = launch_gemm(kDown, v, g, L.max_tiles, s);
+    e = dec ? launch_decode(kDown, true, g, dx, L.max_tiles, s) : launch_gemm(kDown, v, g, L.max_tiles, s);
   }
   if (e == hipSuccess) e = mark(3);
   if (e == hipSuccess) e = launch_combine(ids, tw, ypart, T, k, H, (int)E, eb, y, s);
@@ -167,7 +176,10 @@ nvfp4_status linear_impl(const uint16_t* x, int64_t m, const nvfp4_weight_t* w0,
   g.N = w0->n;
   g.K = w0->k;
   g.out = out;
-  return from_hip(launch_gemm(w1 ? kGated : kLinear, v, g, (m + tr - 1) / tr, s));
+  const GemmMode mode = w1 ? kGated : kLinear;
+  if (v == kDecode && decode_supported(mode, g.K, g.N))
+    return from_hip(launch_decode(mode, false, g, DecodeExtra{}, 1, s));
+  return from_hip(launch_gemm(mode, v, g, (m + tr - 1) / tr, s));
 }
 
 }  // namespace
@@ -241,7 +253,7 @@ nvfp4_status nvfp4_moe_route(const int32_t* topk_ids, int64_t T, int32_t k, int3
   if (T * (int64_t)k > kMaxSlots) return NVFP4_ERR_SHAPE;
   if (!offsets || !perm || !inv || (T > 0 && !topk_ids)) return NVFP4_ERR_NULL;
   return from_hip(launch_route(topk_ids, T * k, n_experts, expert_begin, 16, offsets, perm, inv, nullptr,
-                               nullptr, static_cast<hipStream_t>(stream)));
+                               nullptr, RoutePrep{}, static_cast<hipStream_t>(stream)));
 }
 
 size_t nvfp4_moe_workspace_size(int64_t T, int32_t k, int32_t n_experts, int64_t H, int64_t I) {

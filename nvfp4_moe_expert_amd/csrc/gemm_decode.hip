@@ -1,0 +1,296 @@
+// Decode-shaped grouped NVFP4 GEMM (tiles of at most 16 rows): a weight stream.
+//
+// Passage: TensorFold issue #308, "What the branch does" - routed experts in a
+// grouped NVFP4 kernel, bf16 rows only, weight_scale_2 as the per-expert
+// multiplier. In decode an expert sees one or two rows, so every weight byte is
+// used for one 16x16 MFMA tile and the kernel is bound by HBM bandwidth.
+//
+// Layout of the work (measured on MI355X):
+// * A workgroup = 4 waves = 64 output columns of one tile (for gate/up, the same
+//   16 columns of both weights per wave). Lane (r, q) of a wave owns weight row
+//   n0 + r and, in every 128*U-k stage, the contiguous k range
+//   [kb + 32Uq, kb + 32Uq + 32U): U 128-bit code loads of its own row and ONE
+//   2U-byte load of its block scales. (Loading the scales two bytes at a time
+//   makes half the memory instructions carry 1/64 of the bytes and caps the
+//   stream near 4.8 TB/s; with wide loads it reaches ~5.6 TB/s.)
+// * Stage i+1's weights load into registers while stage i is multiplied; the
+//   register sets ping-pong (the stage loop is unrolled by two).
+// * Codes are dequantized in registers. In the fp16 form one packed convert
+//   turns two e2m1 codes into fp16 and one packed multiply applies the e4m3
+//   scale: 1 VALU op per weight, exact (code*scale has <= 6 significant bits and
+//   lies in [2^-10, 2688]). The activations are then fp16 too, pre-scaled per
+//   row by a power of two 2^p so the row maximum sits in [2^14, 2^15): every
+//   bf16 value down to 2^-28 of its row maximum is exact in fp16, every product
+//   is exact in the fp32 accumulator, and 2^-p is applied in the epilogue. The
+//   bf16 form (2 VALU ops per weight) is used where no pre-scaled rows exist.
+// * Activations are staged through LDS (double-buffered, one barrier per stage).
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace nvfp4 {
+
+namespace decode_detail {
+
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kThreads = 256;
+constexpr int kBlockN = 64;
+
+template <int SEL>
+__device__ __forceinline__ f16x2 e2m1x2_f16(uint32_t w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, SEL);
+}
+
+// 8 codes (one dword) times a block scale held in both halves of s -> 8 fp16 (exact).
+__device__ __forceinline__ f16x8 dequant8_f16(uint32_t w, f16x2 s) {
+  const f16x2 p0 = e2m1x2_f16<0>(w) * s, p1 = e2m1x2_f16<1>(w) * s;
+  const f16x2 p2 = e2m1x2_f16<2>(w) * s, p3 = e2m1x2_f16<3>(w) * s;
+  return __builtin_shufflevector(__builtin_shufflevector(p0, p1, 0, 1, 2, 3),
+                                 __builtin_shufflevector(p2, p3, 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+template <int SEL>
+__device__ __forceinline__ float scale_f32(uint32_t w) {
+  return __builtin_amdgcn_cvt_f32_fp8(w, SEL);
+}
+
+// weight registers of one stage for one weight: U code chunks, 2U scale bytes
+template <int U>
+struct Stage {
+  u32x4 c[U];
+  uint32_t s[(U + 1) / 2];
+};
+
+template <int U>
+__device__ __forceinline__ void load_stage(Stage<U>& st, const uint8_t* codes, const uint8_t* scales, int64_t kb) {
+#pragma unroll
+  for (int i = 0; i < U; ++i) st.c[i] = ld16(codes + kb / 2 + 16 * i);
+  if constexpr (U == 4) {
+    const u32x2 v = *reinterpret_cast<const u32x2*>(scales + kb / 16);
+    st.s[0] = v[0];
+    st.s[1] = v[1];
+  } else if constexpr (U == 2) {
+    st.s[0] = *reinterpret_cast<const uint32_t*>(scales + kb / 16);
+  } else {
+    st.s[0] = *reinterpret_cast<const uint16_t*>(scales + kb / 16);
+  }
+}
+
+// power-of-two exponent p that puts a row maximum m (> 0) in [2^14, 2^15)
+__device__ __forceinline__ int row_exponent(uint32_t max_bits) {
+  if (max_bits == 0) return 0;
+  int e = (int)((max_bits >> 23) & 0xFF) - 127;
+  int p = 14 - e;
+  return p > 126 ? 126 : (p < -126 ? -126 : p);
+}
+
+}  // namespace decode_detail
+
+using namespace decode_detail;
+
+template <int MODE, int U, bool F16>
+__global__ __launch_bounds__(kThreads) void gemm_decode_kernel(GemmArgs a, DecodeExtra d) {
+  constexpr bool kTwo = (MODE == kGateUp || MODE == kGated);
+  constexpr bool kMoe = (MODE == kGateUp || MODE == kDown);
+  constexpr int KC = 128 * U;          // k per stage
+  constexpr int LW = KC + 8;           // LDS row pitch (16-byte pad)
+  __shared__ __attribute__((aligned(16))) uint16_t xs[2][16][LW];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lr = lane & 15, q = lane >> 4;
+  const int64_t N = a.N, K = a.K;
+
+  int e = 0, rb, rows;
+  if (kMoe) {
+    if ((int)blockIdx.x >= *a.n_tiles) return;
+    const int32_t* t = a.tiles + 4 * (int64_t)blockIdx.x;
+    e = t[0];
+    rb = t[1];
+    rows = t[2];
+  } else {
+    rb = (int)blockIdx.x * 16;
+    rows = (int)min((int64_t)16, a.M - rb);
+  }
+
+  const int64_t nrow = (int64_t)blockIdx.y * kBlockN + wave * 16 + lr;   // N % 64 == 0
+  const int64_t wrow = (int64_t)e * N + nrow;
+  const uint8_t* c0 = a.w0.codes + wrow * (K / 2) + 16 * U * q;
+  const uint8_t* s0 = a.w0.scales + wrow * (K / 16) + 2 * U * q;
+  const uint8_t* c1 = kTwo ? a.w1.codes + wrow * (K / 2) + 16 * U * q : nullptr;
+  const uint8_t* s1 = kTwo ? a.w1.scales + wrow * (K / 16) + 2 * U * q : nullptr;
+
+  // activation chunks of this thread: U per stage, chunk i = row xr[i], 8 k at 8*xc[i]
+  const uint16_t* xsrc[U];
+  int xr[U], xc[U];
+  float xscale[U];                   // down, fp16 form: 2^p of the H row
+#pragma unroll
+  for (int i = 0; i < U; ++i) {
+    const int idx = i * kThreads + tid;
+    xr[i] = idx / (16 * U);
+    xc[i] = idx % (16 * U);
+    xsrc[i] = nullptr;
+    xscale[i] = 1.0f;
+    if (xr[i] < rows) {
+      const int p = rb + xr[i];
+      int64_t src;
+      if (MODE == kGateUp) src = a.perm[p] / a.topk;
+      else src = p;
+      const uint16_t* base = (MODE == kGateUp && F16) ? d.x16 : a.x;
+      xsrc[i] = base + src * K + 8 * xc[i];
+      if (MODE == kDown && F16) xscale[i] = ldexpf(1.0f, row_exponent(d.hmax[p]));
+    }
+  }
+  for (int i = tid; i < 2 * 16 * (LW / 8); i += kThreads) {
+    const int b = i / (16 * (LW / 8)), rem = i % (16 * (LW / 8));
+    const int r = rem / (LW / 8), c = rem % (LW / 8);
+    if (r >= rows) st16(&xs[b][r][c * 8], u32x4{0, 0, 0, 0});
+  }
+  auto ldx = [&](u32x4 (&v)[U], int64_t kb) {
+#pragma unroll
+    for (int i = 0; i < U; ++i) v[i] = xsrc[i] ? ld16(xsrc[i] + kb) : u32x4{0, 0, 0, 0};
+  };
+  auto stx = [&](u32x4 (&v)[U], int b) {
+#pragma unroll
+    for (int i = 0; i < U; ++i) {
+      if (xr[i] >= rows) continue;
+      u32x4 o = v[i];
+      if constexpr (MODE == kDown && F16) {
+        // bf16 H row -> fp16 scaled by 2^p (exact for every value >= 2^-28 of the row max)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const f16x2 h2 = {(_Float16)(bf16_lo(v[i][j]) * xscale[i]), (_Float16)(bf16_hi(v[i][j]) * xscale[i])};
+          o[j] = __builtin_bit_cast(uint32_t, h2);
+        }
+      }
+      st16(&xs[b][xr[i]][8 * xc[i]], o);
+    }
+  };
+
+  f32x4 acc0 = {0, 0, 0, 0}, acc1 = {0, 0, 0, 0};
+  auto compute = [&](const Stage<U>& g, const Stage<U>& u, int b) {
+#pragma unroll
+    for (int i = 0; i < U; ++i) {
+      const uint32_t gw = g.s[i / 2] >> (16 * (i & 1));
+      const uint32_t uw = kTwo ? (u.s[i / 2] >> (16 * (i & 1))) : 0u;
+      if constexpr (F16) {
+        const f16x2 sg = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(gw, 1.0f, false);
+        f16x2 su = {};
+        if constexpr (kTwo) su = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(uw, 1.0f, false);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const f16x8 B = *reinterpret_cast<const f16x8*>(&xs[b][lr][32 * U * q + 32 * i + 8 * s]);
+          const f16x2 gs = (s < 2) ? f16x2{sg[0], sg[0]} : f16x2{sg[1], sg[1]};
+          acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(dequant8_f16(g.c[i][s], gs), B, acc0, 0, 0, 0);
+          if constexpr (kTwo) {
+            const f16x2 us = (s < 2) ? f16x2{su[0], su[0]} : f16x2{su[1], su[1]};
+            acc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(dequant8_f16(u.c[i][s], us), B, acc1, 0, 0, 0);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const bf16x8 B = *reinterpret_cast<const bf16x8*>(&xs[b][lr][32 * U * q + 32 * i + 8 * s]);
+          const float gs = (s < 2) ? scale_f32<0>(gw) : scale_f32<1>(gw);
+          acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dequant8(g.c[i][s], gs), B, acc0, 0, 0, 0);
+          if constexpr (kTwo) {
+            const float us = (s < 2) ? scale_f32<0>(uw) : scale_f32<1>(uw);
+            acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dequant8(u.c[i][s], us), B, acc1, 0, 0, 0);
+          }
+        }
+      }
+    }
+  };
+
+  const int nst = (int)(K / KC);
+  Stage<U> Ag, Au, Bg, Bu;
+  u32x4 xv[U];
+  load_stage<U>(Ag, c0, s0, 0);
+  if constexpr (kTwo) load_stage<U>(Au, c1, s1, 0);
+  ldx(xv, 0);
+  stx(xv, 0);
+  __syncthreads();
+  int st = 0;
+  for (; st + 2 <= nst; st += 2) {
+    const int64_t k1 = (int64_t)(st + 1) * KC, k2 = (int64_t)(st + 2) * KC;
+    load_stage<U>(Bg, c0, s0, k1);
+    if constexpr (kTwo) load_stage<U>(Bu, c1, s1, k1);
+    ldx(xv, k1);
+    compute(Ag, Au, 0);
+    stx(xv, 1);
+    __syncthreads();
+    const bool more = st + 2 < nst;
+    if (more) {
+      load_stage<U>(Ag, c0, s0, k2);
+      if constexpr (kTwo) load_stage<U>(Au, c1, s1, k2);
+      ldx(xv, k2);
+    }
+    compute(Bg, Bu, 1);
+    if (more) stx(xv, 0);
+    __syncthreads();
+  }
+  if (st < nst) compute(Ag, Au, 0);
+
+  // ---- epilogue: lane holds D[n = nbase + 4q + r][token lr], r = 0..3
+  if (lr >= rows) return;
+  const int64_t p = rb + lr;
+  const int64_t n0 = (int64_t)blockIdx.y * kBlockN + wave * 16 + 4 * q;
+  float unscale = 1.0f;
+  if constexpr (F16 && MODE == kGateUp) unscale = ldexpf(1.0f, -d.xexp[a.perm[p] / a.topk]);
+  if constexpr (F16 && MODE == kDown) unscale = ldexpf(1.0f, -row_exponent(d.hmax[p]));
+  const float s2a = a.w0.scale_2[e] * unscale;
+  const float s2b = kTwo ? a.w1.scale_2[e] * unscale : 0.0f;
+  float v[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    if constexpr (kTwo) v[r] = silu(s2a * acc0[r]) * (s2b * acc1[r]);
+    else v[r] = s2a * acc0[r];
+  }
+  if constexpr (MODE == kDown) {
+    *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.out) + (int64_t)a.perm[p] * N + n0) =
+        f32x4{v[0], v[1], v[2], v[3]};
+  } else {
+    u32x2 o;
+    o[0] = pack_bf16x2(v[0], v[1]);
+    o[1] = pack_bf16x2(v[2], v[3]);
+    *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(a.out) + p * N + n0) = o;
+    if constexpr (MODE == kGateUp && F16) {
+      // row maximum of |H| as stored (bf16) for the down projection's scaling;
+      // max is order-independent, so the atomics keep the result deterministic
+      float m = 0.0f;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) m = fmaxf(m, fabsf((float)(__bf16)v[r]));
+      m = fmaxf(m, __shfl_xor(m, 16));
+      m = fmaxf(m, __shfl_xor(m, 32));
+      if (q == 0) atomicMax(reinterpret_cast<unsigned int*>(d.hmax + p), __builtin_bit_cast(unsigned int, m));
+    }
+  }
+}
+
+bool decode_supported(GemmMode mode, int64_t K, int64_t N) {
+  (void)mode;
+  return N % kBlockN == 0 && K % 256 == 0 && K >= 256;
+}
+
+template <int MODE, bool F16>
+static hipError_t launch_dec(const GemmArgs& a, const DecodeExtra& d, int64_t grid_tiles, hipStream_t s) {
+  const dim3 grid((unsigned)grid_tiles, (unsigned)(a.N / kBlockN));
+  if (a.K % 512 == 0)
+    hipLaunchKernelGGL((gemm_decode_kernel<MODE, 4, F16>), grid, dim3(kThreads), 0, s, a, d);
+  else
+    hipLaunchKernelGGL((gemm_decode_kernel<MODE, 2, F16>), grid, dim3(kThreads), 0, s, a, d);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode(GemmMode mode, bool f16, const GemmArgs& a, const DecodeExtra& d, int64_t grid_tiles,
+                         hipStream_t s) {
+  if (grid_tiles <= 0) return hipSuccess;
+  switch (mode) {
+    case kGateUp: return f16 ? launch_dec<kGateUp, true>(a, d, grid_tiles, s) : launch_dec<kGateUp, false>(a, d, grid_tiles, s);
+    case kDown: return f16 ? launch_dec<kDown, true>(a, d, grid_tiles, s) : launch_dec<kDown, false>(a, d, grid_tiles, s);
+    case kLinear: return launch_dec<kLinear, false>(a, d, grid_tiles, s);
+    case kGated: return launch_dec<kGated, false>(a, d, grid_tiles, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace nvfp4

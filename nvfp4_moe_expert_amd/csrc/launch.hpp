@@ -41,6 +41,17 @@ int variant_tile_rows(GemmVariant v);
 hipError_t launch_gemm(GemmMode mode, GemmVariant v, const GemmArgs& a, int64_t grid_tiles,
                        hipStream_t s);
 
+// Decode-tile (<= 16 rows) weight-streaming GEMM. The fp16 form (routed gate/up and
+// down only) reads activations pre-scaled by the route/prep kernel.
+struct DecodeExtra {
+  const uint16_t* x16;   // [T][H] fp16: x * 2^xexp[t]
+  const int32_t* xexp;   // [T]
+  uint32_t* hmax;        // [S] bits of max |H| per permuted row (zeroed by the prep)
+};
+bool decode_supported(GemmMode mode, int64_t K, int64_t N);
+hipError_t launch_decode(GemmMode mode, bool f16, const GemmArgs& a, const DecodeExtra& d, int64_t grid_tiles,
+                         hipStream_t s);
+
 hipError_t launch_pack(const uint16_t* w, int batch, int64_t n, int64_t k, uint8_t* codes,
                        uint8_t* scales, float* scale_2, uint32_t* partial, hipStream_t s);
 int pack_nblk(int64_t per_tensor);
@@ -50,9 +61,19 @@ hipError_t launch_dequant(const uint8_t* codes, const uint8_t* scales, const flo
                           hipStream_t s);
 
 // Permutation by expert; also writes the tile list (tile_rows rows per tile) when tiles != null.
+// With prep.x16 != null, extra workgroups also write the pre-scaled fp16 activations
+// (x16, xexp) and zero hmax[S].
+struct RoutePrep {
+  const uint16_t* x;     // [T][H] bf16
+  int64_t T, H;
+  int k;
+  uint16_t* x16;
+  int32_t* xexp;
+  uint32_t* hmax;
+};
 hipError_t launch_route(const int32_t* ids, int64_t S, int E, int expert_begin, int tile_rows,
                         int32_t* offsets, int32_t* perm, int32_t* inv, int32_t* tiles,
-                        int32_t* n_tiles, hipStream_t s);
+                        int32_t* n_tiles, const RoutePrep& prep, hipStream_t s);
 
 hipError_t launch_combine(const int32_t* ids, const float* w, const float* ypart, int64_t T, int k,
                           int64_t H, int E, int expert_begin, uint16_t* y, hipStream_t s);

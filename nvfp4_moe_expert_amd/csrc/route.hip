@@ -32,10 +32,58 @@ __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
   return v;
 }
 
+// Workgroup 1 + t (t < T) of the route kernel: activation row t -> fp16 scaled by 2^p,
+// p putting the row's max |x| in [2^14, 2^15) (bf16 values then convert exactly);
+// also clears the row maxima of the token's k H rows.
+__device__ void prep_row(const RoutePrep& pr, int64_t t) {
+  __shared__ uint32_t red[kRouteThreads / 64];
+  __shared__ int pexp;
+  const int tid = threadIdx.x;
+  const uint16_t* xr = pr.x + t * pr.H;
+  uint32_t m = 0;
+  for (int64_t i = (int64_t)tid * 8; i < pr.H; i += kRouteThreads * 8) {
+    const u32x4 v = ld16(xr + i);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) m = max(m, max(v[j] & 0x7FFFu, (v[j] >> 16) & 0x7FFFu));
+  }
+  for (int off = 32; off >= 1; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
+  if ((tid & 63) == 0) red[tid >> 6] = m;
+  __syncthreads();
+  if (tid == 0) {
+    uint32_t r = 0;
+    for (int i = 0; i < kRouteThreads / 64; ++i) r = max(r, red[i]);
+    int p = 0;
+    if (r != 0) {
+      const int e = (int)((r >> 7) & 0xFF) - 127;   // bf16 exponent of the row max
+      p = 14 - e;
+      p = p > 126 ? 126 : (p < -126 ? -126 : p);
+    }
+    pexp = p;
+    pr.xexp[t] = p;
+  }
+  __syncthreads();
+  const float sc = ldexpf(1.0f, pexp);
+  for (int64_t i = (int64_t)tid * 8; i < pr.H; i += kRouteThreads * 8) {
+    const u32x4 v = ld16(xr + i);
+    u32x4 o;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const _Float16 lo = (_Float16)(bf16_lo(v[j]) * sc), hi = (_Float16)(bf16_hi(v[j]) * sc);
+      o[j] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+    }
+    st16(pr.x16 + t * pr.H + i, o);
+  }
+  for (int j = tid; j < pr.k; j += kRouteThreads) pr.hmax[t * pr.k + j] = 0u;
+}
+
 __global__ __launch_bounds__(kRouteThreads) void route_kernel(
     const int32_t* __restrict__ ids, int S, int E, int eb, int P, int chunk, int tile_rows,
     int32_t* __restrict__ offsets, int32_t* __restrict__ perm, int32_t* __restrict__ inv,
-    int32_t* __restrict__ tiles, int32_t* __restrict__ n_tiles) {
+    int32_t* __restrict__ tiles, int32_t* __restrict__ n_tiles, RoutePrep prep) {
+  if (blockIdx.x > 0) {
+    prep_row(prep, (int64_t)blockIdx.x - 1);
+    return;
+  }
   extern __shared__ int32_t cnt[];      // [P][E]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   for (int i = tid; i < P * E; i += kRouteThreads) cnt[i] = 0;
@@ -120,7 +168,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
 
 hipError_t launch_route(const int32_t* ids, int64_t S, int E, int eb, int tile_rows, int32_t* offsets,
                         int32_t* perm, int32_t* inv, int32_t* tiles, int32_t* n_tiles,
-                        hipStream_t s) {
+                        const RoutePrep& prep, hipStream_t s) {
   int P = kRouteLdsInts / E;
   if (P > kRouteWaves) P = kRouteWaves;
   if (P < 1) P = 1;
@@ -128,8 +176,9 @@ hipError_t launch_route(const int32_t* ids, int64_t S, int E, int eb, int tile_r
   chunk = ((chunk + 63) / 64) * 64;
   if (chunk < 64) chunk = 64;
   const size_t lds = (size_t)P * E * sizeof(int32_t);
-  hipLaunchKernelGGL(route_kernel, dim3(1), dim3(kRouteThreads), lds, s, ids, (int)S, E, eb, P,
-                     (int)chunk, tile_rows, offsets, perm, inv, tiles, n_tiles);
+  const unsigned grid = 1 + (prep.x16 ? (unsigned)prep.T : 0u);
+  hipLaunchKernelGGL(route_kernel, dim3(grid), dim3(kRouteThreads), lds, s, ids, (int)S, E, eb, P,
+                     (int)chunk, tile_rows, offsets, perm, inv, tiles, n_tiles, prep);
   return hipGetLastError();
 }
 

@@ -162,6 +162,7 @@ def test_route_empty_batch():
 # ------------------------------------------------------------------ linear
 @pytest.mark.parametrize("M,N,K,seed", [
     (4, 256, 512, 1),        # single NVFP4 linear workload: X[4,512], W[256,512]
+    (16, 80, 4096, 49), (7, 64, 2048, 50), (3, 48, 1536, 51),   # streaming kernel, N % 64 != 0
     (1, 64, 32, 40), (16, 128, 256, 41), (17, 100, 96, 42), (130, 48, 160, 43),
     (300, 256, 1024, 44), (129, 200, 544, 45),
 ])
@@ -197,7 +198,7 @@ def test_linear_empty_rows():
     assert y.shape == (0, 32)
 
 
-@pytest.mark.parametrize("M,N,K", [(4, 128, 512), (33, 96, 256), (200, 64, 128)])
+@pytest.mark.parametrize("M,N,K", [(4, 128, 512), (33, 96, 256), (200, 64, 128), (5, 48, 2048), (16, 32, 4096)])
 def test_linear_gated_vs_oracle(M, N, K):
     note(f"linear_gated M={M} N={N} K={K}")
     x = synth.bf16_normal((M, K), 1.0, 48, M)
@@ -226,6 +227,10 @@ def _run_moe(x, ids, w, gate, up, down, eb=0):
 
 @pytest.mark.parametrize("T,k,E,H,I,seed", [
     (8, 4, 16, 2048, 512, 2),      # grouped decode MoE workload: 16 experts, top-4, 8 tokens
+    (6, 2, 4, 2048, 1536, 70),     # streaming kernel: gate/up K=2048, down K=1536
+    (3, 2, 2, 4096, 512, 71),      # streaming kernel: gate/up K=4096, down K=512
+    (32, 1, 2, 2048, 512, 72),     # full 16-row decode tiles
+    (40, 2, 3, 512, 2048, 73),     # gate/up K=512 (tiled), down K=2048 with 4 row blocks
     (5, 2, 3, 64, 32, 60),
     (1, 8, 12, 256, 96, 61),
     (200, 2, 4, 128, 64, 62),      # 100 rows per expert: prefill tiles
