@@ -136,7 +136,9 @@ nvfp4_status moe_impl(const uint16_t* x, int64_t T, int64_t H, const int32_t* id
     g.N = I;
     g.K = H;
     g.out = hbuf;
-    e = dec ? launch_decode(kGateUp, true, g, dx, L.max_tiles, s) : launch_gemm(kGateUp, v, g, L.max_tiles, s);
+    e = dec ? launch_decode(kGateUp, true, g, dx, L.max_tiles, s)
+        : (v == kPrefill && prefill_supported(kGateUp, H, I)) ? launch_prefill(kGateUp, g, L.max_tiles, s)
+                                                              : launch_gemm(kGateUp, v, g, L.max_tiles, s);
   }
   if (e == hipSuccess) e = mark(2);
   if (e == hipSuccess) {
@@ -146,7 +148,9 @@ nvfp4_status moe_impl(const uint16_t* x, int64_t T, int64_t H, const int32_t* id
     g.N = H;
     g.K = I;
     g.out = ypart;
-    e = dec ? launch_decode(kDown, true, g, dx, L.max_tiles, s) : launch_gemm(kDown, v, g, L.max_tiles, s);
+    e = dec ? launch_decode(kDown, true, g, dx, L.max_tiles, s)
+        : (v == kPrefill && prefill_supported(kDown, I, H)) ? launch_prefill(kDown, g, L.max_tiles, s)
+                                                            : launch_gemm(kDown, v, g, L.max_tiles, s);
   }
   if (e == hipSuccess) e = mark(3);
   if (e == hipSuccess) e = launch_combine(ids, tw, ypart, T, k, H, (int)E, eb, y, s);
@@ -179,6 +183,7 @@ nvfp4_status linear_impl(const uint16_t* x, int64_t m, const nvfp4_weight_t* w0,
   const GemmMode mode = w1 ? kGated : kLinear;
   if (v == kDecode && decode_supported(mode, g.K, g.N))
     return from_hip(launch_decode(mode, false, g, DecodeExtra{}, 1, s));
+  if (v == kPrefill && prefill_supported(mode, g.K, g.N)) return from_hip(launch_prefill(mode, g, (m + tr - 1) / tr, s));
   return from_hip(launch_gemm(mode, v, g, (m + tr - 1) / tr, s));
 }
 

@@ -49,6 +49,10 @@ struct DecodeExtra {
   uint32_t* hmax;        // [S] bits of max |H| per permuted row (zeroed by the prep)
 };
 bool decode_supported(GemmMode mode, int64_t K, int64_t N);
+
+// Prefill-tile (<= 128 rows) matrix-core GEMM; the tiled kernel covers other shapes.
+bool prefill_supported(GemmMode mode, int64_t K, int64_t N);
+hipError_t launch_prefill(GemmMode mode, const GemmArgs& a, int64_t grid_tiles, hipStream_t s);
 hipError_t launch_decode(GemmMode mode, bool f16, const GemmArgs& a, const DecodeExtra& d, int64_t grid_tiles,
                          hipStream_t s);
 
