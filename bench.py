@@ -55,6 +55,8 @@ def parse():
     p.add_argument("--tokens", type=int, default=64, help="decode batch of the headline step")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-extras", action="store_true", help="only the headline decode step")
+    p.add_argument("--only", choices=["decode", "prefill", "dense", "pack"], default=None,
+                   help="run one workload only (profiling runs); prints its figures")
     p.add_argument("--calibrate-copy-mib", type=int, default=256,
                    help="size of the plain device copy run once (counter calibration)")
     return p.parse_args()
@@ -77,14 +79,16 @@ def main():
     nv.load_library()
 
     # ---------------------------------------------------------------- weights
-    log("drawing the 288-expert layer (bf16 ~ N(0, 0.02)) and packing it on the device")
-    raw = {
-        "gate": synth.torch_bf16_normal((E, I, H), 0.02, 51, dev),
-        "up": synth.torch_bf16_normal((E, I, H), 0.02, 52, dev),
-        "down": synth.torch_bf16_normal((E, H, I), 0.02, 53, dev),
-    }
-    layer = {k: nv.pack(v) for k, v in raw.items()}
-    torch.cuda.synchronize()
+    raw, layer = {}, {}
+    if args.only != "dense":
+        log("drawing the 288-expert layer (bf16 ~ N(0, 0.02)) and packing it on the device")
+        raw.update({
+            "gate": synth.torch_bf16_normal((E, I, H), 0.02, 51, dev),
+            "up": synth.torch_bf16_normal((E, I, H), 0.02, 52, dev),
+            "down": synth.torch_bf16_normal((E, H, I), 0.02, 53, dev),
+        })
+        layer.update({k: nv.pack(v) for k, v in raw.items()})
+        torch.cuda.synchronize()
 
     def decode_inputs(T, seed):
         xs, ids, ws = [], [], []
@@ -143,6 +147,95 @@ def main():
             "gateup_bytes_per_launch": gateup_bytes / steps,
         }
 
+    def run_prefill():
+        log("prefill T=4096 Zipf(1.1)")
+        Tp = 4096
+        ids_np, w_np = synth.zipf_routing(Tp, E, K_TOP, 1.1, 4, synth.S_ROUTE)
+        xp = torch.from_numpy(synth.bf16_normal((Tp, H), 1.0, 4, synth.S_X).view(np.int16)).view(torch.bfloat16).to(dev)
+        idp, wp = torch.from_numpy(ids_np).to(dev), torch.from_numpy(w_np).to(dev)
+        wsp = torch.empty((nv.moe_workspace_size(Tp, K_TOP, E, H, I),), dtype=torch.uint8, device=dev)
+        outp = torch.empty((Tp, H), dtype=torch.bfloat16, device=dev)
+        psteps = max(3, min(args.steps, 20))
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(psteps)]
+        for _ in range(3):
+            nv.moe_grouped(xp, idp, wp, layer["gate"], layer["up"], layer["down"], workspace=wsp, out=outp)
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for i in range(psteps):
+            nv.moe_grouped(xp, idp, wp, layer["gate"], layer["up"], layer["down"], workspace=wsp, out=outp,
+                           events=evs[i])
+        t1.record()
+        torch.cuda.synchronize()
+        ms = t0.elapsed_time(t1) / psteps
+        flops = 6.0 * Tp * K_TOP * H * I
+        st = np.array([[evs[i][j].elapsed_time(evs[i][j + 1]) for j in range(4)] for i in range(psteps)]).mean(0)
+        return {
+            "workload": "prefill-shaped MoE layer, 4096 tokens, Zipf(1.1) routing", "TFLOP/s": round(flops / ms / 1e9, 2),
+            "ms_per_call": round(ms, 4), "frac_mfma_bf16": round(flops / ms / 1e9 / MFMA_BF16_PEAK_TFLOPS, 4),
+            "stages_ms": dict(zip(["route", "gate_up", "down", "combine"], [round(v, 4) for v in st])),
+            "rows_max_expert": int(np.bincount(ids_np.ravel(), minlength=E).max())}
+
+    def run_dense():
+        log("dense MLP 2048 x 4096 -> 12288 -> 4096")
+        M, F = 2048, 12288
+        dg = nv.pack(synth.torch_bf16_normal((F, H), 0.02, 61, dev))
+        du = nv.pack(synth.torch_bf16_normal((F, H), 0.025, 62, dev))
+        dd = nv.pack(synth.torch_bf16_normal((H, F), 0.02, 63, dev))
+        xm = torch.from_numpy(synth.bf16_normal((M, H), 1.0, 5, synth.S_X).view(np.int16)).view(torch.bfloat16).to(dev)
+        hm = torch.empty((M, F), dtype=torch.bfloat16, device=dev)
+        ym = torch.empty((M, H), dtype=torch.bfloat16, device=dev)
+        for _ in range(2):
+            nv.linear_gated(xm, dg, du, out=hm)
+            nv.linear(hm, dd, out=ym)
+        torch.cuda.synchronize()
+        dsteps = max(3, min(args.steps, 10))
+        e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+        tg = td = 0.0
+        for _ in range(dsteps):
+            e0.record()
+            nv.linear_gated(xm, dg, du, out=hm)
+            e1.record()
+            nv.linear(hm, dd, out=ym)
+            e2.record()
+            torch.cuda.synchronize()
+            tg += e0.elapsed_time(e1)
+            td += e1.elapsed_time(e2)
+        tg, td = tg / dsteps, td / dsteps
+        fg, fd = 2.0 * M * H * F * 2, 2.0 * M * F * H
+        return {
+            "workload": "dense Fp4Linear MLP 2048 x 4096 -> 12288 -> 4096", "TFLOP/s": round((fg + fd) / (tg + td) / 1e9, 2),
+            "ms_per_call": round(tg + td, 4), "frac_mfma_bf16": round((fg + fd) / (tg + td) / 1e9 / MFMA_BF16_PEAK_TFLOPS, 4),
+            "gated_ms": round(tg, 4), "down_ms": round(td, 4),
+            "gated_tflops": round(fg / tg / 1e9, 2), "down_tflops": round(fd / td / 1e9, 2)}
+
+    def run_pack():
+        log("pack of 288 experts x 3 projections")
+        pk_steps = 3
+        for k_ in raw:
+            nv.pack(raw[k_])
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(pk_steps):
+            for k_ in raw:
+                nv.pack(raw[k_])
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / pk_steps
+        nw = 3 * E * I * H
+        pbytes = nw * 2 + nw * W_BYTES + 3 * E * 4
+        return {"workload": "pack of 288 experts x 3 projections (4096 x 1536 each)",
+                "GB/s": round(pbytes / (ms * 1e-3) / 1e9, 1), "ms_per_call": round(ms, 3),
+                "frac_hbm": round(pbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+
+    if args.only is not None:
+        # one workload alone (profiling runs): its figures only, no headline line
+        fig = {"decode": lambda: run_decode(args.tokens, args.steps, args.warmup), "prefill": run_prefill,
+               "dense": run_dense, "pack": run_pack}[args.only]()
+        print(json.dumps({"only": args.only, **fig}), flush=True)
+        return
+
     # ------------------------------------------------------- headline: decode
     log(f"decode T={args.tokens}: warmup {args.warmup}, timed {args.steps}")
     head = run_decode(args.tokens, args.steps, args.warmup)
@@ -185,88 +278,9 @@ def main():
                              "stages_ms": {k: round(v, 5) for k, v in r["stage_ms_mean"].items()}}
         result["decode_sweep"] = sweep
 
-        # ------------------------------------------------------- prefill layer
-        log("prefill T=4096 Zipf(1.1)")
-        Tp = 4096
-        ids_np, w_np = synth.zipf_routing(Tp, E, K_TOP, 1.1, 4, synth.S_ROUTE)
-        xp = torch.from_numpy(synth.bf16_normal((Tp, H), 1.0, 4, synth.S_X).view(np.int16)).view(torch.bfloat16).to(dev)
-        idp, wp = torch.from_numpy(ids_np).to(dev), torch.from_numpy(w_np).to(dev)
-        wsp = torch.empty((nv.moe_workspace_size(Tp, K_TOP, E, H, I),), dtype=torch.uint8, device=dev)
-        outp = torch.empty((Tp, H), dtype=torch.bfloat16, device=dev)
-        psteps = max(3, min(args.steps, 20))
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(psteps)]
-        for _ in range(3):
-            nv.moe_grouped(xp, idp, wp, layer["gate"], layer["up"], layer["down"], workspace=wsp, out=outp)
-        torch.cuda.synchronize()
-        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        t0.record()
-        for i in range(psteps):
-            nv.moe_grouped(xp, idp, wp, layer["gate"], layer["up"], layer["down"], workspace=wsp, out=outp,
-                           events=evs[i])
-        t1.record()
-        torch.cuda.synchronize()
-        ms = t0.elapsed_time(t1) / psteps
-        flops = 6.0 * Tp * K_TOP * H * I
-        st = np.array([[evs[i][j].elapsed_time(evs[i][j + 1]) for j in range(4)] for i in range(psteps)]).mean(0)
-        result["prefill"] = {
-            "workload": "prefill-shaped MoE layer, 4096 tokens, Zipf(1.1) routing", "TFLOP/s": round(flops / ms / 1e9, 2),
-            "ms_per_call": round(ms, 4), "frac_mfma_bf16": round(flops / ms / 1e9 / MFMA_BF16_PEAK_TFLOPS, 4),
-            "stages_ms": dict(zip(["route", "gate_up", "down", "combine"], [round(v, 4) for v in st])),
-            "rows_max_expert": int(np.bincount(ids_np.ravel(), minlength=E).max())}
-        del wsp, outp
-
-        # --------------------------------------------------------- dense MLP
-        log("dense MLP 2048 x 4096 -> 12288 -> 4096")
-        M, F = 2048, 12288
-        dg = nv.pack(synth.torch_bf16_normal((F, H), 0.02, 61, dev))
-        du = nv.pack(synth.torch_bf16_normal((F, H), 0.025, 62, dev))
-        dd = nv.pack(synth.torch_bf16_normal((H, F), 0.02, 63, dev))
-        xm = torch.from_numpy(synth.bf16_normal((M, H), 1.0, 5, synth.S_X).view(np.int16)).view(torch.bfloat16).to(dev)
-        hm = torch.empty((M, F), dtype=torch.bfloat16, device=dev)
-        ym = torch.empty((M, H), dtype=torch.bfloat16, device=dev)
-        for _ in range(2):
-            nv.linear_gated(xm, dg, du, out=hm)
-            nv.linear(hm, dd, out=ym)
-        torch.cuda.synchronize()
-        dsteps = max(3, min(args.steps, 10))
-        e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
-        tg = td = 0.0
-        for _ in range(dsteps):
-            e0.record()
-            nv.linear_gated(xm, dg, du, out=hm)
-            e1.record()
-            nv.linear(hm, dd, out=ym)
-            e2.record()
-            torch.cuda.synchronize()
-            tg += e0.elapsed_time(e1)
-            td += e1.elapsed_time(e2)
-        tg, td = tg / dsteps, td / dsteps
-        fg, fd = 2.0 * M * H * F * 2, 2.0 * M * F * H
-        result["dense_mlp"] = {
-            "workload": "dense Fp4Linear MLP 2048 x 4096 -> 12288 -> 4096", "TFLOP/s": round((fg + fd) / (tg + td) / 1e9, 2),
-            "ms_per_call": round(tg + td, 4), "frac_mfma_bf16": round((fg + fd) / (tg + td) / 1e9 / MFMA_BF16_PEAK_TFLOPS, 4),
-            "gated_ms": round(tg, 4), "down_ms": round(td, 4)}
-        del dg, du, dd, xm, hm, ym
-
-        # ---------------------------------------------------------------- pack
-        log("pack of 288 experts x 3 projections")
-        pk_steps = 3
-        for k_ in raw:
-            nv.pack(raw[k_])
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(pk_steps):
-            for k_ in raw:
-                nv.pack(raw[k_])
-        e1.record()
-        torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1) / pk_steps
-        nw = 3 * E * I * H
-        pbytes = nw * 2 + nw * W_BYTES + 3 * E * 4
-        result["pack"] = {"workload": "pack of 288 experts x 3 projections (4096 x 1536 each)",
-                          "GB/s": round(pbytes / (ms * 1e-3) / 1e9, 1), "ms_per_call": round(ms, 3),
-                          "frac_hbm": round(pbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        result["prefill"] = run_prefill()
+        result["dense_mlp"] = run_dense()
+        result["pack"] = run_pack()
 
     # --------------------------------------------- counter calibration copy
     if args.calibrate_copy_mib > 0:

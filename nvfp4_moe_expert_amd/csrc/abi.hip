@@ -114,11 +114,13 @@ nvfp4_status moe_impl(const uint16_t* x, int64_t T, int64_t H, const int32_t* id
   int32_t* n_tiles = at<int32_t>(ws, L.n_tiles);
   uint16_t* hbuf = at<uint16_t>(ws, L.h);
   float* ypart = at<float>(ws, L.ypart);
-  // decode tiles on shapes the weight-stream kernel covers: fp16 form, with prep
+  // fp16 form of the routed GEMMs (x16 and H rows scaled per row by a power of two)
+  // on shapes the decode or prefill kernels cover for both projections
   const bool dec = v == kDecode && decode_supported(kGateUp, H, I) && decode_supported(kDown, I, H);
-  DecodeExtra dx{at<uint16_t>(ws, L.x16), at<int32_t>(ws, L.xexp), at<uint32_t>(ws, L.hmax)};
+  const bool pre = v == kPrefill && prefill_supported(kGateUp, T, H, I) && prefill_supported(kDown, S, I, H);
+  F16Args dx{at<uint16_t>(ws, L.x16), at<int32_t>(ws, L.xexp), at<uint32_t>(ws, L.hmax)};
   RoutePrep prep{};
-  if (dec) prep = RoutePrep{x, T, H, k, at<uint16_t>(ws, L.x16), at<int32_t>(ws, L.xexp), at<uint32_t>(ws, L.hmax)};
+  if (dec || pre) prep = RoutePrep{x, T, H, k, at<uint16_t>(ws, L.x16), at<int32_t>(ws, L.xexp), at<uint32_t>(ws, L.hmax)};
 
   if (e == hipSuccess)
     e = launch_route(ids, S, (int)E, eb, variant_tile_rows(v), offsets, perm, nullptr, tiles, n_tiles, prep, s);
@@ -130,27 +132,32 @@ nvfp4_status moe_impl(const uint16_t* x, int64_t T, int64_t H, const int32_t* id
   g.tiles = tiles;
   g.n_tiles = n_tiles;
   if (e == hipSuccess) {
-    g.x = x;
+    g.x = pre ? dx.x16 : x;
+    g.x_rows = T;
     g.w0 = {gate->codes, gate->scales, gate->scale_2};
     g.w1 = {up->codes, up->scales, up->scale_2};
     g.N = I;
     g.K = H;
     g.out = hbuf;
-    e = dec ? launch_decode(kGateUp, true, g, dx, L.max_tiles, s)
-        : (v == kPrefill && prefill_supported(kGateUp, H, I)) ? launch_prefill(kGateUp, g, L.max_tiles, s)
-                                                              : launch_gemm(kGateUp, v, g, L.max_tiles, s);
+    e = dec   ? launch_decode(kGateUp, true, g, dx, L.max_tiles, s)
+        : pre ? launch_prefill(kGateUp, true, g, dx, L.max_tiles, s)
+        : (v == kPrefill && prefill_supported(kGateUp, T, H, I)) ? launch_prefill(kGateUp, false, g, dx, L.max_tiles, s)
+                                                                 : launch_gemm(kGateUp, v, g, L.max_tiles, s);
   }
+  if (e == hipSuccess && pre) e = launch_h_to_f16(hbuf, dx.hmax, S, I, s);
   if (e == hipSuccess) e = mark(2);
   if (e == hipSuccess) {
     g.x = hbuf;
+    g.x_rows = S;
     g.w0 = {down->codes, down->scales, down->scale_2};
     g.w1 = {nullptr, nullptr, nullptr};
     g.N = H;
     g.K = I;
     g.out = ypart;
-    e = dec ? launch_decode(kDown, true, g, dx, L.max_tiles, s)
-        : (v == kPrefill && prefill_supported(kDown, I, H)) ? launch_prefill(kDown, g, L.max_tiles, s)
-                                                            : launch_gemm(kDown, v, g, L.max_tiles, s);
+    e = dec   ? launch_decode(kDown, true, g, dx, L.max_tiles, s)
+        : pre ? launch_prefill(kDown, true, g, dx, L.max_tiles, s)
+        : (v == kPrefill && prefill_supported(kDown, S, I, H)) ? launch_prefill(kDown, false, g, dx, L.max_tiles, s)
+                                                               : launch_gemm(kDown, v, g, L.max_tiles, s);
   }
   if (e == hipSuccess) e = mark(3);
   if (e == hipSuccess) e = launch_combine(ids, tw, ypart, T, k, H, (int)E, eb, y, s);
@@ -175,6 +182,7 @@ nvfp4_status linear_impl(const uint16_t* x, int64_t m, const nvfp4_weight_t* w0,
   GemmArgs g{};
   g.x = x;
   g.M = m;
+  g.x_rows = m;
   g.w0 = {w0->codes, w0->scales, w0->scale_2};
   if (w1) g.w1 = {w1->codes, w1->scales, w1->scale_2};
   g.N = w0->n;
@@ -182,8 +190,9 @@ nvfp4_status linear_impl(const uint16_t* x, int64_t m, const nvfp4_weight_t* w0,
   g.out = out;
   const GemmMode mode = w1 ? kGated : kLinear;
   if (v == kDecode && decode_supported(mode, g.K, g.N))
-    return from_hip(launch_decode(mode, false, g, DecodeExtra{}, 1, s));
-  if (v == kPrefill && prefill_supported(mode, g.K, g.N)) return from_hip(launch_prefill(mode, g, (m + tr - 1) / tr, s));
+    return from_hip(launch_decode(mode, false, g, F16Args{}, 1, s));
+  if (v == kPrefill && prefill_supported(mode, m, g.K, g.N))
+    return from_hip(launch_prefill(mode, false, g, F16Args{}, (m + tr - 1) / tr, s));
   return from_hip(launch_gemm(mode, v, g, (m + tr - 1) / tr, s));
 }
 

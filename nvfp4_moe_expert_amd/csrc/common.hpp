@@ -17,6 +17,8 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
 // ---------------------------------------------------------------- conversions
 // e4m3fn byte (in the low 8 bits) -> fp32. gfx950's fp8 convert uses the OCP
@@ -60,6 +62,32 @@ __device__ __forceinline__ bf16x8 dequant8(uint32_t w, float scale) {
   r[2] = pack_bf16x2(p2[0] * scale, p2[1] * scale);
   r[3] = pack_bf16x2(p3[0] * scale, p3[1] * scale);
   return __builtin_bit_cast(bf16x8, r);
+}
+
+// fp16 form of the same products: the e2m1 value (<= 6, one significant bit past
+// the leading one) times the e4m3 scale (<= 448, three) has at most six
+// significant bits and lies in [2^-10, 2688], so it is exact in fp16 too.
+template <int SEL>
+__device__ __forceinline__ f16x2 e2m1x2_f16(uint32_t w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, SEL);
+}
+
+// 8 codes (one dword) times a block scale held in both halves of s -> 8 fp16.
+__device__ __forceinline__ f16x8 dequant8_f16(uint32_t w, f16x2 s) {
+  const f16x2 p0 = e2m1x2_f16<0>(w) * s, p1 = e2m1x2_f16<1>(w) * s;
+  const f16x2 p2 = e2m1x2_f16<2>(w) * s, p3 = e2m1x2_f16<3>(w) * s;
+  return __builtin_shufflevector(__builtin_shufflevector(p0, p1, 0, 1, 2, 3),
+                                 __builtin_shufflevector(p2, p3, 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// Power-of-two exponent p that puts a row maximum m (> 0, given by its fp32 bits)
+// in [2^14, 2^15): the row times 2^p then fits fp16 with bf16 values down to
+// 2^-28 of m converting exactly. 0 for an all-zero row.
+__device__ __forceinline__ int row_exponent(uint32_t max_bits) {
+  if (max_bits == 0) return 0;
+  const int e = (int)((max_bits >> 23) & 0xFF) - 127;
+  const int p = 14 - e;
+  return p > 126 ? 126 : (p < -126 ? -126 : p);
 }
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }

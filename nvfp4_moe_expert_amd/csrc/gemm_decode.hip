@@ -31,24 +31,8 @@ namespace nvfp4 {
 
 namespace decode_detail {
 
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-
 constexpr int kThreads = 256;
 constexpr int kBlockN = 64;
-
-template <int SEL>
-__device__ __forceinline__ f16x2 e2m1x2_f16(uint32_t w) {
-  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, SEL);
-}
-
-// 8 codes (one dword) times a block scale held in both halves of s -> 8 fp16 (exact).
-__device__ __forceinline__ f16x8 dequant8_f16(uint32_t w, f16x2 s) {
-  const f16x2 p0 = e2m1x2_f16<0>(w) * s, p1 = e2m1x2_f16<1>(w) * s;
-  const f16x2 p2 = e2m1x2_f16<2>(w) * s, p3 = e2m1x2_f16<3>(w) * s;
-  return __builtin_shufflevector(__builtin_shufflevector(p0, p1, 0, 1, 2, 3),
-                                 __builtin_shufflevector(p2, p3, 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
-}
 
 template <int SEL>
 __device__ __forceinline__ float scale_f32(uint32_t w) {
@@ -77,20 +61,12 @@ __device__ __forceinline__ void load_stage(Stage<U>& st, const uint8_t* codes, c
   }
 }
 
-// power-of-two exponent p that puts a row maximum m (> 0) in [2^14, 2^15)
-__device__ __forceinline__ int row_exponent(uint32_t max_bits) {
-  if (max_bits == 0) return 0;
-  int e = (int)((max_bits >> 23) & 0xFF) - 127;
-  int p = 14 - e;
-  return p > 126 ? 126 : (p < -126 ? -126 : p);
-}
-
 }  // namespace decode_detail
 
 using namespace decode_detail;
 
 template <int MODE, int U, bool F16>
-__global__ __launch_bounds__(kThreads) void gemm_decode_kernel(GemmArgs a, DecodeExtra d) {
+__global__ __launch_bounds__(kThreads) void gemm_decode_kernel(GemmArgs a, F16Args d) {
   constexpr bool kTwo = (MODE == kGateUp || MODE == kGated);
   constexpr bool kMoe = (MODE == kGateUp || MODE == kDown);
   constexpr int KC = 128 * U;          // k per stage
@@ -272,7 +248,7 @@ bool decode_supported(GemmMode mode, int64_t K, int64_t N) {
 }
 
 template <int MODE, bool F16>
-static hipError_t launch_dec(const GemmArgs& a, const DecodeExtra& d, int64_t grid_tiles, hipStream_t s) {
+static hipError_t launch_dec(const GemmArgs& a, const F16Args& d, int64_t grid_tiles, hipStream_t s) {
   const dim3 grid((unsigned)grid_tiles, (unsigned)(a.N / kBlockN));
   if (a.K % 512 == 0)
     hipLaunchKernelGGL((gemm_decode_kernel<MODE, 4, F16>), grid, dim3(kThreads), 0, s, a, d);
@@ -281,7 +257,7 @@ static hipError_t launch_dec(const GemmArgs& a, const DecodeExtra& d, int64_t gr
   return hipGetLastError();
 }
 
-hipError_t launch_decode(GemmMode mode, bool f16, const GemmArgs& a, const DecodeExtra& d, int64_t grid_tiles,
+hipError_t launch_decode(GemmMode mode, bool f16, const GemmArgs& a, const F16Args& d, int64_t grid_tiles,
                          hipStream_t s) {
   if (grid_tiles <= 0) return hipSuccess;
   switch (mode) {

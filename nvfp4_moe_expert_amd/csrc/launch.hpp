@@ -27,6 +27,7 @@ struct GemmArgs {
   const int32_t* tiles;    // MoE only: [max_tiles][4] = (expert, row_begin, rows, 0)
   const int32_t* n_tiles;  // MoE only: device count of valid tiles
   int64_t M;               // dense only: number of rows
+  int64_t x_rows;          // rows of x (tokens for MoE gate/up, slots for down, M for dense)
   WeightDev w0, w1;        // w1 only for the two-weight modes
   int64_t N, K;            // weight rows / inputs
   void* out;               // H / Ypart / Y
@@ -41,19 +42,27 @@ int variant_tile_rows(GemmVariant v);
 hipError_t launch_gemm(GemmMode mode, GemmVariant v, const GemmArgs& a, int64_t grid_tiles,
                        hipStream_t s);
 
-// Decode-tile (<= 16 rows) weight-streaming GEMM. The fp16 form (routed gate/up and
-// down only) reads activations pre-scaled by the route/prep kernel.
-struct DecodeExtra {
+// Inputs of the fp16 form of the routed GEMMs (decode and prefill tiles): the
+// activations are fp16, each row scaled by a power of two so that its bf16
+// values convert exactly.
+struct F16Args {
   const uint16_t* x16;   // [T][H] fp16: x * 2^xexp[t]
   const int32_t* xexp;   // [T]
   uint32_t* hmax;        // [S] bits of max |H| per permuted row (zeroed by the prep)
 };
+// Decode-tile (<= 16 rows) weight-streaming GEMM. The fp16 form (routed gate/up and
+// down only) reads x16 and converts H rows on the fly with hmax.
 bool decode_supported(GemmMode mode, int64_t K, int64_t N);
 
 // Prefill-tile (<= 128 rows) matrix-core GEMM; the tiled kernel covers other shapes.
-bool prefill_supported(GemmMode mode, int64_t K, int64_t N);
-hipError_t launch_prefill(GemmMode mode, const GemmArgs& a, int64_t grid_tiles, hipStream_t s);
-hipError_t launch_decode(GemmMode mode, bool f16, const GemmArgs& a, const DecodeExtra& d, int64_t grid_tiles,
+bool prefill_supported(GemmMode mode, int64_t x_rows, int64_t K, int64_t N);
+// The fp16 form (routed gate/up and down only) takes fp16 activations scaled per
+// row by a power of two: gate/up the prep kernel's x16 (as GemmArgs::x) and xexp,
+// down the H rows after launch_h_to_f16; gate/up records hmax for that conversion.
+hipError_t launch_prefill(GemmMode mode, bool f16, const GemmArgs& a, const F16Args& d, int64_t grid_tiles,
+                          hipStream_t s);
+hipError_t launch_h_to_f16(uint16_t* h, const uint32_t* hmax, int64_t S, int64_t I, hipStream_t s);
+hipError_t launch_decode(GemmMode mode, bool f16, const GemmArgs& a, const F16Args& d, int64_t grid_tiles,
                          hipStream_t s);
 
 hipError_t launch_pack(const uint16_t* w, int batch, int64_t n, int64_t k, uint8_t* codes,

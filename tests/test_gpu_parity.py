@@ -235,6 +235,8 @@ def _run_moe(x, ids, w, gate, up, down, eb=0):
     (1, 8, 12, 256, 96, 61),
     (200, 2, 4, 128, 64, 62),      # 100 rows per expert: prefill tiles
     (64, 8, 20, 256, 160, 63),
+    (300, 4, 6, 512, 256, 74),     # prefill tiles in the fp16 form, 2 tiles per expert (full + ragged)
+    (150, 8, 40, 256, 512, 75),    # prefill fp16 form, 30 rows per expert on average (1-row-block tiles)
 ])
 def test_moe_vs_oracle(T, k, E, H, I, seed):
     note(f"moe T={T} k={k} E={E} H={H} I={I}")
@@ -286,9 +288,12 @@ def test_moe_token_permutation_and_repeat_bitwise(T, k, E, H, I):
     assert np.array_equal(yp, y1[p])
 
 
-def test_moe_k1_matches_dense_mlp_path():
-    # one expert per token with weight 1: the grouped path equals linear_gated then linear
-    T, E, H, I = 24, 3, 256, 128
+@pytest.mark.parametrize("T,I", [(24, 128), (200, 256)])
+def test_moe_k1_matches_dense_mlp_path(T, I):
+    # one expert per token with weight 1: the grouped path equals linear_gated then
+    # linear up to summation order and the fp16 form (the two entry points may use
+    # different kernels)
+    E, H = 3, 256
     ids = np.full((T, 1), 1, np.int32)
     w = np.ones((T, 1), np.float32)
     x, _, _, gate, up, down = _moe_problem(T, 1, E, H, I, 68, sigma=0.05, ids=ids, weights=w)
@@ -297,7 +302,7 @@ def test_moe_k1_matches_dense_mlp_path():
     h = nv.linear_gated(bf16_dev(x), gd, ud)
     y2 = nv.linear(h, dd)
     torch.cuda.synchronize()
-    assert np.array_equal(bf16_host_bits(y), bf16_host_bits(y2))
+    assert_close(bf16_host_f64(y), bf16_host_f64(y2), "moe k=1 vs dense path")
 
 
 def test_moe_timed_events_same_result():
