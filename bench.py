@@ -239,6 +239,7 @@ def main():
     # ------------------------------------------------------- headline: decode
     log(f"decode T={args.tokens}: warmup {args.warmup}, timed {args.steps}")
     head = run_decode(args.tokens, args.steps, args.warmup)
+    traffic = measured_traffic(args.tokens)
     result = {
         "metric": METRIC,
         "value": round(head["gbs"], 2),
@@ -257,7 +258,9 @@ def main():
                    "activations": "bf16", "routing": "top-8 softmax over N(0,1) logits, 32 rotating draws"},
         "roofline": {"bound": "hbm", "kernel": "gemm_decode_kernel<gate_up, fp16 dequant>",
                      "achieved": round(head["gateup_gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(head["gateup_gbs"] / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(head["gateup_gbs"] / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "traffic_over_algorithmic": (round(traffic / head["gateup_bytes_per_launch"], 3)
+                                                  if traffic else None),
                      "algorithmic_bytes_per_launch": round(head["gateup_bytes_per_launch"]),
                      "avg_launch_ms": round(head["stage_ms_mean"]["gate_up"], 5)},
         "stages_ms": {k: round(v, 5) for k, v in head["stage_ms_mean"].items()},
@@ -297,6 +300,30 @@ def main():
         result["cpu_baseline"] = cpu_baseline(raw, torch, synth)
 
     print(json.dumps(result), flush=True)
+
+
+def measured_traffic(tokens):
+    """HBM bytes per gate/up launch from the committed counter summary
+    (profiles/traffic_gemm_decode_T64.md: FETCH_SIZE + WRITE_SIZE, copy-calibrated),
+    or None when it does not apply: another batch, or kernel sources changed since."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "traffic_gemm_decode_T64.md")
+    if tokens != 64 or not os.path.exists(path):
+        return None
+    text = open(path).read()
+    try:
+        rec = json.loads(text.split("```json", 1)[1].split("```", 1)[0])
+    except (IndexError, ValueError):
+        return None
+    h = hashlib.sha256()
+    for f in rec.get("sources", []):
+        fp = os.path.join(ROOT, f)
+        if not os.path.exists(fp):
+            return None
+        h.update(open(fp, "rb").read())
+    if h.hexdigest() != rec.get("sources_sha256"):
+        return None
+    return rec["fetch_bytes_per_launch"] + rec["write_bytes_per_launch"]
 
 
 def cpu_baseline(raw, torch, synth):
