@@ -5,25 +5,29 @@
 // up apart) and "Questions" item 4 (a prompt-shaped expert kernel whose sums
 // do not depend on the chunking).
 //
-// Work decomposition. A workgroup (4 waves, one per SIMD) takes one tile of
-// <= 128 rows of one expert and 256 weight rows: each wave owns 64 weight rows
+// Work decomposition. A workgroup (8 waves, two per SIMD) takes one tile of
+// <= 128 rows of one expert and 512 weight rows: each wave owns 64 weight rows
 // (for gate/up: the same 32 output columns of both weights, so SiLU(gate)*up is
-// formed in registers) against all rows of the tile. v_mfma_f32_32x32x16_bf16 with
+// formed in registers) against all rows of the tile. v_mfma_f32_32x32x16 with
 //   A = weights, dequantized straight from HBM into registers: lane (r, h) of a
-//       32-row block owns row r and, of every 256-k stage, the four 32-k pieces
-//       [kb + 64c + 32h, +32), c = 0..3: four 128-bit code loads in which the two
-//       lanes of a row read 32 adjacent bytes, and one 16-byte scale load;
-//   B = activations, a [128 x 256k] bf16 tile in LDS shared by the 4 waves,
-//       streamed in with direct-to-LDS buffer loads (no registers held while in
-//       flight), double-buffered, one barrier per stage.
-// MFMA step s = 4c + d (0..15) of a stage pairs k = kb + 64c + 8d (h = 0) with
-// kb + 64c + 32 + 8d (h = 1). The number of 32-row blocks multiplied follows the tile's real row
-// count (1..4, picked per tile), so small experts do not pay for padding rows.
+//       32-row block owns row r and the contiguous k range [kb + 128h, +128) of
+//       every 256-k stage: four 128-bit code loads (pieces c of 32 k) and one
+//       8-byte scale load;
+//   B = activations, a [128 x 256k] tile in LDS shared by the 8 waves, streamed
+//       in with direct-to-LDS buffer loads (no registers held while in flight),
+//       double-buffered, one barrier per stage.
+// MFMA step s (0..15) of a stage pairs k = kb + 8s (h = 0) with kb + 128 + 8s
+// (h = 1). The number of 32-row blocks multiplied follows the
+// tile's real row count (1..4, picked per tile), so small experts do not pay for
+// padding rows. Eight waves share each activation tile, so a stage moves 64 KB of
+// activations per 512 weight rows; the two waves of a SIMD hide each other's
+// latencies.
 //
-// Schedule. With one wave per SIMD nothing else hides latency, so the kernel is
-// software-pipelined by hand: step s issues its MFMAs interleaved one by one with
-// the dequant VALU work and LDS reads of step s + 1, and the loads of stage
-// st + 1 are issued two per step over the first steps of stage st.
+// Schedule per wave: step s issues its LDS reads and MFMAs interleaved with the
+// dequant of step s + 1 (sched_group_barrier). The loads of stage st + 1 go out
+// during stage st: one activation load per step, the scales at step 0 (their
+// registers are double-buffered), and code piece c at step 4c + 3, right after
+// its last use (the code registers are single-buffered).
 //
 // Summation order of an output element: stages in increasing k, within a stage
 // MFMA steps s = 0..15, each over its 16 k. It depends only on K.
@@ -34,7 +38,8 @@ namespace nvfp4 {
 
 namespace prefill_detail {
 
-constexpr int kThreads = 256;
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
 constexpr int KC = 256;             // k per stage
 constexpr int SPS = KC / 16;        // MFMA steps per stage
 constexpr int MT = 128;             // max rows per tile
@@ -44,8 +49,8 @@ constexpr int MT = 128;             // max rows per tile
 // compile-time offset.
 constexpr int RSU = KC / 8 + 1;     // 16-byte units per tile row (data + pad)
 constexpr int RSB = 16 * RSU;       // tile row stride in bytes
-constexpr int XI = ((MT * RSU + 63) / 64 + 3) / 4 * 4;  // 1 KB direct-to-LDS loads per stage
-constexpr int XPW = XI / 4;         // of them per wave
+constexpr int XI = ((MT * RSU + 63) / 64 + kWaves - 1) / kWaves * kWaves;  // 1 KB direct-to-LDS loads per stage
+constexpr int XPW = XI / kWaves;    // of them per wave
 constexpr int XBUF = XI * 1024;     // bytes per buffer
 // Buffer descriptor word 3 for raw (untyped) buffer access on gfx9-family parts.
 constexpr int kRsrcWord3 = 0x00020000;
@@ -63,64 +68,64 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int64_t
 template <bool F16> struct Op { typedef bf16x8 T; };
 template <> struct Op<true> { typedef f16x8 T; };
 
-struct WRegs {
-  u32x4 c[2][4];          // [row block][piece c]: k = kb + 64c + 32h .. +32 of one row
-  u32x4 s[2];             // [row block]: the row's 16 scale bytes of the stage
-};
+
 
 }  // namespace prefill_detail
 
 using namespace prefill_detail;
 
-template <int MODE, int NB, bool F16>
+template <int MODE, int NB, bool F16, int WB>
 __device__ __forceinline__ void prefill_body(const GemmArgs& a, const F16Args& d, char* xs, int e, int rb,
                                              int rows) {
   typedef typename Op<F16>::T AT;
   constexpr bool kTwo = (MODE == kGateUp || MODE == kGated);
+  constexpr int W = kTwo ? 2 : WB;     // 32-row weight blocks per wave
   const int tid = threadIdx.x, lane = tid & 63, r32 = lane & 31, h = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t N = a.N, K = a.K;
 
-  // ---- weight rows of this lane: two 32-row blocks
-  // two-weight modes: block 0 = gate rows n0 + r32, block 1 = up rows n0 + r32 (n0 = 128*by + 32*wave)
-  // one-weight modes: block b = rows n0 + 32b + r32 (n0 = 256*by + 64*wave)
+  // ---- weight rows of this lane: W 32-row blocks
+  // two-weight modes: block 0 = gate rows n0 + r32, block 1 = up rows n0 + r32 (n0 = 256*by + 32*wave)
+  // one-weight modes: block b = rows n0 + 32b + r32 (n0 = 32*WB*(8*by + wave))
   // Every load is a buffer load: a descriptor over one expert's codes / scales
   // (or over x) plus a 32-bit per-lane offset and a uniform stage offset.
-  const int64_t nbase = kTwo ? (int64_t)blockIdx.y * 128 + 32 * wave : (int64_t)blockIdx.y * 256 + 64 * wave;
-  __amdgpu_buffer_rsrc_t crs[2], srs[2];
-  uint32_t co[2], so[2];
+  const int64_t nbase = kTwo ? (int64_t)blockIdx.y * (32 * kWaves) + 32 * wave
+                             : (int64_t)blockIdx.y * (32 * WB * kWaves) + 32 * WB * wave;
+  __amdgpu_buffer_rsrc_t crs[W], srs[W];
+  uint32_t co[W], so[W];
 #pragma unroll
-  for (int b = 0; b < 2; ++b) {
+  for (int b = 0; b < W; ++b) {
     int64_t n = kTwo ? nbase + r32 : nbase + 32 * b + r32;
     if (n > N - 1) n = N - 1;                 // rows past N: computed, never stored
     const WeightDev& w = (kTwo && b == 1) ? a.w1 : a.w0;
     crs[b] = rsrc(w.codes + (int64_t)e * N * (K / 2), N * (K / 2));
     srs[b] = rsrc(w.scales + (int64_t)e * N * (K / 16), N * (K / 16));
-    co[b] = (uint32_t)(n * (K / 2) + 16 * h);
-    so[b] = (uint32_t)(n * (K / 16));
+    co[b] = (uint32_t)(n * (K / 2) + 64 * h);
+    so[b] = (uint32_t)(n * (K / 16) + 8 * h);
   }
-  // loads j in [j0, j1) of the 10 per stage: j = 5b + c, c < 4 codes, c = 4 scales
-  auto load_w = [&](WRegs& wr, int kb, int j0, int j1) {
+  // codes: [row block][piece c] (k = kb + 128h + 32c .. +32 of the row), one set;
+  // scales: [set][row block] (the 8 scale bytes of the lane's 128 k), two sets
+  u32x4 wc[W][4];
+  u32x2 wsc[2][W];
+  auto load_codes = [&](int c, int kb) {
 #pragma unroll
-    for (int j = 0; j < 10; ++j) {
-      if (j < j0 || j >= j1) continue;
-      const int b = j / 5, c = j % 5;
-      if (c < 4) wr.c[b][c] = __builtin_amdgcn_raw_buffer_load_b128(crs[b], co[b] + 32 * c, kb / 2, 0);
-      else wr.s[b] = __builtin_amdgcn_raw_buffer_load_b128(srs[b], so[b], kb / 16, 0);
-    }
+    for (int b = 0; b < W; ++b) wc[b][c] = __builtin_amdgcn_raw_buffer_load_b128(crs[b], co[b] + 16 * c, kb / 2, 0);
+  };
+  auto load_scales = [&](int set, int kb) {
+#pragma unroll
+    for (int b = 0; b < W; ++b) wsc[set][b] = __builtin_amdgcn_raw_buffer_load_b64(srs[b], so[b], kb / 16, 0);
   };
 
   // ---- activation tile: 128 rows x KC k per stage, loaded straight into LDS.
   // Load J (of XI) lane l fills 16-byte unit u = 64J + l of the buffer: tile row
   // u / RSU, k chunk u % RSU. The pad unit of each row and the units past the
-  // last row load the row's first chunk (never read). Rows past the tile in the
-  // last load J that holds tile rows load the tile's last row: their results are
-  // never stored. Wave w issues loads J = w + 4i.
+  // last row load the row's first chunk (never read). Rows past the tile load the
+  // tile's last row: their results are never stored. Wave w issues loads J = w + 8i.
   const __amdgpu_buffer_rsrc_t xrs = rsrc(a.x, a.x_rows * K * 2);
   uint32_t xo[XPW];
 #pragma unroll
   for (int i = 0; i < XPW; ++i) {
-    const int u = 64 * (wave + 4 * i) + lane;
+    const int u = 64 * (wave + kWaves * i) + lane;
     int r = u / RSU;
     int c = u % RSU;
     if (c == RSU - 1) c = 0;
@@ -130,120 +135,103 @@ __device__ __forceinline__ void prefill_body(const GemmArgs& a, const F16Args& d
     else src = rb + r;
     xo[i] = (uint32_t)(2 * (src * K + 8 * c));
   }
-  // loads i in [i0, i1) of this wave's XPW; only those that hold rows of the tile
-  // (B columns past the tile then read stale LDS: they only reach results that are
-  // never stored)
-  const int xunits = rows * RSU;
+  // loads i in [i0, i1) of this wave's XPW
   auto issue_x = [&](int kb, int buf, int i0, int i1) {
 #pragma unroll
     for (int i = 0; i < XPW; ++i) {
       if (i < i0 || i >= i1) continue;
-      if (64 * (wave + 4 * i) >= xunits) continue;
-      auto* dst = (__attribute__((address_space(3))) void*)(xs + buf * XBUF + 1024 * (wave + 4 * i));
+      auto* dst = (__attribute__((address_space(3))) void*)(xs + buf * XBUF + 1024 * (wave + kWaves * i));
       __builtin_amdgcn_raw_ptr_buffer_load_lds(xrs, dst, 16, xo[i], 2 * kb, 0, 0);
     }
   };
 
-  f32x16 acc[2][NB];
+  f32x16 acc[W][NB];
 #pragma unroll
-  for (int b = 0; b < 2; ++b)
+  for (int b = 0; b < W; ++b)
 #pragma unroll
     for (int t = 0; t < NB; ++t) acc[b][t] = f32x16{};
 
-  // A operands of MFMA step s = 4c + d: 8 codes (k = kb + 64c + 32h + 8d ..) of each
-  // row block; their scale is byte 4c + 2h + d/2 of the stage's 16
-  const uint32_t hs = 16 * h;
-  auto prep_a = [&](const WRegs& wr, int s, AT (&A)[2]) {
+  // A operands of MFMA step s: 8 codes (k = kb + 128h + 8s ..) of each row block;
+  // their scale is byte s/2 of the lane's 8
+  auto prep_a = [&](int set, int s, AT (&A)[W]) {
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      const uint32_t word = wr.c[b][s / 4][s % 4];
-      const uint32_t sw = wr.s[b][s / 4] >> hs;
+    for (int b = 0; b < W; ++b) {
+      const uint32_t word = wc[b][s / 4][s % 4];
+      const uint32_t sw = wsc[set][b][s / 8];
+      const int g = (s / 2) % 4;
       if constexpr (F16) {
-        const f16x2 s2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sw, 1.0f, false);
-        A[b] = dequant8_f16(word, ((s % 4) < 2) ? f16x2{s2[0], s2[0]} : f16x2{s2[1], s2[1]});
+        const f16x2 s2 = (g >= 2) ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sw, 1.0f, true)
+                                  : __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sw, 1.0f, false);
+        A[b] = dequant8_f16(word, (g % 2 == 0) ? f16x2{s2[0], s2[0]} : f16x2{s2[1], s2[1]});
       } else {
-        A[b] = dequant8(word, ((s % 4) < 2) ? sc<0>(sw) : sc<1>(sw));
+        A[b] = dequant8(word, (g == 0) ? sc<0>(sw) : (g == 1) ? sc<1>(sw) : (g == 2) ? sc<2>(sw) : sc<3>(sw));
       }
     }
   };
-  // B operands of MFMA step s = 4c + d: tile row 32t + r32, 16-byte unit 8c + 4h + d
-  const char* const xrd = xs + r32 * RSB + 64 * h;
+  // B operands of MFMA step s: tile row 32t + r32, 16-byte unit 16h + s
+  const char* const xrd = xs + r32 * RSB + 256 * h;
   auto prep_b = [&](int buf, int s, AT (&B)[NB]) {
 #pragma unroll
     for (int t = 0; t < NB; ++t)
-      B[t] = *reinterpret_cast<const AT*>(xrd + buf * XBUF + t * 32 * RSB + 16 * (8 * (s / 4) + s % 4));
+      B[t] = *reinterpret_cast<const AT*>(xrd + buf * XBUF + t * 32 * RSB + 16 * s);
   };
-  // MFMAs i in [i0, i1) of one step, i = 2t + b
-  auto mma = [&](const AT (&A)[2], const AT (&B)[NB], int i0, int i1) {
+  // MFMAs i in [i0, i1) of one step, i = W*t + b
+  auto mma = [&](const AT (&A)[W], const AT (&B)[NB], int i0, int i1) {
 #pragma unroll
-    for (int i = 0; i < 2 * NB; ++i) {
+    for (int i = 0; i < W * NB; ++i) {
       if (i < i0 || i >= i1) continue;
-      const int t = i / 2, b = i % 2;
+      const int t = i / W, b = i % W;
       if constexpr (F16) acc[b][t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[b], B[t], acc[b][t], 0, 0, 0);
       else acc[b][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[b], B[t], acc[b][t], 0, 0, 0);
     }
   };
 
-  // ---- pipeline. Stage st computes from register set st % 2 and LDS buffer st % 2
-  // while the loads of stage st + 1 go into the other set and buffer (both free
-  // since the previous hand-over), spread over the first steps of the stage: a
-  // burst of loads at one point stalls the LDS reads and MFMAs behind it. The last
-  // stage reloads itself there instead (never read), which keeps the steps free of
-  // branches. The last step of a stage hands over: wait for this wave's loads,
-  // barrier (tile st + 1 complete everywhere, buffer st % 2 free), and prepare
-  // step 0 of stage st + 1.
+  // ---- pipeline. Stage st reads LDS buffer st % 2 and scale set st % 2; the loads
+  // of stage st + 1 are spread over its steps (see the header). The last stage
+  // reloads itself there instead (never read), which keeps the steps free of
+  // branches. The last step hands over: wait for this wave's activation and scale
+  // loads of stage st + 1 (code pieces 2 and 3, issued after the last activation
+  // load, may still be in flight: the four loads behind it), barrier (tile st + 1
+  // complete everywhere, buffer st % 2 free), and prepare step 0 of stage st + 1.
   const int nst = (int)(K / KC);
-  WRegs wa, wb;
   issue_x(0, 0, 0, XPW);
-  load_w(wa, 0, 0, 10);
+  load_scales(0, 0);
+#pragma unroll
+  for (int c = 0; c < 4; ++c) load_codes(c, 0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  AT A[2], B[NB];
-  prep_a(wa, 0, A);
-  prep_b(0, 0, B);
+  AT A[W], B[NB];
 
-  auto stage = [&](const WRegs& cur, WRegs& nxt, int buf, int st) {
+  auto stage = [&](int set, int buf, int st) {
     const int kn = (st + 1 < nst ? st + 1 : st) * KC;
 #pragma unroll
     for (int s = 0; s < SPS; ++s) {
-      AT An[2], Bn[NB];
-      issue_x(kn, buf ^ 1, 2 * s, 2 * s + 2);
-      load_w(nxt, kn, 2 * s, 2 * s + 2);
-      if (s + 1 < SPS) {
-        prep_a(cur, s + 1, An);
-        prep_b(buf, s + 1, Bn);
-        mma(A, B, 0, 2 * NB);
-        // one MFMA, then (early) one LDS read, then a share of the dequant VALU
+      issue_x(kn, buf ^ 1, s, s + 1);
+      if (s == 0) load_scales(set ^ 1, kn);
+      prep_b(buf, s, B);
+      prep_a(set, s, A);
+      if (s % 4 == 3) load_codes(s / 4, kn);   // piece s/4 was last used just above
+      mma(A, B, 0, W * NB);
+      // LDS reads and dequant first, then the MFMAs (the other wave of the SIMD
+      // fills the gaps)
 #pragma unroll
-        for (int i = 0; i < 2 * NB; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          if (i < NB) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x002, (36 + 2 * NB - 1) / (2 * NB), 0);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      } else {
-        mma(A, B, 0, NB);
-        __builtin_amdgcn_sched_barrier(0);
-        __builtin_amdgcn_s_waitcnt(0);
+      for (int i = 0; i < NB; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      if (s + 1 == SPS) {
+        // vmcnt(4) (gfx9 encoding: vmcnt[3:0], expcnt[6:4] = 7 (no wait), lgkmcnt[11:8] = 0)
+        __builtin_amdgcn_s_waitcnt(0x0074);
         __syncthreads();
-        prep_a(nxt, 0, An);
-        prep_b(buf ^ 1, 0, Bn);
-        mma(A, B, NB, 2 * NB);
-        __builtin_amdgcn_sched_barrier(0);
       }
-#pragma unroll
-      for (int b = 0; b < 2; ++b) A[b] = An[b];
-#pragma unroll
-      for (int t = 0; t < NB; ++t) B[t] = Bn[t];
     }
   };
   // Pairs of stages, then an odd last one.
   int st = 0;
   for (; st + 1 < nst; st += 2) {
-    stage(wa, wb, 0, st);
-    stage(wb, wa, 1, st + 1);
+    stage(0, 0, st);
+    stage(1, 1, st + 1);
   }
-  if (st < nst) stage(wa, wb, 0, st);
+  if (st < nst) stage(0, 0, st);
+  __builtin_amdgcn_s_waitcnt(0);   // the last stage's reloads
 
   // ---- epilogue. 32x32 result layout: lane l holds column (row of the tile) l % 32
   // and weight rows 8*(j/4) + 4*(l/32) + j%4, j = 0..15.
@@ -268,7 +256,7 @@ __device__ __forceinline__ void prefill_body(const GemmArgs& a, const F16Args& d
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         v0[j] = acc[0][t][4 * g + j];
-        v1[j] = acc[1][t][4 * g + j];
+        v1[j] = acc[W - 1][t][4 * g + j];
       }
       const int off = 8 * g + 4 * h;            // weight row within the 32-row block
       if constexpr (kTwo) {
@@ -289,7 +277,7 @@ __device__ __forceinline__ void prefill_body(const GemmArgs& a, const F16Args& d
         }
       } else {
 #pragma unroll
-        for (int b = 0; b < 2; ++b) {
+        for (int b = 0; b < W; ++b) {
           const int64_t n = nbase + 32 * b + off;
           if (n >= N) continue;
           const float* vv = b == 0 ? v0 : v1;
@@ -313,7 +301,9 @@ __device__ __forceinline__ void prefill_body(const GemmArgs& a, const F16Args& d
   }
 }
 
-template <int MODE, bool F16>
+// WB (one-weight modes): 32-row weight blocks per wave, 2 (512 weight rows per
+// workgroup) or 1 (256, for grids that would not fill the chip otherwise).
+template <int MODE, bool F16, int WB>
 __global__ __launch_bounds__(kThreads, 1) void gemm_prefill_kernel(GemmArgs a, F16Args d) {
   constexpr bool kMoe = (MODE == kGateUp || MODE == kDown);
   __shared__ __attribute__((aligned(16))) char xs[2 * XBUF];
@@ -330,10 +320,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_prefill_kernel(GemmArgs a, F
   }
   const int nb = (rows + 31) / 32;
   switch (nb) {
-    case 1: prefill_body<MODE, 1, F16>(a, d, xs, e, rb, rows); break;
-    case 2: prefill_body<MODE, 2, F16>(a, d, xs, e, rb, rows); break;
-    case 3: prefill_body<MODE, 3, F16>(a, d, xs, e, rb, rows); break;
-    default: prefill_body<MODE, 4, F16>(a, d, xs, e, rb, rows); break;
+    case 1: prefill_body<MODE, 1, F16, WB>(a, d, xs, e, rb, rows); break;
+    case 2: prefill_body<MODE, 2, F16, WB>(a, d, xs, e, rb, rows); break;
+    case 3: prefill_body<MODE, 3, F16, WB>(a, d, xs, e, rb, rows); break;
+    default: prefill_body<MODE, 4, F16, WB>(a, d, xs, e, rb, rows); break;
   }
 }
 
@@ -344,23 +334,45 @@ bool prefill_supported(GemmMode mode, int64_t x_rows, int64_t K, int64_t N) {
   return K % KC == 0 && K >= KC && N % 32 == 0 && x_rows * K * 2 < lim && N * (K / 2) < lim;
 }
 
+// Compute units of the current device (cached per device).
+static int cu_count() {
+  static int cached[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+template <int MODE, bool F16, int WB>
+static void launch_pf(const GemmArgs& a, const F16Args& d, int64_t grid_tiles, hipStream_t s) {
+  const bool two = (MODE == kGateUp || MODE == kGated);
+  const int64_t nw = two ? 32 * kWaves : 32 * WB * kWaves;     // output columns per workgroup
+  const dim3 grid((unsigned)grid_tiles, (unsigned)((a.N + nw - 1) / nw));
+  hipLaunchKernelGGL((gemm_prefill_kernel<MODE, F16, WB>), grid, dim3(kThreads), 0, s, a, d);
+}
+
 hipError_t launch_prefill(GemmMode mode, bool f16, const GemmArgs& a, const F16Args& d, int64_t grid_tiles,
                           hipStream_t s) {
   if (grid_tiles <= 0) return hipSuccess;
-  const bool two = (mode == kGateUp || mode == kGated);
-  const int64_t nw = two ? 128 : 256;
-  const dim3 grid((unsigned)grid_tiles, (unsigned)((a.N + nw - 1) / nw));
+  // one-weight modes: half-width workgroups when full-width ones would leave CUs idle
+  const bool narrow = grid_tiles * ((a.N + 32 * 2 * kWaves - 1) / (32 * 2 * kWaves)) < 2 * (int64_t)cu_count();
   switch (mode) {
     case kGateUp:
-      if (f16) hipLaunchKernelGGL((gemm_prefill_kernel<kGateUp, true>), grid, dim3(kThreads), 0, s, a, d);
-      else hipLaunchKernelGGL((gemm_prefill_kernel<kGateUp, false>), grid, dim3(kThreads), 0, s, a, d);
+      if (f16) launch_pf<kGateUp, true, 2>(a, d, grid_tiles, s);
+      else launch_pf<kGateUp, false, 2>(a, d, grid_tiles, s);
       break;
     case kDown:
-      if (f16) hipLaunchKernelGGL((gemm_prefill_kernel<kDown, true>), grid, dim3(kThreads), 0, s, a, d);
-      else hipLaunchKernelGGL((gemm_prefill_kernel<kDown, false>), grid, dim3(kThreads), 0, s, a, d);
+      if (f16) narrow ? launch_pf<kDown, true, 1>(a, d, grid_tiles, s) : launch_pf<kDown, true, 2>(a, d, grid_tiles, s);
+      else narrow ? launch_pf<kDown, false, 1>(a, d, grid_tiles, s) : launch_pf<kDown, false, 2>(a, d, grid_tiles, s);
       break;
-    case kLinear: hipLaunchKernelGGL((gemm_prefill_kernel<kLinear, false>), grid, dim3(kThreads), 0, s, a, d); break;
-    case kGated: hipLaunchKernelGGL((gemm_prefill_kernel<kGated, false>), grid, dim3(kThreads), 0, s, a, d); break;
+    case kLinear:
+      narrow ? launch_pf<kLinear, false, 1>(a, d, grid_tiles, s) : launch_pf<kLinear, false, 2>(a, d, grid_tiles, s);
+      break;
+    case kGated: launch_pf<kGated, false, 2>(a, d, grid_tiles, s); break;
   }
   return hipGetLastError();
 }

@@ -165,6 +165,7 @@ def test_route_empty_batch():
     (16, 80, 4096, 49), (7, 64, 2048, 50), (3, 48, 1536, 51),   # streaming kernel, N % 64 != 0
     (1, 64, 32, 40), (16, 128, 256, 41), (17, 100, 96, 42), (130, 48, 160, 43),
     (300, 256, 1024, 44), (129, 200, 544, 45),
+    (4000, 8192, 256, 46),   # prefill tiles, full-width workgroups (grid of 32 x 16), ragged last tile
 ])
 def test_linear_vs_oracle(M, N, K, seed):
     note(f"linear M={M} N={N} K={K}")
