@@ -57,6 +57,8 @@ def parse():
     p.add_argument("--no-extras", action="store_true", help="only the headline decode step")
     p.add_argument("--only", choices=["decode", "prefill", "dense", "pack"], default=None,
                    help="run one workload only (profiling runs); prints its figures")
+    p.add_argument("--layout", choices=["tiled", "rows"], default="tiled",
+                   help="weight layout in HBM: blocks of 32 rows (tiled) or row-major")
     p.add_argument("--calibrate-copy-mib", type=int, default=256,
                    help="size of the plain device copy run once (counter calibration)")
     return p.parse_args()
@@ -77,6 +79,7 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     nv.load_library()
+    lay = nv.LAYOUT_TILED32 if args.layout == "tiled" else nv.LAYOUT_ROWS
 
     # ---------------------------------------------------------------- weights
     raw, layer = {}, {}
@@ -87,7 +90,7 @@ def main():
             "up": synth.torch_bf16_normal((E, I, H), 0.02, 52, dev),
             "down": synth.torch_bf16_normal((E, H, I), 0.02, 53, dev),
         })
-        layer.update({k: nv.pack(v) for k, v in raw.items()})
+        layer.update({k: nv.pack(v, layout=lay) for k, v in raw.items()})
         torch.cuda.synchronize()
 
     def decode_inputs(T, seed):
@@ -179,9 +182,9 @@ def main():
     def run_dense():
         log("dense MLP 2048 x 4096 -> 12288 -> 4096")
         M, F = 2048, 12288
-        dg = nv.pack(synth.torch_bf16_normal((F, H), 0.02, 61, dev))
-        du = nv.pack(synth.torch_bf16_normal((F, H), 0.025, 62, dev))
-        dd = nv.pack(synth.torch_bf16_normal((H, F), 0.02, 63, dev))
+        dg = nv.pack(synth.torch_bf16_normal((F, H), 0.02, 61, dev), layout=lay)
+        du = nv.pack(synth.torch_bf16_normal((F, H), 0.025, 62, dev), layout=lay)
+        dd = nv.pack(synth.torch_bf16_normal((H, F), 0.02, 63, dev), layout=lay)
         xm = torch.from_numpy(synth.bf16_normal((M, H), 1.0, 5, synth.S_X).view(np.int16)).view(torch.bfloat16).to(dev)
         hm = torch.empty((M, F), dtype=torch.bfloat16, device=dev)
         ym = torch.empty((M, H), dtype=torch.bfloat16, device=dev)
@@ -213,13 +216,13 @@ def main():
         log("pack of 288 experts x 3 projections")
         pk_steps = 3
         for k_ in raw:
-            nv.pack(raw[k_])
+            nv.pack(raw[k_], layout=lay)
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for _ in range(pk_steps):
             for k_ in raw:
-                nv.pack(raw[k_])
+                nv.pack(raw[k_], layout=lay)
         e1.record()
         torch.cuda.synchronize()
         ms = e0.elapsed_time(e1) / pk_steps
@@ -255,6 +258,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"decode-shaped MoE layer, {args.tokens} tokens", "experts": E, "top_k": K_TOP,
                    "hidden": H, "intermediate": I, "tokens": args.tokens, "weights": "NVFP4 (e2m1, e4m3/16, fp32 scale_2)",
+                   "weight_layout": args.layout,
                    "activations": "bf16", "routing": "top-8 softmax over N(0,1) logits, 32 rotating draws"},
         "roofline": {"bound": "hbm", "kernel": "gemm_decode_kernel<gate_up, fp16 dequant>",
                      "achieved": round(head["gateup_gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",

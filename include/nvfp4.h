@@ -29,6 +29,22 @@
  *                                       consecutive inputs of a row;
  *             scale_2 [groups]          fp32 in device memory.
  *           A weight is W[n,k] = e2m1(code) * e4m3(scale[n, k/16]) * scale_2.
+ *           `layout` says how codes and scales sit in memory:
+ *             NVFP4_LAYOUT_ROWS    as above, the checkpoint's row-major order;
+ *             NVFP4_LAYOUT_TILED32 the same bytes regrouped by blocks of 32
+ *               rows (n % 32 == 0 and k % 256 == 0 required): for row block
+ *               R = n/32, row r = n%32,
+ *                 code byte of (n, k)  at ((g*n_blocks + R)*(k/32) + k/32)*512
+ *                                          + r*16 + (k%32)/2,
+ *                 scale of (n, k/16)   at ((g*n_blocks + R)*(k/256) + k/256)*512
+ *                                          + r*16 + (k%256)/16,
+ *               (n_blocks = n/32 of the tensor; k here is the input index) so
+ *               that the 32 rows of a block read one 16-byte piece each from a
+ *               contiguous 512-byte run: full-width loads and no partially used
+ *               cache lines. nvfp4_pack writes either layout; nvfp4_relayout
+ *               converts a stored (row-major) checkpoint. Row-major weights of
+ *               any valid shape work everywhere; tiled ones run on the fast
+ *               GEMM paths only (see each entry point).
  * Shapes.   k must be a positive multiple of 32 (whole 16-input groups, in
  *           32-wide tiles); n >= 1; row counts >= 0 (0 is a no-op).
  * Alignment. codes, scales, activations and outputs must be 16-byte aligned.
@@ -54,7 +70,10 @@
 extern "C" {
 #endif
 
-#define NVFP4_ABI_VERSION 1
+#define NVFP4_ABI_VERSION 2
+
+#define NVFP4_LAYOUT_ROWS 0
+#define NVFP4_LAYOUT_TILED32 1
 
 typedef enum nvfp4_status {
   NVFP4_OK = 0,
@@ -67,12 +86,13 @@ typedef enum nvfp4_status {
 } nvfp4_status;
 
 typedef struct nvfp4_weight_t {
-  const uint8_t* codes;   /* [groups, n, k/2] */
-  const uint8_t* scales;  /* [groups, n, k/16] */
+  const uint8_t* codes;   /* [groups, n, k/2] bytes */
+  const uint8_t* scales;  /* [groups, n, k/16] bytes */
   const float* scale_2;   /* [groups] */
   int64_t n;              /* output features (rows) */
   int64_t k;              /* input features, multiple of 32 */
   int32_t groups;         /* number of tensors (experts); 1 for a dense weight */
+  int32_t layout;         /* NVFP4_LAYOUT_ROWS or NVFP4_LAYOUT_TILED32 */
 } nvfp4_weight_t;
 
 /* Version of this interface (NVFP4_ABI_VERSION). */
@@ -97,11 +117,23 @@ const char* nvfp4_status_string(int status);
  * codes   [batch, n, k/2] out;  scales [batch, n, k/16] out;  scale_2 [batch] out.
  * ws      device workspace of at least nvfp4_pack_workspace_size(batch, n, k)
  *         bytes (per-tensor partial maxima); contents need not be initialised.
+ * layout  NVFP4_LAYOUT_ROWS or NVFP4_LAYOUT_TILED32 (then n % 32 == 0 and
+ *         k % 256 == 0, else NVFP4_ERR_SHAPE): where codes and scales go.
  */
 size_t nvfp4_pack_workspace_size(int32_t batch, int64_t n, int64_t k);
 nvfp4_status nvfp4_pack(const uint16_t* w, int32_t batch, int64_t n, int64_t k,
                         uint8_t* codes, uint8_t* scales, float* scale_2,
-                        void* ws, size_t ws_bytes, void* stream);
+                        void* ws, size_t ws_bytes, int32_t layout, void* stream);
+
+/*
+ * nvfp4_relayout - copy the codes and scales of `src` into dst->codes and
+ * dst->scales in dst->layout (a pure permutation of bytes; scale_2 is not
+ * touched, so dst->scale_2 may point at src's). Shapes and groups must match;
+ * the buffers must not overlap. For a checkpoint loaded as stored: relayout it
+ * once to NVFP4_LAYOUT_TILED32 for the fast GEMM paths.
+ * Passage: issue #308 "The checkpoint" (the stored format being regrouped).
+ */
+nvfp4_status nvfp4_relayout(const nvfp4_weight_t* src, const nvfp4_weight_t* dst, void* stream);
 
 /*
  * nvfp4_dequant - debug export of the dequantized weights (bit-exact checks).
@@ -117,7 +149,8 @@ nvfp4_status nvfp4_dequant(const nvfp4_weight_t* w, uint16_t* wq_unscaled, float
  * nvfp4_linear - dense Fp4Linear: y[m, n] = bf16(scale_2 * sum_k x[m,k] * W[n,k]).
  * Passage: issue #308 "What the branch does" (the dense MLP runs on Fp4Linear).
  * x [m, k] bf16; w: groups == 1, w->k == k of x; y [m, n] bf16 out (round to
- * nearest even). m may be 0.
+ * nearest even). m may be 0. A tiled weight needs m*k*2 and n*k/2 below 2^31
+ * bytes (32-bit buffer offsets of the fast paths), else NVFP4_ERR_SHAPE.
  */
 nvfp4_status nvfp4_linear(const uint16_t* x, int64_t m, const nvfp4_weight_t* w, uint16_t* y,
                           void* stream);
@@ -166,7 +199,8 @@ nvfp4_status nvfp4_moe_route(const int32_t* topk_ids, int64_t T, int32_t k, int3
  * gate, up: groups = E, n = I, k = H.   down: groups = E, n = H, k = I.
  * ws       at least nvfp4_moe_workspace_size(T, k, E, H, I) bytes.
  * y        [T, H] bf16 out.
- * Limits: 1 <= E <= 4096, 1 <= k <= 64, H and I multiples of 32.
+ * Limits: 1 <= E <= 4096, 1 <= k <= 64, H and I multiples of 32. gate and up
+ * share one layout; tiled weights need T*H*2, T*k*I*2, I*H/2 below 2^31 bytes.
  */
 size_t nvfp4_moe_workspace_size(int64_t T, int32_t k, int32_t n_experts, int64_t H, int64_t I);
 nvfp4_status nvfp4_moe_grouped(const uint16_t* x, int64_t T, int64_t H, const int32_t* topk_ids,

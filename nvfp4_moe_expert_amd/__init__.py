@@ -7,9 +7,11 @@ workspaces with torch. Every step of the computation runs in the library's
 HIP kernels; there is no fallback. If the library is missing, every call
 raises.
 
-The weight layout is the ModelOpt NVFP4 one read "as stored" (TensorFold issue
+The weight format is the ModelOpt NVFP4 one read "as stored" (TensorFold issue
 #308, section "The checkpoint"): codes [G, N, K/2] uint8 (even k in the low
-nibble), scales [G, N, K/16] e4m3fn bytes, scale_2 [G] float32.
+nibble), scales [G, N, K/16] e4m3fn bytes, scale_2 [G] float32. The same bytes
+can also sit in the library's tiled layout (LAYOUT_TILED32, blocks of 32 rows,
+see include/nvfp4.h); the tensors keep their shapes as byte containers then.
 """
 from __future__ import annotations
 
@@ -21,9 +23,12 @@ import torch
 
 __all__ = [
     "Nvfp4Error", "NVFP4Weight", "load_library", "library_path", "abi_version",
-    "pack", "dequant", "linear", "linear_gated", "moe_route", "moe_grouped",
-    "moe_workspace_size", "pack_workspace_size",
+    "pack", "relayout", "dequant", "linear", "linear_gated", "moe_route", "moe_grouped",
+    "moe_workspace_size", "pack_workspace_size", "LAYOUT_ROWS", "LAYOUT_TILED32",
 ]
+
+LAYOUT_ROWS = 0       # the checkpoint's row-major codes and scales
+LAYOUT_TILED32 = 1    # blocks of 32 rows (n % 32 == 0, k % 256 == 0)
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libnvfp4.so")
@@ -39,7 +44,8 @@ class Nvfp4Error(RuntimeError):
 
 class _Weight(ctypes.Structure):
     _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("scale_2", ctypes.c_void_p),
-                ("n", ctypes.c_int64), ("k", ctypes.c_int64), ("groups", ctypes.c_int32)]
+                ("n", ctypes.c_int64), ("k", ctypes.c_int64), ("groups", ctypes.c_int32),
+                ("layout", ctypes.c_int32)]
 
 
 _P = ctypes.c_void_p
@@ -52,7 +58,8 @@ _SIGNATURES = {
     "nvfp4_abi_version": (ctypes.c_int, []),
     "nvfp4_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "nvfp4_pack_workspace_size": (_SZ, [_I32, _I64, _I64]),
-    "nvfp4_pack": (ctypes.c_int, [_P, _I32, _I64, _I64, _P, _P, _P, _P, _SZ, _P]),
+    "nvfp4_pack": (ctypes.c_int, [_P, _I32, _I64, _I64, _P, _P, _P, _P, _SZ, _I32, _P]),
+    "nvfp4_relayout": (ctypes.c_int, [_WP, _WP, _P]),
     "nvfp4_dequant": (ctypes.c_int, [_WP, _P, _P, _P]),
     "nvfp4_linear": (ctypes.c_int, [_P, _I64, _WP, _P, _P]),
     "nvfp4_linear_gated": (ctypes.c_int, [_P, _I64, _WP, _WP, _P, _P]),
@@ -121,6 +128,7 @@ class NVFP4Weight:
     codes: torch.Tensor    # uint8 [G, N, K/2]
     scales: torch.Tensor   # uint8 [G, N, K/16]
     scale_2: torch.Tensor  # float32 [G]
+    layout: int = LAYOUT_ROWS
 
     def __post_init__(self):
         if self.codes.dim() == 2:
@@ -135,6 +143,8 @@ class NVFP4Weight:
         g, n, k2 = self.codes.shape
         if self.scales.shape != (g, n, k2 * 2 // 16) or self.scale_2.shape != (g,):
             raise ValueError("inconsistent NVFP4 weight shapes")
+        if self.layout not in (LAYOUT_ROWS, LAYOUT_TILED32):
+            raise ValueError(f"unknown layout {self.layout}")
 
     @property
     def groups(self) -> int:
@@ -150,10 +160,11 @@ class NVFP4Weight:
 
     def _struct(self) -> _Weight:
         return _Weight(self.codes.data_ptr(), self.scales.data_ptr(), self.scale_2.data_ptr(),
-                       self.n, self.k, self.groups)
+                       self.n, self.k, self.groups, self.layout)
 
     def expert(self, e: int) -> "NVFP4Weight":
-        return NVFP4Weight(self.codes[e:e + 1], self.scales[e:e + 1], self.scale_2[e:e + 1])
+        # one tensor's bytes are one contiguous block in either layout
+        return NVFP4Weight(self.codes[e:e + 1], self.scales[e:e + 1], self.scale_2[e:e + 1], self.layout)
 
 
 # ---------------------------------------------------------------- entry points
@@ -161,8 +172,8 @@ def pack_workspace_size(batch: int, n: int, k: int) -> int:
     return load_library().nvfp4_pack_workspace_size(batch, n, k)
 
 
-def pack(w: torch.Tensor) -> NVFP4Weight:
-    """BF16 [N, K] or [G, N, K] -> NVFP4 (one scale_2 per tensor)."""
+def pack(w: torch.Tensor, layout: int = LAYOUT_ROWS) -> NVFP4Weight:
+    """BF16 [N, K] or [G, N, K] -> NVFP4 (one scale_2 per tensor), in `layout`."""
     lib = load_library()
     if w.dim() == 2:
         w = w.unsqueeze(0)
@@ -174,9 +185,18 @@ def pack(w: torch.Tensor) -> NVFP4Weight:
     s2 = torch.empty((g,), dtype=torch.float32, device=dev)
     wsb = max(lib.nvfp4_pack_workspace_size(g, n, k), 16)
     ws = torch.empty((wsb,), dtype=torch.uint8, device=dev)
-    _check(lib.nvfp4_pack(_ptr(w), g, n, k, _ptr(codes), _ptr(scales), _ptr(s2), _ptr(ws), wsb, _stream()),
-           "nvfp4_pack")
-    return NVFP4Weight(codes, scales, s2)
+    _check(lib.nvfp4_pack(_ptr(w), g, n, k, _ptr(codes), _ptr(scales), _ptr(s2), _ptr(ws), wsb, layout,
+                          _stream()), "nvfp4_pack")
+    return NVFP4Weight(codes, scales, s2, layout)
+
+
+def relayout(w: NVFP4Weight, layout: int) -> NVFP4Weight:
+    """The same weight with its codes and scales in `layout` (new tensors; scale_2 shared)."""
+    lib = load_library()
+    out = NVFP4Weight(torch.empty_like(w.codes), torch.empty_like(w.scales), w.scale_2, layout)
+    src, dst = w._struct(), out._struct()
+    _check(lib.nvfp4_relayout(ctypes.byref(src), ctypes.byref(dst), _stream()), "nvfp4_relayout")
+    return out
 
 
 def dequant(w: NVFP4Weight, unscaled: bool = True, scaled: bool = True):

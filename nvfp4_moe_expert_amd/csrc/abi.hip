@@ -27,8 +27,25 @@ nvfp4_status check_weight(const nvfp4_weight_t* w) {
   // grid.y of the GEMM counts 64-row blocks of n (<= 65535); dequant grid < 2^31 blocks
   if (w->n > (int64_t)64 * 65535 || w->k > ((int64_t)1 << 31)) return NVFP4_ERR_SHAPE;
   if ((int64_t)w->groups * w->n * (w->k / 8) / 256 >= ((int64_t)1 << 31)) return NVFP4_ERR_SHAPE;
+  if (w->layout != NVFP4_LAYOUT_ROWS && w->layout != NVFP4_LAYOUT_TILED32) return NVFP4_ERR_SHAPE;
+  if (w->layout == NVFP4_LAYOUT_TILED32 && (w->n % 32 != 0 || w->k % 256 != 0)) return NVFP4_ERR_SHAPE;
   if (!aligned16(w->codes) || !aligned16(w->scales)) return NVFP4_ERR_ALIGN;
   return NVFP4_OK;
+}
+
+WeightDev dev_weight(const nvfp4_weight_t* w) {
+  return WeightDev{w->codes, w->scales, w->scale_2, w->layout == NVFP4_LAYOUT_TILED32 ? 1 : 0};
+}
+
+// Which GEMM kernel runs a projection: the decode-tile weight stream, the
+// prefill-tile matrix-core kernel, or the tiled fallback (row-major weights
+// only). Tiled weights take the prefill kernel wherever the decode kernel does
+// not apply; kNone if no kernel covers the call.
+enum Kern { kKDec, kKPre, kKV1, kKNone };
+Kern pick(GemmMode mode, GemmVariant v, bool tiled, int64_t x_rows, int64_t K, int64_t N) {
+  if (v == kDecode && decode_supported(mode, K, N)) return kKDec;
+  if ((v == kPrefill || tiled) && prefill_supported(mode, x_rows, K, N)) return kKPre;
+  return tiled ? kKNone : kKV1;
 }
 
 nvfp4_status from_hip(hipError_t e) { return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP; }
@@ -85,6 +102,7 @@ nvfp4_status moe_impl(const uint16_t* x, int64_t T, int64_t H, const int32_t* id
   if (E > kMaxExperts) return NVFP4_ERR_SHAPE;
   if (gate->k != H || up->k != H || up->n != I || up->groups != E) return NVFP4_ERR_SHAPE;
   if (down->groups != E || down->n != H || down->k != I) return NVFP4_ERR_SHAPE;
+  if (gate->layout != up->layout) return NVFP4_ERR_SHAPE;
   if (T * (int64_t)k > kMaxSlots) return NVFP4_ERR_SHAPE;
   if (T > 0 && (!x || !ids || !tw || !y)) return NVFP4_ERR_NULL;
   if (T > 0 && (!aligned16(x) || !aligned16(y))) return NVFP4_ERR_ALIGN;
@@ -94,6 +112,11 @@ nvfp4_status moe_impl(const uint16_t* x, int64_t T, int64_t H, const int32_t* id
     if (!aligned16(ws)) return NVFP4_ERR_ALIGN;
     if (ws_bytes < L.total) return NVFP4_ERR_WORKSPACE;
   }
+  const int64_t S = T * k;
+  const GemmVariant v = moe_variant(S, E);
+  const Kern kg = pick(kGateUp, v, gate->layout == NVFP4_LAYOUT_TILED32, T, H, I);
+  const Kern kd = pick(kDown, v, down->layout == NVFP4_LAYOUT_TILED32, S, I, H);
+  if (T > 0 && (kg == kKNone || kd == kKNone)) return NVFP4_ERR_SHAPE;
   hipEvent_t ev[5] = {};
   if (events)
     for (int i = 0; i < 5; ++i) {
@@ -106,8 +129,6 @@ nvfp4_status moe_impl(const uint16_t* x, int64_t T, int64_t H, const int32_t* id
     for (int i = 1; i < 5 && e == hipSuccess; ++i) e = mark(i);
     return from_hip(e);
   }
-  const int64_t S = T * k;
-  const GemmVariant v = moe_variant(S, E);
   int32_t* offsets = at<int32_t>(ws, L.offsets);
   int32_t* perm = at<int32_t>(ws, L.perm);
   int32_t* tiles = at<int32_t>(ws, L.tiles);
@@ -115,12 +136,11 @@ nvfp4_status moe_impl(const uint16_t* x, int64_t T, int64_t H, const int32_t* id
   uint16_t* hbuf = at<uint16_t>(ws, L.h);
   float* ypart = at<float>(ws, L.ypart);
   // fp16 form of the routed GEMMs (x16 and H rows scaled per row by a power of two)
-  // on shapes the decode or prefill kernels cover for both projections
-  const bool dec = v == kDecode && decode_supported(kGateUp, H, I) && decode_supported(kDown, I, H);
-  const bool pre = v == kPrefill && prefill_supported(kGateUp, T, H, I) && prefill_supported(kDown, S, I, H);
+  // when the decode or prefill kernels run both projections
+  const bool f16 = kg != kKV1 && kd != kKV1;
   F16Args dx{at<uint16_t>(ws, L.x16), at<int32_t>(ws, L.xexp), at<uint32_t>(ws, L.hmax)};
   RoutePrep prep{};
-  if (dec || pre) prep = RoutePrep{x, T, H, k, at<uint16_t>(ws, L.x16), at<int32_t>(ws, L.xexp), at<uint32_t>(ws, L.hmax)};
+  if (f16) prep = RoutePrep{x, T, H, k, at<uint16_t>(ws, L.x16), at<int32_t>(ws, L.xexp), at<uint32_t>(ws, L.hmax)};
 
   if (e == hipSuccess)
     e = launch_route(ids, S, (int)E, eb, variant_tile_rows(v), offsets, perm, nullptr, tiles, n_tiles, prep, s);
@@ -132,32 +152,32 @@ nvfp4_status moe_impl(const uint16_t* x, int64_t T, int64_t H, const int32_t* id
   g.tiles = tiles;
   g.n_tiles = n_tiles;
   if (e == hipSuccess) {
-    g.x = pre ? dx.x16 : x;
+    g.x = (f16 && kg == kKPre) ? dx.x16 : x;
     g.x_rows = T;
-    g.w0 = {gate->codes, gate->scales, gate->scale_2};
-    g.w1 = {up->codes, up->scales, up->scale_2};
+    g.w0 = dev_weight(gate);
+    g.w1 = dev_weight(up);
     g.N = I;
     g.K = H;
     g.out = hbuf;
-    e = dec   ? launch_decode(kGateUp, true, g, dx, L.max_tiles, s)
-        : pre ? launch_prefill(kGateUp, true, g, dx, L.max_tiles, s)
-        : (v == kPrefill && prefill_supported(kGateUp, T, H, I)) ? launch_prefill(kGateUp, false, g, dx, L.max_tiles, s)
-                                                                 : launch_gemm(kGateUp, v, g, L.max_tiles, s);
+    e = kg == kKDec   ? launch_decode(kGateUp, f16, g, dx, L.max_tiles, s)
+        : kg == kKPre ? launch_prefill(kGateUp, f16, g, dx, L.max_tiles, s)
+                      : launch_gemm(kGateUp, v, g, L.max_tiles, s);
   }
-  if (e == hipSuccess && pre) e = launch_h_to_f16(hbuf, dx.hmax, S, I, s);
+  // the prefill kernel's fp16 form of down reads H converted in place; the decode
+  // kernel converts while staging
+  if (e == hipSuccess && f16 && kd == kKPre) e = launch_h_to_f16(hbuf, dx.hmax, S, I, s);
   if (e == hipSuccess) e = mark(2);
   if (e == hipSuccess) {
     g.x = hbuf;
     g.x_rows = S;
-    g.w0 = {down->codes, down->scales, down->scale_2};
-    g.w1 = {nullptr, nullptr, nullptr};
+    g.w0 = dev_weight(down);
+    g.w1 = WeightDev{nullptr, nullptr, nullptr, 0};
     g.N = H;
     g.K = I;
     g.out = ypart;
-    e = dec   ? launch_decode(kDown, true, g, dx, L.max_tiles, s)
-        : pre ? launch_prefill(kDown, true, g, dx, L.max_tiles, s)
-        : (v == kPrefill && prefill_supported(kDown, S, I, H)) ? launch_prefill(kDown, false, g, dx, L.max_tiles, s)
-                                                               : launch_gemm(kDown, v, g, L.max_tiles, s);
+    e = kd == kKDec   ? launch_decode(kDown, f16, g, dx, L.max_tiles, s)
+        : kd == kKPre ? launch_prefill(kDown, f16, g, dx, L.max_tiles, s)
+                      : launch_gemm(kDown, v, g, L.max_tiles, s);
   }
   if (e == hipSuccess) e = mark(3);
   if (e == hipSuccess) e = launch_combine(ids, tw, ypart, T, k, H, (int)E, eb, y, s);
@@ -177,22 +197,23 @@ nvfp4_status linear_impl(const uint16_t* x, int64_t m, const nvfp4_weight_t* w0,
   if (m == 0) return NVFP4_OK;
   if (!x || !out) return NVFP4_ERR_NULL;
   if (!aligned16(x) || !aligned16(out)) return NVFP4_ERR_ALIGN;
+  if (w1 && w1->layout != w0->layout) return NVFP4_ERR_SHAPE;
   const GemmVariant v = m <= 16 ? kDecode : kPrefill;
-  const int64_t tr = variant_tile_rows(v);
+  const GemmMode mode = w1 ? kGated : kLinear;
+  const Kern kn = pick(mode, v, w0->layout == NVFP4_LAYOUT_TILED32, m, w0->k, w0->n);
+  if (kn == kKNone) return NVFP4_ERR_SHAPE;
   GemmArgs g{};
   g.x = x;
   g.M = m;
   g.x_rows = m;
-  g.w0 = {w0->codes, w0->scales, w0->scale_2};
-  if (w1) g.w1 = {w1->codes, w1->scales, w1->scale_2};
+  g.w0 = dev_weight(w0);
+  if (w1) g.w1 = dev_weight(w1);
   g.N = w0->n;
   g.K = w0->k;
   g.out = out;
-  const GemmMode mode = w1 ? kGated : kLinear;
-  if (v == kDecode && decode_supported(mode, g.K, g.N))
-    return from_hip(launch_decode(mode, false, g, F16Args{}, 1, s));
-  if (v == kPrefill && prefill_supported(mode, m, g.K, g.N))
-    return from_hip(launch_prefill(mode, false, g, F16Args{}, (m + tr - 1) / tr, s));
+  if (kn == kKDec) return from_hip(launch_decode(mode, false, g, F16Args{}, 1, s));
+  const int64_t tr = variant_tile_rows(kn == kKPre ? kPrefill : v);
+  if (kn == kKPre) return from_hip(launch_prefill(mode, false, g, F16Args{}, (m + tr - 1) / tr, s));
   return from_hip(launch_gemm(mode, v, g, (m + tr - 1) / tr, s));
 }
 
@@ -221,15 +242,39 @@ size_t nvfp4_pack_workspace_size(int32_t batch, int64_t n, int64_t k) {
 }
 
 nvfp4_status nvfp4_pack(const uint16_t* w, int32_t batch, int64_t n, int64_t k, uint8_t* codes,
-                        uint8_t* scales, float* scale_2, void* ws, size_t ws_bytes, void* stream) {
+                        uint8_t* scales, float* scale_2, void* ws, size_t ws_bytes, int32_t layout,
+                        void* stream) {
   if (batch < 1 || batch > 65535 || n < 1 || k < 32 || (k % 32) != 0) return NVFP4_ERR_SHAPE;
+  if (layout != NVFP4_LAYOUT_ROWS && layout != NVFP4_LAYOUT_TILED32) return NVFP4_ERR_SHAPE;
+  if (layout == NVFP4_LAYOUT_TILED32 && (n % 32 != 0 || k % 256 != 0)) return NVFP4_ERR_SHAPE;
   if (n * k / 32 > ((int64_t)1 << 38)) return NVFP4_ERR_SHAPE;
   if (!w || !codes || !scales || !scale_2) return NVFP4_ERR_NULL;
   if (!aligned16(w) || !aligned16(codes) || !aligned16(scales)) return NVFP4_ERR_ALIGN;
   if (!ws || ws_bytes < nvfp4_pack_workspace_size(batch, n, k)) return NVFP4_ERR_WORKSPACE;
   if (!aligned16(ws)) return NVFP4_ERR_ALIGN;
   return from_hip(launch_pack(w, batch, n, k, codes, scales, scale_2, static_cast<uint32_t*>(ws),
-                              static_cast<hipStream_t>(stream)));
+                              layout == NVFP4_LAYOUT_TILED32, static_cast<hipStream_t>(stream)));
+}
+
+nvfp4_status nvfp4_relayout(const nvfp4_weight_t* src, const nvfp4_weight_t* dst, void* stream) {
+  nvfp4_status st;
+  if ((st = check_weight(src)) != NVFP4_OK) return st;
+  if ((st = check_weight(dst)) != NVFP4_OK) return st;
+  if (src->n != dst->n || src->k != dst->k || src->groups != dst->groups) return NVFP4_ERR_SHAPE;
+  // the tiled side's constraints hold for both once either is tiled
+  if (src->layout == dst->layout) {
+    if (src->codes == dst->codes && src->scales == dst->scales) return NVFP4_OK;
+    const size_t cb = (size_t)src->groups * src->n * (src->k / 2), sb = cb / 8;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = hipMemcpyAsync(const_cast<uint8_t*>(dst->codes), src->codes, cb, hipMemcpyDeviceToDevice, s);
+    if (e == hipSuccess)
+      e = hipMemcpyAsync(const_cast<uint8_t*>(dst->scales), src->scales, sb, hipMemcpyDeviceToDevice, s);
+    return from_hip(e);
+  }
+  if ((int64_t)src->groups * src->n * (src->k / 32) / 256 >= ((int64_t)1 << 31)) return NVFP4_ERR_SHAPE;
+  return from_hip(launch_relayout(src->codes, src->scales, src->layout == NVFP4_LAYOUT_TILED32, src->groups,
+                                  src->n, src->k, const_cast<uint8_t*>(dst->codes),
+                                  const_cast<uint8_t*>(dst->scales), static_cast<hipStream_t>(stream)));
 }
 
 nvfp4_status nvfp4_dequant(const nvfp4_weight_t* w, uint16_t* wq_unscaled, float* wq_scaled,
@@ -239,7 +284,8 @@ nvfp4_status nvfp4_dequant(const nvfp4_weight_t* w, uint16_t* wq_unscaled, float
   if (!wq_unscaled && !wq_scaled) return NVFP4_ERR_NULL;
   if ((wq_unscaled && !aligned16(wq_unscaled)) || (wq_scaled && !aligned16(wq_scaled)))
     return NVFP4_ERR_ALIGN;
-  return from_hip(launch_dequant(w->codes, w->scales, w->scale_2, w->groups, w->n, w->k, wq_unscaled,
+  return from_hip(launch_dequant(w->codes, w->scales, w->scale_2, w->groups, w->n, w->k,
+                                 w->layout == NVFP4_LAYOUT_TILED32, wq_unscaled,
                                  wq_scaled, static_cast<hipStream_t>(stream)));
 }
 

@@ -90,6 +90,19 @@ __device__ __forceinline__ int row_exponent(uint32_t max_bits) {
   return p > 126 ? 126 : (p < -126 ? -126 : p);
 }
 
+// ------------------------------------------------------------ weight layouts
+// Byte offsets inside one [N, K] tensor. Row-major: the checkpoint's order.
+// Tiled (blocks of 32 rows; N % 32 == 0, K % 256 == 0): the 16-byte code piece
+// (row n, inputs 32j .. 32j+31) sits at ((n/32)*(K/32) + j)*512 + (n%32)*16, and
+// the 16 scale bytes (row n, inputs 256c .. 256c+255) at ((n/32)*(K/256) + c)*512
+// + (n%32)*16, so 32 rows of a block read 512 contiguous bytes.
+__device__ __forceinline__ int64_t code_piece_off(bool tiled, int64_t n, int64_t j, int64_t K) {
+  return tiled ? ((n / 32) * (K / 32) + j) * 512 + (n % 32) * 16 : n * (K / 2) + j * 16;
+}
+__device__ __forceinline__ int64_t scale_off(bool tiled, int64_t n, int64_t b, int64_t K) {
+  return tiled ? ((n / 32) * (K / 256) + b / 16) * 512 + (n % 32) * 16 + (b % 16) : n * (K / 16) + b;
+}
+
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 
 // ------------------------------------------------------------------- loads

@@ -46,24 +46,28 @@ struct Stage {
   uint32_t s[(U + 1) / 2];
 };
 
-template <int U>
+// Stage offsets of a lane's codes and scales: row-major rows advance kb/2 and
+// kb/16 bytes per kb inputs with 16-byte code chunks side by side; in the tiled
+// layout (blocks of 32 rows) a 32-input chunk is 512 bytes on, and 256 inputs of
+// scales are 512 bytes on (2*kb bytes per kb inputs).
+template <int U, bool TL>
 __device__ __forceinline__ void load_codes(Stage<U>& st, const uint8_t* codes, int64_t kb) {
 #pragma unroll
-  for (int i = 0; i < U; ++i) st.c[i] = ld16(codes + kb / 2 + 16 * i);
+  for (int i = 0; i < U; ++i) st.c[i] = ld16(codes + (TL ? 16 * kb : kb / 2) + (TL ? 512 : 16) * i);
 }
 
-template <int U>
+template <int U, bool TL>
 __device__ __forceinline__ void load_stage(Stage<U>& st, const uint8_t* codes, const uint8_t* scales, int64_t kb) {
-#pragma unroll
-  for (int i = 0; i < U; ++i) st.c[i] = ld16(codes + kb / 2 + 16 * i);
+  load_codes<U, TL>(st, codes, kb);
+  const uint8_t* sp = scales + (TL ? 2 * kb : kb / 16);
   if constexpr (U == 4) {
-    const u32x2 v = *reinterpret_cast<const u32x2*>(scales + kb / 16);
+    const u32x2 v = *reinterpret_cast<const u32x2*>(sp);
     st.s[0] = v[0];
     st.s[1] = v[1];
   } else if constexpr (U == 2) {
-    st.s[0] = *reinterpret_cast<const uint32_t*>(scales + kb / 16);
+    st.s[0] = *reinterpret_cast<const uint32_t*>(sp);
   } else {
-    st.s[0] = *reinterpret_cast<const uint16_t*>(scales + kb / 16);
+    st.s[0] = *reinterpret_cast<const uint16_t*>(sp);
   }
 }
 
@@ -75,7 +79,7 @@ using namespace decode_detail;
 // them up front. A row's 128-byte line of scales then is requested once, by its 4
 // lanes together; loaded a stage at a time, the same line is asked for over four
 // stages and a part of those requests misses again (13% more bytes fetched).
-template <int MODE, int U, bool F16, int NS>
+template <int MODE, int U, bool F16, int NS, bool TL>
 __global__ __launch_bounds__(kThreads) void gemm_decode_kernel(GemmArgs a, F16Args d) {
   constexpr bool kTwo = (MODE == kGateUp || MODE == kGated);
   constexpr bool kMoe = (MODE == kGateUp || MODE == kDown);
@@ -100,10 +104,21 @@ __global__ __launch_bounds__(kThreads) void gemm_decode_kernel(GemmArgs a, F16Ar
 
   const int64_t nrow = (int64_t)blockIdx.y * kBlockN + wave * 16 + lr;   // N % 64 == 0
   const int64_t wrow = (int64_t)e * N + nrow;
-  const uint8_t* c0 = a.w0.codes + wrow * (K / 2) + 16 * U * q;
-  const uint8_t* s0 = a.w0.scales + wrow * (K / 16) + 2 * U * q;
-  const uint8_t* c1 = kTwo ? a.w1.codes + wrow * (K / 2) + 16 * U * q : nullptr;
-  const uint8_t* s1 = kTwo ? a.w1.scales + wrow * (K / 16) + 2 * U * q : nullptr;
+  // lane (lr, q): row nrow, inputs [kb + 32Uq, +32U) of each stage
+  int64_t coff, soff;
+  if constexpr (TL) {
+    const int64_t R = nrow / 32, r = nrow % 32;
+    coff = (int64_t)e * N * (K / 2) + (R * (K / 32) + U * q) * 512 + r * 16;
+    soff = (int64_t)e * N * (K / 16) + (R * (K / 256) + (2 * U * q) / 16) * 512 + r * 16 + (2 * U * q) % 16;
+  } else {
+    coff = wrow * (K / 2) + 16 * U * q;
+    soff = wrow * (K / 16) + 2 * U * q;
+  }
+  const uint8_t* c0 = a.w0.codes + coff;
+  const uint8_t* s0 = a.w0.scales + soff;
+  const uint8_t* c1 = kTwo ? a.w1.codes + coff : nullptr;
+  const uint8_t* s1 = kTwo ? a.w1.scales + soff : nullptr;
+  constexpr int64_t SSTEP = TL ? 2 * KC : KC / 16;   // scale bytes from one stage to the next
 
   // activation chunks of this thread: U per stage, chunk i = row xr[i], 8 k at 8*xc[i]
   const uint16_t* xsrc[U];
@@ -209,17 +224,17 @@ __global__ __launch_bounds__(kThreads) void gemm_decode_kernel(GemmArgs a, F16Ar
     for (int st = 0; st < NS; ++st) {
       if (st < nst) {
         if constexpr (SW == 2) {
-          const u32x2 v = *reinterpret_cast<const u32x2*>(s0 + st * (KC / 16));
+          const u32x2 v = *reinterpret_cast<const u32x2*>(s0 + st * SSTEP);
           gs_all[st][0] = v[0];
           gs_all[st][1] = v[1];
           if constexpr (kTwo) {
-            const u32x2 w = *reinterpret_cast<const u32x2*>(s1 + st * (KC / 16));
+            const u32x2 w = *reinterpret_cast<const u32x2*>(s1 + st * SSTEP);
             us_all[st][0] = w[0];
             us_all[st][1] = w[1];
           }
         } else {
-          gs_all[st][0] = *reinterpret_cast<const uint32_t*>(s0 + st * (KC / 16));
-          if constexpr (kTwo) us_all[st][0] = *reinterpret_cast<const uint32_t*>(s1 + st * (KC / 16));
+          gs_all[st][0] = *reinterpret_cast<const uint32_t*>(s0 + st * SSTEP);
+          if constexpr (kTwo) us_all[st][0] = *reinterpret_cast<const uint32_t*>(s1 + st * SSTEP);
         }
       }
       if constexpr (!kTwo) {
@@ -229,8 +244,8 @@ __global__ __launch_bounds__(kThreads) void gemm_decode_kernel(GemmArgs a, F16Ar
     }
     Stage<U> Cg[2], Cu[2];
     u32x4 xv[U];
-    load_codes<U>(Cg[0], c0, 0);
-    if constexpr (kTwo) load_codes<U>(Cu[0], c1, 0);
+    load_codes<U, TL>(Cg[0], c0, 0);
+    if constexpr (kTwo) load_codes<U, TL>(Cu[0], c1, 0);
     ldx(xv, 0);
     stx(xv, 0);
     __syncthreads();
@@ -240,8 +255,8 @@ __global__ __launch_bounds__(kThreads) void gemm_decode_kernel(GemmArgs a, F16Ar
       const int b = st & 1;
       const bool more = st + 1 < nst;
       if (more) {
-        load_codes<U>(Cg[b ^ 1], c0, (int64_t)(st + 1) * KC);
-        if constexpr (kTwo) load_codes<U>(Cu[b ^ 1], c1, (int64_t)(st + 1) * KC);
+        load_codes<U, TL>(Cg[b ^ 1], c0, (int64_t)(st + 1) * KC);
+        if constexpr (kTwo) load_codes<U, TL>(Cu[b ^ 1], c1, (int64_t)(st + 1) * KC);
         ldx(xv, (int64_t)(st + 1) * KC);
       }
       compute_s(Cg[b], Cu[b], gs_all[st], us_all[st], b);
@@ -251,24 +266,24 @@ __global__ __launch_bounds__(kThreads) void gemm_decode_kernel(GemmArgs a, F16Ar
   } else {
   Stage<U> Ag, Au, Bg, Bu;
   u32x4 xv[U];
-  load_stage<U>(Ag, c0, s0, 0);
-  if constexpr (kTwo) load_stage<U>(Au, c1, s1, 0);
+  load_stage<U, TL>(Ag, c0, s0, 0);
+  if constexpr (kTwo) load_stage<U, TL>(Au, c1, s1, 0);
   ldx(xv, 0);
   stx(xv, 0);
   __syncthreads();
   int st = 0;
   for (; st + 2 <= nst; st += 2) {
     const int64_t k1 = (int64_t)(st + 1) * KC, k2 = (int64_t)(st + 2) * KC;
-    load_stage<U>(Bg, c0, s0, k1);
-    if constexpr (kTwo) load_stage<U>(Bu, c1, s1, k1);
+    load_stage<U, TL>(Bg, c0, s0, k1);
+    if constexpr (kTwo) load_stage<U, TL>(Bu, c1, s1, k1);
     ldx(xv, k1);
     compute(Ag, Au, 0);
     stx(xv, 1);
     __syncthreads();
     const bool more = st + 2 < nst;
     if (more) {
-      load_stage<U>(Ag, c0, s0, k2);
-      if constexpr (kTwo) load_stage<U>(Au, c1, s1, k2);
+      load_stage<U, TL>(Ag, c0, s0, k2);
+      if constexpr (kTwo) load_stage<U, TL>(Au, c1, s1, k2);
       ldx(xv, k2);
     }
     compute(Bg, Bu, 1);
@@ -319,18 +334,23 @@ bool decode_supported(GemmMode mode, int64_t K, int64_t N) {
   return N % kBlockN == 0 && K % 256 == 0 && K >= 256;
 }
 
-template <int MODE, bool F16>
+template <int MODE, bool F16, bool TL>
 static hipError_t launch_dec(const GemmArgs& a, const F16Args& d, int64_t grid_tiles, hipStream_t s) {
   constexpr int NS = 8;   // up to 8 stages: scales up front
   const dim3 grid((unsigned)grid_tiles, (unsigned)(a.N / kBlockN));
   if (a.K % 512 == 0) {
-    if (a.K / 512 <= NS) hipLaunchKernelGGL((gemm_decode_kernel<MODE, 4, F16, NS>), grid, dim3(kThreads), 0, s, a, d);
-    else hipLaunchKernelGGL((gemm_decode_kernel<MODE, 4, F16, 0>), grid, dim3(kThreads), 0, s, a, d);
+    if (a.K / 512 <= NS) hipLaunchKernelGGL((gemm_decode_kernel<MODE, 4, F16, NS, TL>), grid, dim3(kThreads), 0, s, a, d);
+    else hipLaunchKernelGGL((gemm_decode_kernel<MODE, 4, F16, 0, TL>), grid, dim3(kThreads), 0, s, a, d);
   } else {
-    if (a.K / 256 <= NS) hipLaunchKernelGGL((gemm_decode_kernel<MODE, 2, F16, NS>), grid, dim3(kThreads), 0, s, a, d);
-    else hipLaunchKernelGGL((gemm_decode_kernel<MODE, 2, F16, 0>), grid, dim3(kThreads), 0, s, a, d);
+    if (a.K / 256 <= NS) hipLaunchKernelGGL((gemm_decode_kernel<MODE, 2, F16, NS, TL>), grid, dim3(kThreads), 0, s, a, d);
+    else hipLaunchKernelGGL((gemm_decode_kernel<MODE, 2, F16, 0, TL>), grid, dim3(kThreads), 0, s, a, d);
   }
   return hipGetLastError();
+}
+
+template <int MODE, bool F16>
+static hipError_t launch_dec(const GemmArgs& a, const F16Args& d, int64_t grid_tiles, hipStream_t s) {
+  return a.w0.tiled ? launch_dec<MODE, F16, true>(a, d, grid_tiles, s) : launch_dec<MODE, F16, false>(a, d, grid_tiles, s);
 }
 
 hipError_t launch_decode(GemmMode mode, bool f16, const GemmArgs& a, const F16Args& d, int64_t grid_tiles,

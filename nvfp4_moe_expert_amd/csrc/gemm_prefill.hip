@@ -74,9 +74,9 @@ template <> struct Op<true> { typedef f16x8 T; };
 
 using namespace prefill_detail;
 
-template <int MODE, int NB, bool F16, int WB>
+template <int MODE, int NB, bool F16, int WB, bool TL>
 __device__ __forceinline__ void prefill_body(const GemmArgs& a, const F16Args& d, char* xs, int e, int rb,
-                                             int rows) {
+                                             int rows, int nblk) {
   typedef typename Op<F16>::T AT;
   constexpr bool kTwo = (MODE == kGateUp || MODE == kGated);
   constexpr int W = kTwo ? 2 : WB;     // 32-row weight blocks per wave
@@ -89,8 +89,8 @@ __device__ __forceinline__ void prefill_body(const GemmArgs& a, const F16Args& d
   // one-weight modes: block b = rows n0 + 32b + r32 (n0 = 32*WB*(8*by + wave))
   // Every load is a buffer load: a descriptor over one expert's codes / scales
   // (or over x) plus a 32-bit per-lane offset and a uniform stage offset.
-  const int64_t nbase = kTwo ? (int64_t)blockIdx.y * (32 * kWaves) + 32 * wave
-                             : (int64_t)blockIdx.y * (32 * WB * kWaves) + 32 * WB * wave;
+  const int64_t nbase = kTwo ? (int64_t)nblk * (32 * kWaves) + 32 * wave
+                             : (int64_t)nblk * (32 * WB * kWaves) + 32 * WB * wave;
   __amdgpu_buffer_rsrc_t crs[W], srs[W];
   uint32_t co[W], so[W];
 #pragma unroll
@@ -100,20 +100,30 @@ __device__ __forceinline__ void prefill_body(const GemmArgs& a, const F16Args& d
     const WeightDev& w = (kTwo && b == 1) ? a.w1 : a.w0;
     crs[b] = rsrc(w.codes + (int64_t)e * N * (K / 2), N * (K / 2));
     srs[b] = rsrc(w.scales + (int64_t)e * N * (K / 16), N * (K / 16));
-    co[b] = (uint32_t)(n * (K / 2) + 64 * h);
-    so[b] = (uint32_t)(n * (K / 16) + 8 * h);
+    if constexpr (TL) {   // blocks of 32 rows: 512-byte runs per 32-input chunk / 256-input scale chunk
+      co[b] = (uint32_t)(((n / 32) * (K / 32) + 4 * h) * 512 + (n % 32) * 16);
+      so[b] = (uint32_t)((n / 32) * (K / 256) * 512 + (n % 32) * 16 + 8 * h);
+    } else {
+      co[b] = (uint32_t)(n * (K / 2) + 64 * h);
+      so[b] = (uint32_t)(n * (K / 16) + 8 * h);
+    }
   }
-  // codes: [row block][piece c] (k = kb + 128h + 32c .. +32 of the row), one set;
-  // scales: [set][row block] (the 8 scale bytes of the lane's 128 k), two sets
-  u32x4 wc[W][4];
+  // codes: [set][row block][piece c] (k = kb + 128h + 32c .. +32 of the row);
+  // scales: [set][row block] (the 8 scale bytes of the lane's 128 k). Tiles of up
+  // to 64 rows (DEEP) keep two code sets and load weights two stages ahead: their
+  // stages are short, and one stage of lead does not cover the memory latency.
+  constexpr bool DEEP = NB <= 2;
+  constexpr int CS = DEEP ? 2 : 1;
+  u32x4 wc[CS][W][4];
   u32x2 wsc[2][W];
-  auto load_codes = [&](int c, int kb) {
+  auto load_codes = [&](int cs, int c, int kb) {
 #pragma unroll
-    for (int b = 0; b < W; ++b) wc[b][c] = __builtin_amdgcn_raw_buffer_load_b128(crs[b], co[b] + 16 * c, kb / 2, 0);
+    for (int b = 0; b < W; ++b)
+      wc[cs][b][c] = __builtin_amdgcn_raw_buffer_load_b128(crs[b], co[b] + (TL ? 512 : 16) * c, TL ? 16 * kb : kb / 2, 0);
   };
   auto load_scales = [&](int set, int kb) {
 #pragma unroll
-    for (int b = 0; b < W; ++b) wsc[set][b] = __builtin_amdgcn_raw_buffer_load_b64(srs[b], so[b], kb / 16, 0);
+    for (int b = 0; b < W; ++b) wsc[set][b] = __builtin_amdgcn_raw_buffer_load_b64(srs[b], so[b], TL ? 2 * kb : kb / 16, 0);
   };
 
   // ---- activation tile: 128 rows x KC k per stage, loaded straight into LDS.
@@ -156,7 +166,7 @@ __device__ __forceinline__ void prefill_body(const GemmArgs& a, const F16Args& d
   auto prep_a = [&](int set, int s, AT (&A)[W]) {
 #pragma unroll
     for (int b = 0; b < W; ++b) {
-      const uint32_t word = wc[b][s / 4][s % 4];
+      const uint32_t word = wc[DEEP ? set : 0][b][s / 4][s % 4];
       const uint32_t sw = wsc[set][b][s / 8];
       const int g = (s / 2) % 4;
       if constexpr (F16) {
@@ -197,20 +207,43 @@ __device__ __forceinline__ void prefill_body(const GemmArgs& a, const F16Args& d
   issue_x(0, 0, 0, XPW);
   load_scales(0, 0);
 #pragma unroll
-  for (int c = 0; c < 4; ++c) load_codes(c, 0);
+  for (int c = 0; c < 4; ++c) load_codes(0, c, 0);
+  if constexpr (DEEP) {
+    const int k1 = (nst > 1 ? 1 : 0) * KC;
+    load_scales(1, k1);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) load_codes(1, c, k1);
+  }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   AT A[W], B[NB];
 
+  // Stage st uses LDS buffer st % 2, scale set st % 2 and (DEEP) code set st % 2.
+  // Activation loads of stage st + 1 go out one per step in steps 0..8.
+  //   normal: scales of st + 1 at step 0 into the other set, code piece c of st + 1
+  //           at step 4c + 3 (its last use); at the hand-over the four code loads of
+  //           steps 11 and 15 may still be in flight;
+  //   DEEP:   code piece c of st + 2 at step 9 + c (c < 3) and 15, scales of st + 2
+  //           at step 15, all into this stage's sets; the ten loads after the last
+  //           activation load may be in flight at the hand-over.
   auto stage = [&](int set, int buf, int st) {
     const int kn = (st + 1 < nst ? st + 1 : st) * KC;
+    const int kn2 = (st + 2 < nst ? st + 2 : nst - 1) * KC;
 #pragma unroll
     for (int s = 0; s < SPS; ++s) {
       issue_x(kn, buf ^ 1, s, s + 1);
-      if (s == 0) load_scales(set ^ 1, kn);
+      if (!DEEP && s == 0) load_scales(set ^ 1, kn);
       prep_b(buf, s, B);
       prep_a(set, s, A);
-      if (s % 4 == 3) load_codes(s / 4, kn);   // piece s/4 was last used just above
+      if constexpr (DEEP) {
+        if (s >= 9 && s <= 11) load_codes(set, s - 9, kn2);
+        if (s == 15) {
+          load_codes(set, 3, kn2);
+          load_scales(set, kn2);
+        }
+      } else {
+        if (s % 4 == 3) load_codes(0, s / 4, kn);   // piece s/4 was last used just above
+      }
       mma(A, B, 0, W * NB);
       // LDS reads and dequant first, then the MFMAs (the other wave of the SIMD
       // fills the gaps)
@@ -218,8 +251,10 @@ __device__ __forceinline__ void prefill_body(const GemmArgs& a, const F16Args& d
       for (int i = 0; i < NB; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       __builtin_amdgcn_sched_barrier(0);
       if (s + 1 == SPS) {
-        // vmcnt(4) (gfx9 encoding: vmcnt[3:0], expcnt[6:4] = 7 (no wait), lgkmcnt[11:8] = 0)
-        __builtin_amdgcn_s_waitcnt(0x0074);
+        // vmcnt(4) or vmcnt(10); gfx9 encoding: vmcnt[3:0], expcnt[6:4] = 7 (no
+        // wait), lgkmcnt[11:8] = 0
+        if constexpr (DEEP) __builtin_amdgcn_s_waitcnt(0x007A);
+        else __builtin_amdgcn_s_waitcnt(0x0074);
         __syncthreads();
       }
     }
@@ -303,27 +338,38 @@ __device__ __forceinline__ void prefill_body(const GemmArgs& a, const F16Args& d
 
 // WB (one-weight modes): 32-row weight blocks per wave, 2 (512 weight rows per
 // workgroup) or 1 (256, for grids that would not fill the chip otherwise).
-template <int MODE, bool F16, int WB>
+template <int MODE, bool F16, int WB, bool TL>
 __global__ __launch_bounds__(kThreads, 1) void gemm_prefill_kernel(GemmArgs a, F16Args d) {
   constexpr bool kMoe = (MODE == kGateUp || MODE == kDown);
   __shared__ __attribute__((aligned(16))) char xs[2 * XBUF];
-  int e = 0, rb, rows;
+  int e = 0, rb, rows, nblk;
   if (kMoe) {
-    if ((int)blockIdx.x >= *a.n_tiles) return;
-    const int32_t* t = a.tiles + 4 * (int64_t)blockIdx.x;
+    // Workgroups are dealt to the 8 XCDs round-robin by linear id. Remap so that
+    // each XCD runs whole tiles (tile = 8*j + xcd), all n-blocks of a tile one
+    // after another: the tile's activation rows stay in that XCD's L2 across its
+    // n-blocks instead of being fetched again for each one.
+    const int nby = (int)gridDim.y;
+    const int64_t lin = (int64_t)blockIdx.x + (int64_t)gridDim.x * blockIdx.y;
+    const int xcd = (int)(lin % 8);
+    const int64_t j = lin / 8;
+    const int64_t tile = (j / nby) * 8 + xcd;
+    nblk = (int)(j % nby);
+    if (tile >= *a.n_tiles) return;
+    const int32_t* t = a.tiles + 4 * tile;
     e = t[0];
     rb = t[1];
     rows = t[2];
   } else {
+    nblk = (int)blockIdx.y;
     rb = (int)blockIdx.x * MT;
     rows = (int)min((int64_t)MT, a.M - rb);
   }
   const int nb = (rows + 31) / 32;
   switch (nb) {
-    case 1: prefill_body<MODE, 1, F16, WB>(a, d, xs, e, rb, rows); break;
-    case 2: prefill_body<MODE, 2, F16, WB>(a, d, xs, e, rb, rows); break;
-    case 3: prefill_body<MODE, 3, F16, WB>(a, d, xs, e, rb, rows); break;
-    default: prefill_body<MODE, 4, F16, WB>(a, d, xs, e, rb, rows); break;
+    case 1: prefill_body<MODE, 1, F16, WB, TL>(a, d, xs, e, rb, rows, nblk); break;
+    case 2: prefill_body<MODE, 2, F16, WB, TL>(a, d, xs, e, rb, rows, nblk); break;
+    case 3: prefill_body<MODE, 3, F16, WB, TL>(a, d, xs, e, rb, rows, nblk); break;
+    default: prefill_body<MODE, 4, F16, WB, TL>(a, d, xs, e, rb, rows, nblk); break;
   }
 }
 
@@ -349,10 +395,15 @@ static int cu_count() {
 
 template <int MODE, bool F16, int WB>
 static void launch_pf(const GemmArgs& a, const F16Args& d, int64_t grid_tiles, hipStream_t s) {
+  static_assert(WB == 1 || WB == 2, "weight blocks per wave");
   const bool two = (MODE == kGateUp || MODE == kGated);
   const int64_t nw = two ? 32 * kWaves : 32 * WB * kWaves;     // output columns per workgroup
-  const dim3 grid((unsigned)grid_tiles, (unsigned)((a.N + nw - 1) / nw));
-  hipLaunchKernelGGL((gemm_prefill_kernel<MODE, F16, WB>), grid, dim3(kThreads), 0, s, a, d);
+  // routed modes: the grid holds ceil(tiles/8)*8 tiles' worth of workgroups (the
+  // kernel maps them XCD by XCD); x * y is all that matters there
+  const int64_t gt = (MODE == kGateUp || MODE == kDown) ? (grid_tiles + 7) / 8 * 8 : grid_tiles;
+  const dim3 grid((unsigned)gt, (unsigned)((a.N + nw - 1) / nw));
+  if (a.w0.tiled) hipLaunchKernelGGL((gemm_prefill_kernel<MODE, F16, WB, true>), grid, dim3(kThreads), 0, s, a, d);
+  else hipLaunchKernelGGL((gemm_prefill_kernel<MODE, F16, WB, false>), grid, dim3(kThreads), 0, s, a, d);
 }
 
 hipError_t launch_prefill(GemmMode mode, bool f16, const GemmArgs& a, const F16Args& d, int64_t grid_tiles,

@@ -18,6 +18,7 @@ struct WeightDev {
   const uint8_t* codes;
   const uint8_t* scales;
   const float* scale_2;
+  int tiled;               // NVFP4_LAYOUT_TILED32 (blocks of 32 rows), else row-major
 };
 
 struct GemmArgs {
@@ -66,11 +67,14 @@ hipError_t launch_decode(GemmMode mode, bool f16, const GemmArgs& a, const F16Ar
                          hipStream_t s);
 
 hipError_t launch_pack(const uint16_t* w, int batch, int64_t n, int64_t k, uint8_t* codes,
-                       uint8_t* scales, float* scale_2, uint32_t* partial, hipStream_t s);
+                       uint8_t* scales, float* scale_2, uint32_t* partial, bool tiled, hipStream_t s);
+// codes and scales of `groups` [n, k] tensors from one layout into the other
+hipError_t launch_relayout(const uint8_t* codes, const uint8_t* scales, bool from_tiled, int64_t groups,
+                           int64_t n, int64_t k, uint8_t* codes_out, uint8_t* scales_out, hipStream_t s);
 int pack_nblk(int64_t per_tensor);
 
 hipError_t launch_dequant(const uint8_t* codes, const uint8_t* scales, const float* scale_2,
-                          int groups, int64_t n, int64_t k, uint16_t* unscaled, float* scaled,
+                          int groups, int64_t n, int64_t k, bool tiled, uint16_t* unscaled, float* scaled,
                           hipStream_t s);
 
 // Permutation by expert; also writes the tile list (tile_rows rows per tile) when tiles != null.

@@ -79,7 +79,7 @@ __device__ __forceinline__ uint32_t e2m1_rne(float q) {
 // One thread packs 32 consecutive elements of a row (two 16-blocks).
 __global__ __launch_bounds__(kPackThreads) void pack_quant_kernel(
     const uint16_t* __restrict__ w, int64_t n, int64_t k, int nblk, const uint32_t* __restrict__ partial,
-    uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, float* __restrict__ scale_2) {
+    uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, float* __restrict__ scale_2, int tiled) {
   const int g = blockIdx.y;
   __shared__ float s_scale2;
   if (threadIdx.x < 64) {
@@ -133,8 +133,8 @@ __global__ __launch_bounds__(kPackThreads) void pack_quant_kernel(
     }
     sbytes |= byte << (8 * blk);
   }
-  st16(codes + (int64_t)g * n * (k / 2) + row * (k / 2) + c32 * 16, out);
-  *reinterpret_cast<uint16_t*>(scales + (int64_t)g * n * (k / 16) + row * (k / 16) + c32 * 2) =
+  st16(codes + (int64_t)g * n * (k / 2) + code_piece_off(tiled, row, c32, k), out);
+  *reinterpret_cast<uint16_t*>(scales + (int64_t)g * n * (k / 16) + scale_off(tiled, row, 2 * c32, k)) =
       (uint16_t)sbytes;
 }
 
@@ -142,14 +142,15 @@ __global__ __launch_bounds__(kPackThreads) void pack_quant_kernel(
 __global__ __launch_bounds__(kPackThreads) void dequant_kernel(
     const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
     const float* __restrict__ scale_2, int64_t n, int64_t k, int64_t total8,
-    uint16_t* __restrict__ unscaled, float* __restrict__ scaled) {
+    uint16_t* __restrict__ unscaled, float* __restrict__ scaled, int tiled) {
   const int64_t u = (int64_t)blockIdx.x * kPackThreads + threadIdx.x;
   if (u >= total8) return;
   const int64_t per_group8 = n * k / 8;
   const int64_t g = u / per_group8, r = u % per_group8;
   const int64_t row = r / (k / 8), c8 = r % (k / 8);
-  const uint32_t w = *reinterpret_cast<const uint32_t*>(codes + g * n * (k / 2) + row * (k / 2) + c8 * 4);
-  const float s = e4m3_to_f32(scales[g * n * (k / 16) + row * (k / 16) + c8 / 2]);
+  const uint32_t w =
+      *reinterpret_cast<const uint32_t*>(codes + g * n * (k / 2) + code_piece_off(tiled, row, c8 / 4, k) + (c8 % 4) * 4);
+  const float s = e4m3_to_f32(scales[g * n * (k / 16) + scale_off(tiled, row, c8 / 2, k)]);
   const bf16x8 d = dequant8(w, s);
   const int64_t o = g * n * k + row * k + c8 * 8;
   if (unscaled) st16(unscaled + o, __builtin_bit_cast(u32x4, d));
@@ -179,7 +180,7 @@ int pack_nblk(int64_t per_tensor) {
 }
 
 hipError_t launch_pack(const uint16_t* w, int batch, int64_t n, int64_t k, uint8_t* codes,
-                       uint8_t* scales, float* scale_2, uint32_t* partial, hipStream_t s) {
+                       uint8_t* scales, float* scale_2, uint32_t* partial, bool tiled, hipStream_t s) {
   const int64_t per_tensor = n * k;
   const int nblk = pack_nblk(per_tensor);
   hipLaunchKernelGGL(pack_amax_kernel, dim3(nblk, batch), dim3(kPackThreads), 0, s, w, per_tensor,
@@ -189,17 +190,48 @@ hipError_t launch_pack(const uint16_t* w, int batch, int64_t n, int64_t k, uint8
   const int64_t units = n * (k / 32);
   const int64_t gx = (units + kPackThreads - 1) / kPackThreads;
   hipLaunchKernelGGL(pack_quant_kernel, dim3((unsigned)gx, batch), dim3(kPackThreads), 0, s, w, n, k,
-                     nblk, partial, codes, scales, scale_2);
+                     nblk, partial, codes, scales, scale_2, (int)tiled);
+  return hipGetLastError();
+}
+
+// One thread moves one 16-byte code piece (row n, inputs 32j ..) and, for the
+// first K/256 pieces of a row, one 16-byte scale piece (row n, inputs 256c ..).
+__global__ __launch_bounds__(kPackThreads) void relayout_kernel(const uint8_t* __restrict__ codes,
+                                                                const uint8_t* __restrict__ scales,
+                                                                int from_tiled, int64_t total, int64_t n,
+                                                                int64_t k, uint8_t* __restrict__ codes_out,
+                                                                uint8_t* __restrict__ scales_out) {
+  const int64_t u = (int64_t)blockIdx.x * kPackThreads + threadIdx.x;
+  if (u >= total) return;
+  const int64_t per_group = n * (k / 32);
+  const int64_t g = u / per_group, r = u % per_group;
+  const int64_t row = r / (k / 32), j = r % (k / 32);
+  const bool ft = from_tiled != 0;
+  const int64_t cbase = g * n * (k / 2);
+  st16(codes_out + cbase + code_piece_off(!ft, row, j, k), ld16(codes + cbase + code_piece_off(ft, row, j, k)));
+  if (j < k / 256) {
+    const int64_t sbase = g * n * (k / 16);
+    st16(scales_out + sbase + scale_off(!ft, row, 16 * j, k), ld16(scales + sbase + scale_off(ft, row, 16 * j, k)));
+  }
+}
+
+hipError_t launch_relayout(const uint8_t* codes, const uint8_t* scales, bool from_tiled, int64_t groups,
+                           int64_t n, int64_t k, uint8_t* codes_out, uint8_t* scales_out, hipStream_t s) {
+  const int64_t total = groups * n * (k / 32);
+  if (total == 0) return hipSuccess;
+  const int64_t gx = (total + kPackThreads - 1) / kPackThreads;
+  hipLaunchKernelGGL(relayout_kernel, dim3((unsigned)gx), dim3(kPackThreads), 0, s, codes, scales,
+                     (int)from_tiled, total, n, k, codes_out, scales_out);
   return hipGetLastError();
 }
 
 hipError_t launch_dequant(const uint8_t* codes, const uint8_t* scales, const float* scale_2,
-                          int groups, int64_t n, int64_t k, uint16_t* unscaled, float* scaled,
+                          int groups, int64_t n, int64_t k, bool tiled, uint16_t* unscaled, float* scaled,
                           hipStream_t s) {
   const int64_t total8 = (int64_t)groups * n * k / 8;
   const int64_t gx = (total8 + kPackThreads - 1) / kPackThreads;
   hipLaunchKernelGGL(dequant_kernel, dim3((unsigned)gx), dim3(kPackThreads), 0, s, codes, scales,
-                     scale_2, n, k, total8, unscaled, scaled);
+                     scale_2, n, k, total8, unscaled, scaled, (int)tiled);
   return hipGetLastError();
 }
 

@@ -44,14 +44,14 @@ def test_binding_covers_every_symbol():
 
 def test_version_and_status_strings():
     lib = nv.load_library()
-    assert nv.abi_version() == 1
+    assert nv.abi_version() == 2
     for code in range(7):
         assert lib.nvfp4_status_string(code)
     assert b"unknown" in lib.nvfp4_status_string(99)
 
 
-def _w(n=64, k=128, groups=1, codes=A, scales=A, s2=A):
-    return nv._Weight(codes, scales, s2, n, k, groups)
+def _w(n=64, k=128, groups=1, codes=A, scales=A, s2=A, layout=0):
+    return nv._Weight(codes, scales, s2, n, k, groups, layout)
 
 
 def P(v):
@@ -62,6 +62,8 @@ def P(v):
     (dict(k=48), ESHAPE), (dict(k=16), ESHAPE), (dict(k=0), ESHAPE), (dict(n=0), ESHAPE),
     (dict(groups=0), ESHAPE), (dict(codes=0), ENULL), (dict(scales=0), ENULL), (dict(s2=0), ENULL),
     (dict(codes=A + 4), EALIGN), (dict(scales=A + 8), EALIGN), (dict(groups=2), ESHAPE),
+    (dict(layout=2), ESHAPE), (dict(layout=1), ESHAPE),            # tiled needs k % 256 == 0
+    (dict(layout=1, n=48, k=256), ESHAPE),                        # ... and n % 32 == 0
 ])
 def test_linear_rejects_bad_weight(kw, status):
     lib = nv.load_library()
@@ -93,13 +95,29 @@ def test_pack_validation():
     ws = lib.nvfp4_pack_workspace_size(3, 64, 128)
     assert ws > 0
     args = lambda **o: [P(o.get("w", A)), o.get("batch", 3), o.get("n", 64), o.get("k", 128), P(o.get("codes", A)),
-                        P(o.get("scales", A)), P(o.get("s2", A)), P(o.get("ws", B)), o.get("wsb", ws), None]
+                        P(o.get("scales", A)), P(o.get("s2", A)), P(o.get("ws", B)), o.get("wsb", ws),
+                        o.get("layout", 0), None]
     assert lib.nvfp4_pack(*args(k=40)) == ESHAPE
     assert lib.nvfp4_pack(*args(batch=0)) == ESHAPE
     assert lib.nvfp4_pack(*args(w=0)) == ENULL
     assert lib.nvfp4_pack(*args(codes=A + 1)) == EALIGN
     assert lib.nvfp4_pack(*args(wsb=ws - 1)) == EWS
     assert lib.nvfp4_pack(*args(ws=0)) == EWS
+    assert lib.nvfp4_pack(*args(layout=1)) == ESHAPE          # tiled: k % 256 != 0
+    assert lib.nvfp4_pack(*args(layout=1, k=256, n=40, wsb=lib.nvfp4_pack_workspace_size(3, 40, 256))) == ESHAPE
+    assert lib.nvfp4_pack(*args(layout=7)) == ESHAPE
+
+
+def test_relayout_validation():
+    lib = nv.load_library()
+    src, dst = _w(n=64, k=256), _w(n=64, k=256, layout=1, codes=B, scales=B)
+    assert lib.nvfp4_relayout(ctypes.byref(src), None, None) == ENULL
+    bad = _w(n=32, k=256, layout=1, codes=B, scales=B)
+    assert lib.nvfp4_relayout(ctypes.byref(src), ctypes.byref(bad), None) == ESHAPE
+    odd = _w(n=64, k=128, layout=1, codes=B, scales=B)
+    assert lib.nvfp4_relayout(ctypes.byref(_w(n=64, k=128)), ctypes.byref(odd), None) == ESHAPE
+    # same layout and same buffers: nothing to do
+    assert lib.nvfp4_relayout(ctypes.byref(src), ctypes.byref(src), None) == OK
 
 
 def test_dequant_validation():
@@ -122,9 +140,9 @@ def test_route_validation():
 
 
 def _moe(lib, T=8, H=256, k=4, E=16, I=128, eb=0, x=A, ids=A, tw=A, y=B, ws=B, wsb=None, **wo):
-    g = _w(n=wo.get("gn", I), k=wo.get("gk", H), groups=wo.get("gg", E))
-    u = _w(n=wo.get("un", I), k=wo.get("uk", H), groups=wo.get("ug", E))
-    d = _w(n=wo.get("dn", H), k=wo.get("dk", I), groups=wo.get("dg", E))
+    g = _w(n=wo.get("gn", I), k=wo.get("gk", H), groups=wo.get("gg", E), layout=wo.get("gl", 0))
+    u = _w(n=wo.get("un", I), k=wo.get("uk", H), groups=wo.get("ug", E), layout=wo.get("ul", 0))
+    d = _w(n=wo.get("dn", H), k=wo.get("dk", I), groups=wo.get("dg", E), layout=wo.get("dl", 0))
     if wsb is None:
         wsb = lib.nvfp4_moe_workspace_size(T, k, E, H, I)
     return lib.nvfp4_moe_grouped(P(x), T, H, P(ids), P(tw), k, eb, ctypes.byref(g), ctypes.byref(u),
@@ -149,6 +167,8 @@ def test_moe_validation():
     assert _moe(lib, ws=0) == EWS
     assert _moe(lib, wsb=lib.nvfp4_moe_workspace_size(8, 4, 16, 256, 128) - 1) == EWS
     assert _moe(lib, E=4097) == ESHAPE
+    assert _moe(lib, gl=1, ul=0, H=256, I=256, gn=256, un=256, dk=256) == ESHAPE   # gate and up layouts differ
+    assert _moe(lib, dl=1) == ESHAPE              # tiled down needs k = I % 256 == 0
 
 
 def test_moe_empty_batch_is_noop():

@@ -13,7 +13,7 @@ import torch
 
 import nvfp4_moe_expert_amd as nv
 import synth
-from gpu_util import DEV, assert_close, bf16_dev, bf16_host_bits, bf16_host_f64, note, weight_dev
+from gpu_util import DEV, assert_close, bf16_dev, bf16_host_bits, bf16_host_f64, note, tile32, weight_dev
 from oracle import formats as F
 from oracle import mlp as OM
 from oracle import nvfp4 as ONV
@@ -316,3 +316,67 @@ def test_moe_timed_events_same_result():
     assert np.array_equal(bf16_host_bits(y2), y1)
     times = [ev[i].elapsed_time(ev[i + 1]) for i in range(4)]
     assert all(t >= 0 for t in times)
+
+
+# ------------------------------------------------------------------ tiled layout
+TILED = nv.LAYOUT_TILED32
+
+
+def test_pack_tiled_bit_exact_and_relayout_roundtrip():
+    w = synth.bf16_normal((3, 96, 512), 0.03, 80)
+    note("pack tiled (3, 96, 512)")
+    gt = nv.pack(bf16_dev(w), layout=TILED)
+    gr = nv.pack(bf16_dev(w))
+    back = nv.relayout(gt, nv.LAYOUT_ROWS)
+    fwd = nv.relayout(gr, TILED)
+    torch.cuda.synchronize()
+    c, s, s2 = ONV.pack_batch(w)
+    ct, st = tile32(c, s)
+    assert np.array_equal(gt.codes.cpu().numpy(), ct)
+    assert np.array_equal(gt.scales.cpu().numpy(), st)
+    assert np.array_equal(gt.scale_2.cpu().numpy().view(np.uint32), s2.view(np.uint32))
+    assert torch.equal(fwd.codes, gt.codes) and torch.equal(fwd.scales, gt.scales)
+    assert torch.equal(back.codes, gr.codes) and torch.equal(back.scales, gr.scales)
+
+
+def test_dequant_tiled_matches_rows():
+    w = ONV.pack_batch(synth.bf16_normal((2, 64, 256), 0.05, 81))
+    ur, sr = nv.dequant(weight_dev(w))
+    ut, stl = nv.dequant(weight_dev(w, TILED))
+    torch.cuda.synchronize()
+    assert torch.equal(ur.view(torch.int16), ut.view(torch.int16))
+    assert torch.equal(sr.view(torch.int32), stl.view(torch.int32))
+
+
+@pytest.mark.parametrize("M,N,K", [
+    (4, 256, 512),       # decode kernel
+    (16, 96, 256),       # n % 64 != 0: the prefill kernel takes tiled weights
+    (300, 256, 1024),    # prefill, half-width workgroups
+    (4000, 8192, 256),   # prefill, full-width workgroups
+])
+def test_linear_tiled_vs_oracle_and_rows(M, N, K):
+    note(f"linear tiled M={M} N={N} K={K}")
+    x = synth.bf16_normal((M, K), 1.0, 82, synth.S_X, M)
+    w = ONV.pack(synth.bf16_normal((N, K), 0.02, 82, synth.S_W, M))
+    yt = nv.linear(bf16_dev(x), weight_dev(w, TILED))
+    yr = nv.linear(bf16_dev(x), weight_dev(w))
+    torch.cuda.synchronize()
+    assert_close(bf16_host_f64(yt), OM.linear(x, w), "linear tiled")
+    if N % 64 == 0 or M > 16:       # same kernel for both layouts: same bits
+        assert np.array_equal(bf16_host_bits(yt), bf16_host_bits(yr))
+
+
+@pytest.mark.parametrize("T,k,E,H,I,seed", [
+    (8, 4, 16, 2048, 512, 83),      # decode tiles
+    (300, 4, 6, 512, 256, 84),      # prefill tiles, full and ragged
+    (150, 8, 40, 256, 512, 85),     # prefill tiles, ~30 rows per expert
+])
+def test_moe_tiled_vs_oracle_and_rows(T, k, E, H, I, seed):
+    note(f"moe tiled T={T} k={k} E={E} H={H} I={I}")
+    x, ids, w, gate, up, down = _moe_problem(T, k, E, H, I, seed, sigma=0.05)
+    args = (bf16_dev(x), torch.from_numpy(ids).to(DEV), torch.from_numpy(w).to(DEV))
+    yt = nv.moe_grouped(*args, weight_dev(gate, TILED), weight_dev(up, TILED), weight_dev(down, TILED))
+    yr = nv.moe_grouped(*args, weight_dev(gate), weight_dev(up), weight_dev(down))
+    torch.cuda.synchronize()
+    assert_close(bf16_host_f64(yt), OM.moe(x, ids, w, gate, up, down), "moe tiled")
+    assert np.array_equal(bf16_host_bits(yt), bf16_host_bits(yr))
