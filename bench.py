@@ -242,7 +242,7 @@ def main():
     # ------------------------------------------------------- headline: decode
     log(f"decode T={args.tokens}: warmup {args.warmup}, timed {args.steps}")
     head = run_decode(args.tokens, args.steps, args.warmup)
-    traffic = measured_traffic(args.tokens)
+    traffic = measured_traffic(args.tokens, args.layout)
     result = {
         "metric": METRIC,
         "value": round(head["gbs"], 2),
@@ -289,6 +289,19 @@ def main():
         result["dense_mlp"] = run_dense()
         result["pack"] = run_pack()
 
+        # the same headline step on the other weight layout (same values, other byte order)
+        other = "rows" if args.layout == "tiled" else "tiled"
+        log(f"decode T={args.tokens}, {other} weight layout")
+        kept = dict(layer)
+        to = nv.LAYOUT_ROWS if other == "rows" else nv.LAYOUT_TILED32
+        layer.update({k: nv.relayout(v, to) for k, v in kept.items()})
+        r = run_decode(args.tokens, args.steps, args.warmup)
+        result[f"decode_T{args.tokens}_{other}_layout"] = {
+            "GB/s": round(r["gbs"], 1), "ms_per_step": round(r["ms_per_step"], 5),
+            "gateup_kernel_gbs": round(r["gateup_gbs"], 1), "down_kernel_gbs": round(r["down_gbs"], 1)}
+        layer.update(kept)
+        del kept
+
     # --------------------------------------------- counter calibration copy
     if args.calibrate_copy_mib > 0:
         n = args.calibrate_copy_mib * (1 << 20) // 4
@@ -306,10 +319,11 @@ def main():
     print(json.dumps(result), flush=True)
 
 
-def measured_traffic(tokens):
+def measured_traffic(tokens, layout):
     """HBM bytes per gate/up launch from the committed counter summary
     (profiles/traffic_gemm_decode_T64.md: FETCH_SIZE + WRITE_SIZE, copy-calibrated),
-    or None when it does not apply: another batch, or kernel sources changed since."""
+    or None when it does not apply: another batch or weight layout, or kernel
+    sources changed since."""
     import hashlib
     path = os.path.join(ROOT, "profiles", "traffic_gemm_decode_T64.md")
     if tokens != 64 or not os.path.exists(path):
@@ -325,7 +339,7 @@ def measured_traffic(tokens):
         if not os.path.exists(fp):
             return None
         h.update(open(fp, "rb").read())
-    if h.hexdigest() != rec.get("sources_sha256"):
+    if h.hexdigest() != rec.get("sources_sha256") or rec.get("layout") != layout:
         return None
     return rec["fetch_bytes_per_launch"] + rec["write_bytes_per_launch"]
 
