@@ -329,6 +329,147 @@ __global__ __launch_bounds__(kThreads) void gemm_decode_kernel(GemmArgs a, F16Ar
   }
 }
 
+// Routed down projection (fp16 form) with K <= 2048 (K = I): the whole
+// activation tile (<= 16 rows x K) is staged in LDS once, and each wave then
+// streams NB consecutive 64-row blocks of weights (its 16 rows of each) with the
+// code loads LA stages ahead. No barrier after the staging, one prologue for NB
+// blocks: with the per-stage tile (K / 512 = 3 stages for K = 1536) the short
+// workgroups spent a large part of their life filling the pipeline.
+template <int MODE, bool F16, int NST, int NB, bool TL>
+__global__ __launch_bounds__(kThreads) void gemm_decode_res_kernel(GemmArgs a, F16Args d) {
+  static_assert(MODE == kDown || MODE == kLinear, "one-weight modes");
+  constexpr bool kMoe = (MODE == kDown);
+  constexpr int U = 4, KC = 128 * U, KT = NST * KC, LW = KT + 8;
+  constexpr int G = NB * NST;   // stages of a wave's stream
+  constexpr int LA = 2;         // stages in flight ahead of the one multiplied
+  constexpr int XU = 16 * (KT / 8) / kThreads;   // 16-byte activation units per thread
+  __shared__ __attribute__((aligned(16))) uint16_t xs[16][LW];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lr = lane & 15, q = lane >> 4;
+  const int64_t N = a.N;
+
+  int e = 0, rb, rows;
+  if (kMoe) {
+    if ((int)blockIdx.x >= *a.n_tiles) return;
+    const int32_t* t = a.tiles + 4 * (int64_t)blockIdx.x;
+    e = t[0];
+    rb = t[1];
+    rows = t[2];
+  } else {
+    rb = (int)blockIdx.x * 16;
+    rows = (int)min((int64_t)16, a.M - rb);
+  }
+
+  // block j of this wave: rows nrow + 64j; in both layouts 64 rows are 32*K code
+  // bytes and 4*K scale bytes further on
+  const int64_t nrow = (int64_t)blockIdx.y * (kBlockN * NB) + wave * 16 + lr;
+  int64_t coff, soff;
+  if constexpr (TL) {
+    const int64_t R = nrow / 32, r = nrow % 32;
+    coff = (int64_t)e * N * (KT / 2) + (R * (KT / 32) + U * q) * 512 + r * 16;
+    soff = (int64_t)e * N * (KT / 16) + (R * (KT / 256) + (2 * U * q) / 16) * 512 + r * 16 + (2 * U * q) % 16;
+  } else {
+    const int64_t wrow = (int64_t)e * N + nrow;
+    coff = wrow * (KT / 2) + 16 * U * q;
+    soff = wrow * (KT / 16) + 2 * U * q;
+  }
+  const uint8_t* c0 = a.w0.codes + coff;
+  const uint8_t* s0 = a.w0.scales + soff;
+  constexpr int64_t SSTEP = TL ? 2 * KC : KC / 16;
+  auto cptr = [&](int g) { return c0 + (int64_t)(g / NST) * 32 * KT; };
+  auto kofs = [&](int g) { return (int64_t)(g % NST) * KC; };
+
+  Stage<U> C[LA + 1];
+#pragma unroll
+  for (int g = 0; g < LA && g < G; ++g) load_codes<U, TL>(C[g], cptr(g), kofs(g));
+  u32x2 sc[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g)
+    sc[g] = *reinterpret_cast<const u32x2*>(s0 + (int64_t)(g / NST) * 4 * KT + (g % NST) * SSTEP);
+
+  // ---- the activation tile, converted to fp16 * 2^p per row in the fp16 form
+  {
+    u32x4 hv[XU];
+    float hs[XU];
+#pragma unroll
+    for (int i = 0; i < XU; ++i) {
+      const int u = i * kThreads + tid, r = u / (KT / 8), c = u % (KT / 8);
+      hv[i] = u32x4{0, 0, 0, 0};
+      hs[i] = 1.0f;
+      if (r < rows) {
+        hv[i] = ld16(a.x + (int64_t)(rb + r) * KT + 8 * c);
+        if constexpr (F16) hs[i] = ldexpf(1.0f, row_exponent(d.hmax[rb + r]));
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < XU; ++i) {
+      const int u = i * kThreads + tid, r = u / (KT / 8), c = u % (KT / 8);
+      u32x4 o = hv[i];
+      if constexpr (F16) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const f16x2 h2 = {(_Float16)(bf16_lo(hv[i][j]) * hs[i]), (_Float16)(bf16_hi(hv[i][j]) * hs[i])};
+          o[j] = __builtin_bit_cast(uint32_t, h2);
+        }
+      }
+      st16(&xs[r][8 * c], o);
+    }
+  }
+  __syncthreads();
+
+  const bool live = lr < rows;
+  const int64_t p = rb + lr;
+  float s2 = a.w0.scale_2[e];
+  if constexpr (F16) {
+    if (live) s2 *= ldexpf(1.0f, -row_exponent(d.hmax[p]));
+  }
+  const int64_t orow = kMoe ? (live ? (int64_t)a.perm[p] : 0) : p;
+
+  f32x4 acc = {0, 0, 0, 0};
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    if (g + LA < G) load_codes<U, TL>(C[(g + LA) % (LA + 1)], cptr(g + LA), kofs(g + LA));
+    const Stage<U>& cs = C[g % (LA + 1)];
+    const int kb = (g % NST) * KC;
+#pragma unroll
+    for (int i = 0; i < U; ++i) {
+      const uint32_t sw = sc[g][i / 2] >> (16 * (i & 1));
+      if constexpr (F16) {
+        const f16x2 sf = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sw, 1.0f, false);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const f16x8 B = *reinterpret_cast<const f16x8*>(&xs[lr][kb + 32 * U * q + 32 * i + 8 * s]);
+          const f16x2 gs = (s < 2) ? f16x2{sf[0], sf[0]} : f16x2{sf[1], sf[1]};
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(dequant8_f16(cs.c[i][s], gs), B, acc, 0, 0, 0);
+        }
+      } else {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const bf16x8 B = *reinterpret_cast<const bf16x8*>(&xs[lr][kb + 32 * U * q + 32 * i + 8 * s]);
+          const float gs = (s < 2) ? scale_f32<0>(sw) : scale_f32<1>(sw);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dequant8(cs.c[i][s], gs), B, acc, 0, 0, 0);
+        }
+      }
+    }
+    if (g % NST == NST - 1) {
+      // block g / NST done: lane holds D[n = n0 + 4q + r][token lr]
+      if (live) {
+        const int64_t n0 = (int64_t)blockIdx.y * (kBlockN * NB) + (g / NST) * kBlockN + wave * 16 + 4 * q;
+        if constexpr (MODE == kDown) {
+          *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.out) + orow * N + n0) =
+              f32x4{s2 * acc[0], s2 * acc[1], s2 * acc[2], s2 * acc[3]};
+        } else {
+          u32x2 o;
+          o[0] = pack_bf16x2(s2 * acc[0], s2 * acc[1]);
+          o[1] = pack_bf16x2(s2 * acc[2], s2 * acc[3]);
+          *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(a.out) + orow * N + n0) = o;
+        }
+      }
+      acc = f32x4{0, 0, 0, 0};
+    }
+  }
+}
+
 bool decode_supported(GemmMode mode, int64_t K, int64_t N) {
   (void)mode;
   return N % kBlockN == 0 && K % 256 == 0 && K >= 256;
@@ -337,6 +478,26 @@ bool decode_supported(GemmMode mode, int64_t K, int64_t N) {
 template <int MODE, bool F16, bool TL>
 static hipError_t launch_dec(const GemmArgs& a, const F16Args& d, int64_t grid_tiles, hipStream_t s) {
   constexpr int NS = 8;   // up to 8 stages: scales up front
+  if constexpr (MODE == kDown && F16) {   // the bf16 form needs too many registers here
+    if (a.K % 512 == 0 && a.K <= 2048 && a.N % (kBlockN * 4) == 0) {
+      // 64-row blocks per wave stream: as many as keep >= 4 workgroups per CU
+      const int64_t want = 4 * (int64_t)cu_count();
+      const int nb = grid_tiles * (a.N / (kBlockN * 4)) >= want ? 4 : grid_tiles * (a.N / (kBlockN * 2)) >= want ? 2 : 1;
+      switch (nb * 8 + (int)(a.K / 512)) {
+#define NVFP4_RES(NB_, NST_)                                                                                    \
+  case NB_ * 8 + NST_:                                                                                           \
+    hipLaunchKernelGGL((gemm_decode_res_kernel<MODE, F16, NST_, NB_, TL>),                                     \
+                       dim3((unsigned)grid_tiles, (unsigned)(a.N / (kBlockN * NB_))), dim3(kThreads), 0, s, a, d); \
+    break;
+        NVFP4_RES(1, 1) NVFP4_RES(1, 2) NVFP4_RES(1, 3) NVFP4_RES(1, 4)
+        NVFP4_RES(2, 1) NVFP4_RES(2, 2) NVFP4_RES(2, 3) NVFP4_RES(2, 4)
+        NVFP4_RES(4, 1) NVFP4_RES(4, 2) NVFP4_RES(4, 3) NVFP4_RES(4, 4)
+#undef NVFP4_RES
+        default: return hipErrorInvalidValue;
+      }
+      return hipGetLastError();
+    }
+  }
   const dim3 grid((unsigned)grid_tiles, (unsigned)(a.N / kBlockN));
   if (a.K % 512 == 0) {
     if (a.K / 512 <= NS) hipLaunchKernelGGL((gemm_decode_kernel<MODE, 4, F16, NS, TL>), grid, dim3(kThreads), 0, s, a, d);

@@ -145,11 +145,13 @@ __device__ __forceinline__ void prefill_body(const GemmArgs& a, const F16Args& d
     else src = rb + r;
     xo[i] = (uint32_t)(2 * (src * K + 8 * c));
   }
-  // loads i in [i0, i1) of this wave's XPW
+  // loads i in [i0, i1) of this wave's XPW; only the loads that fill the NB
+  // 32-row blocks the MFMAs read are issued
+  constexpr int XN = (32 * NB * RSU + 63) / 64;
   auto issue_x = [&](int kb, int buf, int i0, int i1) {
 #pragma unroll
     for (int i = 0; i < XPW; ++i) {
-      if (i < i0 || i >= i1) continue;
+      if (i < i0 || i >= i1 || wave + kWaves * i >= XN) continue;
       auto* dst = (__attribute__((address_space(3))) void*)(xs + buf * XBUF + 1024 * (wave + kWaves * i));
       __builtin_amdgcn_raw_ptr_buffer_load_lds(xrs, dst, 16, xo[i], 2 * kb, 0, 0);
     }
@@ -200,8 +202,8 @@ __device__ __forceinline__ void prefill_body(const GemmArgs& a, const F16Args& d
   // of stage st + 1 are spread over its steps (see the header). The last stage
   // reloads itself there instead (never read), which keeps the steps free of
   // branches. The last step hands over: wait for this wave's activation and scale
-  // loads of stage st + 1 (code pieces 2 and 3, issued after the last activation
-  // load, may still be in flight: the four loads behind it), barrier (tile st + 1
+  // loads of stage st + 1 (only the code loads issued after the last activation
+  // load may still be in flight: 2W of them, 5W with DEEP), barrier (tile st + 1
   // complete everywhere, buffer st % 2 free), and prepare step 0 of stage st + 1.
   const int nst = (int)(K / KC);
   issue_x(0, 0, 0, XPW);
@@ -221,11 +223,12 @@ __device__ __forceinline__ void prefill_body(const GemmArgs& a, const F16Args& d
   // Stage st uses LDS buffer st % 2, scale set st % 2 and (DEEP) code set st % 2.
   // Activation loads of stage st + 1 go out one per step in steps 0..8.
   //   normal: scales of st + 1 at step 0 into the other set, code piece c of st + 1
-  //           at step 4c + 3 (its last use); at the hand-over the four code loads of
+  //           at step 4c + 3 (its last use); at the hand-over the 2W code loads of
   //           steps 11 and 15 may still be in flight;
   //   DEEP:   code piece c of st + 2 at step 9 + c (c < 3) and 15, scales of st + 2
-  //           at step 15, all into this stage's sets; the ten loads after the last
+  //           at step 15, all into this stage's sets; the 5W loads after the last
   //           activation load may be in flight at the hand-over.
+  // (A wave whose activation loads end before step 8 waits for more: still safe.)
   auto stage = [&](int set, int buf, int st) {
     const int kn = (st + 1 < nst ? st + 1 : st) * KC;
     const int kn2 = (st + 2 < nst ? st + 2 : nst - 1) * KC;
@@ -251,10 +254,11 @@ __device__ __forceinline__ void prefill_body(const GemmArgs& a, const F16Args& d
       for (int i = 0; i < NB; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       __builtin_amdgcn_sched_barrier(0);
       if (s + 1 == SPS) {
-        // vmcnt(4) or vmcnt(10); gfx9 encoding: vmcnt[3:0], expcnt[6:4] = 7 (no
-        // wait), lgkmcnt[11:8] = 0
-        if constexpr (DEEP) __builtin_amdgcn_s_waitcnt(0x007A);
-        else __builtin_amdgcn_s_waitcnt(0x0074);
+        // vmcnt(5W) or vmcnt(2W); gfx9 encoding: vmcnt[3:0] (<= 10 here),
+        // expcnt[6:4] = 7 (no wait), lgkmcnt[11:8] = 0
+        constexpr int kVm = DEEP ? 5 * W : 2 * W;
+        static_assert(kVm <= 15, "vmcnt field");
+        __builtin_amdgcn_s_waitcnt(0x0070 | kVm);
         __syncthreads();
       }
     }
@@ -380,8 +384,7 @@ bool prefill_supported(GemmMode mode, int64_t x_rows, int64_t K, int64_t N) {
   return K % KC == 0 && K >= KC && N % 32 == 0 && x_rows * K * 2 < lim && N * (K / 2) < lim;
 }
 
-// Compute units of the current device (cached per device).
-static int cu_count() {
+int cu_count() {
   static int cached[64] = {};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;

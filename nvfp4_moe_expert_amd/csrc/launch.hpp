@@ -34,6 +34,9 @@ struct GemmArgs {
   void* out;               // H / Ypart / Y
 };
 
+// Compute units of the current device (cached per device; 256 if the query fails).
+int cu_count();
+
 // Tile-shape variants of the grouped GEMM.
 //   decode : 16-row tiles, activations read straight into MFMA registers;
 //   prefill: 128-row tiles, activations staged through LDS and shared by 4 waves.

@@ -2,14 +2,17 @@
 //
 // route: one workgroup of 16 waves.
 //   1. histogram of local expert ids, split into P slot ranges (LDS atomics:
-//      counting is order-free);
-//   2. one wavefront turns the per-range counts into exclusive offsets with a
-//      wavefront prefix scan (each lane owns a run of experts, the runs' totals
-//      are scanned across lanes), then into a cursor per (range, expert);
-//      the same wave writes the tile list (expert, first row, rows);
+//      counting is order-free); the lanes of a wave that hold the same expert
+//      add their count with one atomic;
+//   2. every thread owns a run of experts: it totals them over the ranges, a
+//      workgroup prefix scan turns the totals into exclusive offsets, and the
+//      owner turns its counts into a cursor per (range, expert) and writes its
+//      part of the tile list (expert, first row, rows);
 //   3. each range's wave walks its slots in order, 64 at a time: a slot's
 //      rank among earlier lanes with the same expert plus that expert's cursor
 //      is its position, so the order within an expert is slot order (stable).
+//   The lanes holding the same expert are found with one ballot per bit of the
+//   expert id (at most 13), not a pass over the 64 lanes.
 // combine: y[t] = bf16(sum_j w[t,j] * Ypart[t*k+j]) over local slots, j in
 // order - a fixed-order gather instead of a scatter-add, so results are
 // bitwise reproducible (deterministic batch execution, as on the model card
@@ -22,6 +25,19 @@ namespace nvfp4 {
 constexpr int kRouteThreads = 1024;
 constexpr int kRouteWaves = kRouteThreads / 64;
 constexpr int kRouteLdsInts = 16384;   // per-(range, expert) counters: 64 KB
+
+// Lanes of this wave whose value equals this lane's (v in [-1, 2^bits - 1]).
+__device__ __forceinline__ uint64_t match_lanes(int v, int bits) {
+  uint64_t m = __builtin_amdgcn_read_exec();
+  const uint64_t neg = __builtin_amdgcn_ballot_w64(v < 0);
+  m &= (v < 0) ? neg : ~neg;
+  for (int b = 0; b < bits; ++b) {
+    const bool bit = (v >> b) & 1;
+    const uint64_t bal = __builtin_amdgcn_ballot_w64(bit);
+    m &= bit ? bal : ~bal;
+  }
+  return m;
+}
 
 __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
 #pragma unroll
@@ -88,16 +104,27 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   for (int i = tid; i < P * E; i += kRouteThreads) cnt[i] = 0;
   __syncthreads();
-  // 1. histogram per slot range
-  for (int s = tid; s < S; s += kRouteThreads) {
-    int e = ids[s] - eb;
-    if (e >= 0 && e < E) atomicAdd(&cnt[(s / chunk) * E + e], 1);
+  int bits = 0;
+  while ((1 << bits) < E) ++bits;
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  // 1. histogram per slot range; chunk is a multiple of 64, so a wave's 64 slots
+  // lie in one range
+  for (int base = wave * 64; base < S; base += kRouteThreads) {
+    const int s = base + lane;
+    int e = -1;
+    if (s < S) {
+      e = ids[s] - eb;
+      if (e < 0 || e >= E) e = -1;
+    }
+    const uint64_t m = match_lanes(e, bits);
+    if (e >= 0 && (m & below) == 0) atomicAdd(&cnt[(base / chunk) * E + e], __builtin_popcountll(m));
   }
   __syncthreads();
-  // 2. wavefront scan (wave 0)
-  if (wave == 0) {
-    const int run = (E + 63) / 64;
-    const int e0 = min(lane * run, E), e1 = min(e0 + run, E);
+  // 2. per-expert totals, workgroup scan, cursors and tile list
+  {
+    __shared__ int wrows[kRouteWaves], wtl[kRouteWaves];
+    const int run = (E + kRouteThreads - 1) / kRouteThreads;
+    const int e0 = min(tid * run, E), e1 = min(e0 + run, E);
     int rows = 0, ntl = 0;
     for (int e = e0; e < e1; ++e) {
       int tot = 0;
@@ -107,12 +134,22 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
     }
     const int rows_incl = wave_incl_scan(rows, lane);
     const int tl_incl = wave_incl_scan(ntl, lane);
-    int off = rows_incl - rows, toff = tl_incl - ntl;
+    if (lane == 63) {
+      wrows[wave] = rows_incl;
+      wtl[wave] = tl_incl;
+    }
+    __syncthreads();
+    int rbase = 0, tbase = 0;
+    for (int w = 0; w < wave; ++w) {
+      rbase += wrows[w];
+      tbase += wtl[w];
+    }
+    int off = rbase + rows_incl - rows, toff = tbase + tl_incl - ntl;
     for (int e = e0; e < e1; ++e) {
       offsets[e] = off;
       int cur = off;
       for (int p = 0; p < P; ++p) {   // counts -> cursors, range by range
-        int c = cnt[p * E + e];
+        const int c = cnt[p * E + e];
         cnt[p * E + e] = cur;
         cur += c;
       }
@@ -127,9 +164,9 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
       }
       off = cur;
     }
-    if (lane == 63) {
-      offsets[E] = rows_incl;
-      if (n_tiles) *n_tiles = tl_incl;
+    if (tid == kRouteThreads - 1) {
+      offsets[E] = rbase + rows_incl;
+      if (n_tiles) *n_tiles = tbase + tl_incl;
     }
   }
   __syncthreads();
@@ -143,13 +180,8 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
         e = ids[s] - eb;
         if (e < 0 || e >= E) e = -1;
       }
-      int rank = 0, tot = 0;
-      for (int j = 0; j < 64; ++j) {
-        const int ej = __builtin_amdgcn_readlane(e, j);
-        const int same = (ej == e) ? 1 : 0;
-        tot += same;
-        rank += (j < lane) ? same : 0;
-      }
+      const uint64_t m = match_lanes(e, bits);
+      const int rank = __builtin_popcountll(m & below), tot = __builtin_popcountll(m);
       if (e >= 0) {
         const int pos = cnt[wave * E + e] + rank;
         perm[pos] = s;
@@ -182,7 +214,10 @@ hipError_t launch_route(const int32_t* ids, int64_t S, int E, int eb, int tile_r
   return hipGetLastError();
 }
 
-// One thread: 8 consecutive outputs of one token.
+// One thread: 8 consecutive outputs of one token. KM > 0 (k <= KM): the ids,
+// weights and partial rows of all k slots are loaded before the sum, so the
+// loads overlap; the sum runs over j in order either way.
+template <int KM>
 __global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict__ ids,
                                                       const float* __restrict__ w,
                                                       const float* __restrict__ ypart, int64_t T, int k,
@@ -193,17 +228,47 @@ __global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict_
   if (u >= T * per_tok) return;
   const int64_t t = u / per_tok, c8 = u % per_tok;
   float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  for (int j = 0; j < k; ++j) {
-    const int64_t slot = t * k + j;
-    const int e = ids[slot] - eb;
-    if (e < 0 || e >= E) continue;
-    const float wt = w[slot];
-    const f32x4* src = reinterpret_cast<const f32x4*>(ypart + slot * H + c8 * 8);
-    const f32x4 a = src[0], b = src[1];
+  if constexpr (KM > 0) {
+    bool ok[KM];
+    float wt[KM];
+    f32x4 a[KM], b[KM];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      acc[i] += wt * a[i];
-      acc[4 + i] += wt * b[i];
+    for (int j = 0; j < KM; ++j) {
+      const int e = (j < k) ? ids[t * k + j] - eb : -1;
+      ok[j] = e >= 0 && e < E;
+      wt[j] = ok[j] ? w[t * k + j] : 0.0f;
+    }
+#pragma unroll
+    for (int j = 0; j < KM; ++j) {
+      a[j] = b[j] = f32x4{0, 0, 0, 0};
+      if (ok[j]) {
+        const f32x4* src = reinterpret_cast<const f32x4*>(ypart + (t * k + j) * H + c8 * 8);
+        a[j] = src[0];
+        b[j] = src[1];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < KM; ++j) {
+      if (!ok[j]) continue;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[i] += wt[j] * a[j][i];
+        acc[4 + i] += wt[j] * b[j][i];
+      }
+    }
+  } else {
+    for (int j = 0; j < k; ++j) {
+      const int64_t slot = t * k + j;
+      const int e = ids[slot] - eb;
+      if (e < 0 || e >= E) continue;
+      const float wt = w[slot];
+      const f32x4* src = reinterpret_cast<const f32x4*>(ypart + slot * H + c8 * 8);
+      const f32x4 a = src[0], b = src[1];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[i] += wt * a[i];
+        acc[4 + i] += wt * b[i];
+      }
     }
   }
   u32x4 o;
@@ -216,8 +281,10 @@ hipError_t launch_combine(const int32_t* ids, const float* w, const float* ypart
                           int64_t H, int E, int eb, uint16_t* y, hipStream_t s) {
   const int64_t n = T * (H / 8);
   const int64_t gx = (n + 255) / 256;
-  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)gx), dim3(256), 0, s, ids, w, ypart, T, k, H, E,
-                     eb, y);
+  if (k <= 8)
+    hipLaunchKernelGGL(combine_kernel<8>, dim3((unsigned)gx), dim3(256), 0, s, ids, w, ypart, T, k, H, E, eb, y);
+  else
+    hipLaunchKernelGGL(combine_kernel<0>, dim3((unsigned)gx), dim3(256), 0, s, ids, w, ypart, T, k, H, E, eb, y);
   return hipGetLastError();
 }
 
