@@ -24,6 +24,9 @@
 //   is exact in the fp32 accumulator, and 2^-p is applied in the epilogue. The
 //   bf16 form (2 VALU ops per weight) is used where no pre-scaled rows exist.
 // * Activations are staged through LDS (double-buffered, one barrier per stage).
+#include <algorithm>
+#include <mutex>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -32,6 +35,16 @@ namespace nvfp4 {
 namespace decode_detail {
 
 constexpr int kThreads = 256;
+
+// threadIdx.x through an opaque move: in the persistent loop this keeps the
+// compiler from hoisting every per-thread index out of the loop and holding it in
+// registers across the whole item body (it costs one VALU op per item).
+__device__ __forceinline__ int opaque_tid() {
+  int t = (int)threadIdx.x;
+  asm volatile("; opaque" : "+v"(t));
+  __builtin_assume(t >= 0 && t < kThreads);
+  return t;
+}
 constexpr int kBlockN = 64;
 
 template <int SEL>
@@ -79,30 +92,30 @@ using namespace decode_detail;
 // them up front. A row's 128-byte line of scales then is requested once, by its 4
 // lanes together; loaded a stage at a time, the same line is asked for over four
 // stages and a part of those requests misses again (13% more bytes fetched).
+// One work item: tile `tile` (16 rows) x 64-row block `by` of the weights.
 template <int MODE, int U, bool F16, int NS, bool TL>
-__global__ __launch_bounds__(kThreads) void gemm_decode_kernel(GemmArgs a, F16Args d) {
+__device__ __forceinline__ void decode_item(const GemmArgs& a, const F16Args& d,
+                                            uint16_t (&xs)[2][16][128 * U + 8], int tile, int by) {
   constexpr bool kTwo = (MODE == kGateUp || MODE == kGated);
   constexpr bool kMoe = (MODE == kGateUp || MODE == kDown);
   constexpr int KC = 128 * U;          // k per stage
   constexpr int LW = KC + 8;           // LDS row pitch (16-byte pad)
-  __shared__ __attribute__((aligned(16))) uint16_t xs[2][16][LW];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lr = lane & 15, q = lane >> 4;
+  const int tid = opaque_tid(), lane = tid & 63, wave = tid >> 6, lr = lane & 15, q = lane >> 4;
   const int64_t N = a.N, K = a.K;
 
   int e = 0, rb, rows;
   if (kMoe) {
-    if ((int)blockIdx.x >= *a.n_tiles) return;
-    const int32_t* t = a.tiles + 4 * (int64_t)blockIdx.x;
+    const int32_t* t = a.tiles + 4 * (int64_t)tile;
     e = t[0];
     rb = t[1];
     rows = t[2];
   } else {
-    rb = (int)blockIdx.x * 16;
+    rb = tile * 16;
     rows = (int)min((int64_t)16, a.M - rb);
   }
 
-  const int64_t nrow = (int64_t)blockIdx.y * kBlockN + wave * 16 + lr;   // N % 64 == 0
+  const int64_t nrow = (int64_t)by * kBlockN + wave * 16 + lr;   // N % 64 == 0
   const int64_t wrow = (int64_t)e * N + nrow;
   // lane (lr, q): row nrow, inputs [kb + 32Uq, +32U) of each stage
   int64_t coff, soff;
@@ -296,7 +309,7 @@ __global__ __launch_bounds__(kThreads) void gemm_decode_kernel(GemmArgs a, F16Ar
   // ---- epilogue: lane holds D[n = nbase + 4q + r][token lr], r = 0..3
   if (lr >= rows) return;
   const int64_t p = rb + lr;
-  const int64_t n0 = (int64_t)blockIdx.y * kBlockN + wave * 16 + 4 * q;
+  const int64_t n0 = (int64_t)by * kBlockN + wave * 16 + 4 * q;
   float unscale = 1.0f;
   if constexpr (F16 && MODE == kGateUp) unscale = ldexpf(1.0f, -d.xexp[a.perm[p] / a.topk]);
   if constexpr (F16 && MODE == kDown) unscale = ldexpf(1.0f, -row_exponent(d.hmax[p]));
@@ -329,6 +342,30 @@ __global__ __launch_bounds__(kThreads) void gemm_decode_kernel(GemmArgs a, F16Ar
   }
 }
 
+// PER: persistent routed form. The grid holds as many workgroups as fit on the
+// device at once, and workgroup w takes items w, w + grid, ... of the n_tiles x
+// N/64 items (all of the same size), so every workgroup streams the same number
+// of bytes and they end together (one-shot workgroups of the short down
+// projection leave a tail in which too few are live to keep HBM busy).
+template <int MODE, int U, bool F16, int NS, bool TL, bool PER>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(PER ? 3 : 1))) void gemm_decode_kernel(
+    GemmArgs a, F16Args d) {
+  constexpr bool kMoe = (MODE == kGateUp || MODE == kDown);
+  __shared__ __attribute__((aligned(16))) uint16_t xs[2][16][128 * U + 8];
+  if constexpr (PER) {
+    static_assert(kMoe, "persistent form is for the routed modes");
+    const int nby = (int)(a.N / kBlockN);
+    const int total = *a.n_tiles * nby;   // <= grid_tiles * nby < 2^31 (host)
+    for (int it = blockIdx.x; it < total; it += gridDim.x) {
+      __syncthreads();   // the previous item's last LDS reads are done
+      decode_item<MODE, U, F16, NS, TL>(a, d, xs, it / nby, it % nby);
+    }
+  } else {
+    if (kMoe && (int)blockIdx.x >= *a.n_tiles) return;
+    decode_item<MODE, U, F16, NS, TL>(a, d, xs, (int)blockIdx.x, (int)blockIdx.y);
+  }
+}
+
 // Routed down projection (fp16 form) with K <= 2048 (K = I): the whole
 // activation tile (<= 16 rows x K) is staged in LDS once, and each wave then
 // streams NB consecutive 64-row blocks of weights (its 16 rows of each) with the
@@ -336,33 +373,32 @@ __global__ __launch_bounds__(kThreads) void gemm_decode_kernel(GemmArgs a, F16Ar
 // blocks: with the per-stage tile (K / 512 = 3 stages for K = 1536) the short
 // workgroups spent a large part of their life filling the pipeline.
 template <int MODE, bool F16, int NST, int NB, bool TL>
-__global__ __launch_bounds__(kThreads) void gemm_decode_res_kernel(GemmArgs a, F16Args d) {
+__device__ __forceinline__ void res_item(const GemmArgs& a, const F16Args& d, uint16_t (&xs)[16][NST * 512 + 8],
+                                         int tile, int by) {
   static_assert(MODE == kDown || MODE == kLinear, "one-weight modes");
   constexpr bool kMoe = (MODE == kDown);
-  constexpr int U = 4, KC = 128 * U, KT = NST * KC, LW = KT + 8;
+  constexpr int U = 4, KC = 128 * U, KT = NST * KC;
   constexpr int G = NB * NST;   // stages of a wave's stream
   constexpr int LA = 2;         // stages in flight ahead of the one multiplied
   constexpr int XU = 16 * (KT / 8) / kThreads;   // 16-byte activation units per thread
-  __shared__ __attribute__((aligned(16))) uint16_t xs[16][LW];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lr = lane & 15, q = lane >> 4;
+  const int tid = opaque_tid(), lane = tid & 63, wave = tid >> 6, lr = lane & 15, q = lane >> 4;
   const int64_t N = a.N;
 
   int e = 0, rb, rows;
   if (kMoe) {
-    if ((int)blockIdx.x >= *a.n_tiles) return;
-    const int32_t* t = a.tiles + 4 * (int64_t)blockIdx.x;
+    const int32_t* t = a.tiles + 4 * (int64_t)tile;
     e = t[0];
     rb = t[1];
     rows = t[2];
   } else {
-    rb = (int)blockIdx.x * 16;
+    rb = tile * 16;
     rows = (int)min((int64_t)16, a.M - rb);
   }
 
   // block j of this wave: rows nrow + 64j; in both layouts 64 rows are 32*K code
   // bytes and 4*K scale bytes further on
-  const int64_t nrow = (int64_t)blockIdx.y * (kBlockN * NB) + wave * 16 + lr;
+  const int64_t nrow = (int64_t)by * (kBlockN * NB) + wave * 16 + lr;
   int64_t coff, soff;
   if constexpr (TL) {
     const int64_t R = nrow / 32, r = nrow % 32;
@@ -454,7 +490,7 @@ __global__ __launch_bounds__(kThreads) void gemm_decode_res_kernel(GemmArgs a, F
     if (g % NST == NST - 1) {
       // block g / NST done: lane holds D[n = n0 + 4q + r][token lr]
       if (live) {
-        const int64_t n0 = (int64_t)blockIdx.y * (kBlockN * NB) + (g / NST) * kBlockN + wave * 16 + 4 * q;
+        const int64_t n0 = (int64_t)by * (kBlockN * NB) + (g / NST) * kBlockN + wave * 16 + 4 * q;
         if constexpr (MODE == kDown) {
           *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.out) + orow * N + n0) =
               f32x4{s2 * acc[0], s2 * acc[1], s2 * acc[2], s2 * acc[3]};
@@ -467,12 +503,68 @@ __global__ __launch_bounds__(kThreads) void gemm_decode_res_kernel(GemmArgs a, F
       }
       acc = f32x4{0, 0, 0, 0};
     }
+    // keep each stage's LDS reads inside the stage: hoisting later stages' B
+    // operands ahead (nothing orders them after the staging barrier) costs more
+    // registers than the workgroups per CU can spare
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+template <int MODE, bool F16, int NST, int NB, bool TL, bool PER>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(PER ? 3 : 1))) void gemm_decode_res_kernel(
+    GemmArgs a, F16Args d) {
+  constexpr bool kMoe = (MODE == kDown);
+  __shared__ __attribute__((aligned(16))) uint16_t xs[16][NST * 512 + 8];
+  if constexpr (PER) {
+    static_assert(kMoe, "persistent form is for the routed modes");
+    const int nby = (int)(a.N / (kBlockN * NB));
+    const int total = *a.n_tiles * nby;   // <= grid_tiles * nby < 2^31 (host)
+    for (int it = blockIdx.x; it < total; it += gridDim.x) {
+      __syncthreads();   // the previous item's last LDS reads are done
+      res_item<MODE, F16, NST, NB, TL>(a, d, xs, it / nby, it % nby);
+    }
+  } else {
+    if (kMoe && (int)blockIdx.x >= *a.n_tiles) return;
+    res_item<MODE, F16, NST, NB, TL>(a, d, xs, (int)blockIdx.x, (int)blockIdx.y);
   }
 }
 
 bool decode_supported(GemmMode mode, int64_t K, int64_t N) {
   (void)mode;
   return N % kBlockN == 0 && K % 256 == 0 && K >= 256;
+}
+
+// Workgroups of `kern` resident on the current device at once (cached).
+static int64_t resident_wgs(const void* kern) {
+  static std::mutex mu;
+  static struct { const void* k; int dev; int64_t n; } cache[128];
+  static int used = 0;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = -1;
+  std::lock_guard<std::mutex> lock(mu);
+  for (int i = 0; i < used; ++i)
+    if (cache[i].k == kern && cache[i].dev == dev) return cache[i].n;
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, kThreads, 0) != hipSuccess || per_cu < 1) per_cu = 1;
+  const int64_t n = (int64_t)per_cu * cu_count();
+  if (used < 128) cache[used++] = {kern, dev, n};
+  return n;
+}
+
+// One-shot grid (tiles, N / rows per workgroup), or (persistent != null) a
+// persistent grid of at most the resident workgroup count.
+static void launch_items(const void* one_shot, const void* persistent, int64_t grid_tiles, int64_t nby,
+                         const GemmArgs& a, const F16Args& d, hipStream_t s) {
+  GemmArgs aa = a;
+  F16Args dd = d;
+  void* args[] = {&aa, &dd};
+  const int64_t items = grid_tiles * nby;
+  if (persistent && items < ((int64_t)1 << 31)) {   // the kernel counts items in 32 bits
+    const int64_t g = std::min(items, resident_wgs(persistent));
+    (void)hipLaunchKernel(persistent, dim3((unsigned)g), dim3(kThreads), args, 0, s);
+  } else {
+    (void)hipLaunchKernel(one_shot, dim3((unsigned)grid_tiles, (unsigned)nby), dim3(kThreads), args, 0, s);
+  }
 }
 
 template <int MODE, bool F16, bool TL>
@@ -484,10 +576,11 @@ static hipError_t launch_dec(const GemmArgs& a, const F16Args& d, int64_t grid_t
       const int64_t want = 4 * (int64_t)cu_count();
       const int nb = grid_tiles * (a.N / (kBlockN * 4)) >= want ? 4 : grid_tiles * (a.N / (kBlockN * 2)) >= want ? 2 : 1;
       switch (nb * 8 + (int)(a.K / 512)) {
-#define NVFP4_RES(NB_, NST_)                                                                                    \
-  case NB_ * 8 + NST_:                                                                                           \
-    hipLaunchKernelGGL((gemm_decode_res_kernel<MODE, F16, NST_, NB_, TL>),                                     \
-                       dim3((unsigned)grid_tiles, (unsigned)(a.N / (kBlockN * NB_))), dim3(kThreads), 0, s, a, d); \
+#define NVFP4_RES(NB_, NST_)                                                                          \
+  case NB_ * 8 + NST_:                                                                                 \
+    launch_items((const void*)gemm_decode_res_kernel<MODE, F16, NST_, NB_, TL, false>,                \
+                 (const void*)gemm_decode_res_kernel<MODE, F16, NST_, NB_, TL, true>, grid_tiles,       \
+                 a.N / (kBlockN * NB_), a, d, s);                                                      \
     break;
         NVFP4_RES(1, 1) NVFP4_RES(1, 2) NVFP4_RES(1, 3) NVFP4_RES(1, 4)
         NVFP4_RES(2, 1) NVFP4_RES(2, 2) NVFP4_RES(2, 3) NVFP4_RES(2, 4)
@@ -498,14 +591,21 @@ static hipError_t launch_dec(const GemmArgs& a, const F16Args& d, int64_t grid_t
       return hipGetLastError();
     }
   }
-  const dim3 grid((unsigned)grid_tiles, (unsigned)(a.N / kBlockN));
+  const int64_t nby = a.N / kBlockN;
+  // persistent for the routed down projection (its workgroups are short); the
+  // gate/up loop body would need more registers than three waves per SIMD allow
+#define NVFP4_DEC(U_, NS_)                                                                                      \
+  launch_items((const void*)gemm_decode_kernel<MODE, U_, F16, NS_, TL, false>,                                  \
+               MODE == kDown ? (const void*)gemm_decode_kernel<MODE, U_, F16, NS_, TL, MODE == kDown> : nullptr, \
+               grid_tiles, nby, a, d, s)
   if (a.K % 512 == 0) {
-    if (a.K / 512 <= NS) hipLaunchKernelGGL((gemm_decode_kernel<MODE, 4, F16, NS, TL>), grid, dim3(kThreads), 0, s, a, d);
-    else hipLaunchKernelGGL((gemm_decode_kernel<MODE, 4, F16, 0, TL>), grid, dim3(kThreads), 0, s, a, d);
+    if (a.K / 512 <= NS) NVFP4_DEC(4, NS);
+    else NVFP4_DEC(4, 0);
   } else {
-    if (a.K / 256 <= NS) hipLaunchKernelGGL((gemm_decode_kernel<MODE, 2, F16, NS, TL>), grid, dim3(kThreads), 0, s, a, d);
-    else hipLaunchKernelGGL((gemm_decode_kernel<MODE, 2, F16, 0, TL>), grid, dim3(kThreads), 0, s, a, d);
+    if (a.K / 256 <= NS) NVFP4_DEC(2, NS);
+    else NVFP4_DEC(2, 0);
   }
+#undef NVFP4_DEC
   return hipGetLastError();
 }
 
