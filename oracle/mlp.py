@@ -25,8 +25,8 @@ from __future__ import annotations
 
 import numpy as np
 
-from .formats import bf16_to_f32
-from .nvfp4 import dequant_unscaled
+from .formats import bf16_to_f32, f32_to_bf16
+from .nvfp4 import dequant_unscaled, quantize_act
 
 F64 = np.float64
 
@@ -121,4 +121,49 @@ def moe(x_bits, ids, weights, gate, up, down, expert_begin: int = 0, return_slot
         y += w[:, j:j + 1] * slots[:, j]
     if return_slots:
         return y, slots
+    return y
+
+
+def act_fake_quant(x_bits, input_scale) -> np.ndarray:
+    """bf16 activations -> the values their static NVFP4 quantization represents,
+    e2m1(code) * e4m3(byte) * input_scale, float64 (exact: a 6-significant-bit
+    value times a float32)."""
+    codes, scales = quantize_act(x_bits, input_scale)
+    return dequant_unscaled(codes, scales) * F64(np.float32(input_scale))
+
+
+def moe_w4a4(x_bits, ids, weights, gate, up, down, in_scale_gu, in_scale_d, expert_begin: int = 0):
+    """Routed expert MLP with W4A4 activations (the checkpoint's own FP4 x FP4 math,
+    TensorFold issue #308, "What the branch does" and "Questions", item 1; model
+    card "GLM-5.3-Flash-NVFP4-W4A4-Experts", "Quantization boundary").
+
+    As ``moe``, with two activation quantizations, each against one calibrated
+    scale for all experts of the layer (the card's activation-scale policy takes a
+    percentile across experts per projection):
+      x_t -> act_fake_quant(x_t, in_scale_gu) before gate/up;
+      h   -> bf16(h) (rounded through float32, as the intermediate is stored), then
+             act_fake_quant(., in_scale_d) before down.
+    The contractions are float64 as in ``moe``."""
+    xq = act_fake_quant(x_bits, in_scale_gu)
+    ids = np.asarray(ids, dtype=np.int64)
+    w = np.asarray(weights, dtype=np.float32).astype(F64)
+    T, k = ids.shape
+    H = xq.shape[1]
+    E = gate[0].shape[0]
+    y = np.zeros((T, H), F64)
+    slots = np.zeros((T, k, H), F64)
+    for e in range(E):
+        tt, jj = np.nonzero(ids == e + expert_begin)
+        if tt.size == 0:
+            continue
+        wg, s2g = _w64((gate[0][e], gate[1][e], gate[2][e]))
+        wu, s2u = _w64((up[0][e], up[1][e], up[2][e]))
+        wd, s2d = _w64((down[0][e], down[1][e], down[2][e]))
+        xe = xq[tt]
+        h = silu(s2g * (xe @ wg.T)) * (s2u * (xe @ wu.T))
+        h_bits = f32_to_bf16(h.astype(np.float32))
+        hq = act_fake_quant(h_bits, in_scale_d)
+        slots[tt, jj] = s2d * (hq @ wd.T)
+    for j in range(k):
+        y += w[:, j:j + 1] * slots[:, j]
     return y

@@ -22,6 +22,15 @@ correctly rounded division and no fused multiply-add:
   5. two codes per byte, even k in the low nibble.
 Readings for the degenerate cases: a tensor that is all zero gets scale_2 = 0,
 scale bytes 0 and codes 0; a block whose s_eff is 0 gets codes 0.
+
+Static activation quantization (the W4A4 form of the model card
+"GLM-5.3-Flash-NVFP4-W4A4-Experts", section "Quantization boundary": NVFP4
+weights with calibrated activation scales; TensorFold issue #308 notes that an
+input_scale is stored beside each weight). Reading: an activation row is
+quantized by steps 3-5 above with the calibrated input_scale in the place of
+scale_2; nothing is computed from the activations' own amax. A block whose
+amax exceeds 6 * 448 * input_scale saturates: its scale byte is 0x7E and its
+codes clamp at 6.
 """
 from __future__ import annotations
 
@@ -33,6 +42,27 @@ GROUP = 16
 F32 = np.float32
 
 
+def _quantize_blocks(w: np.ndarray, gscale):
+    """Steps 3-5 of the recipe for float32 values w [N, K] against the global scale
+    gscale (scale_2, or an activation's input_scale): (codes [N, K/2], scale bytes [N, K/16])."""
+    N, K = w.shape
+    gscale = F32(gscale)
+    if gscale == 0:
+        return np.zeros((N, K // 2), np.uint8), np.zeros((N, K // GROUP), np.uint8)
+    blocks = w.reshape(N, K // GROUP, GROUP)
+    bamax = np.max(np.abs(blocks), axis=2)               # float32, exact
+    with np.errstate(over="ignore"):
+        v = (bamax / F32(6.0)) / gscale                  # two correctly rounded fp32 divisions
+    sbyte = e4m3_encode(v)
+    s_eff = e4m3_decode(sbyte).astype(F32) * gscale      # one fp32 rounding
+    with np.errstate(divide="ignore", invalid="ignore"):
+        q = blocks / s_eff[:, :, None]                    # fp32 division
+    code = e2m1_encode(np.where(s_eff[:, :, None] == 0, F32(0.0), q))
+    code = np.where(s_eff[:, :, None] == 0, np.uint8(0), code).reshape(N, K)
+    codes = (code[:, 0::2] | (code[:, 1::2] << 4)).astype(np.uint8)
+    return codes, sbyte.astype(np.uint8)
+
+
 def pack(w_bits: np.ndarray):
     """One tensor: bf16 bits [N, K] -> (codes uint8 [N,K/2], scales uint8 [N,K/16], scale_2 float32)."""
     w_bits = np.asarray(w_bits, dtype=np.uint16)
@@ -42,19 +72,18 @@ def pack(w_bits: np.ndarray):
     w = bf16_to_f32(w_bits)                               # exact
     amax = F32(np.max(np.abs(w))) if w.size else F32(0)
     scale_2 = F32(amax / F32(2688.0))
-    if scale_2 == 0:
-        return (np.zeros((N, K // 2), np.uint8), np.zeros((N, K // GROUP), np.uint8), F32(0.0))
-    blocks = w.reshape(N, K // GROUP, GROUP)
-    bamax = np.max(np.abs(blocks), axis=2)               # float32, exact
-    v = (bamax / F32(6.0)) / scale_2                     # two correctly rounded fp32 divisions
-    sbyte = e4m3_encode(v)
-    s_eff = e4m3_decode(sbyte).astype(F32) * scale_2     # one fp32 rounding
-    with np.errstate(divide="ignore", invalid="ignore"):
-        q = blocks / s_eff[:, :, None]                    # fp32 division
-    code = e2m1_encode(np.where(s_eff[:, :, None] == 0, F32(0.0), q))
-    code = np.where(s_eff[:, :, None] == 0, np.uint8(0), code).reshape(N, K)
-    codes = (code[:, 0::2] | (code[:, 1::2] << 4)).astype(np.uint8)
-    return codes, sbyte.astype(np.uint8), scale_2
+    codes, sbyte = _quantize_blocks(w, scale_2)
+    return codes, sbyte, scale_2
+
+
+def quantize_act(x_bits: np.ndarray, input_scale):
+    """Static NVFP4 activation quantization: bf16 bits [M, K] and a calibrated fp32
+    input_scale -> (codes uint8 [M, K/2], scale bytes uint8 [M, K/16]). The value
+    represented is e2m1(code) * e4m3(byte) * input_scale."""
+    x_bits = np.asarray(x_bits, dtype=np.uint16)
+    if x_bits.shape[-1] % GROUP:
+        raise ValueError("K must be a multiple of 16")
+    return _quantize_blocks(bf16_to_f32(x_bits), input_scale)
 
 
 def pack_batch(w_bits: np.ndarray):

@@ -13,6 +13,7 @@ import oracle.nvfp4
 import test_oracle_formats as TF
 import test_oracle_mlp as TM
 import test_oracle_pack as TP
+import test_oracle_w4a4 as TW
 
 
 @contextlib.contextmanager
@@ -39,9 +40,9 @@ def _fails(fn, *args):
 
 MUTANTS = [
     # (module, function, anchor, replacement, pins that must catch it)
-    (oracle.nvfp4, "pack", "code[:, 0::2] | (code[:, 1::2] << 4)", "code[:, 1::2] | (code[:, 0::2] << 4)",
+    (oracle.nvfp4, "_quantize_blocks", "code[:, 0::2] | (code[:, 1::2] << 4)", "code[:, 1::2] | (code[:, 0::2] << 4)",
      [TP.test_pack_golden_hand_derived, TP.test_nibble_order_against_brute_weight]),
-    (oracle.nvfp4, "pack", "(bamax / F32(6.0)) / scale_2", "bamax / scale_2",
+    (oracle.nvfp4, "_quantize_blocks", "(bamax / F32(6.0)) / gscale", "bamax / gscale",
      [lambda: TP.test_pack_invariants(0), TP.test_pack_golden_hand_derived]),
     (oracle.nvfp4, "pack", "F32(amax / F32(2688.0))", "F32(amax / F32(448.0))",
      [lambda: TP.test_pack_invariants(0), TP.test_pack_golden_hand_derived]),
@@ -66,6 +67,15 @@ MUTANTS = [
      [TM.test_moe_vs_brute]),
     (oracle.mlp, "route", "perm_parts.append(slots)", "perm_parts.append(slots[::-1])",
      [lambda: TM.test_route_vs_stable_argsort_and_brute(20, 3, 5, 10, 0, 30)]),
+    # W4A4: the activation's own amax in place of the calibrated scale; a dropped
+    # input scale; H quantized against the gate/up scale
+    (oracle.nvfp4, "quantize_act", "_quantize_blocks(bf16_to_f32(x_bits), input_scale)",
+     "_quantize_blocks(bf16_to_f32(x_bits), F32(np.max(np.abs(bf16_to_f32(x_bits))) / F32(2688.0)))",
+     [lambda: TW.test_quantize_act_round_trip_on_grid(1.0), TW.test_quantize_act_saturation_hand_derived]),
+    (oracle.mlp, "act_fake_quant", "dequant_unscaled(codes, scales) * F64(np.float32(input_scale))",
+     "dequant_unscaled(codes, scales)", [TW.test_moe_w4a4_k1_reduces_to_pinned_dense_pieces]),
+    (oracle.mlp, "moe_w4a4", "hq = act_fake_quant(h_bits, in_scale_d)", "hq = act_fake_quant(h_bits, in_scale_gu)",
+     [TW.test_moe_w4a4_k1_reduces_to_pinned_dense_pieces]),
 ]
 
 
