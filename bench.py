@@ -55,7 +55,7 @@ def parse():
     p.add_argument("--tokens", type=int, default=64, help="decode batch of the headline step")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-extras", action="store_true", help="only the headline decode step")
-    p.add_argument("--only", choices=["decode", "prefill", "dense", "pack"], default=None,
+    p.add_argument("--only", choices=["decode", "prefill", "dense", "pack", "w4a4"], default=None,
                    help="run one workload only (profiling runs); prints its figures")
     p.add_argument("--layout", choices=["tiled", "rows"], default="tiled",
                    help="weight layout in HBM: blocks of 32 rows (tiled) or row-major")
@@ -150,6 +150,71 @@ def main():
             "gateup_bytes_per_launch": gateup_bytes / steps,
         }
 
+    def w4a4_scales():
+        """Synthetic calibration following the model card's policy (per expert the
+        amax of each projection's input, the 99th percentile across experts, a 5%
+        margin, / 2688) on 18 of the 288 experts and 256 N(0, 1) calibration rows,
+        in fp32 on the dequantized weights. The scales decide how often a block
+        saturates, not how much work a call does."""
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(77)
+        xf = torch.randn((256, H), generator=gen, device=dev).to(torch.bfloat16).float()
+        ax, ah = [], []
+        for e in range(0, E, 16):
+            _, gs = nv.dequant(layer["gate"].expert(e), unscaled=False)
+            _, us = nv.dequant(layer["up"].expert(e), unscaled=False)
+            hh = torch.nn.functional.silu(xf @ gs[0].T) * (xf @ us[0].T)
+            ax.append(xf.abs().max().item())
+            ah.append(hh.abs().max().item())
+        f = lambda a: float(np.float32(1.05 * np.percentile(a, 99) / 2688.0))
+        return torch.tensor([f(ax), f(ah)], dtype=torch.float32, device=dev)
+
+    def run_w4a4(T_dec, steps, warmup):
+        """W4A4 activations (nvfp4_moe_grouped_w4a4): the decode step at T_dec and
+        the prefill layer, plain timed loops."""
+        log(f"W4A4: decode T={T_dec}, prefill T=4096")
+        sc = w4a4_scales()
+        x, ids, w, touched = decode_inputs(T_dec, 3)
+        ws = torch.empty((nv.moe_workspace_size(T_dec, K_TOP, E, H, I),), dtype=torch.uint8, device=dev)
+        out = torch.empty((T_dec, H), dtype=torch.bfloat16, device=dev)
+        call = lambda r: nv.moe_grouped(x[r], ids[r], w[r], layer["gate"], layer["up"], layer["down"], workspace=ws,
+                                        out=out, input_scales=sc)
+        for i in range(warmup):
+            call(i % ROTATE)
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for i in range(steps):
+            call((warmup + i) % ROTATE)
+        t1.record()
+        torch.cuda.synchronize()
+        ms = t0.elapsed_time(t1)
+        dec_bytes = sum(alg_bytes(T_dec, touched[(warmup + i) % ROTATE]) for i in range(steps))
+        Tp = 4096
+        ids_np, w_np = synth.zipf_routing(Tp, E, K_TOP, 1.1, 4, synth.S_ROUTE)
+        xp = torch.from_numpy(synth.bf16_normal((Tp, H), 1.0, 4, synth.S_X).view(np.int16)).view(torch.bfloat16).to(dev)
+        idp, wp = torch.from_numpy(ids_np).to(dev), torch.from_numpy(w_np).to(dev)
+        wsp = torch.empty((nv.moe_workspace_size(Tp, K_TOP, E, H, I),), dtype=torch.uint8, device=dev)
+        outp = torch.empty((Tp, H), dtype=torch.bfloat16, device=dev)
+        pcall = lambda: nv.moe_grouped(xp, idp, wp, layer["gate"], layer["up"], layer["down"], workspace=wsp,
+                                       out=outp, input_scales=sc)
+        for _ in range(3):
+            pcall()
+        torch.cuda.synchronize()
+        psteps = max(3, min(steps, 20))
+        t0.record()
+        for _ in range(psteps):
+            pcall()
+        t1.record()
+        torch.cuda.synchronize()
+        pms = t0.elapsed_time(t1) / psteps
+        flops = 6.0 * Tp * K_TOP * H * I
+        return {"input_scales": [round(v, 9) for v in sc.tolist()],
+                f"decode_T{T_dec}": {"GB/s": round(dec_bytes / (ms * 1e-3) / 1e9, 1), "ms_per_step": round(ms / steps, 5),
+                                     "frac_hbm": round(dec_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+                "prefill_T4096_zipf": {"TFLOP/s": round(flops / pms / 1e9, 2), "ms_per_call": round(pms, 4),
+                                       "frac_mfma_bf16": round(flops / pms / 1e9 / MFMA_BF16_PEAK_TFLOPS, 4)}}
+
     def run_prefill():
         log("prefill T=4096 Zipf(1.1)")
         Tp = 4096
@@ -235,7 +300,8 @@ def main():
     if args.only is not None:
         # one workload alone (profiling runs): its figures only, no headline line
         fig = {"decode": lambda: run_decode(args.tokens, args.steps, args.warmup), "prefill": run_prefill,
-               "dense": run_dense, "pack": run_pack}[args.only]()
+               "dense": run_dense, "pack": run_pack,
+               "w4a4": lambda: run_w4a4(args.tokens, args.steps, args.warmup)}[args.only]()
         print(json.dumps({"only": args.only, **fig}), flush=True)
         return
 
@@ -288,6 +354,7 @@ def main():
         result["prefill"] = run_prefill()
         result["dense_mlp"] = run_dense()
         result["pack"] = run_pack()
+        result["w4a4"] = run_w4a4(args.tokens, args.steps, args.warmup)
 
         # the same headline step on the other weight layout (same values, other byte order)
         other = "rows" if args.layout == "tiled" else "tiled"

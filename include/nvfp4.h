@@ -70,7 +70,7 @@
 extern "C" {
 #endif
 
-#define NVFP4_ABI_VERSION 2
+#define NVFP4_ABI_VERSION 3
 
 #define NVFP4_LAYOUT_ROWS 0
 #define NVFP4_LAYOUT_TILED32 1
@@ -81,7 +81,7 @@ typedef enum nvfp4_status {
   NVFP4_ERR_SHAPE = 2,       /* inconsistent or unsupported sizes (k % 32 != 0, n < 1, ...) */
   NVFP4_ERR_ALIGN = 3,       /* a pointer is not 16-byte aligned */
   NVFP4_ERR_WORKSPACE = 4,   /* workspace missing or smaller than the *_workspace_size() figure */
-  NVFP4_ERR_UNSUPPORTED = 5, /* a request outside W4A16 (e.g. FP4 activations) */
+  NVFP4_ERR_UNSUPPORTED = 5, /* a request the kernels do not cover (e.g. W4A4 on fallback shapes) */
   NVFP4_ERR_HIP = 6          /* the HIP runtime reported an error when enqueueing */
 } nvfp4_status;
 
@@ -220,6 +220,50 @@ nvfp4_status nvfp4_moe_grouped_timed(const uint16_t* x, int64_t T, int64_t H,
                                      const nvfp4_weight_t* up, const nvfp4_weight_t* down,
                                      void* ws, size_t ws_bytes, uint16_t* y, void* stream,
                                      void* const* events);
+
+/*
+ * nvfp4_quantize_act - static NVFP4 quantization of bf16 activations, the W4A4
+ * form (model card "GLM-5.3-Flash-NVFP4-W4A4-Experts", section "Quantization
+ * boundary": NVFP4 weights with calibrated activations; TensorFold issue #308,
+ * section "The checkpoint": an input_scale is stored beside each weight).
+ *
+ * Each 16-block of a row is quantized by the pack's block steps with the
+ * calibrated input_scale in place of scale_2: byte = e4m3_rne(block_amax / 6 /
+ * input_scale) (saturating at 448: larger activations clamp), code =
+ * e2m1_rne(x / (e4m3(byte) * input_scale)). Nothing depends on the row's own amax.
+ *
+ *   x            [rows, k] bf16, device, 16-byte aligned.
+ *   input_scale  one fp32 in device memory (4-byte aligned); 0 gives all-zero output.
+ *   codes        [rows, k/2] out, device, 16-byte aligned (even k in the low nibble).
+ *   scales       [rows, k/16] out (e4m3 bytes), device, 16-byte aligned.
+ * Errors: ERR_SHAPE unless k % 32 == 0, k >= 32 and 0 <= rows <= 2^30; ERR_NULL,
+ * ERR_ALIGN as stated; rows == 0 is a no-op.
+ */
+nvfp4_status nvfp4_quantize_act(const uint16_t* x, int64_t rows, int64_t k, const float* input_scale,
+                                uint8_t* codes, uint8_t* scales, void* stream);
+
+/*
+ * nvfp4_moe_grouped_w4a4 - the routed expert MLP with W4A4 activations (the
+ * checkpoint's own FP4 x FP4 math that TensorFold issue #308 defers, "What the
+ * branch does" and "Questions", item 1).
+ *
+ * As nvfp4_moe_grouped (same arguments, workspace size, ownership and errors),
+ * plus two calibrated activation scales, each one fp32 in device memory, shared
+ * by all experts of the layer (the model card's activation-scale policy takes a
+ * percentile across experts per projection):
+ *   input_scale_gate_up - x is quantized (nvfp4_quantize_act) before gate/up;
+ *   input_scale_down    - H, rounded to bf16 as stored, is quantized before down.
+ * The quantized values e2m1 * e4m3 are exact in fp16, so the GEMMs run on them
+ * exactly and the input scales multiply the fp32 results. ERR_NULL if either
+ * scale pointer is null; ERR_UNSUPPORTED for shapes that only the fallback GEMM
+ * covers (H and I multiples of 256 with N multiples of 32/64 are covered).
+ */
+nvfp4_status nvfp4_moe_grouped_w4a4(const uint16_t* x, int64_t T, int64_t H, const int32_t* topk_ids,
+                                    const float* topk_w, int32_t k, int32_t expert_begin,
+                                    const nvfp4_weight_t* gate, const nvfp4_weight_t* up,
+                                    const nvfp4_weight_t* down, const float* input_scale_gate_up,
+                                    const float* input_scale_down, void* ws, size_t ws_bytes, uint16_t* y,
+                                    void* stream);
 
 #ifdef __cplusplus
 }

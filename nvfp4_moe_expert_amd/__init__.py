@@ -69,6 +69,9 @@ _SIGNATURES = {
     "nvfp4_moe_grouped": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _I32, _I32, _WP, _WP, _WP, _P, _SZ, _P, _P]),
     "nvfp4_moe_grouped_timed": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _I32, _I32, _WP, _WP, _WP, _P, _SZ, _P,
                                                _P, ctypes.POINTER(_P)]),
+    "nvfp4_moe_grouped_w4a4": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _I32, _I32, _WP, _WP, _WP, _P, _P, _P, _SZ,
+                                              _P, _P]),
+    "nvfp4_quantize_act": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _P, _P]),
 }
 
 
@@ -260,13 +263,22 @@ def moe_workspace_size(T: int, k: int, n_experts: int, H: int, I: int) -> int:
 
 def moe_grouped(x: torch.Tensor, topk_ids: torch.Tensor, topk_w: torch.Tensor, gate: NVFP4Weight,
                 up: NVFP4Weight, down: NVFP4Weight, expert_begin: int = 0, workspace: torch.Tensor | None = None,
-                out: torch.Tensor | None = None, events=None) -> torch.Tensor:
+                out: torch.Tensor | None = None, events=None, input_scales=None) -> torch.Tensor:
     """Routed expert MLP of one MoE layer: y[T, H] bf16.
 
     events: optional sequence of 5 torch.cuda.Event; the library records them on the
     current stream before the first kernel and after the route, gate/up, down and
-    combine stages."""
+    combine stages.
+    input_scales: None (W4A16), or a float32 device tensor [2] holding the
+    calibrated activation scales (gate/up input, down input) for W4A4
+    (nvfp4_moe_grouped_w4a4; not combined with events)."""
     lib = load_library()
+    if input_scales is not None:
+        _need(input_scales, torch.float32, "input_scales", 1)
+        if input_scales.numel() != 2:
+            raise ValueError("input_scales must hold 2 floats (gate/up input, down input)")
+        if events is not None:
+            raise ValueError("events are not recorded by the W4A4 entry point")
     _need(x, torch.bfloat16, "x", 2)
     _need(topk_ids, torch.int32, "topk_ids", 2)
     _need(topk_w, torch.float32, "topk_w", 2)
@@ -285,6 +297,10 @@ def moe_grouped(x: torch.Tensor, topk_ids: torch.Tensor, topk_w: torch.Tensor, g
     g, u, d = gate._struct(), up._struct(), down._struct()
     args = (_ptr(x), T, H, _ptr(topk_ids), _ptr(topk_w), k, expert_begin, ctypes.byref(g), ctypes.byref(u),
             ctypes.byref(d), _ptr(workspace), workspace.numel(), _ptr(out), _stream())
+    if input_scales is not None:
+        st = lib.nvfp4_moe_grouped_w4a4(*args[:10], _ptr(input_scales), _ptr(input_scales[1:]), *args[10:])
+        _check(st, "nvfp4_moe_grouped_w4a4")
+        return out
     if events is None:
         st = lib.nvfp4_moe_grouped(*args)
     else:
@@ -297,3 +313,18 @@ def moe_grouped(x: torch.Tensor, topk_ids: torch.Tensor, topk_w: torch.Tensor, g
         st = lib.nvfp4_moe_grouped_timed(*args, arr)
     _check(st, "nvfp4_moe_grouped")
     return out
+
+
+def quantize_act(x: torch.Tensor, input_scale: torch.Tensor):
+    """Static NVFP4 activation quantization (W4A4): bf16 x [rows, k] and a float32
+    device tensor holding the calibrated input_scale -> (codes uint8 [rows, k/2],
+    scales uint8 [rows, k/16])."""
+    lib = load_library()
+    _need(x, torch.bfloat16, "x", 2)
+    _need(input_scale, torch.float32, "input_scale", 1)
+    rows, k = x.shape
+    codes = torch.empty((rows, k // 2), dtype=torch.uint8, device=x.device)
+    scales = torch.empty((rows, k // 16), dtype=torch.uint8, device=x.device)
+    st = lib.nvfp4_quantize_act(_ptr(x), rows, k, _ptr(input_scale), _ptr(codes), _ptr(scales), _stream())
+    _check(st, "nvfp4_quantize_act")
+    return codes, scales

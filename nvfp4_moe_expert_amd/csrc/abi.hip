@@ -89,10 +89,15 @@ T* at(void* base, size_t off) {
   return reinterpret_cast<T*>(reinterpret_cast<char*>(base) + off);
 }
 
+// in_gu / in_d: null for W4A16; for W4A4 the device pointers of the two calibrated
+// activation input scales (gate/up input x, down input H).
 nvfp4_status moe_impl(const uint16_t* x, int64_t T, int64_t H, const int32_t* ids, const float* tw,
                       int32_t k, int32_t eb, const nvfp4_weight_t* gate, const nvfp4_weight_t* up,
                       const nvfp4_weight_t* down, void* ws, size_t ws_bytes, uint16_t* y,
-                      hipStream_t s, void* const* events) {
+                      hipStream_t s, void* const* events, const float* in_gu = nullptr,
+                      const float* in_d = nullptr) {
+  const bool w4a4 = in_gu || in_d;
+  if (w4a4 && !(in_gu && in_d)) return NVFP4_ERR_NULL;
   nvfp4_status st;
   if ((st = check_weight(gate)) != NVFP4_OK) return st;
   if ((st = check_weight(up)) != NVFP4_OK) return st;
@@ -117,6 +122,9 @@ nvfp4_status moe_impl(const uint16_t* x, int64_t T, int64_t H, const int32_t* id
   const Kern kg = pick(kGateUp, v, gate->layout == NVFP4_LAYOUT_TILED32, T, H, I);
   const Kern kd = pick(kDown, v, down->layout == NVFP4_LAYOUT_TILED32, S, I, H);
   if (T > 0 && (kg == kKNone || kd == kKNone)) return NVFP4_ERR_SHAPE;
+  // W4A4 runs on the fp16 form (quantized activations are exact in fp16), which
+  // the decode and prefill kernels provide
+  if (w4a4 && T > 0 && (kg == kKV1 || kd == kKV1)) return NVFP4_ERR_UNSUPPORTED;
   hipEvent_t ev[5] = {};
   if (events)
     for (int i = 0; i < 5; ++i) {
@@ -140,7 +148,8 @@ nvfp4_status moe_impl(const uint16_t* x, int64_t T, int64_t H, const int32_t* id
   const bool f16 = kg != kKV1 && kd != kKV1;
   F16Args dx{at<uint16_t>(ws, L.x16), at<int32_t>(ws, L.xexp), at<uint32_t>(ws, L.hmax)};
   RoutePrep prep{};
-  if (f16) prep = RoutePrep{x, T, H, k, at<uint16_t>(ws, L.x16), at<int32_t>(ws, L.xexp), at<uint32_t>(ws, L.hmax)};
+  if (f16)
+    prep = RoutePrep{x, T, H, k, at<uint16_t>(ws, L.x16), at<int32_t>(ws, L.xexp), at<uint32_t>(ws, L.hmax), in_gu};
 
   if (e == hipSuccess)
     e = launch_route(ids, S, (int)E, eb, variant_tile_rows(v), offsets, perm, nullptr, tiles, n_tiles, prep, s);
@@ -159,10 +168,13 @@ nvfp4_status moe_impl(const uint16_t* x, int64_t T, int64_t H, const int32_t* id
     g.N = I;
     g.K = H;
     g.out = hbuf;
+    g.act_scale = in_gu;
     e = kg == kKDec   ? launch_decode(kGateUp, f16, g, dx, L.max_tiles, s)
         : kg == kKPre ? launch_prefill(kGateUp, f16, g, dx, L.max_tiles, s)
                       : launch_gemm(kGateUp, v, g, L.max_tiles, s);
   }
+  // W4A4: H quantized in place (its row maxima replace the ones gate/up recorded)
+  if (e == hipSuccess && w4a4) e = launch_act_fakequant_rows(hbuf, dx.hmax, S, I, in_d, s);
   // the prefill kernel's fp16 form of down reads H converted in place; the decode
   // kernel converts while staging
   if (e == hipSuccess && f16 && kd == kKPre) e = launch_h_to_f16(hbuf, dx.hmax, S, I, s);
@@ -175,6 +187,7 @@ nvfp4_status moe_impl(const uint16_t* x, int64_t T, int64_t H, const int32_t* id
     g.N = H;
     g.K = I;
     g.out = ypart;
+    g.act_scale = in_d;
     e = kd == kKDec   ? launch_decode(kDown, f16, g, dx, L.max_tiles, s)
         : kd == kKPre ? launch_prefill(kDown, f16, g, dx, L.max_tiles, s)
                       : launch_gemm(kDown, v, g, L.max_tiles, s);
@@ -339,6 +352,27 @@ nvfp4_status nvfp4_moe_grouped_timed(const uint16_t* x, int64_t T, int64_t H,
   if (!events) return NVFP4_ERR_NULL;
   return moe_impl(x, T, H, topk_ids, topk_w, k, expert_begin, gate, up, down, ws, ws_bytes, y,
                   static_cast<hipStream_t>(stream), events);
+}
+
+nvfp4_status nvfp4_moe_grouped_w4a4(const uint16_t* x, int64_t T, int64_t H, const int32_t* topk_ids,
+                                    const float* topk_w, int32_t k, int32_t expert_begin,
+                                    const nvfp4_weight_t* gate, const nvfp4_weight_t* up,
+                                    const nvfp4_weight_t* down, const float* input_scale_gate_up,
+                                    const float* input_scale_down, void* ws, size_t ws_bytes, uint16_t* y,
+                                    void* stream) {
+  if (!input_scale_gate_up || !input_scale_down) return NVFP4_ERR_NULL;
+  return moe_impl(x, T, H, topk_ids, topk_w, k, expert_begin, gate, up, down, ws, ws_bytes, y,
+                  static_cast<hipStream_t>(stream), nullptr, input_scale_gate_up, input_scale_down);
+}
+
+nvfp4_status nvfp4_quantize_act(const uint16_t* x, int64_t rows, int64_t k, const float* input_scale,
+                                uint8_t* codes, uint8_t* scales, void* stream) {
+  if (rows < 0 || k < 32 || k % 32 != 0 || rows > kMaxSlots) return NVFP4_ERR_SHAPE;
+  if (rows == 0) return NVFP4_OK;
+  if (!x || !input_scale || !codes || !scales) return NVFP4_ERR_NULL;
+  if (!aligned16(x) || !aligned16(codes) || !aligned16(scales) || (reinterpret_cast<uintptr_t>(input_scale) & 3))
+    return NVFP4_ERR_ALIGN;
+  return from_hip(launch_act_quant(x, rows, k, input_scale, codes, scales, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

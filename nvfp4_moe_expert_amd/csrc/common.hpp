@@ -80,6 +80,74 @@ __device__ __forceinline__ f16x8 dequant8_f16(uint32_t w, f16x2 s) {
                                  __builtin_shufflevector(p2, p3, 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
+// ------------------------------------------------------------------ encoders
+// NVFP4 quantization of a 16-block (the pack recipe's steps per block, every
+// step in fp32, correctly rounded division, no contraction): against a global
+// scale gs (a weight's scale_2, or an activation's calibrated input_scale),
+// byte = e4m3_rne(block_amax / 6 / gs), s_eff = e4m3(byte) * gs, and each code =
+// e2m1_rne(value / s_eff) with the sign bit of the quotient.
+
+// |bf16| ordered as an unsigned integer: for non-NaN values the magnitude bits
+// (sign cleared) compare exactly like the magnitudes.
+__device__ __forceinline__ uint32_t absmax8(u32x4 v) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint32_t a = v[i] & 0x7FFFu, b = (v[i] >> 16) & 0x7FFFu;
+    m = max(m, max(a, b));
+  }
+  return m;
+}
+
+// e4m3fn byte of a v >= 0 (not NaN), round to nearest even, saturating at 448 (0x7E).
+__device__ __forceinline__ uint32_t e4m3_rne(float v) {
+  if (v >= 448.0f) return 0x7Eu;
+  if (v < 0.015625f) {                       // below 2^-6: subnormal grid of 2^-9
+    float m = __builtin_rintf(v * 512.0f);  // exact scaling, ties to even; 8 -> 0x08 (min normal)
+    return (uint32_t)m;
+  }
+  uint32_t b = __builtin_bit_cast(uint32_t, v);
+  int e = (int)(b >> 23) - 127;              // v = 2^e * 1.f, -6 <= e <= 8
+  uint32_t m3 = (b >> 20) & 7u, rem = b & 0xFFFFFu;
+  if (rem > 0x80000u || (rem == 0x80000u && (m3 & 1u))) ++m3;
+  if (m3 == 8u) { m3 = 0; ++e; }
+  uint32_t code = ((uint32_t)(e + 7) << 3) | m3;
+  return code > 0x7Eu ? 0x7Eu : code;
+}
+
+// e2m1 code of q: nearest even, clamped at 6, sign bit of q. Midpoints
+// 0.25 .. 5.0 are passed when above them, or when on them and the upper code is even.
+__device__ __forceinline__ uint32_t e2m1_rne(float q) {
+  float a = fabsf(q);
+  uint32_t idx = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
+                 (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +
+                 (uint32_t)(a > 5.0f);
+  return idx | ((__builtin_bit_cast(uint32_t, q) >> 31) << 3);
+}
+
+// Scale byte of a block whose amax has the bf16 magnitude bits `amax16`; s_eff
+// receives e4m3(byte) * gs (0 when gs is 0, whose blocks get byte 0 and codes 0).
+__device__ __forceinline__ uint32_t block_byte(uint32_t amax16, float gs, float& s_eff) {
+  s_eff = 0.0f;
+  if (gs == 0.0f) return 0u;
+  const float bamax = __builtin_bit_cast(float, amax16 << 16);
+  const uint32_t byte = e4m3_rne((bamax / 6.0f) / gs);
+  s_eff = e4m3_to_f32(byte) * gs;
+  return byte;
+}
+
+// Codes of 8 bf16 values (one u32x4) -> one dword, element 2j in the low nibble of byte j.
+__device__ __forceinline__ uint32_t quant8(u32x4 v, float s_eff) {
+  uint32_t word = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t lo = (s_eff != 0.0f) ? e2m1_rne(bf16_lo(v[i]) / s_eff) : 0u;
+    const uint32_t hi = (s_eff != 0.0f) ? e2m1_rne(bf16_hi(v[i]) / s_eff) : 0u;
+    word |= (lo | (hi << 4)) << (8 * i);
+  }
+  return word;
+}
+
 // Power-of-two exponent p that puts a row maximum m (> 0, given by its fp32 bits)
 // in [2^14, 2^15): the row times 2^p then fits fp16 with bf16 values down to
 // 2^-28 of m converting exactly. 0 for an all-zero row.

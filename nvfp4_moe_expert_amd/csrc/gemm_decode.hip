@@ -313,6 +313,7 @@ __device__ __forceinline__ void decode_item(const GemmArgs& a, const F16Args& d,
   float unscale = 1.0f;
   if constexpr (F16 && MODE == kGateUp) unscale = ldexpf(1.0f, -d.xexp[a.perm[p] / a.topk]);
   if constexpr (F16 && MODE == kDown) unscale = ldexpf(1.0f, -row_exponent(d.hmax[p]));
+  if (a.act_scale) unscale *= *a.act_scale;   // W4A4: the activations' input_scale
   const float s2a = a.w0.scale_2[e] * unscale;
   const float s2b = kTwo ? a.w1.scale_2[e] * unscale : 0.0f;
   float v[4];
@@ -459,6 +460,7 @@ __device__ __forceinline__ void res_item(const GemmArgs& a, const F16Args& d, ui
   if constexpr (F16) {
     if (live) s2 *= ldexpf(1.0f, -row_exponent(d.hmax[p]));
   }
+  if (a.act_scale) s2 *= *a.act_scale;   // W4A4: the activations' input_scale
   const int64_t orow = kMoe ? (live ? (int64_t)a.perm[p] : 0) : p;
 
   f32x4 acc = {0, 0, 0, 0};

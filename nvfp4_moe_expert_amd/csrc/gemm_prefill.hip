@@ -277,8 +277,9 @@ __device__ __forceinline__ void prefill_body(const GemmArgs& a, const F16Args& d
   // fp16 form: the activation row was scaled by 2^p; the results are scaled back
   // here (exactly: a power of two). Routed gate/up also records max |H| of each
   // row as stored (order-free max, so deterministic) for the fp16 form of down.
-  const float s2a0 = a.w0.scale_2[e];
-  const float s2b0 = kTwo ? a.w1.scale_2[e] : 0.0f;
+  const float act = a.act_scale ? *a.act_scale : 1.0f;   // W4A4: the activations' input_scale
+  const float s2a0 = a.w0.scale_2[e] * act;
+  const float s2b0 = kTwo ? a.w1.scale_2[e] * act : 0.0f;
 #pragma unroll
   for (int t = 0; t < NB; ++t) {
     const int tok = 32 * t + r32;

@@ -32,6 +32,7 @@ struct GemmArgs {
   WeightDev w0, w1;        // w1 only for the two-weight modes
   int64_t N, K;            // weight rows / inputs
   void* out;               // H / Ypart / Y
+  const float* act_scale;  // W4A4: the activations' input_scale (device), applied in the epilogue; else null
 };
 
 // Compute units of the current device (cached per device; 256 if the query fails).
@@ -76,6 +77,15 @@ hipError_t launch_relayout(const uint8_t* codes, const uint8_t* scales, bool fro
                            int64_t n, int64_t k, uint8_t* codes_out, uint8_t* scales_out, hipStream_t s);
 int pack_nblk(int64_t per_tensor);
 
+// Static NVFP4 activation quantization (W4A4) of [rows, k] bf16 rows with the
+// input_scale at `input_scale` (device): codes and scale bytes, row-major.
+hipError_t launch_act_quant(const uint16_t* x, int64_t rows, int64_t k, const float* input_scale, uint8_t* codes,
+                            uint8_t* scales, hipStream_t s);
+// The same quantization of H rows in place (values become e2m1 * e4m3, exact in
+// bf16) and hmax[row] = bits of the largest |value| of the row.
+hipError_t launch_act_fakequant_rows(uint16_t* h, uint32_t* hmax, int64_t rows, int64_t k, const float* input_scale,
+                                     hipStream_t s);
+
 hipError_t launch_dequant(const uint8_t* codes, const uint8_t* scales, const float* scale_2,
                           int groups, int64_t n, int64_t k, bool tiled, uint16_t* unscaled, float* scaled,
                           hipStream_t s);
@@ -90,6 +100,7 @@ struct RoutePrep {
   uint16_t* x16;
   int32_t* xexp;
   uint32_t* hmax;
+  const float* act_scale;   // W4A4: x16 holds the NVFP4-quantized rows (unscaled values), xexp 0
 };
 hipError_t launch_route(const int32_t* ids, int64_t S, int E, int expert_begin, int tile_rows,
                         int32_t* offsets, int32_t* perm, int32_t* inv, int32_t* tiles,

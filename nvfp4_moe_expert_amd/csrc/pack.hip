@@ -17,18 +17,6 @@ namespace nvfp4 {
 
 constexpr int kPackThreads = 256;
 
-// |bf16| ordered as an unsigned integer: for non-NaN values the magnitude bits
-// (sign cleared) compare exactly like the magnitudes.
-__device__ __forceinline__ uint32_t absmax8(u32x4 v) {
-  uint32_t m = 0;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    uint32_t a = v[i] & 0x7FFFu, b = (v[i] >> 16) & 0x7FFFu;
-    m = max(m, max(a, b));
-  }
-  return m;
-}
-
 __global__ __launch_bounds__(kPackThreads) void pack_amax_kernel(const uint16_t* __restrict__ w,
                                                                  int64_t per_tensor, int nblk,
                                                                  uint32_t* __restrict__ partial) {
@@ -48,32 +36,6 @@ __global__ __launch_bounds__(kPackThreads) void pack_amax_kernel(const uint16_t*
     for (int i = 1; i < kPackThreads / 64; ++i) r = max(r, red[i]);
     partial[(int64_t)g * nblk + blockIdx.x] = r;
   }
-}
-
-// e4m3fn byte of a finite v >= 0, round to nearest even, saturating at 448 (0x7E).
-__device__ __forceinline__ uint32_t e4m3_rne(float v) {
-  if (v >= 448.0f) return 0x7Eu;
-  if (v < 0.015625f) {                       // below 2^-6: subnormal grid of 2^-9
-    float m = __builtin_rintf(v * 512.0f);  // exact scaling, ties to even; 8 -> 0x08 (min normal)
-    return (uint32_t)m;
-  }
-  uint32_t b = __builtin_bit_cast(uint32_t, v);
-  int e = (int)(b >> 23) - 127;              // v = 2^e * 1.f, -6 <= e <= 8
-  uint32_t m3 = (b >> 20) & 7u, rem = b & 0xFFFFFu;
-  if (rem > 0x80000u || (rem == 0x80000u && (m3 & 1u))) ++m3;
-  if (m3 == 8u) { m3 = 0; ++e; }
-  uint32_t code = ((uint32_t)(e + 7) << 3) | m3;
-  return code > 0x7Eu ? 0x7Eu : code;
-}
-
-// e2m1 code of q: nearest even, clamped at 6, sign bit of q. Midpoints
-// 0.25 .. 5.0 are passed when above them, or when on them and the upper code is even.
-__device__ __forceinline__ uint32_t e2m1_rne(float q) {
-  float a = fabsf(q);
-  uint32_t idx = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
-                 (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +
-                 (uint32_t)(a > 5.0f);
-  return idx | ((__builtin_bit_cast(uint32_t, q) >> 31) << 3);
 }
 
 // One thread packs 32 consecutive elements of a row (two 16-blocks).
@@ -108,34 +70,74 @@ __global__ __launch_bounds__(kPackThreads) void pack_quant_kernel(
 #pragma unroll
   for (int blk = 0; blk < 2; ++blk) {
     const u32x4 a = v[2 * blk], b = v[2 * blk + 1];
-    uint32_t byte = 0;
-    float s_eff = 0.0f;
-    if (s2 != 0.0f) {
-      float bamax = __builtin_bit_cast(float, max(absmax8(a), absmax8(b)) << 16);
-      float vv = (bamax / 6.0f) / s2;
-      byte = e4m3_rne(vv);
-      s_eff = e4m3_to_f32(byte) * s2;
-    }
-    uint32_t c[16];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      uint32_t wa = (i < 4) ? a[i] : b[i - 4];
-      float lo = bf16_lo(wa), hi = bf16_hi(wa);
-      c[2 * i] = (s_eff != 0.0f) ? e2m1_rne(lo / s_eff) : 0u;
-      c[2 * i + 1] = (s_eff != 0.0f) ? e2m1_rne(hi / s_eff) : 0u;
-    }
-#pragma unroll
-    for (int d = 0; d < 2; ++d) {
-      uint32_t word = 0;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) word |= c[8 * d + j] << (4 * j);
-      out[2 * blk + d] = word;
-    }
+    float s_eff;
+    const uint32_t byte = block_byte(max(absmax8(a), absmax8(b)), s2, s_eff);
+    out[2 * blk] = quant8(a, s_eff);
+    out[2 * blk + 1] = quant8(b, s_eff);
     sbytes |= byte << (8 * blk);
   }
   st16(codes + (int64_t)g * n * (k / 2) + code_piece_off(tiled, row, c32, k), out);
   *reinterpret_cast<uint16_t*>(scales + (int64_t)g * n * (k / 16) + scale_off(tiled, row, 2 * c32, k)) =
       (uint16_t)sbytes;
+}
+
+// Static activation quantization (the W4A4 form): the block steps of the pack
+// with a calibrated input_scale (one fp32 in device memory) in place of scale_2.
+// One thread: 32 consecutive elements of a row -> 16 code bytes, 2 scale bytes
+// (row-major, the layout of a stored weight).
+__global__ __launch_bounds__(kPackThreads) void act_quant_kernel(const uint16_t* __restrict__ x, int64_t rows,
+                                                                 int64_t k, const float* __restrict__ gs_ptr,
+                                                                 uint8_t* __restrict__ codes,
+                                                                 uint8_t* __restrict__ scales) {
+  const int64_t per_row = k / 32;
+  const int64_t u = (int64_t)blockIdx.x * kPackThreads + threadIdx.x;
+  if (u >= rows * per_row) return;
+  const int64_t row = u / per_row, c32 = u % per_row;
+  const float gs = *gs_ptr;
+  const uint16_t* src = x + row * k + c32 * 32;
+  u32x4 v[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) v[i] = ld16(src + 8 * i);
+  u32x4 out;
+  uint32_t sbytes = 0;
+#pragma unroll
+  for (int blk = 0; blk < 2; ++blk) {
+    float s_eff;
+    sbytes |= block_byte(max(absmax8(v[2 * blk]), absmax8(v[2 * blk + 1])), gs, s_eff) << (8 * blk);
+    out[2 * blk] = quant8(v[2 * blk], s_eff);
+    out[2 * blk + 1] = quant8(v[2 * blk + 1], s_eff);
+  }
+  st16(codes + row * (k / 2) + c32 * 16, out);
+  *reinterpret_cast<uint16_t*>(scales + row * (k / 16) + c32 * 2) = (uint16_t)sbytes;
+}
+
+// The same quantization of the routed intermediate H, in place: each bf16 value
+// becomes e2m1(code) * e4m3(byte), the quantized value without input_scale (exact
+// in bf16), and hmax[row] the fp32 bits of the row's largest magnitude, which
+// the fp16 form of the down projection scales the row by. One wave per row, one
+// 16-block per lane.
+__global__ __launch_bounds__(256) void act_fakequant_rows_kernel(uint16_t* __restrict__ h,
+                                                                 uint32_t* __restrict__ hmax, int64_t rows,
+                                                                 int64_t k, const float* __restrict__ gs_ptr) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const float gs = *gs_ptr;
+  uint16_t* r = h + row * k;
+  uint32_t m = 0;
+  for (int64_t c = lane; c < k / 16; c += 64) {
+    const u32x4 a = ld16(r + 16 * c), b = ld16(r + 16 * c + 8);
+    float s_eff;
+    const uint32_t byte = block_byte(max(absmax8(a), absmax8(b)), gs, s_eff);
+    const float sv = e4m3_to_f32(byte);
+    const u32x4 da = __builtin_bit_cast(u32x4, dequant8(quant8(a, s_eff), sv));
+    const u32x4 db = __builtin_bit_cast(u32x4, dequant8(quant8(b, s_eff), sv));
+    st16(r + 16 * c, da);
+    st16(r + 16 * c + 8, db);
+    m = max(m, max(absmax8(da), absmax8(db)));
+  }
+  for (int off = 32; off >= 1; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
+  if (lane == 0) hmax[row] = m << 16;
 }
 
 // One thread dequantizes 8 elements (one dword of codes).
@@ -232,6 +234,27 @@ hipError_t launch_dequant(const uint8_t* codes, const uint8_t* scales, const flo
   const int64_t gx = (total8 + kPackThreads - 1) / kPackThreads;
   hipLaunchKernelGGL(dequant_kernel, dim3((unsigned)gx), dim3(kPackThreads), 0, s, codes, scales,
                      scale_2, n, k, total8, unscaled, scaled, (int)tiled);
+  return hipGetLastError();
+}
+
+}  // namespace nvfp4
+
+namespace nvfp4 {
+
+hipError_t launch_act_quant(const uint16_t* x, int64_t rows, int64_t k, const float* input_scale, uint8_t* codes,
+                            uint8_t* scales, hipStream_t s) {
+  const int64_t units = rows * (k / 32);
+  if (units <= 0) return hipSuccess;
+  hipLaunchKernelGGL(act_quant_kernel, dim3((unsigned)((units + kPackThreads - 1) / kPackThreads)),
+                     dim3(kPackThreads), 0, s, x, rows, k, input_scale, codes, scales);
+  return hipGetLastError();
+}
+
+hipError_t launch_act_fakequant_rows(uint16_t* h, uint32_t* hmax, int64_t rows, int64_t k, const float* input_scale,
+                                     hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  hipLaunchKernelGGL(act_fakequant_rows_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, h, hmax, rows, k,
+                     input_scale);
   return hipGetLastError();
 }
 

@@ -56,6 +56,24 @@ __device__ void prep_row(const RoutePrep& pr, int64_t t) {
   __shared__ int pexp;
   const int tid = threadIdx.x;
   const uint16_t* xr = pr.x + t * pr.H;
+  if (pr.act_scale) {
+    // W4A4: the row's static NVFP4 quantization (lanes 2j, 2j+1 hold one 16-block),
+    // stored as its unscaled values e2m1 * e4m3 in fp16 (exact); input_scale is
+    // applied in the GEMM epilogue, so the row exponent is 0
+    const float gs = *pr.act_scale;
+    for (int64_t i = (int64_t)tid * 8; i < pr.H; i += kRouteThreads * 8) {
+      const u32x4 v = ld16(xr + i);
+      uint32_t am = absmax8(v);
+      am = max(am, (uint32_t)__shfl_xor((int)am, 1));
+      float s_eff;
+      const uint32_t byte = block_byte(am, gs, s_eff);
+      const _Float16 sv = (_Float16)e4m3_to_f32(byte);
+      st16(pr.x16 + t * pr.H + i, __builtin_bit_cast(u32x4, dequant8_f16(quant8(v, s_eff), f16x2{sv, sv})));
+    }
+    if (tid == 0) pr.xexp[t] = 0;
+    for (int j = tid; j < pr.k; j += kRouteThreads) pr.hmax[t * pr.k + j] = 0u;
+    return;
+  }
   uint32_t m = 0;
   for (int64_t i = (int64_t)tid * 8; i < pr.H; i += kRouteThreads * 8) {
     const u32x4 v = ld16(xr + i);

@@ -44,7 +44,7 @@ def test_binding_covers_every_symbol():
 
 def test_version_and_status_strings():
     lib = nv.load_library()
-    assert nv.abi_version() == 2
+    assert nv.abi_version() == 3
     for code in range(7):
         assert lib.nvfp4_status_string(code)
     assert b"unknown" in lib.nvfp4_status_string(99)
@@ -169,6 +169,39 @@ def test_moe_validation():
     assert _moe(lib, E=4097) == ESHAPE
     assert _moe(lib, gl=1, ul=0, H=256, I=256, gn=256, un=256, dk=256) == ESHAPE   # gate and up layouts differ
     assert _moe(lib, dl=1) == ESHAPE              # tiled down needs k = I % 256 == 0
+
+
+def _moe_w4a4(lib, s_gu=A, s_d=A + 4, T=8, H=256, k=4, E=16, I=128, **kw):
+    g = _w(n=I, k=H, groups=E)
+    u = _w(n=I, k=H, groups=E)
+    d = _w(n=H, k=I, groups=E)
+    wsb = kw.get("wsb", lib.nvfp4_moe_workspace_size(T, k, E, H, I))
+    return lib.nvfp4_moe_grouped_w4a4(P(kw.get("x", A)), T, H, P(A), P(A), k, 0, ctypes.byref(g), ctypes.byref(u),
+                                      ctypes.byref(d), P(s_gu), P(s_d), P(kw.get("ws", B)), wsb, P(B), None)
+
+
+def test_moe_w4a4_validation():
+    lib = nv.load_library()
+    assert _moe_w4a4(lib, s_gu=0) == ENULL
+    assert _moe_w4a4(lib, s_d=0) == ENULL
+    assert _moe_w4a4(lib, x=0) == ENULL
+    assert _moe_w4a4(lib, ws=0) == EWS
+    assert _moe_w4a4(lib, T=0, wsb=0) == OK
+
+
+def test_quantize_act_validation():
+    lib = nv.load_library()
+    q = lambda x=A, rows=4, k=64, s=A, c=B, sc=B + 4096: lib.nvfp4_quantize_act(P(x), rows, k, P(s), P(c), P(sc), None)
+    assert q(k=48) == ESHAPE
+    assert q(k=16) == ESHAPE
+    assert q(rows=-1) == ESHAPE
+    assert q(rows=0, x=0) == OK
+    assert q(x=0) == ENULL
+    assert q(s=0) == ENULL
+    assert q(c=0) == ENULL
+    assert q(x=A + 2) == EALIGN
+    assert q(sc=B + 4098) == EALIGN
+    assert q(s=A + 2) == EALIGN
 
 
 def test_moe_empty_batch_is_noop():
