@@ -18,6 +18,9 @@ What it computes, and from which passage:
 * ``mlp``      - the dense Fp4Linear (gate and up apart, each with its own tensor
   scale), the expert permutation, and the routed expert MLP
   (grouped gate/up, SiLU(gate)*up, grouped down, routing-weighted sum).
+* ``block``    - the steps either side of the routed experts: the BF16 router
+  with top-k softmax selection, the shared-expert BF16 MLP, and the MoE block
+  (routed + shared).
 * ``brute``    - float64 pure-Python loops on tiny shapes, used only to pin the
   vectorised oracle.
 
@@ -32,4 +35,4 @@ formats, hand-derived golden bytes, invariants of the pack, brute force,
 exact integer arithmetic, and library sorts. No function here is
 "parity unpinned".
 """
-from . import formats, nvfp4, mlp, brute  # noqa: F401
+from . import formats, nvfp4, mlp, block, brute  # noqa: F401

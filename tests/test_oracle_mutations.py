@@ -7,12 +7,14 @@ import textwrap
 
 import pytest
 
+import oracle.block
 import oracle.formats
 import oracle.mlp
 import oracle.nvfp4
 import test_oracle_formats as TF
 import test_oracle_mlp as TM
 import test_oracle_pack as TP
+import test_oracle_block as TB
 import test_oracle_w4a4 as TW
 
 
@@ -76,6 +78,15 @@ MUTANTS = [
      "dequant_unscaled(codes, scales)", [TW.test_moe_w4a4_k1_reduces_to_pinned_dense_pieces]),
     (oracle.mlp, "moe_w4a4", "hq = act_fake_quant(h_bits, in_scale_d)", "hq = act_fake_quant(h_bits, in_scale_gu)",
      [TW.test_moe_w4a4_k1_reduces_to_pinned_dense_pieces]),
+    # router and shared expert: ties to the higher index; softmax over all experts;
+    # gate and up swapped
+    (oracle.block, "topk_softmax", "key=lambda e: (-logits[t, e], e)", "key=lambda e: (-logits[t, e], -e)",
+     [TB.test_topk_ties_go_to_the_lower_index]),
+    (oracle.block, "topk_softmax", "z = np.exp(sel - sel.max(axis=1, keepdims=True))\n    return ids.astype(np.int32), z / z.sum(axis=1, keepdims=True)",
+     "z = np.exp(sel - sel.max(axis=1, keepdims=True))\n    return ids.astype(np.int32), z / np.exp(logits - sel.max(axis=1, keepdims=True)).sum(axis=1, keepdims=True)",
+     [lambda: TB.test_topk_matches_stable_argsort(7, 16, 4)]),
+    (oracle.block, "shared_mlp", "h = silu(x @ _bf(wg_bits).T) * (x @ _bf(wu_bits).T)", "h = silu(x @ _bf(wu_bits).T) * (x @ _bf(wg_bits).T)",
+     [TB.test_shared_mlp_reduces_to_dense_nvfp4_mlp]),
 ]
 
 
