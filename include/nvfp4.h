@@ -70,7 +70,7 @@
 extern "C" {
 #endif
 
-#define NVFP4_ABI_VERSION 3
+#define NVFP4_ABI_VERSION 4
 
 #define NVFP4_LAYOUT_ROWS 0
 #define NVFP4_LAYOUT_TILED32 1
@@ -264,6 +264,60 @@ nvfp4_status nvfp4_moe_grouped_w4a4(const uint16_t* x, int64_t T, int64_t H, con
                                     const nvfp4_weight_t* down, const float* input_scale_gate_up,
                                     const float* input_scale_down, void* ws, size_t ws_bytes, uint16_t* y,
                                     void* stream);
+
+/* ------------------------------------------------------------------------
+ * The BF16 steps either side of the routed experts (TensorFold issue #308,
+ * "What the branch does": the shared expert runs as a BF16 MLP; model card
+ * "GLM-5.3-Flash-NVFP4-W4A4-Experts", "Quantization boundary": routers and
+ * shared experts stay BF16). bf16 weights are plain row-major [out, in] device
+ * arrays, 16-byte aligned; products accumulate in fp32 (MFMA); small batches
+ * split the inputs over workgroups and sum the splits in a fixed order, so
+ * results are reproducible.
+ * ------------------------------------------------------------------------ */
+
+/*
+ * nvfp4_router_topk - router logits and top-k selection.
+ *   logits[t, e] = sum_h x[t, h] * w_router[e, h] (fp32); the k largest (ties to
+ *   the lower expert index) go to topk_ids[t, 0..k) in decreasing order, and
+ *   topk_w[t, j] is the softmax over the k selected logits.
+ *   x [T, H] bf16; w_router [n_experts, H] bf16; ws of
+ *   nvfp4_router_workspace_size(T, H, n_experts) bytes (16-byte aligned);
+ *   topk_ids [T, k] int32 and topk_w [T, k] fp32 out (4-byte aligned).
+ * Errors: ERR_SHAPE unless H % 32 == 0, n_experts % 4 == 0, 1 <= k <=
+ * min(64, n_experts), n_experts <= 4096; ERR_NULL, ERR_ALIGN, ERR_WORKSPACE.
+ */
+size_t nvfp4_router_workspace_size(int64_t T, int64_t H, int32_t n_experts);
+nvfp4_status nvfp4_router_topk(const uint16_t* x, int64_t T, int64_t H, const uint16_t* w_router,
+                               int32_t n_experts, int32_t k, void* ws, size_t ws_bytes, int32_t* topk_ids,
+                               float* topk_w, void* stream);
+
+/*
+ * nvfp4_bf16_mlp - the shared-expert BF16 MLP:
+ *   y[m, :] = (SiLU(x . w_gate^T) * (x . w_up^T)) . w_down^T, fp32 out [M, H];
+ *   the intermediate [M, Is] is rounded to bf16 (the down product's operand).
+ *   x [M, H] bf16; w_gate, w_up [Is, H] bf16; w_down [H, Is] bf16; ws of
+ *   nvfp4_bf16_mlp_workspace_size(M, H, Is) bytes.
+ * Errors: ERR_SHAPE unless H and Is are multiples of 32; ERR_NULL, ERR_ALIGN,
+ * ERR_WORKSPACE.
+ */
+size_t nvfp4_bf16_mlp_workspace_size(int64_t M, int64_t H, int64_t Is);
+nvfp4_status nvfp4_bf16_mlp(const uint16_t* x, int64_t M, int64_t H, const uint16_t* w_gate, const uint16_t* w_up,
+                            const uint16_t* w_down, int64_t Is, void* ws, size_t ws_bytes, float* y, void* stream);
+
+/*
+ * nvfp4_moe_block - one MoE block: router (nvfp4_router_topk over the
+ * gate->groups experts), routed NVFP4 experts (nvfp4_moe_grouped with
+ * expert_begin 0) and the shared expert (nvfp4_bf16_mlp, Is = shared
+ * intermediate size), summed: y[t] = bf16(sum_j w[t,j] * expert_j(x_t) +
+ * shared(x_t)), the shared term added after the k routed slots.
+ *   ws of nvfp4_moe_block_workspace_size(T, k, E, H, I, Is) bytes.
+ * Errors: those of the three parts.
+ */
+size_t nvfp4_moe_block_workspace_size(int64_t T, int32_t k, int32_t n_experts, int64_t H, int64_t I, int64_t Is);
+nvfp4_status nvfp4_moe_block(const uint16_t* x, int64_t T, int64_t H, const uint16_t* w_router, int32_t k,
+                             const nvfp4_weight_t* gate, const nvfp4_weight_t* up, const nvfp4_weight_t* down,
+                             const uint16_t* shared_gate, const uint16_t* shared_up, const uint16_t* shared_down,
+                             int64_t Is, void* ws, size_t ws_bytes, uint16_t* y, void* stream);
 
 #ifdef __cplusplus
 }

@@ -72,6 +72,12 @@ _SIGNATURES = {
     "nvfp4_moe_grouped_w4a4": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _I32, _I32, _WP, _WP, _WP, _P, _P, _P, _SZ,
                                               _P, _P]),
     "nvfp4_quantize_act": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _P, _P]),
+    "nvfp4_router_workspace_size": (_SZ, [_I64, _I64, _I32]),
+    "nvfp4_router_topk": (ctypes.c_int, [_P, _I64, _I64, _P, _I32, _I32, _P, _SZ, _P, _P, _P]),
+    "nvfp4_bf16_mlp_workspace_size": (_SZ, [_I64, _I64, _I64]),
+    "nvfp4_bf16_mlp": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _P, _I64, _P, _SZ, _P, _P]),
+    "nvfp4_moe_block_workspace_size": (_SZ, [_I64, _I32, _I32, _I64, _I64, _I64]),
+    "nvfp4_moe_block": (ctypes.c_int, [_P, _I64, _I64, _P, _I32, _WP, _WP, _WP, _P, _P, _P, _I64, _P, _SZ, _P, _P]),
 }
 
 
@@ -328,3 +334,67 @@ def quantize_act(x: torch.Tensor, input_scale: torch.Tensor):
     st = lib.nvfp4_quantize_act(_ptr(x), rows, k, _ptr(input_scale), _ptr(codes), _ptr(scales), _stream())
     _check(st, "nvfp4_quantize_act")
     return codes, scales
+
+
+# ---------------------------------------------------------------- BF16 steps either side
+def router_topk(x: torch.Tensor, w_router: torch.Tensor, k: int, workspace: torch.Tensor | None = None):
+    """Router logits x . w_router^T (fp32), top-k (ties to the lower index) and the
+    softmax over the selected: (ids int32 [T, k], weights float32 [T, k])."""
+    lib = load_library()
+    _need(x, torch.bfloat16, "x", 2)
+    _need(w_router, torch.bfloat16, "w_router", 2)
+    T, H = x.shape
+    E = w_router.shape[0]
+    if w_router.shape[1] != H:
+        raise ValueError("w_router must be [E, H]")
+    if workspace is None:
+        workspace = torch.empty((max(lib.nvfp4_router_workspace_size(T, H, E), 256),), dtype=torch.uint8,
+                                device=x.device)
+    ids = torch.empty((T, k), dtype=torch.int32, device=x.device)
+    w = torch.empty((T, k), dtype=torch.float32, device=x.device)
+    _check(lib.nvfp4_router_topk(_ptr(x), T, H, _ptr(w_router), E, k, _ptr(workspace), workspace.numel(), _ptr(ids),
+                                 _ptr(w), _stream()), "nvfp4_router_topk")
+    return ids, w
+
+
+def bf16_mlp(x: torch.Tensor, w_gate: torch.Tensor, w_up: torch.Tensor, w_down: torch.Tensor,
+             workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """Shared-expert BF16 MLP: fp32 [M, H] = (SiLU(x.Wg^T) * (x.Wu^T)) . Wd^T."""
+    lib = load_library()
+    for t, n in ((x, "x"), (w_gate, "w_gate"), (w_up, "w_up"), (w_down, "w_down")):
+        _need(t, torch.bfloat16, n, 2)
+    M, H = x.shape
+    Is = w_gate.shape[0]
+    if w_gate.shape != (Is, H) or w_up.shape != (Is, H) or w_down.shape != (H, Is):
+        raise ValueError("shared expert shapes: gate, up [Is, H]; down [H, Is]")
+    if workspace is None:
+        workspace = torch.empty((max(lib.nvfp4_bf16_mlp_workspace_size(M, H, Is), 256),), dtype=torch.uint8,
+                                device=x.device)
+    y = torch.empty((M, H), dtype=torch.float32, device=x.device)
+    _check(lib.nvfp4_bf16_mlp(_ptr(x), M, H, _ptr(w_gate), _ptr(w_up), _ptr(w_down), Is, _ptr(workspace),
+                              workspace.numel(), _ptr(y), _stream()), "nvfp4_bf16_mlp")
+    return y
+
+
+def moe_block(x: torch.Tensor, w_router: torch.Tensor, k: int, gate: NVFP4Weight, up: NVFP4Weight,
+              down: NVFP4Weight, shared_gate: torch.Tensor, shared_up: torch.Tensor, shared_down: torch.Tensor,
+              workspace: torch.Tensor | None = None, out: torch.Tensor | None = None) -> torch.Tensor:
+    """One MoE block: router + routed NVFP4 experts + shared BF16 expert -> y [T, H] bf16."""
+    lib = load_library()
+    _need(x, torch.bfloat16, "x", 2)
+    for t, n in ((w_router, "w_router"), (shared_gate, "shared_gate"), (shared_up, "shared_up"),
+                 (shared_down, "shared_down")):
+        _need(t, torch.bfloat16, n, 2)
+    T, H = x.shape
+    Is = shared_gate.shape[0]
+    E, I = gate.groups, gate.n
+    if workspace is None:
+        workspace = torch.empty((max(lib.nvfp4_moe_block_workspace_size(T, k, E, H, I, Is), 256),),
+                                dtype=torch.uint8, device=x.device)
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
+    g, u, d = gate._struct(), up._struct(), down._struct()
+    _check(lib.nvfp4_moe_block(_ptr(x), T, H, _ptr(w_router), k, ctypes.byref(g), ctypes.byref(u), ctypes.byref(d),
+                               _ptr(shared_gate), _ptr(shared_up), _ptr(shared_down), Is, _ptr(workspace),
+                               workspace.numel(), _ptr(out), _stream()), "nvfp4_moe_block")
+    return out

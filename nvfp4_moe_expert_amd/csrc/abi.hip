@@ -6,6 +6,8 @@
 // argument check runs before the first launch, so an error writes nothing.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+
 #include "../../include/nvfp4.h"
 #include "launch.hpp"
 
@@ -95,7 +97,7 @@ nvfp4_status moe_impl(const uint16_t* x, int64_t T, int64_t H, const int32_t* id
                       int32_t k, int32_t eb, const nvfp4_weight_t* gate, const nvfp4_weight_t* up,
                       const nvfp4_weight_t* down, void* ws, size_t ws_bytes, uint16_t* y,
                       hipStream_t s, void* const* events, const float* in_gu = nullptr,
-                      const float* in_d = nullptr) {
+                      const float* in_d = nullptr, const float* extra = nullptr) {
   const bool w4a4 = in_gu || in_d;
   if (w4a4 && !(in_gu && in_d)) return NVFP4_ERR_NULL;
   nvfp4_status st;
@@ -193,10 +195,36 @@ nvfp4_status moe_impl(const uint16_t* x, int64_t T, int64_t H, const int32_t* id
                       : launch_gemm(kDown, v, g, L.max_tiles, s);
   }
   if (e == hipSuccess) e = mark(3);
-  if (e == hipSuccess) e = launch_combine(ids, tw, ypart, T, k, H, (int)E, eb, y, s);
+  if (e == hipSuccess) e = launch_combine(ids, tw, ypart, T, k, H, (int)E, eb, extra, y, s);
   if (e == hipSuccess) e = mark(4);
   return from_hip(e);
 }
+
+// ---- BF16 steps either side of the routed experts
+struct BlockLayout {
+  size_t logits, ids, w, hs, ys, part, moe, total;
+};
+
+size_t part_bytes(int64_t T, int64_t E, int64_t H, int64_t Is) {
+  return std::max({bf16_gemm_partial_bytes(T, E, H, false), bf16_gemm_partial_bytes(T, Is, H, true),
+                   bf16_gemm_partial_bytes(T, H, Is, false), (size_t)256});
+}
+
+BlockLayout block_layout(int64_t T, int k, int64_t E, int64_t H, int64_t I, int64_t Is) {
+  BlockLayout L{};
+  size_t off = 0;
+  L.logits = off; off += round_up(sizeof(float) * (size_t)(T * E > 0 ? T * E : 1));
+  L.ids = off;    off += round_up(sizeof(int32_t) * (size_t)(T * k > 0 ? T * k : 1));
+  L.w = off;      off += round_up(sizeof(float) * (size_t)(T * k > 0 ? T * k : 1));
+  L.hs = off;     off += round_up(sizeof(uint16_t) * (size_t)(T * Is > 0 ? T * Is : 1));
+  L.ys = off;     off += round_up(sizeof(float) * (size_t)(T * H > 0 ? T * H : 1));
+  L.part = off;   off += round_up(part_bytes(T, E, H, Is));
+  L.moe = off;    off += moe_layout(T, k, E, H, I).total;
+  L.total = off;
+  return L;
+}
+
+bool bf16_shape_ok(int64_t N, int64_t K) { return N >= 4 && N % 4 == 0 && K >= 32 && K % 32 == 0; }
 
 nvfp4_status linear_impl(const uint16_t* x, int64_t m, const nvfp4_weight_t* w0,
                          const nvfp4_weight_t* w1, uint16_t* out, hipStream_t s) {
@@ -373,6 +401,96 @@ nvfp4_status nvfp4_quantize_act(const uint16_t* x, int64_t rows, int64_t k, cons
   if (!aligned16(x) || !aligned16(codes) || !aligned16(scales) || (reinterpret_cast<uintptr_t>(input_scale) & 3))
     return NVFP4_ERR_ALIGN;
   return from_hip(launch_act_quant(x, rows, k, input_scale, codes, scales, static_cast<hipStream_t>(stream)));
+}
+
+size_t nvfp4_router_workspace_size(int64_t T, int64_t H, int32_t n_experts) {
+  if (T < 0 || H < 1 || n_experts < 1) return 0;
+  return round_up(sizeof(float) * (size_t)(T * n_experts > 0 ? T * n_experts : 1)) +
+         round_up(bf16_gemm_partial_bytes(T, n_experts, H, false) + 256);
+}
+
+nvfp4_status nvfp4_router_topk(const uint16_t* x, int64_t T, int64_t H, const uint16_t* w_router,
+                               int32_t n_experts, int32_t k, void* ws, size_t ws_bytes, int32_t* topk_ids,
+                               float* topk_w, void* stream) {
+  if (T < 0 || T > kMaxSlots || n_experts < 1 || n_experts > kMaxExperts || k < 1 || k > kMaxTopk ||
+      k > n_experts || !bf16_shape_ok(n_experts, H))
+    return NVFP4_ERR_SHAPE;
+  if (T == 0) return NVFP4_OK;
+  if (!x || !w_router || !topk_ids || !topk_w || !ws) return NVFP4_ERR_NULL;
+  if (!aligned16(x) || !aligned16(w_router) || !aligned16(ws) || (reinterpret_cast<uintptr_t>(topk_ids) & 3) ||
+      (reinterpret_cast<uintptr_t>(topk_w) & 3))
+    return NVFP4_ERR_ALIGN;
+  if (ws_bytes < nvfp4_router_workspace_size(T, H, n_experts)) return NVFP4_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float* logits = reinterpret_cast<float*>(ws);
+  float* part = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) +
+                                         round_up(sizeof(float) * (size_t)(T * n_experts)));
+  hipError_t e = launch_bf16_gemm(false, x, w_router, nullptr, T, n_experts, H, logits, part, s);
+  if (e == hipSuccess) e = launch_topk_softmax(logits, T, n_experts, k, topk_ids, topk_w, s);
+  return from_hip(e);
+}
+
+size_t nvfp4_bf16_mlp_workspace_size(int64_t M, int64_t H, int64_t Is) {
+  if (M < 0 || H < 1 || Is < 1) return 0;
+  return round_up(sizeof(uint16_t) * (size_t)(M * Is > 0 ? M * Is : 1)) +
+         round_up(std::max(bf16_gemm_partial_bytes(M, Is, H, true), bf16_gemm_partial_bytes(M, H, Is, false)) + 256);
+}
+
+nvfp4_status nvfp4_bf16_mlp(const uint16_t* x, int64_t M, int64_t H, const uint16_t* w_gate, const uint16_t* w_up,
+                            const uint16_t* w_down, int64_t Is, void* ws, size_t ws_bytes, float* y, void* stream) {
+  if (M < 0 || M > kMaxSlots || !bf16_shape_ok(Is, H) || !bf16_shape_ok(H, Is)) return NVFP4_ERR_SHAPE;
+  if (M == 0) return NVFP4_OK;
+  if (!x || !w_gate || !w_up || !w_down || !ws || !y) return NVFP4_ERR_NULL;
+  if (!aligned16(x) || !aligned16(w_gate) || !aligned16(w_up) || !aligned16(w_down) || !aligned16(ws) ||
+      !aligned16(y))
+    return NVFP4_ERR_ALIGN;
+  if (ws_bytes < nvfp4_bf16_mlp_workspace_size(M, H, Is)) return NVFP4_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint16_t* h = reinterpret_cast<uint16_t*>(ws);
+  float* part = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + round_up(sizeof(uint16_t) * (size_t)(M * Is)));
+  hipError_t e = launch_bf16_gemm(true, x, w_gate, w_up, M, Is, H, h, part, s);
+  if (e == hipSuccess) e = launch_bf16_gemm(false, h, w_down, nullptr, M, H, Is, y, part, s);
+  return from_hip(e);
+}
+
+size_t nvfp4_moe_block_workspace_size(int64_t T, int32_t k, int32_t n_experts, int64_t H, int64_t I, int64_t Is) {
+  if (T < 0 || k < 1 || n_experts < 1 || H < 1 || I < 1 || Is < 1) return 0;
+  return block_layout(T, k, n_experts, H, I, Is).total;
+}
+
+nvfp4_status nvfp4_moe_block(const uint16_t* x, int64_t T, int64_t H, const uint16_t* w_router, int32_t k,
+                             const nvfp4_weight_t* gate, const nvfp4_weight_t* up, const nvfp4_weight_t* down,
+                             const uint16_t* shared_gate, const uint16_t* shared_up, const uint16_t* shared_down,
+                             int64_t Is, void* ws, size_t ws_bytes, uint16_t* y, void* stream) {
+  nvfp4_status st;
+  if ((st = check_weight(gate)) != NVFP4_OK) return st;
+  const int64_t E = gate->groups, I = gate->n;
+  if (T < 0 || k < 1 || k > kMaxTopk || k > E || E > kMaxExperts || !bf16_shape_ok(E, H) ||
+      !bf16_shape_ok(Is, H) || !bf16_shape_ok(H, Is))
+    return NVFP4_ERR_SHAPE;
+  if (T == 0) return NVFP4_OK;
+  if (!x || !w_router || !shared_gate || !shared_up || !shared_down || !ws || !y) return NVFP4_ERR_NULL;
+  if (!aligned16(x) || !aligned16(w_router) || !aligned16(shared_gate) || !aligned16(shared_up) ||
+      !aligned16(shared_down) || !aligned16(ws) || !aligned16(y))
+    return NVFP4_ERR_ALIGN;
+  const BlockLayout L = block_layout(T, k, E, H, I, Is);
+  if (ws_bytes < L.total) return NVFP4_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float* logits = at<float>(ws, L.logits);
+  int32_t* ids = at<int32_t>(ws, L.ids);
+  float* tw = at<float>(ws, L.w);
+  uint16_t* hs = at<uint16_t>(ws, L.hs);
+  float* ys = at<float>(ws, L.ys);
+  float* part = at<float>(ws, L.part);
+  // router, then the shared expert (its fp32 result is added by the routed MLP's
+  // combine, after the k routed slots), then the routed experts
+  hipError_t e = launch_bf16_gemm(false, x, w_router, nullptr, T, E, H, logits, part, s);
+  if (e == hipSuccess) e = launch_topk_softmax(logits, T, (int)E, k, ids, tw, s);
+  if (e == hipSuccess) e = launch_bf16_gemm(true, x, shared_gate, shared_up, T, Is, H, hs, part, s);
+  if (e == hipSuccess) e = launch_bf16_gemm(false, hs, shared_down, nullptr, T, H, Is, ys, part, s);
+  if (e != hipSuccess) return from_hip(e);
+  return moe_impl(x, T, H, ids, tw, k, 0, gate, up, down, at<void>(ws, L.moe), ws_bytes - L.moe, y, s, nullptr,
+                  nullptr, nullptr, ys);
 }
 
 }  // extern "C"

@@ -1,0 +1,259 @@
+// The BF16 steps either side of the routed experts: router logits with top-k
+// softmax selection, and the shared-expert BF16 MLP (TensorFold issue #308,
+// "What the branch does": the shared expert runs as a BF16 MLP; the model card
+// "GLM-5.3-Flash-NVFP4-W4A4-Experts", "Quantization boundary": routers and
+// shared experts stay BF16).
+//
+// bf16 GEMM, C[m, n] = sum_k X[m, k] * W[n, k] (activations and weights both
+// K-contiguous), on v_mfma_f32_32x32x16_bf16 with fp32 accumulation:
+// * a workgroup of 4 waves takes 64 activation rows x 64 weight rows (of each of
+//   NW weight matrices: 2 for the gated form, whose gate and up rows n are
+//   multiplied by the same wave, so SiLU(gate) * up is formed in registers);
+// * wave (t, w) multiplies activation rows 32t.. against weight rows 32w.. with
+//   A = weights and B = activations, both read from LDS; the K loop runs in
+//   stages of 32 inputs, double-buffered in LDS, the next stage's tiles loaded
+//   into registers while the current one is multiplied;
+// * small batches split K over up to 16 workgroups per tile; every split writes
+//   its fp32 partial tile and a second kernel sums the splits in split order,
+//   so the result does not depend on scheduling.
+#include <algorithm>
+
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace nvfp4 {
+
+namespace block_detail {
+
+constexpr int kThreads = 256;
+constexpr int BM = 64;        // activation rows per workgroup
+constexpr int BN = 64;        // weight rows per workgroup (per weight matrix)
+constexpr int BK = 32;        // inputs per stage
+constexpr int LDW = BK + 8;   // LDS row pitch in bf16 (16-byte pad: conflict-free 16-byte reads)
+
+__device__ __forceinline__ u32x4 ld16_guard(const uint16_t* p, bool ok) {
+  return ok ? ld16(p) : u32x4{0, 0, 0, 0};
+}
+
+}  // namespace block_detail
+
+using namespace block_detail;
+
+// NW weight matrices (1: plain, 2: gate and up). Output per MODE:
+//   kBf16F32  - C fp32 [M, N] (splits == 1) or the split's partial;
+//   kBf16Gated- H bf16 [M, N] = bf16(SiLU(C_gate) * C_up) (splits == 1), or the
+//               split's partials of C_gate and C_up ([2][M][N]).
+enum Bf16Mode : int { kBf16F32 = 0, kBf16Gated = 1 };
+
+template <int MODE>
+__global__ __launch_bounds__(kThreads) void bf16_gemm_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w0,
+                                                             const uint16_t* __restrict__ w1, int64_t M, int64_t N,
+                                                             int64_t K, int64_t k_per_split, void* __restrict__ out,
+                                                             float* __restrict__ partial) {
+  constexpr int NW = MODE == kBf16Gated ? 2 : 1;
+  __shared__ __attribute__((aligned(16))) uint16_t xs[2][BM][LDW];
+  __shared__ __attribute__((aligned(16))) uint16_t ws[2][NW * BN][LDW];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wt = wave >> 1, wn = wave & 1;
+  const int64_t m0 = (int64_t)blockIdx.x * BM, n0 = (int64_t)blockIdx.y * BN;
+  const int64_t kb0 = (int64_t)blockIdx.z * k_per_split;
+  const int64_t kb1 = std::min(K, kb0 + k_per_split);
+  const int nst = (int)((kb1 - kb0) / BK);
+
+  // global -> LDS: thread tid moves 16 bytes (8 inputs) of row tid / 4, chunk tid % 4
+  const int lr = tid >> 2, lc = (tid & 3) * 8;
+  const bool xok = m0 + lr < M;
+  const uint16_t* xp = x + (xok ? (m0 + lr) * K : 0) + lc;
+  const uint16_t* wp[NW];
+  bool wok[NW];
+#pragma unroll
+  for (int j = 0; j < NW; ++j) {
+    wok[j] = n0 + lr < N;
+    wp[j] = (j == 0 ? w0 : w1) + (wok[j] ? (n0 + lr) * K : 0) + lc;
+  }
+  u32x4 rx, rw[NW];
+  auto load = [&](int64_t kb) {
+    rx = ld16_guard(xp + kb, xok);
+#pragma unroll
+    for (int j = 0; j < NW; ++j) rw[j] = ld16_guard(wp[j] + kb, wok[j]);
+  };
+  auto store = [&](int b) {
+    st16(&xs[b][lr][lc], rx);
+#pragma unroll
+    for (int j = 0; j < NW; ++j) st16(&ws[b][j * BN + lr][lc], rw[j]);
+  };
+
+  f32x16 acc[NW];
+#pragma unroll
+  for (int j = 0; j < NW; ++j) acc[j] = f32x16{};
+
+  if (nst > 0) {
+    load(kb0);
+    store(0);
+  }
+  __syncthreads();
+  for (int st = 0; st < nst; ++st) {
+    const int b = st & 1;
+    if (st + 1 < nst) load(kb0 + (int64_t)(st + 1) * BK);
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      const int kk = 16 * ks + 8 * (lane >> 5);
+      const bf16x8 B = *reinterpret_cast<const bf16x8*>(&xs[b][32 * wt + (lane & 31)][kk]);
+#pragma unroll
+      for (int j = 0; j < NW; ++j) {
+        const bf16x8 A = *reinterpret_cast<const bf16x8*>(&ws[b][j * BN + 32 * wn + (lane & 31)][kk]);
+        acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, B, acc[j], 0, 0, 0);
+      }
+    }
+    if (st + 1 < nst) store(b ^ 1);
+    __syncthreads();
+  }
+
+  // lane holds C[token m0 + 32wt + lane%32][weight row n0 + 32wn + 8(r/4) + 4(lane/32) + r%4]
+  const int64_t m = m0 + 32 * wt + (lane & 31);
+  if (m >= M) return;
+  const bool split = partial != nullptr;
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const int64_t n = n0 + 32 * wn + 8 * g + 4 * (lane >> 5);
+    if (n >= N) continue;   // N % 4 == 0: the 4 rows are all in or all out
+    if (split) {
+#pragma unroll
+      for (int j = 0; j < NW; ++j) {
+        float* dst = partial + ((int64_t)blockIdx.z * NW + j) * M * N + m * N + n;
+        *reinterpret_cast<f32x4*>(dst) = f32x4{acc[j][4 * g], acc[j][4 * g + 1], acc[j][4 * g + 2], acc[j][4 * g + 3]};
+      }
+    } else if constexpr (MODE == kBf16F32) {
+      *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) + m * N + n) =
+          f32x4{acc[0][4 * g], acc[0][4 * g + 1], acc[0][4 * g + 2], acc[0][4 * g + 3]};
+    } else {
+      float h[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) h[r] = silu(acc[0][4 * g + r]) * acc[NW - 1][4 * g + r];
+      u32x2 o;
+      o[0] = pack_bf16x2(h[0], h[1]);
+      o[1] = pack_bf16x2(h[2], h[3]);
+      *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(out) + m * N + n) = o;
+    }
+  }
+}
+
+// Sum of the splits in split order, then the epilogue of MODE. One thread: 4 outputs.
+template <int MODE>
+__global__ __launch_bounds__(256) void bf16_reduce_kernel(const float* __restrict__ partial, int splits, int64_t M,
+                                                          int64_t N, void* __restrict__ out) {
+  constexpr int NW = MODE == kBf16Gated ? 2 : 1;
+  const int64_t u = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (u >= M * N) return;
+  f32x4 s[NW];
+#pragma unroll
+  for (int j = 0; j < NW; ++j) s[j] = f32x4{0, 0, 0, 0};
+  for (int z = 0; z < splits; ++z)
+#pragma unroll
+    for (int j = 0; j < NW; ++j) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(partial + ((int64_t)z * NW + j) * M * N + u);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) s[j][r] += v[r];
+    }
+  if constexpr (MODE == kBf16F32) {
+    *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) + u) = s[0];
+  } else {
+    u32x2 o;
+    o[0] = pack_bf16x2(silu(s[0][0]) * s[1][0], silu(s[0][1]) * s[1][1]);
+    o[1] = pack_bf16x2(silu(s[0][2]) * s[1][2], silu(s[0][3]) * s[1][3]);
+    *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(out) + u) = o;
+  }
+}
+
+// Top-k of each row of fp32 logits [T, E] (ties to the lower index) and the
+// softmax over the selected. One wave per row; k rounds of a wave-wide arg-max.
+__global__ __launch_bounds__(256) void topk_softmax_kernel(const float* __restrict__ logits, int64_t T, int E, int k,
+                                                           int32_t* __restrict__ ids, float* __restrict__ w) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const float* row = logits + t * E;
+  uint64_t taken = 0;   // bit i: expert lane + 64 i already selected (E <= 4096)
+  float sel_v = 0.0f, top = 0.0f, sum = 0.0f;
+  int sel_e = 0;
+  for (int r = 0; r < k; ++r) {
+    float bv = -INFINITY;
+    int be = 0x7FFFFFFF;
+    for (int i = 0, e = lane; e < E; ++i, e += 64) {
+      if ((taken >> i) & 1) continue;
+      const float v = row[e];
+      if (v > bv || (v == bv && e < be)) {
+        bv = v;
+        be = e;
+      }
+    }
+    for (int off = 32; off >= 1; off >>= 1) {
+      const float ov = __shfl_xor(bv, off);
+      const int oe = __shfl_xor(be, off);
+      if (ov > bv || (ov == bv && oe < be)) {
+        bv = ov;
+        be = oe;
+      }
+    }
+    if ((be & 63) == lane) taken |= 1ull << (be >> 6);
+    if (r == 0) top = bv;
+    const float p = expf(bv - top);
+    sum += p;
+    if (lane == r) {
+      sel_v = p;
+      sel_e = be;
+    }
+  }
+  if (lane < k) {
+    ids[t * k + lane] = sel_e;
+    w[t * k + lane] = sel_v / sum;
+  }
+}
+
+// ------------------------------------------------------------------ launchers
+static int splits_for(int64_t tiles, int64_t K) {
+  // about two workgroups per CU in all; each split keeps >= 256 inputs
+  if (tiles < 1) return 1;
+  const int64_t want = (2 * (int64_t)cu_count() + tiles - 1) / tiles;
+  const int64_t most = std::max<int64_t>(1, K / 256);
+  return (int)std::max<int64_t>(1, std::min<int64_t>({want, most, 16}));
+}
+
+size_t bf16_gemm_partial_bytes(int64_t M, int64_t N, int64_t K, bool gated) {
+  if (M <= 0 || N <= 0 || K <= 0) return 0;
+  const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+  const int s = splits_for(tiles, K);
+  return s > 1 ? (size_t)s * (gated ? 2 : 1) * (size_t)M * (size_t)N * sizeof(float) : 0;
+}
+
+hipError_t launch_bf16_gemm(bool gated, const uint16_t* x, const uint16_t* w0, const uint16_t* w1, int64_t M,
+                            int64_t N, int64_t K, void* out, float* partial, hipStream_t s) {
+  if (M <= 0) return hipSuccess;
+  const int64_t gm = (M + BM - 1) / BM, gn = (N + BN - 1) / BN;
+  const int splits = splits_for(gm * gn, K);
+  int64_t kps = (K / splits + BK - 1) / BK * BK;
+  const int gz = (int)((K + kps - 1) / kps);
+  float* part = gz > 1 ? partial : nullptr;
+  const dim3 grid((unsigned)gm, (unsigned)gn, (unsigned)gz);
+  if (gated)
+    hipLaunchKernelGGL(bf16_gemm_kernel<kBf16Gated>, grid, dim3(kThreads), 0, s, x, w0, w1, M, N, K, kps, out, part);
+  else
+    hipLaunchKernelGGL(bf16_gemm_kernel<kBf16F32>, grid, dim3(kThreads), 0, s, x, w0, w1, M, N, K, kps, out, part);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || gz == 1) return e;
+  const unsigned rg = (unsigned)((M * N / 4 + 255) / 256);
+  if (gated)
+    hipLaunchKernelGGL(bf16_reduce_kernel<kBf16Gated>, dim3(rg), dim3(256), 0, s, part, gz, M, N, out);
+  else
+    hipLaunchKernelGGL(bf16_reduce_kernel<kBf16F32>, dim3(rg), dim3(256), 0, s, part, gz, M, N, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_topk_softmax(const float* logits, int64_t T, int E, int k, int32_t* ids, float* w, hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  hipLaunchKernelGGL(topk_softmax_kernel, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, s, logits, T, E, k, ids, w);
+  return hipGetLastError();
+}
+
+}  // namespace nvfp4

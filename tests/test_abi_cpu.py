@@ -44,7 +44,7 @@ def test_binding_covers_every_symbol():
 
 def test_version_and_status_strings():
     lib = nv.load_library()
-    assert nv.abi_version() == 3
+    assert nv.abi_version() == 4
     for code in range(7):
         assert lib.nvfp4_status_string(code)
     assert b"unknown" in lib.nvfp4_status_string(99)
@@ -218,3 +218,38 @@ def test_workspace_sizes_monotone_and_cover_buffers():
     assert b >= S * 1536 * 2 + S * 4096 * 4          # H (bf16) and Ypart (fp32)
     assert lib.nvfp4_moe_workspace_size(0, 8, 288, 4096, 1536) > 0
     assert lib.nvfp4_moe_workspace_size(4, 0, 288, 4096, 1536) == 0
+
+
+def test_block_validation():
+    lib = nv.load_library()
+    r = lambda T=4, H=256, E=16, k=2, ws=B, wsb=None, x=A, ids=B, w=B + 4096: lib.nvfp4_router_topk(
+        P(x), T, H, P(A), E, k, P(ws), lib.nvfp4_router_workspace_size(T, H, E) if wsb is None else wsb, P(ids), P(w),
+        None)
+    assert r(H=48) == ESHAPE                 # H % 32
+    assert r(E=18) == ESHAPE                 # E % 4
+    assert r(k=17) == ESHAPE                 # k > E
+    assert r(k=0) == ESHAPE
+    assert r(T=0, x=0) == OK
+    assert r(x=0) == ENULL
+    assert r(x=A + 2) == EALIGN
+    assert r(ids=B + 2) == EALIGN
+    assert r(wsb=16) == EWS
+    m = lambda M=4, H=256, Is=128, ws=B, wsb=None, y=B: lib.nvfp4_bf16_mlp(
+        P(A), M, H, P(A), P(A), P(A), Is, P(ws), lib.nvfp4_bf16_mlp_workspace_size(M, H, Is) if wsb is None else wsb,
+        P(y), None)
+    assert m(Is=100) == ESHAPE
+    assert m(H=40) == ESHAPE
+    assert m(M=0) == OK
+    assert m(y=0) == ENULL
+    assert m(y=B + 8) == EALIGN
+    assert m(wsb=8) == EWS
+    gw = _w(n=128, k=256, groups=16)
+    dw = _w(n=256, k=128, groups=16)
+    blk = lambda T=8, k=4, Is=128, wsb=None, sg=A: lib.nvfp4_moe_block(
+        P(A), T, 256, P(A), k, ctypes.byref(gw), ctypes.byref(gw), ctypes.byref(dw), P(sg), P(A), P(A), Is, P(B),
+        lib.nvfp4_moe_block_workspace_size(T, k, 16, 256, 128, Is) if wsb is None else wsb, P(B), None)
+    assert blk(k=17) == ESHAPE
+    assert blk(Is=100) == ESHAPE
+    assert blk(sg=0) == ENULL
+    assert blk(wsb=64) == EWS
+    assert blk(T=0) == OK

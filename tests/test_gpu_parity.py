@@ -457,3 +457,67 @@ def test_moe_w4a4_vs_oracle(T, k, E, H, I, seed, layout):
     # and only by it: W4A16 on the same weights is a different (closer to BF16) answer
     ref16 = OM.moe(x, ids, w, gate, up, down)
     assert np.max(np.abs(ref - ref16)) > 1e-3 * np.max(np.abs(ref16))
+
+
+# ------------------------------------------------------------------ router, shared expert, MoE block
+from oracle import block as OB  # noqa: E402
+
+
+def _margins(lg, k):
+    """Smallest gap among the k + 1 largest logits of each row, relative to the row's max |logit|."""
+    s = -np.sort(-lg, axis=1)[:, :k + 1]
+    return np.min(s[:, :-1] - s[:, 1:], axis=1) / np.max(np.abs(lg), axis=1)
+
+
+def _router_case(T, E, H, seed):
+    x = synth.bf16_normal((T, H), 1.0, seed, synth.S_X)
+    wr = synth.bf16_normal((E, H), 0.02, seed, 77)
+    return x, wr
+
+
+@pytest.mark.parametrize("T,E,H,k,seed", [(5, 16, 256, 4, 100), (64, 288, 4096, 8, 101), (300, 288, 4096, 8, 102)])
+def test_router_topk_vs_oracle(T, E, H, k, seed):
+    note(f"router T={T} E={E} H={H} k={k}")
+    x, wr = _router_case(T, E, H, seed)
+    ids, w = nv.router_topk(bf16_dev(x), bf16_dev(wr), k)
+    torch.cuda.synchronize()
+    ids, w = ids.cpu().numpy(), w.cpu().numpy().astype(np.float64)
+    oid, ow, lg = OB.router(x, wr, k)
+    # where the oracle's top k + 1 logits are separated by more than the fp32 sum's
+    # error (~1e-5 of the row scale here), the choice and order are unique
+    clear = _margins(lg, k) > 1e-4
+    assert clear.mean() > 0.9
+    assert np.array_equal(ids[clear], oid[clear])
+    assert np.allclose(w[clear], ow[clear], rtol=2e-5, atol=1e-6)
+    # elsewhere: k distinct experts whose logits are within the error of the oracle's top k
+    for t in np.nonzero(~clear)[0]:
+        assert len(set(ids[t].tolist())) == k
+        kth = np.sort(lg[t])[-k]
+        assert np.all(lg[t, ids[t]] >= kth - 1e-4 * np.max(np.abs(lg[t])))
+
+
+@pytest.mark.parametrize("M,H,Is,seed", [(1, 4096, 1536, 103), (64, 4096, 1536, 104), (300, 2048, 512, 105),
+                                         (1024, 1024, 2048, 106)])
+def test_bf16_mlp_vs_oracle(M, H, Is, seed):
+    note(f"bf16 mlp M={M} H={H} Is={Is}")
+    x = synth.bf16_normal((M, H), 1.0, seed, synth.S_X)
+    sg, su, sd = (synth.bf16_normal(s, 0.02, seed, 80 + i) for i, s in enumerate([(Is, H), (Is, H), (H, Is)]))
+    y = nv.bf16_mlp(bf16_dev(x), bf16_dev(sg), bf16_dev(su), bf16_dev(sd))
+    torch.cuda.synchronize()
+    assert_close(y.cpu().numpy(), OB.shared_mlp(x, sg, su, sd), "bf16 mlp")
+
+
+@pytest.mark.parametrize("T,k,E,H,I,Is,seed", [(8, 4, 16, 2048, 512, 512, 107), (300, 4, 16, 512, 256, 256, 108)])
+def test_moe_block_vs_oracle(T, k, E, H, I, Is, seed):
+    note(f"moe block T={T} k={k} E={E} H={H} I={I} Is={Is}")
+    x, wr = _router_case(T, E, H, seed)
+    gate = ONV.pack_batch(synth.expert_weights(E, I, H, 0.05, seed, synth.S_GATE))
+    up = ONV.pack_batch(synth.expert_weights(E, I, H, 0.05, seed, synth.S_UP))
+    down = ONV.pack_batch(synth.expert_weights(E, H, I, 0.05, seed, synth.S_DOWN))
+    sg, su, sd = (synth.bf16_normal(s, 0.05, seed, 90 + i) for i, s in enumerate([(Is, H), (Is, H), (H, Is)]))
+    y_ref, oid, _, lg = OB.moe_block(x, wr, k, gate, up, down, sg, su, sd)
+    assert _margins(lg, k).min() > 1e-4          # the routing is unique for this input
+    y = nv.moe_block(bf16_dev(x), bf16_dev(wr), k, weight_dev(gate), weight_dev(up), weight_dev(down),
+                     bf16_dev(sg), bf16_dev(su), bf16_dev(sd))
+    torch.cuda.synchronize()
+    assert_close(bf16_host_f64(y), y_ref, "moe block")
