@@ -55,7 +55,7 @@ def parse():
     p.add_argument("--tokens", type=int, default=64, help="decode batch of the headline step")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-extras", action="store_true", help="only the headline decode step")
-    p.add_argument("--only", choices=["decode", "prefill", "dense", "pack", "w4a4"], default=None,
+    p.add_argument("--only", choices=["decode", "prefill", "dense", "pack", "w4a4", "block"], default=None,
                    help="run one workload only (profiling runs); prints its figures")
     p.add_argument("--layout", choices=["tiled", "rows"], default="tiled",
                    help="weight layout in HBM: blocks of 32 rows (tiled) or row-major")
@@ -215,6 +215,39 @@ def main():
                 "prefill_T4096_zipf": {"TFLOP/s": round(flops / pms / 1e9, 2), "ms_per_call": round(pms, 4),
                                        "frac_mfma_bf16": round(flops / pms / 1e9 / MFMA_BF16_PEAK_TFLOPS, 4)}}
 
+    def run_block(T_dec, steps, warmup):
+        """The whole MoE block (nvfp4_moe_block): BF16 router over the 288 experts
+        (top-8 softmax), routed NVFP4 experts, BF16 shared expert (intermediate 1536,
+        a reading: the pages do not size it), at the decode batch and at 4096 tokens."""
+        log(f"MoE block: T={T_dec} and T=4096")
+        Is = I
+        wr = synth.torch_bf16_normal((E, H), 0.02, 71, dev)
+        sg = synth.torch_bf16_normal((Is, H), 0.02, 72, dev)
+        su = synth.torch_bf16_normal((Is, H), 0.02, 73, dev)
+        sd = synth.torch_bf16_normal((H, Is), 0.02, 74, dev)
+        out = {}
+        for T in (T_dec, 4096):
+            xs = [torch.from_numpy(synth.bf16_normal((T, H), 1.0, 6, synth.S_X, T, r).view(np.int16))
+                  .view(torch.bfloat16).to(dev) for r in range(ROTATE if T <= 64 else 1)]
+            ws = torch.empty((nv.moe_block_workspace_size(T, K_TOP, E, H, I, Is),), dtype=torch.uint8, device=dev)
+            y = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+            call = lambda r: nv.moe_block(xs[r % len(xs)], wr, K_TOP, layer["gate"], layer["up"], layer["down"],
+                                          sg, su, sd, workspace=ws, out=y)
+            n = steps if T <= 64 else max(3, min(steps, 20))
+            for i in range(warmup if T <= 64 else 3):
+                call(i)
+            torch.cuda.synchronize()
+            t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            t0.record()
+            for i in range(n):
+                call(i)
+            t1.record()
+            torch.cuda.synchronize()
+            ms = t0.elapsed_time(t1) / n
+            out[f"T{T}_ms_per_call"] = round(ms, 4)
+        return {"workload": "MoE block: router 288 x 4096 + routed NVFP4 experts + shared BF16 expert 4096 -> 1536",
+                **out}
+
     def run_prefill():
         log("prefill T=4096 Zipf(1.1)")
         Tp = 4096
@@ -301,7 +334,8 @@ def main():
         # one workload alone (profiling runs): its figures only, no headline line
         fig = {"decode": lambda: run_decode(args.tokens, args.steps, args.warmup), "prefill": run_prefill,
                "dense": run_dense, "pack": run_pack,
-               "w4a4": lambda: run_w4a4(args.tokens, args.steps, args.warmup)}[args.only]()
+               "w4a4": lambda: run_w4a4(args.tokens, args.steps, args.warmup),
+               "block": lambda: run_block(args.tokens, args.steps, args.warmup)}[args.only]()
         print(json.dumps({"only": args.only, **fig}), flush=True)
         return
 
@@ -355,6 +389,7 @@ def main():
         result["dense_mlp"] = run_dense()
         result["pack"] = run_pack()
         result["w4a4"] = run_w4a4(args.tokens, args.steps, args.warmup)
+        result["moe_block"] = run_block(args.tokens, args.steps, args.warmup)
 
         # the same headline step on the other weight layout (same values, other byte order)
         other = "rows" if args.layout == "tiled" else "tiled"

@@ -283,7 +283,7 @@ nvfp4_status nvfp4_moe_grouped_w4a4(const uint16_t* x, int64_t T, int64_t H, con
  *   x [T, H] bf16; w_router [n_experts, H] bf16; ws of
  *   nvfp4_router_workspace_size(T, H, n_experts) bytes (16-byte aligned);
  *   topk_ids [T, k] int32 and topk_w [T, k] fp32 out (4-byte aligned).
- * Errors: ERR_SHAPE unless H % 32 == 0, n_experts % 4 == 0, 1 <= k <=
+ * Errors: ERR_SHAPE unless H % 64 == 0, n_experts % 4 == 0, 1 <= k <=
  * min(64, n_experts), n_experts <= 4096; ERR_NULL, ERR_ALIGN, ERR_WORKSPACE.
  */
 size_t nvfp4_router_workspace_size(int64_t T, int64_t H, int32_t n_experts);
@@ -297,7 +297,7 @@ nvfp4_status nvfp4_router_topk(const uint16_t* x, int64_t T, int64_t H, const ui
  *   the intermediate [M, Is] is rounded to bf16 (the down product's operand).
  *   x [M, H] bf16; w_gate, w_up [Is, H] bf16; w_down [H, Is] bf16; ws of
  *   nvfp4_bf16_mlp_workspace_size(M, H, Is) bytes.
- * Errors: ERR_SHAPE unless H and Is are multiples of 32; ERR_NULL, ERR_ALIGN,
+ * Errors: ERR_SHAPE unless H and Is are multiples of 64; ERR_NULL, ERR_ALIGN,
  * ERR_WORKSPACE.
  */
 size_t nvfp4_bf16_mlp_workspace_size(int64_t M, int64_t H, int64_t Is);

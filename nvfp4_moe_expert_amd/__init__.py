@@ -398,3 +398,7 @@ def moe_block(x: torch.Tensor, w_router: torch.Tensor, k: int, gate: NVFP4Weight
                                _ptr(shared_gate), _ptr(shared_up), _ptr(shared_down), Is, _ptr(workspace),
                                workspace.numel(), _ptr(out), _stream()), "nvfp4_moe_block")
     return out
+
+
+def moe_block_workspace_size(T: int, k: int, n_experts: int, H: int, I: int, Is: int) -> int:
+    return load_library().nvfp4_moe_block_workspace_size(T, k, n_experts, H, I, Is)

@@ -224,7 +224,7 @@ BlockLayout block_layout(int64_t T, int k, int64_t E, int64_t H, int64_t I, int6
   return L;
 }
 
-bool bf16_shape_ok(int64_t N, int64_t K) { return N >= 4 && N % 4 == 0 && K >= 32 && K % 32 == 0; }
+bool bf16_shape_ok(int64_t N, int64_t K) { return N >= 4 && N % 4 == 0 && K >= 64 && K % 64 == 0; }
 
 nvfp4_status linear_impl(const uint16_t* x, int64_t m, const nvfp4_weight_t* w0,
                          const nvfp4_weight_t* w1, uint16_t* out, hipStream_t s) {

@@ -11,8 +11,9 @@
 //   multiplied by the same wave, so SiLU(gate) * up is formed in registers);
 // * wave (t, w) multiplies activation rows 32t.. against weight rows 32w.. with
 //   A = weights and B = activations, both read from LDS; the K loop runs in
-//   stages of 32 inputs, double-buffered in LDS, the next stage's tiles loaded
-//   into registers while the current one is multiplied;
+//   stages of 64 inputs, double-buffered in LDS, the next stage's tiles loaded
+//   into registers while the current one is multiplied (small batches are
+//   bound by how many weight bytes are in flight, hence the deep stage);
 // * small batches split K over up to 16 workgroups per tile; every split writes
 //   its fp32 partial tile and a second kernel sums the splits in split order,
 //   so the result does not depend on scheduling.
@@ -28,7 +29,8 @@ namespace block_detail {
 constexpr int kThreads = 256;
 constexpr int BM = 64;        // activation rows per workgroup
 constexpr int BN = 64;        // weight rows per workgroup (per weight matrix)
-constexpr int BK = 32;        // inputs per stage
+constexpr int BK = 64;        // inputs per stage
+constexpr int LPR = BK / 8 / 4;   // 16-byte loads per thread per 64-row tile and stage
 constexpr int LDW = BK + 8;   // LDS row pitch in bf16 (16-byte pad: conflict-free 16-byte reads)
 
 __device__ __forceinline__ u32x4 ld16_guard(const uint16_t* p, bool ok) {
@@ -61,7 +63,8 @@ __global__ __launch_bounds__(kThreads) void bf16_gemm_kernel(const uint16_t* __r
   const int64_t kb1 = std::min(K, kb0 + k_per_split);
   const int nst = (int)((kb1 - kb0) / BK);
 
-  // global -> LDS: thread tid moves 16 bytes (8 inputs) of row tid / 4, chunk tid % 4
+  // global -> LDS: load i of thread tid moves 16 bytes (8 inputs) of row tid / 4,
+  // inputs 8 * (tid % 4) + 32 * i of the stage
   const int lr = tid >> 2, lc = (tid & 3) * 8;
   const bool xok = m0 + lr < M;
   const uint16_t* xp = x + (xok ? (m0 + lr) * K : 0) + lc;
@@ -72,16 +75,22 @@ __global__ __launch_bounds__(kThreads) void bf16_gemm_kernel(const uint16_t* __r
     wok[j] = n0 + lr < N;
     wp[j] = (j == 0 ? w0 : w1) + (wok[j] ? (n0 + lr) * K : 0) + lc;
   }
-  u32x4 rx, rw[NW];
+  u32x4 rx[LPR], rw[NW][LPR];
   auto load = [&](int64_t kb) {
-    rx = ld16_guard(xp + kb, xok);
 #pragma unroll
-    for (int j = 0; j < NW; ++j) rw[j] = ld16_guard(wp[j] + kb, wok[j]);
+    for (int i = 0; i < LPR; ++i) {
+      rx[i] = ld16_guard(xp + kb + 32 * i, xok);
+#pragma unroll
+      for (int j = 0; j < NW; ++j) rw[j][i] = ld16_guard(wp[j] + kb + 32 * i, wok[j]);
+    }
   };
   auto store = [&](int b) {
-    st16(&xs[b][lr][lc], rx);
 #pragma unroll
-    for (int j = 0; j < NW; ++j) st16(&ws[b][j * BN + lr][lc], rw[j]);
+    for (int i = 0; i < LPR; ++i) {
+      st16(&xs[b][lr][lc + 32 * i], rx[i]);
+#pragma unroll
+      for (int j = 0; j < NW; ++j) st16(&ws[b][j * BN + lr][lc + 32 * i], rw[j][i]);
+    }
   };
 
   f32x16 acc[NW];

@@ -110,7 +110,7 @@ hipError_t launch_route(const int32_t* ids, int64_t S, int E, int expert_begin, 
 hipError_t launch_combine(const int32_t* ids, const float* w, const float* ypart, int64_t T, int k,
                           int64_t H, int E, int expert_begin, const float* extra, uint16_t* y, hipStream_t s);
 
-// bf16 GEMM C[m, n] = sum_k x[m, k] * w[n, k] (K % 32 == 0, N % 4 == 0): fp32 C, or
+// bf16 GEMM C[m, n] = sum_k x[m, k] * w[n, k] (K % 64 == 0, N % 4 == 0): fp32 C, or
 // (gated) bf16 SiLU(x.w0^T) * (x.w1^T). `partial` holds bf16_gemm_partial_bytes
 // of scratch for the K-split of small batches (unused when that is 0).
 size_t bf16_gemm_partial_bytes(int64_t M, int64_t N, int64_t K, bool gated);
