@@ -521,3 +521,71 @@ def test_moe_block_vs_oracle(T, k, E, H, I, Is, seed):
                      bf16_dev(sg), bf16_dev(su), bf16_dev(sd))
     torch.cuda.synchronize()
     assert_close(bf16_host_f64(y), y_ref, "moe block")
+
+
+# ------------------------------------------------------------------ edge cases of the added entry points
+def test_moe_w4a4_expert_parallel_slice_duplicates_and_saturation():
+    # expert_begin 4 of 12 ids, duplicate ids, and an input scale small enough that
+    # most blocks of x saturate (byte 0x7E, codes clamped at 6)
+    T, k, E, H, I = 30, 4, 4, 256, 256
+    g = np.random.default_rng(5)
+    ids = g.integers(0, 12, (T, k)).astype(np.int32)
+    ids[:, 1] = ids[:, 0]
+    w = g.uniform(0.1, 1.0, (T, k)).astype(np.float32)
+    x, _, _, gate, up, down = _moe_problem(T, k, E, H, I, 109, sigma=0.05, ids=ids, weights=w)
+    s_gu, s_d = np.float32(0.5 / 2688), np.float32(4.0 / 2688)
+    y = nv.moe_grouped(bf16_dev(x), torch.from_numpy(ids).to(DEV), torch.from_numpy(w).to(DEV), weight_dev(gate),
+                       weight_dev(up), weight_dev(down), expert_begin=4, input_scales=_scale_dev(s_gu, s_d))
+    torch.cuda.synchronize()
+    ref = OM.moe_w4a4(x, ids, w, gate, up, down, s_gu, s_d, expert_begin=4)
+    assert_close(bf16_host_f64(y), ref, "moe w4a4 ep slice")
+    _, sc = ONV.quantize_act(x, s_gu)
+    assert (sc == 0x7E).mean() > 0.5          # the saturating case is exercised
+
+
+def test_moe_w4a4_token_permutation_and_repeat_bitwise():
+    T, k, E, H, I = 64, 8, 32, 512, 1536
+    x, ids, w, gate, up, down = _moe_problem(T, k, E, H, I, 110, sigma=0.05)
+    sc = _scale_dev(4.0 / 2688, 1.0 / 2688)
+    run = lambda xx, ii, ww: bf16_host_bits(nv.moe_grouped(
+        bf16_dev(xx), torch.from_numpy(ii).to(DEV), torch.from_numpy(ww).to(DEV), weight_dev(gate, 1),
+        weight_dev(up, 1), weight_dev(down, 1), input_scales=sc))
+    y1, y2 = run(x, ids, w), run(x, ids, w)
+    assert np.array_equal(y1, y2)
+    p = np.random.default_rng(2).permutation(T)
+    assert np.array_equal(run(x[p], ids[p], w[p]), y1[p])
+
+
+def test_moe_w4a4_rejects_fallback_shapes():
+    # H = 128 is covered only by the fallback GEMM, which has no W4A4 form
+    x, ids, w, gate, up, down = _moe_problem(8, 2, 4, 128, 64, 111)
+    with pytest.raises(RuntimeError):
+        nv.moe_grouped(bf16_dev(x), torch.from_numpy(ids).to(DEV), torch.from_numpy(w).to(DEV), weight_dev(gate),
+                       weight_dev(up), weight_dev(down), input_scales=_scale_dev(0.01, 0.01))
+
+
+@pytest.mark.parametrize("T,E,k", [(1, 20, 20), (3, 20, 1), (33, 8, 2)])
+def test_router_small_and_all_experts(T, E, k):
+    note(f"router T={T} E={E} k={k}")
+    x, wr = _router_case(T, E, 256, 112 + E + k)
+    ids, w = nv.router_topk(bf16_dev(x), bf16_dev(wr), k)
+    torch.cuda.synchronize()
+    oid, ow, lg = OB.router(x, wr, k)
+    assert _margins(lg, min(k, E - 1)).min() > 1e-4
+    assert np.array_equal(ids.cpu().numpy(), oid)
+    assert np.allclose(w.cpu().numpy(), ow, rtol=2e-5, atol=1e-6)
+
+
+def test_moe_block_single_token():
+    T, k, E, H, I, Is, seed = 1, 4, 16, 512, 256, 256, 113
+    x, wr = _router_case(T, E, H, seed)
+    gate = ONV.pack_batch(synth.expert_weights(E, I, H, 0.05, seed, synth.S_GATE))
+    up = ONV.pack_batch(synth.expert_weights(E, I, H, 0.05, seed, synth.S_UP))
+    down = ONV.pack_batch(synth.expert_weights(E, H, I, 0.05, seed, synth.S_DOWN))
+    sg, su, sd = (synth.bf16_normal(s, 0.05, seed, 90 + i) for i, s in enumerate([(Is, H), (Is, H), (H, Is)]))
+    y_ref, _, _, lg = OB.moe_block(x, wr, k, gate, up, down, sg, su, sd)
+    assert _margins(lg, k).min() > 1e-4
+    y = nv.moe_block(bf16_dev(x), bf16_dev(wr), k, weight_dev(gate), weight_dev(up), weight_dev(down),
+                     bf16_dev(sg), bf16_dev(su), bf16_dev(sd))
+    torch.cuda.synchronize()
+    assert_close(bf16_host_f64(y), y_ref, "moe block T=1")
