@@ -67,8 +67,8 @@ def parse():
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this benchmark runs on one GPU; multi-GPU sharding is not part of "
-                                   "this build (see DESIGN.md for how the path would shard)",
+        print(json.dumps({"error": "this benchmark runs on one GPU only: the library has no multi-GPU "
+                                   "(expert- or tensor-parallel) path; run it with --gpus 1",
                           "n_gpus": args.gpus}))
         sys.exit(2)
     import torch

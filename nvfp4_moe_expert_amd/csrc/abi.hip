@@ -97,7 +97,7 @@ nvfp4_status moe_impl(const uint16_t* x, int64_t T, int64_t H, const int32_t* id
                       int32_t k, int32_t eb, const nvfp4_weight_t* gate, const nvfp4_weight_t* up,
                       const nvfp4_weight_t* down, void* ws, size_t ws_bytes, uint16_t* y,
                       hipStream_t s, void* const* events, const float* in_gu = nullptr,
-                      const float* in_d = nullptr, const float* extra = nullptr) {
+                      const float* in_d = nullptr, const float* extra = nullptr, int extra_splits = 1) {
   const bool w4a4 = in_gu || in_d;
   if (w4a4 && !(in_gu && in_d)) return NVFP4_ERR_NULL;
   nvfp4_status st;
@@ -195,7 +195,7 @@ nvfp4_status moe_impl(const uint16_t* x, int64_t T, int64_t H, const int32_t* id
                       : launch_gemm(kDown, v, g, L.max_tiles, s);
   }
   if (e == hipSuccess) e = mark(3);
-  if (e == hipSuccess) e = launch_combine(ids, tw, ypart, T, k, H, (int)E, eb, extra, y, s);
+  if (e == hipSuccess) e = launch_combine(ids, tw, ypart, T, k, H, (int)E, eb, extra, extra_splits, y, s);
   if (e == hipSuccess) e = mark(4);
   return from_hip(e);
 }
@@ -425,8 +425,10 @@ nvfp4_status nvfp4_router_topk(const uint16_t* x, int64_t T, int64_t H, const ui
   float* logits = reinterpret_cast<float*>(ws);
   float* part = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) +
                                          round_up(sizeof(float) * (size_t)(T * n_experts)));
-  hipError_t e = launch_bf16_gemm(false, x, w_router, nullptr, T, n_experts, H, logits, part, s);
-  if (e == hipSuccess) e = launch_topk_softmax(logits, T, n_experts, k, topk_ids, topk_w, s);
+  int splits = 1;
+  hipError_t e = launch_bf16_gemm(false, x, w_router, nullptr, T, n_experts, H, logits, part, s, &splits);
+  if (e == hipSuccess)
+    e = launch_topk_softmax(splits > 1 ? part : logits, splits, T, n_experts, k, topk_ids, topk_w, s);
   return from_hip(e);
 }
 
@@ -483,14 +485,17 @@ nvfp4_status nvfp4_moe_block(const uint16_t* x, int64_t T, int64_t H, const uint
   float* ys = at<float>(ws, L.ys);
   float* part = at<float>(ws, L.part);
   // router, then the shared expert (its fp32 result is added by the routed MLP's
-  // combine, after the k routed slots), then the routed experts
-  hipError_t e = launch_bf16_gemm(false, x, w_router, nullptr, T, E, H, logits, part, s);
-  if (e == hipSuccess) e = launch_topk_softmax(logits, T, (int)E, k, ids, tw, s);
+  // combine, after the k routed slots), then the routed experts. The router's and
+  // the shared down product's K splits are summed by their consumers (top-k,
+  // combine); `part` is free again once each consumer ran, in stream order.
+  int rs = 1, ds = 1;
+  hipError_t e = launch_bf16_gemm(false, x, w_router, nullptr, T, E, H, logits, part, s, &rs);
+  if (e == hipSuccess) e = launch_topk_softmax(rs > 1 ? part : logits, rs, T, (int)E, k, ids, tw, s);
   if (e == hipSuccess) e = launch_bf16_gemm(true, x, shared_gate, shared_up, T, Is, H, hs, part, s);
-  if (e == hipSuccess) e = launch_bf16_gemm(false, hs, shared_down, nullptr, T, H, Is, ys, part, s);
+  if (e == hipSuccess) e = launch_bf16_gemm(false, hs, shared_down, nullptr, T, H, Is, ys, part, s, &ds);
   if (e != hipSuccess) return from_hip(e);
   return moe_impl(x, T, H, ids, tw, k, 0, gate, up, down, at<void>(ws, L.moe), ws_bytes - L.moe, y, s, nullptr,
-                  nullptr, nullptr, ys);
+                  nullptr, nullptr, ds > 1 ? part : ys, ds);
 }
 
 }  // extern "C"

@@ -175,14 +175,33 @@ __global__ __launch_bounds__(256) void bf16_reduce_kernel(const float* __restric
   }
 }
 
-// Top-k of each row of fp32 logits [T, E] (ties to the lower index) and the
-// softmax over the selected. One wave per row; k rounds of a wave-wide arg-max.
-__global__ __launch_bounds__(256) void topk_softmax_kernel(const float* __restrict__ logits, int64_t T, int E, int k,
-                                                           int32_t* __restrict__ ids, float* __restrict__ w) {
-  const int lane = threadIdx.x & 63;
-  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;
-  const float* row = logits + t * E;
+// Top-k of each row of fp32 logits (the sum of `splits` partial rows
+// [splits][T][E], in split order), ties to the lower index, and the softmax over
+// the selected. One wave per row: the row is summed once into LDS, then k rounds
+// of a wave-wide arg-max run on it.
+constexpr int kTopkMaxE = 4096;
+constexpr int kMaxSplits = 16;   // the most K splits splits_for() makes
+__global__ __launch_bounds__(256) void topk_softmax_kernel(const float* __restrict__ logits, int splits, int64_t T,
+                                                           int E, int k, int32_t* __restrict__ ids,
+                                                           float* __restrict__ w) {
+  __shared__ float rows[4][kTopkMaxE];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int64_t t = (int64_t)blockIdx.x * 4 + wv;
+  if (t >= T) return;   // whole wave: no barrier below
+  float* row = rows[wv];
+  for (int e = lane; e < E; e += 64) {
+    float p[kMaxSplits];   // all split loads in flight together, then summed in split order
+#pragma unroll
+    for (int z = 0; z < kMaxSplits; ++z) p[z] = z < splits ? logits[(int64_t)z * T * E + t * E + e] : 0.0f;
+    float v = p[0];
+#pragma unroll
+    for (int z = 1; z < kMaxSplits; ++z)
+      if (z < splits) v += p[z];
+    row[e] = v;
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   uint64_t taken = 0;   // bit i: expert lane + 64 i already selected (E <= 4096)
   float sel_v = 0.0f, top = 0.0f, sum = 0.0f;
   int sel_e = 0;
@@ -226,7 +245,7 @@ static int splits_for(int64_t tiles, int64_t K) {
   if (tiles < 1) return 1;
   const int64_t want = (2 * (int64_t)cu_count() + tiles - 1) / tiles;
   const int64_t most = std::max<int64_t>(1, K / 256);
-  return (int)std::max<int64_t>(1, std::min<int64_t>({want, most, 16}));
+  return (int)std::max<int64_t>(1, std::min<int64_t>({want, most, (int64_t)kMaxSplits}));
 }
 
 size_t bf16_gemm_partial_bytes(int64_t M, int64_t N, int64_t K, bool gated) {
@@ -237,7 +256,8 @@ size_t bf16_gemm_partial_bytes(int64_t M, int64_t N, int64_t K, bool gated) {
 }
 
 hipError_t launch_bf16_gemm(bool gated, const uint16_t* x, const uint16_t* w0, const uint16_t* w1, int64_t M,
-                            int64_t N, int64_t K, void* out, float* partial, hipStream_t s) {
+                            int64_t N, int64_t K, void* out, float* partial, hipStream_t s, int* splits_left) {
+  if (splits_left) *splits_left = 1;
   if (M <= 0) return hipSuccess;
   const int64_t gm = (M + BM - 1) / BM, gn = (N + BN - 1) / BN;
   const int splits = splits_for(gm * gn, K);
@@ -251,6 +271,10 @@ hipError_t launch_bf16_gemm(bool gated, const uint16_t* x, const uint16_t* w0, c
     hipLaunchKernelGGL(bf16_gemm_kernel<kBf16F32>, grid, dim3(kThreads), 0, s, x, w0, w1, M, N, K, kps, out, part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || gz == 1) return e;
+  if (splits_left && !gated) {   // the consumer sums the fp32 splits itself
+    *splits_left = gz;
+    return e;
+  }
   const unsigned rg = (unsigned)((M * N / 4 + 255) / 256);
   if (gated)
     hipLaunchKernelGGL(bf16_reduce_kernel<kBf16Gated>, dim3(rg), dim3(256), 0, s, part, gz, M, N, out);
@@ -259,9 +283,11 @@ hipError_t launch_bf16_gemm(bool gated, const uint16_t* x, const uint16_t* w0, c
   return hipGetLastError();
 }
 
-hipError_t launch_topk_softmax(const float* logits, int64_t T, int E, int k, int32_t* ids, float* w, hipStream_t s) {
+hipError_t launch_topk_softmax(const float* logits, int splits, int64_t T, int E, int k, int32_t* ids, float* w,
+                               hipStream_t s) {
   if (T <= 0) return hipSuccess;
-  hipLaunchKernelGGL(topk_softmax_kernel, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, s, logits, T, E, k, ids, w);
+  hipLaunchKernelGGL(topk_softmax_kernel, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, s, logits, splits, T, E, k,
+                     ids, w);
   return hipGetLastError();
 }
 

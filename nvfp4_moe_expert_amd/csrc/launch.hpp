@@ -106,17 +106,25 @@ hipError_t launch_route(const int32_t* ids, int64_t S, int E, int expert_begin, 
                         int32_t* offsets, int32_t* perm, int32_t* inv, int32_t* tiles,
                         int32_t* n_tiles, const RoutePrep& prep, hipStream_t s);
 
-// y[t] = bf16(sum_j w[t,j] * Ypart[t*k+j] (j in order) + extra[t]); extra may be null.
+// y[t] = bf16(sum_j w[t,j] * Ypart[t*k+j] (j in order) + extra[t]); extra may be null,
+// or hold `extra_splits` partials [extra_splits][T][H] summed in split order.
 hipError_t launch_combine(const int32_t* ids, const float* w, const float* ypart, int64_t T, int k,
-                          int64_t H, int E, int expert_begin, const float* extra, uint16_t* y, hipStream_t s);
+                          int64_t H, int E, int expert_begin, const float* extra, int extra_splits, uint16_t* y,
+                          hipStream_t s);
 
 // bf16 GEMM C[m, n] = sum_k x[m, k] * w[n, k] (K % 64 == 0, N % 4 == 0): fp32 C, or
 // (gated) bf16 SiLU(x.w0^T) * (x.w1^T). `partial` holds bf16_gemm_partial_bytes
 // of scratch for the K-split of small batches (unused when that is 0).
 size_t bf16_gemm_partial_bytes(int64_t M, int64_t N, int64_t K, bool gated);
+// With splits_left != null, an fp32 result split over K is left as its partials
+// ([*splits_left][M][N] in `partial`, summed in split order by the consumer);
+// otherwise (and when there is no split) the result is in `out`.
 hipError_t launch_bf16_gemm(bool gated, const uint16_t* x, const uint16_t* w0, const uint16_t* w1, int64_t M,
-                            int64_t N, int64_t K, void* out, float* partial, hipStream_t s);
-// Per row of fp32 logits [T, E]: the k largest (ties to the lower index) and their softmax.
-hipError_t launch_topk_softmax(const float* logits, int64_t T, int E, int k, int32_t* ids, float* w, hipStream_t s);
+                            int64_t N, int64_t K, void* out, float* partial, hipStream_t s,
+                            int* splits_left = nullptr);
+// Per row of fp32 logits ([splits][T][E], summed in split order): the k largest
+// (ties to the lower index) and their softmax.
+hipError_t launch_topk_softmax(const float* logits, int splits, int64_t T, int E, int k, int32_t* ids, float* w,
+                               hipStream_t s);
 
 }  // namespace nvfp4

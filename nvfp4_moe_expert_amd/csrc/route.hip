@@ -240,7 +240,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict_
                                                       const float* __restrict__ w,
                                                       const float* __restrict__ ypart, int64_t T, int k,
                                                       int64_t H, int E, int eb, const float* __restrict__ extra,
-                                                      uint16_t* __restrict__ y) {
+                                                      int extra_splits, uint16_t* __restrict__ y) {
   const int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t per_tok = H / 8;
   if (u >= T * per_tok) return;
@@ -290,8 +290,17 @@ __global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict_
     }
   }
   if (extra) {   // a contribution summed after the routed slots (the shared expert)
-    const f32x4* ex = reinterpret_cast<const f32x4*>(extra + t * H + c8 * 8);
-    const f32x4 a = ex[0], b = ex[1];
+    f32x4 a = {0, 0, 0, 0}, b = {0, 0, 0, 0};
+#pragma unroll 4
+    for (int z = 0; z < extra_splits; ++z) {   // its K splits, in split order
+      const f32x4* ex = reinterpret_cast<const f32x4*>(extra + (int64_t)z * T * H + t * H + c8 * 8);
+      const f32x4 p = ex[0], q = ex[1];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        a[i] += p[i];
+        b[i] += q[i];
+      }
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       acc[i] += a[i];
@@ -305,13 +314,14 @@ __global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict_
 }
 
 hipError_t launch_combine(const int32_t* ids, const float* w, const float* ypart, int64_t T, int k,
-                          int64_t H, int E, int eb, const float* extra, uint16_t* y, hipStream_t s) {
+                          int64_t H, int E, int eb, const float* extra, int extra_splits, uint16_t* y,
+                          hipStream_t s) {
   const int64_t n = T * (H / 8);
   const int64_t gx = (n + 255) / 256;
   if (k <= 8)
-    hipLaunchKernelGGL(combine_kernel<8>, dim3((unsigned)gx), dim3(256), 0, s, ids, w, ypart, T, k, H, E, eb, extra, y);
+    hipLaunchKernelGGL(combine_kernel<8>, dim3((unsigned)gx), dim3(256), 0, s, ids, w, ypart, T, k, H, E, eb, extra, extra_splits, y);
   else
-    hipLaunchKernelGGL(combine_kernel<0>, dim3((unsigned)gx), dim3(256), 0, s, ids, w, ypart, T, k, H, E, eb, extra, y);
+    hipLaunchKernelGGL(combine_kernel<0>, dim3((unsigned)gx), dim3(256), 0, s, ids, w, ypart, T, k, H, E, eb, extra, extra_splits, y);
   return hipGetLastError();
 }
 
