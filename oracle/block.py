@@ -16,7 +16,11 @@ of scope):
 * the k largest logits are selected, ties going to the lower expert index;
 * the routing weights are the softmax over the k selected logits;
 * shared expert: y_s = (SiLU(x . Wsg^T) * (x . Wsu^T)) . Wsd^T with bf16 weights;
-* MoE block: y = routed MLP (``mlp.moe``) + shared expert, both float64.
+* MoE block: y = routed MLP (``mlp.moe``) + shared expert, both float64;
+* BF16 routed experts (the MTP layer's draft experts kept in BF16, the
+  alternative to packing them that TensorFold issue #308 asks about, "What the
+  branch does"): ``moe_bf16`` is ``mlp.moe`` with bf16 weights and no tensor
+  scale.
 """
 from __future__ import annotations
 
@@ -71,3 +75,26 @@ def moe_block(x_bits, wr_bits, k: int, gate, up, down, wsg_bits, wsu_bits, wsd_b
     ids, w, lg = router(x_bits, wr_bits, k)
     y = moe(x_bits, ids, w.astype(np.float32), gate, up, down) + shared_mlp(x_bits, wsg_bits, wsu_bits, wsd_bits)
     return y, ids, w, lg
+
+
+def moe_bf16(x_bits, ids, weights, wg_bits, wu_bits, wd_bits, expert_begin: int = 0):
+    """Routed expert MLP on BF16 expert weights (gate, up [E, I, H]; down [E, H, I]),
+    float64, with the routing rules of ``mlp.moe``: for each local slot (t, j) of
+    expert e, h = SiLU(x_t . Wg_e^T) * (x_t . Wu_e^T), y_t += w[t, j] * h . Wd_e^T."""
+    x = _bf(x_bits)
+    ids = np.asarray(ids, dtype=np.int64)
+    w = np.asarray(weights, dtype=np.float32).astype(F64)
+    T, k = ids.shape
+    E = wg_bits.shape[0]
+    y = np.zeros((T, x.shape[1]), F64)
+    slots = np.zeros((T, k, x.shape[1]), F64)
+    for e in range(E):
+        tt, jj = np.nonzero(ids == e + expert_begin)
+        if tt.size == 0:
+            continue
+        xe = x[tt]
+        h = silu(xe @ _bf(wg_bits[e]).T) * (xe @ _bf(wu_bits[e]).T)
+        slots[tt, jj] = h @ _bf(wd_bits[e]).T
+    for j in range(k):
+        y += w[:, j:j + 1] * slots[:, j]
+    return y

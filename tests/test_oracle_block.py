@@ -77,3 +77,28 @@ def test_moe_block_is_routed_plus_shared_and_permutes():
     yp, idp, _, _ = block.moe_block(x[p], wr, k, gate, up, down, sg, su, sd)
     assert np.array_equal(idp, ids[p])
     assert np.allclose(yp, y[p], rtol=1e-13, atol=1e-13 * np.max(np.abs(y)))
+
+
+def test_moe_bf16_reduces_to_nvfp4_moe_on_exact_weights():
+    # bf16 expert weights that are exactly NVFP4 values with scale_2 = 1: the BF16
+    # routed MLP and the pinned NVFP4 routed MLP are the same function
+    T, k, E, H, I = 7, 2, 3, 64, 32
+    g = np.random.default_rng(972)
+
+    def exact(n, kk):
+        c4 = g.integers(0, 16, (E, n, kk)).astype(np.uint8)
+        codes = (c4[..., 0::2] | (c4[..., 1::2] << 4)).astype(np.uint8)
+        scales = g.integers(0x28, 0x40, (E, n, kk // 16)).astype(np.uint8)
+        vals = nvfp4.dequant_unscaled(codes, scales)
+        bits = F.f32_to_bf16(vals.astype(np.float32))
+        assert np.array_equal(F.bf16_to_f32(bits).astype(np.float64), vals)
+        return bits, (codes, scales, np.ones(E, np.float32))
+
+    (bg, pg), (bu, pu), (bd, pd) = exact(I, H), exact(I, H), exact(H, I)
+    x = synth.bf16_normal((T, H), 1.0, 973)
+    ids, w = synth.topk_softmax_routing(T, E, k, 974)
+    yb = block.moe_bf16(x, ids, w, bg, bu, bd)
+    yn = mlp.moe(x, ids, w, pg, pu, pd)
+    assert np.allclose(yb, yn, rtol=1e-12, atol=1e-12 * np.max(np.abs(yn)))
+    # skipped ids contribute nothing
+    assert not block.moe_bf16(x, ids, w, bg, bu, bd, expert_begin=E).any()

@@ -87,6 +87,8 @@ MUTANTS = [
      [lambda: TB.test_topk_matches_stable_argsort(7, 16, 4)]),
     (oracle.block, "shared_mlp", "h = silu(x @ _bf(wg_bits).T) * (x @ _bf(wu_bits).T)", "h = silu(x @ _bf(wu_bits).T) * (x @ _bf(wg_bits).T)",
      [TB.test_shared_mlp_reduces_to_dense_nvfp4_mlp]),
+    (oracle.block, "moe_bf16", "slots[tt, jj] = h @ _bf(wd_bits[e]).T", "slots[tt, jj] = h @ _bf(wd_bits[e])[:, ::-1].T",
+     [TB.test_moe_bf16_reduces_to_nvfp4_moe_on_exact_weights]),
 ]
 
 
