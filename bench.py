@@ -55,7 +55,7 @@ def parse():
     p.add_argument("--tokens", type=int, default=64, help="decode batch of the headline step")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-extras", action="store_true", help="only the headline decode step")
-    p.add_argument("--only", choices=["decode", "prefill", "dense", "pack", "w4a4", "block"], default=None,
+    p.add_argument("--only", choices=["decode", "prefill", "dense", "pack", "w4a4", "block", "bf16"], default=None,
                    help="run one workload only (profiling runs); prints its figures")
     p.add_argument("--layout", choices=["tiled", "rows"], default="tiled",
                    help="weight layout in HBM: blocks of 32 rows (tiled) or row-major")
@@ -248,6 +248,52 @@ def main():
         return {"workload": "MoE block: router 288 x 4096 + routed NVFP4 experts + shared BF16 expert 4096 -> 1536",
                 **out}
 
+    def run_bf16_experts(T_dec, steps, warmup):
+        """The routed experts on their BF16 weights (nvfp4_moe_grouped_bf16, the MTP
+        draft experts' alternative to packing), on the same bf16 draws the pack
+        reads: decode at T_dec (HBM: 2 B per weight) and the prefill layer."""
+        log(f"BF16 routed experts: decode T={T_dec}, prefill T=4096")
+        x, ids, w, touched = decode_inputs(T_dec, 3)
+        ws = torch.empty((nv.moe_grouped_bf16_workspace_size(T_dec, K_TOP, E, H, I),), dtype=torch.uint8, device=dev)
+        out = torch.empty((T_dec, H), dtype=torch.bfloat16, device=dev)
+        call = lambda r: nv.moe_grouped_bf16(x[r], ids[r], w[r], raw["gate"], raw["up"], raw["down"], workspace=ws,
+                                             out=out)
+        for i in range(warmup):
+            call(i % ROTATE)
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for i in range(steps):
+            call((warmup + i) % ROTATE)
+        t1.record()
+        torch.cuda.synchronize()
+        ms = t0.elapsed_time(t1)
+        bpe = 3 * I * H * 2
+        dec_bytes = sum(touched[(warmup + i) % ROTATE] * bpe + 2 * T_dec * H * 2 + 2 * T_dec * K_TOP * 4
+                        for i in range(steps))
+        Tp = 4096
+        ids_np, w_np = synth.zipf_routing(Tp, E, K_TOP, 1.1, 4, synth.S_ROUTE)
+        xp = torch.from_numpy(synth.bf16_normal((Tp, H), 1.0, 4, synth.S_X).view(np.int16)).view(torch.bfloat16).to(dev)
+        idp, wp = torch.from_numpy(ids_np).to(dev), torch.from_numpy(w_np).to(dev)
+        wsp = torch.empty((nv.moe_grouped_bf16_workspace_size(Tp, K_TOP, E, H, I),), dtype=torch.uint8, device=dev)
+        outp = torch.empty((Tp, H), dtype=torch.bfloat16, device=dev)
+        pcall = lambda: nv.moe_grouped_bf16(xp, idp, wp, raw["gate"], raw["up"], raw["down"], workspace=wsp, out=outp)
+        for _ in range(2):
+            pcall()
+        torch.cuda.synchronize()
+        psteps = max(3, min(steps, 10))
+        t0.record()
+        for _ in range(psteps):
+            pcall()
+        t1.record()
+        torch.cuda.synchronize()
+        pms = t0.elapsed_time(t1) / psteps
+        flops = 6.0 * Tp * K_TOP * H * I
+        return {f"decode_T{T_dec}": {"GB/s": round(dec_bytes / (ms * 1e-3) / 1e9, 1), "ms_per_step": round(ms / steps, 5),
+                                     "frac_hbm": round(dec_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+                "prefill_T4096_zipf": {"TFLOP/s": round(flops / pms / 1e9, 2), "ms_per_call": round(pms, 4),
+                                       "frac_mfma_bf16": round(flops / pms / 1e9 / MFMA_BF16_PEAK_TFLOPS, 4)}}
+
     def run_prefill():
         log("prefill T=4096 Zipf(1.1)")
         Tp = 4096
@@ -335,7 +381,8 @@ def main():
         fig = {"decode": lambda: run_decode(args.tokens, args.steps, args.warmup), "prefill": run_prefill,
                "dense": run_dense, "pack": run_pack,
                "w4a4": lambda: run_w4a4(args.tokens, args.steps, args.warmup),
-               "block": lambda: run_block(args.tokens, args.steps, args.warmup)}[args.only]()
+               "block": lambda: run_block(args.tokens, args.steps, args.warmup),
+               "bf16": lambda: run_bf16_experts(args.tokens, args.steps, args.warmup)}[args.only]()
         print(json.dumps({"only": args.only, **fig}), flush=True)
         return
 
@@ -390,6 +437,7 @@ def main():
         result["pack"] = run_pack()
         result["w4a4"] = run_w4a4(args.tokens, args.steps, args.warmup)
         result["moe_block"] = run_block(args.tokens, args.steps, args.warmup)
+        result["bf16_experts"] = run_bf16_experts(args.tokens, args.steps, args.warmup)
 
         # the same headline step on the other weight layout (same values, other byte order)
         other = "rows" if args.layout == "tiled" else "tiled"

@@ -70,7 +70,7 @@
 extern "C" {
 #endif
 
-#define NVFP4_ABI_VERSION 4
+#define NVFP4_ABI_VERSION 5
 
 #define NVFP4_LAYOUT_ROWS 0
 #define NVFP4_LAYOUT_TILED32 1
@@ -318,6 +318,25 @@ nvfp4_status nvfp4_moe_block(const uint16_t* x, int64_t T, int64_t H, const uint
                              const nvfp4_weight_t* gate, const nvfp4_weight_t* up, const nvfp4_weight_t* down,
                              const uint16_t* shared_gate, const uint16_t* shared_up, const uint16_t* shared_down,
                              int64_t Is, void* ws, size_t ws_bytes, uint16_t* y, void* stream);
+
+/*
+ * nvfp4_moe_grouped_bf16 - the routed expert MLP on BF16 expert weights: the MTP
+ * layer's draft experts kept in BF16, the alternative to packing them to NVFP4
+ * at load that TensorFold issue #308 asks about ("What the branch does").
+ *
+ * Same routing, arguments and ownership as nvfp4_moe_grouped, with plain bf16
+ * weights w_gate, w_up [n_experts, I, H] and w_down [n_experts, H, I] (device,
+ * row-major, 16-byte aligned; no tensor scale) and a workspace of
+ * nvfp4_moe_grouped_bf16_workspace_size(T, k, n_experts, H, I) bytes. fp32
+ * accumulation (MFMA), H rounded to bf16 as the down product's operand, the
+ * weighted sum over j in order. Errors: ERR_SHAPE unless H and I are multiples
+ * of 64; ERR_NULL, ERR_ALIGN, ERR_WORKSPACE.
+ */
+size_t nvfp4_moe_grouped_bf16_workspace_size(int64_t T, int32_t k, int32_t n_experts, int64_t H, int64_t I);
+nvfp4_status nvfp4_moe_grouped_bf16(const uint16_t* x, int64_t T, int64_t H, const int32_t* topk_ids,
+                                    const float* topk_w, int32_t k, int32_t expert_begin, const uint16_t* w_gate,
+                                    const uint16_t* w_up, const uint16_t* w_down, int32_t n_experts, int64_t I,
+                                    void* ws, size_t ws_bytes, uint16_t* y, void* stream);
 
 #ifdef __cplusplus
 }

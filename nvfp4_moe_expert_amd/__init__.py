@@ -78,6 +78,9 @@ _SIGNATURES = {
     "nvfp4_bf16_mlp": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _P, _I64, _P, _SZ, _P, _P]),
     "nvfp4_moe_block_workspace_size": (_SZ, [_I64, _I32, _I32, _I64, _I64, _I64]),
     "nvfp4_moe_block": (ctypes.c_int, [_P, _I64, _I64, _P, _I32, _WP, _WP, _WP, _P, _P, _P, _I64, _P, _SZ, _P, _P]),
+    "nvfp4_moe_grouped_bf16_workspace_size": (_SZ, [_I64, _I32, _I32, _I64, _I64]),
+    "nvfp4_moe_grouped_bf16": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _I32, _I32, _P, _P, _P, _I32, _I64, _P, _SZ,
+                                              _P, _P]),
 }
 
 
@@ -402,3 +405,33 @@ def moe_block(x: torch.Tensor, w_router: torch.Tensor, k: int, gate: NVFP4Weight
 
 def moe_block_workspace_size(T: int, k: int, n_experts: int, H: int, I: int, Is: int) -> int:
     return load_library().nvfp4_moe_block_workspace_size(T, k, n_experts, H, I, Is)
+
+
+def moe_grouped_bf16(x: torch.Tensor, topk_ids: torch.Tensor, topk_w: torch.Tensor, w_gate: torch.Tensor,
+                     w_up: torch.Tensor, w_down: torch.Tensor, expert_begin: int = 0,
+                     workspace: torch.Tensor | None = None, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Routed expert MLP on BF16 expert weights (gate, up [E, I, H]; down [E, H, I]): y [T, H] bf16."""
+    lib = load_library()
+    _need(x, torch.bfloat16, "x", 2)
+    _need(topk_ids, torch.int32, "topk_ids", 2)
+    _need(topk_w, torch.float32, "topk_w", 2)
+    for t, n in ((w_gate, "w_gate"), (w_up, "w_up"), (w_down, "w_down")):
+        _need(t, torch.bfloat16, n, 3)
+    T, H = x.shape
+    k = topk_ids.shape[1]
+    E, I = w_gate.shape[0], w_gate.shape[1]
+    if w_gate.shape != (E, I, H) or w_up.shape != (E, I, H) or w_down.shape != (E, H, I):
+        raise ValueError("expert weights: gate, up [E, I, H]; down [E, H, I]")
+    if workspace is None:
+        workspace = torch.empty((max(lib.nvfp4_moe_grouped_bf16_workspace_size(T, k, E, H, I), 256),),
+                                dtype=torch.uint8, device=x.device)
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
+    _check(lib.nvfp4_moe_grouped_bf16(_ptr(x), T, H, _ptr(topk_ids), _ptr(topk_w), k, expert_begin, _ptr(w_gate),
+                                      _ptr(w_up), _ptr(w_down), E, I, _ptr(workspace), workspace.numel(), _ptr(out),
+                                      _stream()), "nvfp4_moe_grouped_bf16")
+    return out
+
+
+def moe_grouped_bf16_workspace_size(T: int, k: int, n_experts: int, H: int, I: int) -> int:
+    return load_library().nvfp4_moe_grouped_bf16_workspace_size(T, k, n_experts, H, I)

@@ -498,4 +498,50 @@ nvfp4_status nvfp4_moe_block(const uint16_t* x, int64_t T, int64_t H, const uint
                   nullptr, nullptr, ds > 1 ? part : ys, ds);
 }
 
+size_t nvfp4_moe_grouped_bf16_workspace_size(int64_t T, int32_t k, int32_t n_experts, int64_t H, int64_t I) {
+  if (T < 0 || k < 1 || n_experts < 1 || H < 1 || I < 1) return 0;
+  const int64_t S = T * k, max_tiles = S / 64 + (S < n_experts ? S : n_experts);
+  return round_up(sizeof(int32_t) * (size_t)(n_experts + 1)) + round_up(sizeof(int32_t) * (size_t)(S > 0 ? S : 1)) +
+         round_up(sizeof(int32_t) * 4 * (size_t)(max_tiles > 0 ? max_tiles : 1)) + 256 +
+         round_up(sizeof(uint16_t) * (size_t)(S * I > 0 ? S * I : 1)) +
+         round_up(sizeof(float) * (size_t)(S * H > 0 ? S * H : 1));
+}
+
+nvfp4_status nvfp4_moe_grouped_bf16(const uint16_t* x, int64_t T, int64_t H, const int32_t* topk_ids,
+                                    const float* topk_w, int32_t k, int32_t expert_begin, const uint16_t* w_gate,
+                                    const uint16_t* w_up, const uint16_t* w_down, int32_t n_experts, int64_t I,
+                                    void* ws, size_t ws_bytes, uint16_t* y, void* stream) {
+  if (T < 0 || k < 1 || k > kMaxTopk || n_experts < 1 || n_experts > kMaxExperts || T * (int64_t)k > kMaxSlots ||
+      !bf16_shape_ok(I, H) || !bf16_shape_ok(H, I) || H % 8 != 0)
+    return NVFP4_ERR_SHAPE;
+  if (T == 0) return NVFP4_OK;
+  if (!x || !topk_ids || !topk_w || !w_gate || !w_up || !w_down || !ws || !y) return NVFP4_ERR_NULL;
+  if (!aligned16(x) || !aligned16(w_gate) || !aligned16(w_up) || !aligned16(w_down) || !aligned16(ws) ||
+      !aligned16(y))
+    return NVFP4_ERR_ALIGN;
+  if (ws_bytes < nvfp4_moe_grouped_bf16_workspace_size(T, k, n_experts, H, I)) return NVFP4_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t S = T * k, max_tiles = S / 64 + (S < n_experts ? S : n_experts);
+  char* p = reinterpret_cast<char*>(ws);
+  int32_t* offsets = reinterpret_cast<int32_t*>(p);
+  p += round_up(sizeof(int32_t) * (size_t)(n_experts + 1));
+  int32_t* perm = reinterpret_cast<int32_t*>(p);
+  p += round_up(sizeof(int32_t) * (size_t)S);
+  int32_t* tiles = reinterpret_cast<int32_t*>(p);
+  p += round_up(sizeof(int32_t) * 4 * (size_t)max_tiles);
+  int32_t* n_tiles = reinterpret_cast<int32_t*>(p);
+  p += 256;
+  uint16_t* h = reinterpret_cast<uint16_t*>(p);
+  p += round_up(sizeof(uint16_t) * (size_t)(S * I));
+  float* ypart = reinterpret_cast<float*>(p);
+  hipError_t e = launch_route(topk_ids, S, n_experts, expert_begin, 64, offsets, perm, nullptr, tiles, n_tiles,
+                              RoutePrep{}, s);
+  if (e == hipSuccess)
+    e = launch_bf16_grouped(true, x, w_gate, w_up, tiles, n_tiles, max_tiles, perm, k, I, H, h, s);
+  if (e == hipSuccess)
+    e = launch_bf16_grouped(false, h, w_down, nullptr, tiles, n_tiles, max_tiles, perm, 0, H, I, ypart, s);
+  if (e == hipSuccess) e = launch_combine(topk_ids, topk_w, ypart, T, k, H, n_experts, expert_begin, nullptr, 1, y, s);
+  return from_hip(e);
+}
+
 }  // extern "C"

@@ -47,18 +47,43 @@ using namespace block_detail;
 //               split's partials of C_gate and C_up ([2][M][N]).
 enum Bf16Mode : int { kBf16F32 = 0, kBf16Gated = 1 };
 
-template <int MODE>
+// Grouped form (routed experts with bf16 weights): workgroup x takes tile x of
+// the route's tile list (expert e, rows rb .. rb+rows of the permuted order, at
+// most 64); weights are expert e's [N, K]; activation row r is x[perm[rb+r] /
+// topk] (topk > 0: gate/up on tokens) or x[rb+r] (topk == 0: down on H rows in
+// permuted order); results go to row rb+r (gate/up: H) or to slot perm[rb+r]
+// (down: Ypart). No K split.
+struct Bf16Group {
+  const int32_t* tiles;    // null: plain GEMM
+  const int32_t* n_tiles;
+  const int32_t* perm;
+  int topk;
+  int64_t w_stride;        // elements of one expert's weight
+};
+
+template <int MODE, bool GROUPED>
 __global__ __launch_bounds__(kThreads) void bf16_gemm_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w0,
                                                              const uint16_t* __restrict__ w1, int64_t M, int64_t N,
                                                              int64_t K, int64_t k_per_split, void* __restrict__ out,
-                                                             float* __restrict__ partial) {
+                                                             float* __restrict__ partial, Bf16Group grp) {
   constexpr int NW = MODE == kBf16Gated ? 2 : 1;
   __shared__ __attribute__((aligned(16))) uint16_t xs[2][BM][LDW];
   __shared__ __attribute__((aligned(16))) uint16_t ws[2][NW * BN][LDW];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wt = wave >> 1, wn = wave & 1;
-  const int64_t m0 = (int64_t)blockIdx.x * BM, n0 = (int64_t)blockIdx.y * BN;
+  int64_t m0 = (int64_t)blockIdx.x * BM, rb = 0;
+  if constexpr (GROUPED) {
+    const int tile = (int)blockIdx.x;
+    if (tile >= *grp.n_tiles) return;
+    const int32_t* t = grp.tiles + 4 * (int64_t)tile;
+    w0 += (int64_t)t[0] * grp.w_stride;
+    if (NW == 2) w1 += (int64_t)t[0] * grp.w_stride;
+    rb = t[1];
+    M = t[2];   // rows of this tile
+    m0 = 0;
+  }
+  const int64_t n0 = (int64_t)blockIdx.y * BN;
   const int64_t kb0 = (int64_t)blockIdx.z * k_per_split;
   const int64_t kb1 = std::min(K, kb0 + k_per_split);
   const int nst = (int)((kb1 - kb0) / BK);
@@ -67,7 +92,11 @@ __global__ __launch_bounds__(kThreads) void bf16_gemm_kernel(const uint16_t* __r
   // inputs 8 * (tid % 4) + 32 * i of the stage
   const int lr = tid >> 2, lc = (tid & 3) * 8;
   const bool xok = m0 + lr < M;
-  const uint16_t* xp = x + (xok ? (m0 + lr) * K : 0) + lc;
+  int64_t xrow = m0 + lr;
+  if constexpr (GROUPED) {
+    if (xok) xrow = grp.topk > 0 ? grp.perm[rb + lr] / grp.topk : rb + lr;
+  }
+  const uint16_t* xp = x + (xok ? xrow * K : 0) + lc;
   const uint16_t* wp[NW];
   bool wok[NW];
 #pragma unroll
@@ -120,9 +149,10 @@ __global__ __launch_bounds__(kThreads) void bf16_gemm_kernel(const uint16_t* __r
   }
 
   // lane holds C[token m0 + 32wt + lane%32][weight row n0 + 32wn + 8(r/4) + 4(lane/32) + r%4]
-  const int64_t m = m0 + 32 * wt + (lane & 31);
+  int64_t m = m0 + 32 * wt + (lane & 31);
   if (m >= M) return;
-  const bool split = partial != nullptr;
+  if constexpr (GROUPED) m = (MODE == kBf16F32) ? grp.perm[rb + m] : rb + m;   // output row
+  const bool split = !GROUPED && partial != nullptr;
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
     const int64_t n = n0 + 32 * wn + 8 * g + 4 * (lane >> 5);
@@ -255,6 +285,21 @@ size_t bf16_gemm_partial_bytes(int64_t M, int64_t N, int64_t K, bool gated) {
   return s > 1 ? (size_t)s * (gated ? 2 : 1) * (size_t)M * (size_t)N * sizeof(float) : 0;
 }
 
+hipError_t launch_bf16_grouped(bool gated, const uint16_t* x, const uint16_t* w0, const uint16_t* w1,
+                               const int32_t* tiles, const int32_t* n_tiles, int64_t max_tiles, const int32_t* perm,
+                               int topk, int64_t N, int64_t K, void* out, hipStream_t s) {
+  if (max_tiles <= 0) return hipSuccess;
+  const Bf16Group grp{tiles, n_tiles, perm, topk, N * K};
+  const dim3 grid((unsigned)max_tiles, (unsigned)((N + BN - 1) / BN), 1u);
+  if (gated)
+    hipLaunchKernelGGL((bf16_gemm_kernel<kBf16Gated, true>), grid, dim3(kThreads), 0, s, x, w0, w1, (int64_t)0, N, K,
+                       K, out, nullptr, grp);
+  else
+    hipLaunchKernelGGL((bf16_gemm_kernel<kBf16F32, true>), grid, dim3(kThreads), 0, s, x, w0, w1, (int64_t)0, N, K,
+                       K, out, nullptr, grp);
+  return hipGetLastError();
+}
+
 hipError_t launch_bf16_gemm(bool gated, const uint16_t* x, const uint16_t* w0, const uint16_t* w1, int64_t M,
                             int64_t N, int64_t K, void* out, float* partial, hipStream_t s, int* splits_left) {
   if (splits_left) *splits_left = 1;
@@ -265,10 +310,13 @@ hipError_t launch_bf16_gemm(bool gated, const uint16_t* x, const uint16_t* w0, c
   const int gz = (int)((K + kps - 1) / kps);
   float* part = gz > 1 ? partial : nullptr;
   const dim3 grid((unsigned)gm, (unsigned)gn, (unsigned)gz);
+  const Bf16Group none{};
   if (gated)
-    hipLaunchKernelGGL(bf16_gemm_kernel<kBf16Gated>, grid, dim3(kThreads), 0, s, x, w0, w1, M, N, K, kps, out, part);
+    hipLaunchKernelGGL((bf16_gemm_kernel<kBf16Gated, false>), grid, dim3(kThreads), 0, s, x, w0, w1, M, N, K, kps, out,
+                       part, none);
   else
-    hipLaunchKernelGGL(bf16_gemm_kernel<kBf16F32>, grid, dim3(kThreads), 0, s, x, w0, w1, M, N, K, kps, out, part);
+    hipLaunchKernelGGL((bf16_gemm_kernel<kBf16F32, false>), grid, dim3(kThreads), 0, s, x, w0, w1, M, N, K, kps, out,
+                       part, none);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || gz == 1) return e;
   if (splits_left && !gated) {   // the consumer sums the fp32 splits itself

@@ -44,7 +44,7 @@ def test_binding_covers_every_symbol():
 
 def test_version_and_status_strings():
     lib = nv.load_library()
-    assert nv.abi_version() == 4
+    assert nv.abi_version() == 5
     for code in range(7):
         assert lib.nvfp4_status_string(code)
     assert b"unknown" in lib.nvfp4_status_string(99)
@@ -253,3 +253,18 @@ def test_block_validation():
     assert blk(sg=0) == ENULL
     assert blk(wsb=64) == EWS
     assert blk(T=0) == OK
+
+
+def test_moe_grouped_bf16_validation():
+    lib = nv.load_library()
+    f = lambda T=8, H=256, k=2, E=4, I=128, x=A, wsb=None, ws=B: lib.nvfp4_moe_grouped_bf16(
+        P(x), T, H, P(A), P(A), k, 0, P(A), P(A), P(A), E, I, P(ws),
+        lib.nvfp4_moe_grouped_bf16_workspace_size(T, k, E, H, I) if wsb is None else wsb, P(B), None)
+    assert f(I=100) == ESHAPE
+    assert f(H=96) == ESHAPE
+    assert f(k=0) == ESHAPE
+    assert f(E=0) == ESHAPE
+    assert f(T=0, x=0) == OK
+    assert f(x=0) == ENULL
+    assert f(x=A + 2) == EALIGN
+    assert f(wsb=64) == EWS

@@ -589,3 +589,31 @@ def test_moe_block_single_token():
                      bf16_dev(sg), bf16_dev(su), bf16_dev(sd))
     torch.cuda.synchronize()
     assert_close(bf16_host_f64(y), y_ref, "moe block T=1")
+
+
+# ------------------------------------------------------------------ BF16 routed experts
+@pytest.mark.parametrize("T,k,E,H,I,seed,eb", [
+    (8, 4, 16, 2048, 512, 114, 0),      # decode-like: ~2 rows per expert
+    (300, 4, 6, 512, 256, 115, 0),      # 200 rows per expert: 4 tiles of 64, the last ragged
+    (1, 8, 12, 256, 128, 116, 0),       # one token
+    (30, 4, 4, 256, 128, 117, 4),       # expert-parallel slice (ids 0..11, local 4..7), duplicates
+])
+def test_moe_grouped_bf16_vs_oracle(T, k, E, H, I, seed, eb):
+    note(f"moe bf16 T={T} k={k} E={E} H={H} I={I} eb={eb}")
+    x = synth.bf16_normal((T, H), 1.0, seed, synth.S_X)
+    if eb:
+        g = np.random.default_rng(seed)
+        ids = g.integers(0, 3 * E, (T, k)).astype(np.int32)
+        ids[:, 1] = ids[:, 0]
+        w = g.uniform(0.1, 1.0, (T, k)).astype(np.float32)
+    else:
+        ids, w = synth.topk_softmax_routing(T, E, k, seed, synth.S_ROUTE)
+    wg = synth.expert_weights(E, I, H, 0.05, seed, synth.S_GATE)
+    wu = synth.expert_weights(E, I, H, 0.05, seed, synth.S_UP)
+    wd = synth.expert_weights(E, H, I, 0.05, seed, synth.S_DOWN)
+    y = nv.moe_grouped_bf16(bf16_dev(x), torch.from_numpy(ids.astype(np.int32)).to(DEV),
+                            torch.from_numpy(w.astype(np.float32)).to(DEV), bf16_dev(wg), bf16_dev(wu), bf16_dev(wd),
+                            expert_begin=eb)
+    torch.cuda.synchronize()
+    ref = OB.moe_bf16(x, ids, w, wg, wu, wd, expert_begin=eb)
+    assert_close(bf16_host_f64(y), ref, "moe bf16")
