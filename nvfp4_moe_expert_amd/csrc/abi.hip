@@ -43,8 +43,11 @@ WeightDev dev_weight(const nvfp4_weight_t* w) {
 // prefill-tile matrix-core kernel, or the tiled fallback (row-major weights
 // only). Tiled weights take the prefill kernel wherever the decode kernel does
 // not apply; kNone if no kernel covers the call.
-enum Kern { kKDec, kKPre, kKV1, kKNone };
+enum Kern { kKDec, kKPre, kKV1, kKNone, kKDecS };
 Kern pick(GemmMode mode, GemmVariant v, bool tiled, int64_t x_rows, int64_t K, int64_t N) {
+  // tiny batches: gate/up splits K over the waves (its 8 stages of 512 inputs are the
+  // long pole); down (few stages) keeps the decode kernels, on the same 4-row tiles
+  if (v == kDecodeSmall) return mode == kGateUp ? kKDecS : (decode_supported(mode, K, N) ? kKDec : kKV1);
   if (v == kDecode && decode_supported(mode, K, N)) return kKDec;
   if ((v == kPrefill || tiled) && prefill_supported(mode, x_rows, K, N)) return kKPre;
   return tiled ? kKNone : kKV1;
@@ -60,16 +63,18 @@ struct MoeLayout {
   int64_t max_tiles;
 };
 
-// Decode tiles (16 rows) when the average local expert gets at most 16 rows, else prefill tiles.
-GemmVariant moe_variant(int64_t S, int64_t E) {
+// Decode tiles (16 rows) when the average local expert gets at most 16 rows, else prefill tiles;
+// for at most 32 slots, 4-row tiles with gate/up's K split over the waves (when the shapes fit).
+GemmVariant moe_variant(int64_t S, int64_t E, int64_t H, int64_t I) {
   const int64_t busy = S < E ? S : E;
+  if (S <= 32 && decode_small_supported(H, I) && decode_supported(kDown, I, H)) return kDecodeSmall;
   return (busy > 0 && S <= 16 * busy) ? kDecode : kPrefill;
 }
 
 MoeLayout moe_layout(int64_t T, int k, int64_t E, int64_t H, int64_t I) {
   MoeLayout L{};
   const int64_t S = T * k;
-  const int64_t tr = variant_tile_rows(moe_variant(S, E));
+  const int64_t tr = variant_tile_rows(moe_variant(S, E, H, I));
   // sum over experts of ceil(rows/tr) <= floor(S/tr) + (number of non-empty experts)
   L.max_tiles = S / tr + (S < E ? S : E);
   size_t off = 0;
@@ -120,7 +125,7 @@ nvfp4_status moe_impl(const uint16_t* x, int64_t T, int64_t H, const int32_t* id
     if (ws_bytes < L.total) return NVFP4_ERR_WORKSPACE;
   }
   const int64_t S = T * k;
-  const GemmVariant v = moe_variant(S, E);
+  const GemmVariant v = moe_variant(S, E, H, I);
   const Kern kg = pick(kGateUp, v, gate->layout == NVFP4_LAYOUT_TILED32, T, H, I);
   const Kern kd = pick(kDown, v, down->layout == NVFP4_LAYOUT_TILED32, S, I, H);
   if (T > 0 && (kg == kKNone || kd == kKNone)) return NVFP4_ERR_SHAPE;
@@ -171,7 +176,8 @@ nvfp4_status moe_impl(const uint16_t* x, int64_t T, int64_t H, const int32_t* id
     g.K = H;
     g.out = hbuf;
     g.act_scale = in_gu;
-    e = kg == kKDec   ? launch_decode(kGateUp, f16, g, dx, L.max_tiles, s)
+    e = kg == kKDecS  ? launch_decode_small(kGateUp, g, dx, L.max_tiles, s)
+        : kg == kKDec ? launch_decode(kGateUp, f16, g, dx, L.max_tiles, s)
         : kg == kKPre ? launch_prefill(kGateUp, f16, g, dx, L.max_tiles, s)
                       : launch_gemm(kGateUp, v, g, L.max_tiles, s);
   }
@@ -190,7 +196,8 @@ nvfp4_status moe_impl(const uint16_t* x, int64_t T, int64_t H, const int32_t* id
     g.K = I;
     g.out = ypart;
     g.act_scale = in_d;
-    e = kd == kKDec   ? launch_decode(kDown, f16, g, dx, L.max_tiles, s)
+    e = kd == kKDecS  ? launch_decode_small(kDown, g, dx, L.max_tiles, s)
+        : kd == kKDec ? launch_decode(kDown, f16, g, dx, L.max_tiles, s)
         : kd == kKPre ? launch_prefill(kDown, f16, g, dx, L.max_tiles, s)
                       : launch_gemm(kDown, v, g, L.max_tiles, s);
   }

@@ -235,7 +235,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs a) {
   }
 }
 
-int variant_tile_rows(GemmVariant v) { return v == kDecode ? 16 : 128; }
+int variant_tile_rows(GemmVariant v) { return v == kDecodeSmall ? 4 : v == kDecode ? 16 : 128; }
 
 template <int MODE>
 static hipError_t launch_mode(GemmVariant v, const GemmArgs& a, int64_t grid_tiles, hipStream_t s) {

@@ -531,6 +531,179 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(PER ? 
   }
 }
 
+// Tiny batches (tiles of at most 4 rows, routed modes, fp16 form): the grid of
+// 64-row workgroups is too small to fill the chip (one token: 8 experts x 24
+// blocks of gate/up), and each workgroup streams K in a row of dependent stages.
+// Here the 4 waves of a workgroup take the same 16 weight rows and split the
+// stages of K among themselves (wave w: stages w, w + 4, ...), so there are 4x
+// the workgroups with a quarter of the stages each. The whole activation tile
+// (<= 4 rows x K <= 4096, fp16) sits in LDS; the waves' partial sums are added
+// through LDS in wave order, then wave 0 applies the epilogue.
+constexpr int kSmallRows = 4;
+constexpr int kSmallMaxK = 4096;
+
+template <int MODE, bool TL>
+__global__ __launch_bounds__(kThreads) void gemm_decode_ks_kernel(GemmArgs a, F16Args d) {
+  static_assert(MODE == kGateUp || MODE == kDown, "routed modes");
+  constexpr bool kTwo = MODE == kGateUp;
+  constexpr int U = 4, KC = 128 * U;
+  __shared__ __attribute__((aligned(16))) uint16_t xs[kSmallRows][kSmallMaxK + 8];
+  __shared__ f32x4 red[3][2][64];
+
+  if ((int)blockIdx.x >= *a.n_tiles) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lr = lane & 15, q = lane >> 4;
+  const int64_t N = a.N, K = a.K;
+  const int32_t* t = a.tiles + 4 * (int64_t)blockIdx.x;
+  const int e = t[0], rb = t[1], rows = t[2];
+
+  const int64_t nrow = (int64_t)blockIdx.y * 16 + lr;
+  int64_t coff, soff;
+  if constexpr (TL) {
+    const int64_t R = nrow / 32, r = nrow % 32;
+    coff = (int64_t)e * N * (K / 2) + (R * (K / 32) + U * q) * 512 + r * 16;
+    soff = (int64_t)e * N * (K / 16) + (R * (K / 256) + (2 * U * q) / 16) * 512 + r * 16 + (2 * U * q) % 16;
+  } else {
+    const int64_t wrow = (int64_t)e * N + nrow;
+    coff = wrow * (K / 2) + 16 * U * q;
+    soff = wrow * (K / 16) + 2 * U * q;
+  }
+  const uint8_t* c0 = a.w0.codes + coff;
+  const uint8_t* s0 = a.w0.scales + soff;
+  const uint8_t* c1 = kTwo ? a.w1.codes + coff : nullptr;
+  const uint8_t* s1 = kTwo ? a.w1.scales + soff : nullptr;
+  const int64_t SSTEP = TL ? 2 * KC : KC / 16;
+  const int nst = (int)(K / KC);
+
+  // this wave's first stage goes out before the activation staging
+  Stage<U> Cg[2], Cu[2];
+  u32x2 sg[2], su[2];
+  auto load = [&](int b, int st) {
+    load_codes<U, TL>(Cg[b], c0, (int64_t)st * KC);
+    sg[b] = *reinterpret_cast<const u32x2*>(s0 + st * SSTEP);
+    if constexpr (kTwo) {
+      load_codes<U, TL>(Cu[b], c1, (int64_t)st * KC);
+      su[b] = *reinterpret_cast<const u32x2*>(s1 + st * SSTEP);
+    }
+  };
+  if (wave < nst) load(0, wave);
+
+  // activation rows in fp16: gate/up reads the prep's x16 row of the slot's token,
+  // down converts its bf16 H row with the row's power of two
+  for (int64_t u = tid; u < kSmallRows * (K / 8); u += kThreads) {
+    const int r = (int)(u / (K / 8));
+    const int64_t c = u % (K / 8);
+    u32x4 o = {0, 0, 0, 0};
+    if (r < rows) {
+      if constexpr (kTwo) {
+        o = ld16(d.x16 + (int64_t)(a.perm[rb + r] / a.topk) * K + 8 * c);
+      } else {
+        const u32x4 v = ld16(a.x + (int64_t)(rb + r) * K + 8 * c);
+        const float sc = ldexpf(1.0f, row_exponent(d.hmax[rb + r]));
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const f16x2 h2 = {(_Float16)(bf16_lo(v[j]) * sc), (_Float16)(bf16_hi(v[j]) * sc)};
+          o[j] = __builtin_bit_cast(uint32_t, h2);
+        }
+      }
+    }
+    st16(&xs[r][8 * c], o);
+  }
+  __syncthreads();
+
+  f32x4 acc0 = {0, 0, 0, 0}, acc1 = {0, 0, 0, 0};
+  const f16x8 zero8 = {};
+  // stage st from register set b (a literal at each call, so the sets stay in registers)
+  auto step = [&](const int b, int st) {
+    if (st + 4 < nst) load(b ^ 1, st + 4);
+    const int64_t kb = (int64_t)st * KC;
+#pragma unroll
+    for (int i = 0; i < U; ++i) {
+      const f16x2 sgf = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sg[b][i / 2] >> (16 * (i & 1)), 1.0f, false);
+      f16x2 suf = {};
+      if constexpr (kTwo) suf = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(su[b][i / 2] >> (16 * (i & 1)), 1.0f, false);
+#pragma unroll
+      for (int sst = 0; sst < 4; ++sst) {
+        const f16x8 B = lr < kSmallRows
+                            ? *reinterpret_cast<const f16x8*>(&xs[lr < kSmallRows ? lr : 0][kb + 32 * U * q + 32 * i + 8 * sst])
+                            : zero8;
+        const f16x2 gs = (sst < 2) ? f16x2{sgf[0], sgf[0]} : f16x2{sgf[1], sgf[1]};
+        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(dequant8_f16(Cg[b].c[i][sst], gs), B, acc0, 0, 0, 0);
+        if constexpr (kTwo) {
+          const f16x2 us = (sst < 2) ? f16x2{suf[0], suf[0]} : f16x2{suf[1], suf[1]};
+          acc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(dequant8_f16(Cu[b].c[i][sst], us), B, acc1, 0, 0, 0);
+        }
+      }
+    }
+  };
+  for (int st = wave; st < nst; st += 8) {
+    step(0, st);
+    if (st + 4 < nst) step(1, st + 4);
+  }
+
+  // partial sums of waves 1..3 to wave 0, added in wave order
+  if (wave > 0) {
+    red[wave - 1][0][lane] = acc0;
+    if constexpr (kTwo) red[wave - 1][1][lane] = acc1;
+  }
+  __syncthreads();
+  if (wave > 0) return;
+#pragma unroll
+  for (int w = 0; w < 3; ++w) {
+    const f32x4 p0 = red[w][0][lane];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc0[r] += p0[r];
+    if constexpr (kTwo) {
+      const f32x4 p1 = red[w][1][lane];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc1[r] += p1[r];
+    }
+  }
+
+  // ---- epilogue: lane holds D[n = 16 by + 4q + r][token lr], r = 0..3
+  if (lr >= rows) return;
+  const int64_t p = rb + lr;
+  const int64_t n0 = (int64_t)blockIdx.y * 16 + 4 * q;
+  float unscale = kTwo ? ldexpf(1.0f, -d.xexp[a.perm[p] / a.topk]) : ldexpf(1.0f, -row_exponent(d.hmax[p]));
+  if (a.act_scale) unscale *= *a.act_scale;   // W4A4: the activations' input_scale
+  const float s2a = a.w0.scale_2[e] * unscale;
+  const float s2b = kTwo ? a.w1.scale_2[e] * unscale : 0.0f;
+  float v[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) v[r] = kTwo ? silu(s2a * acc0[r]) * (s2b * acc1[r]) : s2a * acc0[r];
+  if constexpr (MODE == kDown) {
+    *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.out) + (int64_t)a.perm[p] * N + n0) =
+        f32x4{v[0], v[1], v[2], v[3]};
+  } else {
+    u32x2 o;
+    o[0] = pack_bf16x2(v[0], v[1]);
+    o[1] = pack_bf16x2(v[2], v[3]);
+    *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(a.out) + p * N + n0) = o;
+    // row maximum of |H| as stored, for the down projection's fp16 scaling (order-free)
+    float m = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) m = fmaxf(m, fabsf((float)(__bf16)v[r]));
+    m = fmaxf(m, __shfl_xor(m, 16));
+    m = fmaxf(m, __shfl_xor(m, 32));
+    if (q == 0) atomicMax(reinterpret_cast<unsigned int*>(d.hmax + p), __builtin_bit_cast(unsigned int, m));
+  }
+}
+
+bool decode_small_supported(int64_t K, int64_t N) {
+  return K % 512 == 0 && K >= 512 && K <= kSmallMaxK && N % 16 == 0;
+}
+
+hipError_t launch_decode_small(GemmMode mode, const GemmArgs& a, const F16Args& d, int64_t grid_tiles,
+                               hipStream_t s) {
+  if (grid_tiles <= 0) return hipSuccess;
+  const dim3 grid((unsigned)grid_tiles, (unsigned)(a.N / 16));
+  const bool tl = a.w0.tiled;
+  // gate/up only: down has few stages (K = I) and keeps the decode kernels
+  if (mode != kGateUp) return hipErrorInvalidValue;
+  if (tl) hipLaunchKernelGGL((gemm_decode_ks_kernel<kGateUp, true>), grid, dim3(kThreads), 0, s, a, d);
+  else hipLaunchKernelGGL((gemm_decode_ks_kernel<kGateUp, false>), grid, dim3(kThreads), 0, s, a, d);
+  return hipGetLastError();
+}
+
 bool decode_supported(GemmMode mode, int64_t K, int64_t N) {
   (void)mode;
   return N % kBlockN == 0 && K % 256 == 0 && K >= 256;

@@ -39,9 +39,10 @@ struct GemmArgs {
 int cu_count();
 
 // Tile-shape variants of the grouped GEMM.
-//   decode : 16-row tiles, activations read straight into MFMA registers;
-//   prefill: 128-row tiles, activations staged through LDS and shared by 4 waves.
-enum GemmVariant : int { kDecode = 0, kPrefill = 1 };
+//   decode : 16-row tiles, activations staged through LDS per stage;
+//   prefill: 128-row tiles, activations staged through LDS and shared by 8 waves;
+//   small  : 4-row tiles of tiny batches, K split over the 4 waves of a workgroup.
+enum GemmVariant : int { kDecode = 0, kPrefill = 1, kDecodeSmall = 2 };
 int variant_tile_rows(GemmVariant v);
 
 hipError_t launch_gemm(GemmMode mode, GemmVariant v, const GemmArgs& a, int64_t grid_tiles,
@@ -58,6 +59,11 @@ struct F16Args {
 // Decode-tile (<= 16 rows) weight-streaming GEMM. The fp16 form (routed gate/up and
 // down only) reads x16 and converts H rows on the fly with hmax.
 bool decode_supported(GemmMode mode, int64_t K, int64_t N);
+
+// Tiny-batch tiles (<= 4 rows, routed modes, fp16 form): K % 512 == 0, K <= 4096, N % 16 == 0.
+bool decode_small_supported(int64_t K, int64_t N);
+hipError_t launch_decode_small(GemmMode mode, const GemmArgs& a, const F16Args& d, int64_t grid_tiles,
+                               hipStream_t s);
 
 // Prefill-tile (<= 128 rows) matrix-core GEMM; the tiled kernel covers other shapes.
 bool prefill_supported(GemmMode mode, int64_t x_rows, int64_t K, int64_t N);
