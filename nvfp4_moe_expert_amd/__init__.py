@@ -22,10 +22,13 @@ from dataclasses import dataclass
 import torch
 
 __all__ = [
-    "Nvfp4Error", "NVFP4Weight", "load_library", "library_path", "abi_version",
+    "Nvfp4Error", "NVFP4Weight", "load_library", "library_path", "abi_version", "ABI_VERSION",
     "pack", "relayout", "dequant", "linear", "linear_gated", "moe_route", "moe_grouped",
     "moe_workspace_size", "pack_workspace_size", "LAYOUT_ROWS", "LAYOUT_TILED32",
 ]
+
+# interface version this binding was written against (NVFP4_ABI_VERSION in include/nvfp4.h)
+ABI_VERSION = 5
 
 LAYOUT_ROWS = 0       # the checkpoint's row-major codes and scales
 LAYOUT_TILED32 = 1    # blocks of 32 rows (n % 32 == 0, k % 256 == 0)
@@ -99,6 +102,9 @@ def load_library():
             fn = getattr(lib, name)
             fn.restype = res
             fn.argtypes = args
+        if lib.nvfp4_abi_version() != ABI_VERSION:
+            raise RuntimeError(f"{_LIB_PATH} has ABI version {lib.nvfp4_abi_version()}, the binding expects "
+                               f"{ABI_VERSION}: rebuild it")
         _lib = lib
     return _lib
 

@@ -44,7 +44,9 @@ def test_binding_covers_every_symbol():
 
 def test_version_and_status_strings():
     lib = nv.load_library()
-    assert nv.abi_version() == 5
+    assert nv.abi_version() == nv.ABI_VERSION
+    with open(HEADER) as f:
+        assert f"#define NVFP4_ABI_VERSION {nv.ABI_VERSION}\n" in f.read()
     for code in range(7):
         assert lib.nvfp4_status_string(code)
     assert b"unknown" in lib.nvfp4_status_string(99)
