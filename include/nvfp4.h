@@ -175,7 +175,11 @@ nvfp4_status nvfp4_linear_gated(const uint16_t* x, int64_t m, const nvfp4_weight
  *           entries past offsets[n_experts] are left unspecified;
  *   inv     [T*k] int32: the position of each slot in perm, -1 if skipped.
  * The counts are a histogram; the offsets come from a wavefront prefix scan.
- * ws: at least nvfp4_moe_route_workspace_size(T, k, n_experts) bytes.
+ * ws: optional 16-byte aligned device scratch. With at least
+ * nvfp4_moe_route_workspace_size(T, k, n_experts) bytes (0 for at most 4096
+ * slots, else 4 bytes per expert for each of at most 64 windows of slots), a
+ * larger batch is counted and scattered by one workgroup per window; with less,
+ * or ws = NULL, one workgroup routes it. The result is the same either way.
  * Limits: 1 <= n_experts <= 4096, 1 <= k <= 64.
  */
 size_t nvfp4_moe_route_workspace_size(int64_t T, int32_t k, int32_t n_experts);

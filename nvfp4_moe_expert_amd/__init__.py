@@ -258,8 +258,10 @@ def linear_gated(x: torch.Tensor, w_gate: NVFP4Weight, w_up: NVFP4Weight,
     return out
 
 
-def moe_route(topk_ids: torch.Tensor, n_experts: int, expert_begin: int = 0):
-    """(offsets [E+1], perm [T*k] (valid prefix), inv [T*k]) - the stable permutation by expert."""
+def moe_route(topk_ids: torch.Tensor, n_experts: int, expert_begin: int = 0, scratch: bool = True):
+    """(offsets [E+1], perm [T*k] (valid prefix), inv [T*k]) - the stable permutation by expert.
+
+    scratch=False passes no workspace, so one workgroup routes every batch size."""
     lib = load_library()
     _need(topk_ids, torch.int32, "topk_ids", 2)
     T, k = topk_ids.shape
@@ -267,8 +269,10 @@ def moe_route(topk_ids: torch.Tensor, n_experts: int, expert_begin: int = 0):
     offsets = torch.empty((n_experts + 1,), dtype=torch.int32, device=dev)
     perm = torch.empty((max(T * k, 1),), dtype=torch.int32, device=dev)
     inv = torch.empty((max(T * k, 1),), dtype=torch.int32, device=dev)
+    nbytes = lib.nvfp4_moe_route_workspace_size(T, k, n_experts) if scratch else 0
+    ws = torch.empty((nbytes,), dtype=torch.uint8, device=dev) if nbytes else None
     _check(lib.nvfp4_moe_route(_ptr(topk_ids), T, k, n_experts, expert_begin, _ptr(offsets), _ptr(perm),
-                               _ptr(inv), None, 0, _stream()), "nvfp4_moe_route")
+                               _ptr(inv), _ptr(ws), nbytes, _stream()), "nvfp4_moe_route")
     return offsets, perm[: T * k], inv[: T * k]
 
 

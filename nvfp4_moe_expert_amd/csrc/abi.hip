@@ -159,7 +159,9 @@ nvfp4_status moe_impl(const uint16_t* x, int64_t T, int64_t H, const int32_t* id
     prep = RoutePrep{x, T, H, k, at<uint16_t>(ws, L.x16), at<int32_t>(ws, L.xexp), at<uint32_t>(ws, L.hmax), in_gu};
 
   if (e == hipSuccess)
-    e = launch_route(ids, S, (int)E, eb, variant_tile_rows(v), offsets, perm, nullptr, tiles, n_tiles, prep, s);
+    // Ypart is not written before down: it holds the route's scratch meanwhile
+    e = launch_route(ids, S, (int)E, eb, variant_tile_rows(v), offsets, perm, nullptr, tiles, n_tiles, prep, s,
+                     at<int32_t>(ws, L.ypart), L.x16 - L.ypart);
   if (e == hipSuccess) e = mark(1);
 
   GemmArgs g{};
@@ -349,19 +351,20 @@ nvfp4_status nvfp4_linear_gated(const uint16_t* x, int64_t m, const nvfp4_weight
 }
 
 size_t nvfp4_moe_route_workspace_size(int64_t T, int32_t k, int32_t n_experts) {
-  (void)T; (void)k; (void)n_experts;
-  return 0;
+  if (T < 0 || k < 1 || n_experts < 1) return 0;
+  return route_scratch_bytes(T * (int64_t)k, n_experts);
 }
 
 nvfp4_status nvfp4_moe_route(const int32_t* topk_ids, int64_t T, int32_t k, int32_t n_experts,
                              int32_t expert_begin, int32_t* offsets, int32_t* perm, int32_t* inv,
                              void* ws, size_t ws_bytes, void* stream) {
-  (void)ws; (void)ws_bytes;
   if (T < 0 || k < 1 || k > kMaxTopk || n_experts < 1 || n_experts > kMaxExperts) return NVFP4_ERR_SHAPE;
   if (T * (int64_t)k > kMaxSlots) return NVFP4_ERR_SHAPE;
   if (!offsets || !perm || !inv || (T > 0 && !topk_ids)) return NVFP4_ERR_NULL;
+  if (ws && !aligned16(ws)) return NVFP4_ERR_ALIGN;
   return from_hip(launch_route(topk_ids, T * k, n_experts, expert_begin, 16, offsets, perm, inv, nullptr,
-                               nullptr, RoutePrep{}, static_cast<hipStream_t>(stream)));
+                               nullptr, RoutePrep{}, static_cast<hipStream_t>(stream),
+                               static_cast<int32_t*>(ws), ws ? ws_bytes : 0));
 }
 
 size_t nvfp4_moe_workspace_size(int64_t T, int32_t k, int32_t n_experts, int64_t H, int64_t I) {
@@ -541,8 +544,9 @@ nvfp4_status nvfp4_moe_grouped_bf16(const uint16_t* x, int64_t T, int64_t H, con
   uint16_t* h = reinterpret_cast<uint16_t*>(p);
   p += round_up(sizeof(uint16_t) * (size_t)(S * I));
   float* ypart = reinterpret_cast<float*>(p);
+  // Ypart is not written before down: it holds the route's scratch meanwhile
   hipError_t e = launch_route(topk_ids, S, n_experts, expert_begin, 64, offsets, perm, nullptr, tiles, n_tiles,
-                              RoutePrep{}, s);
+                              RoutePrep{}, s, reinterpret_cast<int32_t*>(ypart), sizeof(float) * (size_t)(S * H));
   if (e == hipSuccess)
     e = launch_bf16_grouped(true, x, w_gate, w_up, tiles, n_tiles, max_tiles, perm, k, I, H, h, s);
   if (e == hipSuccess)

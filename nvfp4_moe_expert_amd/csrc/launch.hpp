@@ -107,10 +107,15 @@ struct RoutePrep {
   int32_t* xexp;
   uint32_t* hmax;
   const float* act_scale;   // W4A4: x16 holds the NVFP4-quantized rows (unscaled values), xexp 0
+  int rpb;                  // rows per prep workgroup (set by launch_route)
 };
 hipError_t launch_route(const int32_t* ids, int64_t S, int E, int expert_begin, int tile_rows,
                         int32_t* offsets, int32_t* perm, int32_t* inv, int32_t* tiles,
-                        int32_t* n_tiles, const RoutePrep& prep, hipStream_t s);
+                        int32_t* n_tiles, const RoutePrep& prep, hipStream_t s,
+                        int32_t* scratch = nullptr, size_t scratch_bytes = 0);
+// Device scratch that lets launch_route spread a large batch over several
+// workgroups (0 when one workgroup routes it); with less, one workgroup does.
+size_t route_scratch_bytes(int64_t S, int E);
 
 // y[t] = bf16(sum_j w[t,j] * Ypart[t*k+j] (j in order) + extra[t]); extra may be null,
 // or hold `extra_splits` partials [extra_splits][T][H] summed in split order.

@@ -17,6 +17,8 @@
 // order - a fixed-order gather instead of a scatter-add, so results are
 // bitwise reproducible (deterministic batch execution, as on the model card
 // "GLM-5.3-Flash-NVFP4-W4A4-Experts", opening section).
+#include <algorithm>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -48,187 +50,356 @@ __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
   return v;
 }
 
-// Workgroup 1 + t (t < T) of the route kernel: activation row t -> fp16 scaled by 2^p,
-// p putting the row's max |x| in [2^14, 2^15) (bf16 values then convert exactly);
-// also clears the row maxima of the token's k H rows.
+// Workgroups 1.. of the route kernel: one wave per activation row t -> fp16
+// scaled by 2^p, p putting the row's max |x| in [2^14, 2^15) (bf16 values then
+// convert exactly); also clears the row maxima of the token's k H rows. A wave
+// reduces its row with shuffles alone, no barrier; a row of up to 4096 inputs is
+// read once and held in registers (8 loads in flight per lane). A workgroup
+// takes `rpb` rows (1..16): few rows per workgroup for small batches, so the
+// rows spread over many compute units, 16 for large ones.
+constexpr int kPrepRegChunks = 8;   // 512-input chunks of a row held in registers
+
+__device__ __forceinline__ uint32_t absmax_bf16x8(const u32x4& v) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) m = max(m, max(v[j] & 0x7FFFu, (v[j] >> 16) & 0x7FFFu));
+  return m;
+}
+
+__device__ __forceinline__ u32x4 to_f16_scaled(const u32x4& v, float sc) {
+  u32x4 o;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const _Float16 lo = (_Float16)(bf16_lo(v[j]) * sc), hi = (_Float16)(bf16_hi(v[j]) * sc);
+    o[j] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+  }
+  return o;
+}
+
 __device__ void prep_row(const RoutePrep& pr, int64_t t) {
-  __shared__ uint32_t red[kRouteThreads / 64];
-  __shared__ int pexp;
-  const int tid = threadIdx.x;
+  const int lane = threadIdx.x & 63;
   const uint16_t* xr = pr.x + t * pr.H;
+  uint16_t* orow = pr.x16 + t * pr.H;
   if (pr.act_scale) {
     // W4A4: the row's static NVFP4 quantization (lanes 2j, 2j+1 hold one 16-block),
     // stored as its unscaled values e2m1 * e4m3 in fp16 (exact); input_scale is
     // applied in the GEMM epilogue, so the row exponent is 0
     const float gs = *pr.act_scale;
-    for (int64_t i = (int64_t)tid * 8; i < pr.H; i += kRouteThreads * 8) {
+    for (int64_t i = (int64_t)lane * 8; i < pr.H; i += 64 * 8) {
       const u32x4 v = ld16(xr + i);
       uint32_t am = absmax8(v);
       am = max(am, (uint32_t)__shfl_xor((int)am, 1));
       float s_eff;
       const uint32_t byte = block_byte(am, gs, s_eff);
       const _Float16 sv = (_Float16)e4m3_to_f32(byte);
-      st16(pr.x16 + t * pr.H + i, __builtin_bit_cast(u32x4, dequant8_f16(quant8(v, s_eff), f16x2{sv, sv})));
+      st16(orow + i, __builtin_bit_cast(u32x4, dequant8_f16(quant8(v, s_eff), f16x2{sv, sv})));
     }
-    if (tid == 0) pr.xexp[t] = 0;
-    for (int j = tid; j < pr.k; j += kRouteThreads) pr.hmax[t * pr.k + j] = 0u;
+    if (lane == 0) pr.xexp[t] = 0;
+    for (int j = lane; j < pr.k; j += 64) pr.hmax[t * pr.k + j] = 0u;
     return;
   }
+  const bool in_regs = pr.H <= 512 * kPrepRegChunks;
+  u32x4 v[kPrepRegChunks];
   uint32_t m = 0;
-  for (int64_t i = (int64_t)tid * 8; i < pr.H; i += kRouteThreads * 8) {
-    const u32x4 v = ld16(xr + i);
+  if (in_regs) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) m = max(m, max(v[j] & 0x7FFFu, (v[j] >> 16) & 0x7FFFu));
+    for (int c = 0; c < kPrepRegChunks; ++c) {
+      const int64_t i = (int64_t)c * 512 + lane * 8;
+      v[c] = i < pr.H ? ld16(xr + i) : u32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int c = 0; c < kPrepRegChunks; ++c) m = max(m, absmax_bf16x8(v[c]));
+  } else {
+    for (int64_t i = (int64_t)lane * 8; i < pr.H; i += 512) m = max(m, absmax_bf16x8(ld16(xr + i)));
   }
   for (int off = 32; off >= 1; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
-  if ((tid & 63) == 0) red[tid >> 6] = m;
-  __syncthreads();
-  if (tid == 0) {
-    uint32_t r = 0;
-    for (int i = 0; i < kRouteThreads / 64; ++i) r = max(r, red[i]);
-    int p = 0;
-    if (r != 0) {
-      const int e = (int)((r >> 7) & 0xFF) - 127;   // bf16 exponent of the row max
-      p = 14 - e;
-      p = p > 126 ? 126 : (p < -126 ? -126 : p);
-    }
-    pexp = p;
-    pr.xexp[t] = p;
+  int p = 0;
+  if (m != 0) {
+    const int e = (int)((m >> 7) & 0xFF) - 127;   // bf16 exponent of the row max
+    p = 14 - e;
+    p = p > 126 ? 126 : (p < -126 ? -126 : p);
   }
-  __syncthreads();
-  const float sc = ldexpf(1.0f, pexp);
-  for (int64_t i = (int64_t)tid * 8; i < pr.H; i += kRouteThreads * 8) {
-    const u32x4 v = ld16(xr + i);
-    u32x4 o;
+  if (lane == 0) pr.xexp[t] = p;
+  const float sc = ldexpf(1.0f, p);
+  if (in_regs) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const _Float16 lo = (_Float16)(bf16_lo(v[j]) * sc), hi = (_Float16)(bf16_hi(v[j]) * sc);
-      o[j] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+    for (int c = 0; c < kPrepRegChunks; ++c) {
+      const int64_t i = (int64_t)c * 512 + lane * 8;
+      if (i < pr.H) st16(orow + i, to_f16_scaled(v[c], sc));
     }
-    st16(pr.x16 + t * pr.H + i, o);
+  } else {
+    for (int64_t i = (int64_t)lane * 8; i < pr.H; i += 512) st16(orow + i, to_f16_scaled(ld16(xr + i), sc));
   }
-  for (int j = tid; j < pr.k; j += kRouteThreads) pr.hmax[t * pr.k + j] = 0u;
+  for (int j = lane; j < pr.k; j += 64) pr.hmax[t * pr.k + j] = 0u;
 }
 
-__global__ __launch_bounds__(kRouteThreads) void route_kernel(
-    const int32_t* __restrict__ ids, int S, int E, int eb, int P, int chunk, int tile_rows,
-    int32_t* __restrict__ offsets, int32_t* __restrict__ perm, int32_t* __restrict__ inv,
-    int32_t* __restrict__ tiles, int32_t* __restrict__ n_tiles, RoutePrep prep) {
-  if (blockIdx.x > 0) {
-    prep_row(prep, (int64_t)blockIdx.x - 1);
-    return;
-  }
-  extern __shared__ int32_t cnt[];      // [P][E]
+// ---- the three steps, over the slot window [s0, s1) of one workgroup
+
+// 1. histogram of the window's local expert ids into cnt[P][E]: range p holds
+// slots [s0 + p*chunk, +chunk) (chunk a multiple of 64, so a wave's 64 slots lie
+// in one range). Ends with a barrier.
+__device__ void range_hist(const int32_t* __restrict__ ids, int s0, int s1, int E, int eb, int P, int chunk,
+                           int bits, int32_t* cnt) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   for (int i = tid; i < P * E; i += kRouteThreads) cnt[i] = 0;
   __syncthreads();
-  int bits = 0;
-  while ((1 << bits) < E) ++bits;
-  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  // 1. histogram per slot range; chunk is a multiple of 64, so a wave's 64 slots
-  // lie in one range
-  for (int base = wave * 64; base < S; base += kRouteThreads) {
+  for (int base = s0 + wave * 64; base < s1; base += kRouteThreads) {
     const int s = base + lane;
     int e = -1;
-    if (s < S) {
+    if (s < s1) {
       e = ids[s] - eb;
       if (e < 0 || e >= E) e = -1;
     }
     const uint64_t m = match_lanes(e, bits);
-    if (e >= 0 && (m & below) == 0) atomicAdd(&cnt[(base / chunk) * E + e], __builtin_popcountll(m));
+    if (e >= 0 && (m & below) == 0) atomicAdd(&cnt[((base - s0) / chunk) * E + e], __builtin_popcountll(m));
   }
   __syncthreads();
-  // 2. per-expert totals, workgroup scan, cursors and tile list
-  {
-    __shared__ int wrows[kRouteWaves], wtl[kRouteWaves];
-    const int run = (E + kRouteThreads - 1) / kRouteThreads;
-    const int e0 = min(tid * run, E), e1 = min(e0 + run, E);
-    int rows = 0, ntl = 0;
-    for (int e = e0; e < e1; ++e) {
-      int tot = 0;
-      for (int p = 0; p < P; ++p) tot += cnt[p * E + e];
-      rows += tot;
-      ntl += (tot + tile_rows - 1) / tile_rows;
-    }
-    const int rows_incl = wave_incl_scan(rows, lane);
-    const int tl_incl = wave_incl_scan(ntl, lane);
-    if (lane == 63) {
-      wrows[wave] = rows_incl;
-      wtl[wave] = tl_incl;
-    }
-    __syncthreads();
-    int rbase = 0, tbase = 0;
-    for (int w = 0; w < wave; ++w) {
-      rbase += wrows[w];
-      tbase += wtl[w];
-    }
-    int off = rbase + rows_incl - rows, toff = tbase + tl_incl - ntl;
-    for (int e = e0; e < e1; ++e) {
-      offsets[e] = off;
-      int cur = off;
-      for (int p = 0; p < P; ++p) {   // counts -> cursors, range by range
-        const int c = cnt[p * E + e];
-        cnt[p * E + e] = cur;
-        cur += c;
+}
+
+// 2. Given per-expert totals (total(e)), a workgroup scan gives the exclusive
+// offsets, the tile list (expert, first row, rows) and the tile count; then
+// cursors(e, first) is called once per expert with its first position.
+template <typename Total, typename Cursors>
+__device__ void scan_experts(int E, int tile_rows, Total total, Cursors cursors, int32_t* __restrict__ offsets,
+                             int32_t* __restrict__ tiles, int32_t* __restrict__ n_tiles) {
+  __shared__ int wrows[kRouteWaves], wtl[kRouteWaves];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int run = (E + kRouteThreads - 1) / kRouteThreads;
+  const int e0 = min(tid * run, E), e1 = min(e0 + run, E);
+  int rows = 0, ntl = 0;
+  for (int e = e0; e < e1; ++e) {
+    const int tot = total(e);
+    rows += tot;
+    ntl += (tot + tile_rows - 1) / tile_rows;
+  }
+  const int rows_incl = wave_incl_scan(rows, lane);
+  const int tl_incl = wave_incl_scan(ntl, lane);
+  if (lane == 63) {
+    wrows[wave] = rows_incl;
+    wtl[wave] = tl_incl;
+  }
+  __syncthreads();
+  int rbase = 0, tbase = 0;
+  for (int w = 0; w < wave; ++w) {
+    rbase += wrows[w];
+    tbase += wtl[w];
+  }
+  int off = rbase + rows_incl - rows, toff = tbase + tl_incl - ntl;
+  for (int e = e0; e < e1; ++e) {
+    offsets[e] = off;
+    const int tot = cursors(e, off);
+    if (tiles) {
+      for (int r = 0; r < tot; r += tile_rows, ++toff) {
+        tiles[4 * toff + 0] = e;
+        tiles[4 * toff + 1] = off + r;
+        tiles[4 * toff + 2] = min(tile_rows, tot - r);
+        tiles[4 * toff + 3] = 0;
       }
-      const int tot = cur - off;
-      if (tiles) {
-        for (int r = 0; r < tot; r += tile_rows, ++toff) {
-          tiles[4 * toff + 0] = e;
-          tiles[4 * toff + 1] = off + r;
-          tiles[4 * toff + 2] = min(tile_rows, tot - r);
-          tiles[4 * toff + 3] = 0;
+    }
+    off += tot;
+  }
+  if (tid == kRouteThreads - 1) {
+    offsets[E] = rbase + rows_incl;
+    if (n_tiles) *n_tiles = tbase + tl_incl;
+  }
+}
+
+// counts cnt[p][e] -> cursors, range by range from `first`; returns the total
+__device__ __forceinline__ int counts_to_cursors(int32_t* cnt, int P, int E, int e, int first) {
+  int cur = first;
+  for (int p = 0; p < P; ++p) {
+    const int c = cnt[p * E + e];
+    cnt[p * E + e] = cur;
+    cur += c;
+  }
+  return cur - first;
+}
+
+// 3. stable scatter of the window: wave p < P walks range p in slot order; a
+// slot's position is its expert's cursor plus its rank among earlier lanes of
+// the same expert.
+__device__ void range_scatter(const int32_t* __restrict__ ids, int s0, int s1, int E, int eb, int P, int chunk,
+                              int bits, int32_t* cnt, int32_t* __restrict__ perm, int32_t* __restrict__ inv) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  if (wave >= P) return;
+  const int r_begin = s0 + wave * chunk, r_end = min(s1, r_begin + chunk);
+  for (int base = r_begin; base < r_end; base += 64) {
+    const int s = base + lane;
+    int e = -1;
+    if (s < r_end) {
+      e = ids[s] - eb;
+      if (e < 0 || e >= E) e = -1;
+    }
+    const uint64_t m = match_lanes(e, bits);
+    const int rank = __builtin_popcountll(m & below), tot = __builtin_popcountll(m);
+    if (e >= 0) {
+      const int pos = cnt[wave * E + e] + rank;
+      perm[pos] = s;
+      if (inv) inv[s] = pos;
+    } else if (s < r_end && inv) {
+      inv[s] = -1;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    if (e >= 0 && rank == tot - 1) cnt[wave * E + e] += tot;
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
+__device__ __forceinline__ int id_bits(int E) {
+  int bits = 0;
+  while ((1 << bits) < E) ++bits;
+  return bits;
+}
+
+__device__ __forceinline__ bool prep_block(const RoutePrep& prep, int64_t pb) {
+  if (pb < 0) return false;
+  const int w = threadIdx.x >> 6;
+  const int64_t t = pb * prep.rpb + w;
+  if (w < prep.rpb && t < prep.T) prep_row(prep, t);
+  return true;
+}
+
+// One workgroup routes all S slots (workgroups 1.. run the activation prep).
+__global__ __launch_bounds__(kRouteThreads) void route_kernel(
+    const int32_t* __restrict__ ids, int S, int E, int eb, int P, int chunk, int tile_rows,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ perm, int32_t* __restrict__ inv,
+    int32_t* __restrict__ tiles, int32_t* __restrict__ n_tiles, RoutePrep prep) {
+  if (prep_block(prep, (int64_t)blockIdx.x - 1)) return;
+  extern __shared__ int32_t cnt[];      // [P][E]
+  const int bits = id_bits(E);
+  range_hist(ids, 0, S, E, eb, P, chunk, bits, cnt);
+  scan_experts(
+      E, tile_rows,
+      [&](int e) {
+        int tot = 0;
+        for (int p = 0; p < P; ++p) tot += cnt[p * E + e];
+        return tot;
+      },
+      [&](int e, int first) { return counts_to_cursors(cnt, P, E, e, first); }, offsets, tiles, n_tiles);
+  __syncthreads();
+  range_scatter(ids, 0, S, E, eb, P, chunk, bits, cnt, perm, inv);
+}
+
+// Large batches: the same three steps over NB workgroups of C slots each (the
+// single workgroup's ballot work grows with S and ran ~50 us at 32768 slots).
+// count: workgroup b's per-expert totals -> wsum[b][E] (workgroups NB.. run the
+// activation prep); scan: one workgroup turns them into offsets, the tile list
+// and each workgroup's first position per expert (in place: wsum[b][e] becomes
+// offsets[e] + the rows of expert e in workgroups < b); scatter: workgroup b
+// recounts its window per range and scatters from those bases. Workgroup order
+// then range order then slot order: the permutation stays stable.
+__global__ __launch_bounds__(kRouteThreads) void route_count_kernel(
+    const int32_t* __restrict__ ids, int S, int E, int eb, int P, int chunk, int C, int NB,
+    int32_t* __restrict__ wsum, RoutePrep prep) {
+  if (prep_block(prep, (int64_t)blockIdx.x - NB)) return;
+  extern __shared__ int32_t cnt[];      // [P][E]
+  const int s0 = (int)blockIdx.x * C, s1 = min(S, s0 + C);
+  range_hist(ids, s0, s1, E, eb, P, chunk, id_bits(E), cnt);
+  for (int e = threadIdx.x; e < E; e += kRouteThreads) {
+    int tot = 0;
+    for (int p = 0; p < P; ++p) tot += cnt[p * E + e];
+    wsum[(int64_t)blockIdx.x * E + e] = tot;
+  }
+}
+
+__global__ __launch_bounds__(kRouteThreads) void route_scan_kernel(int E, int NB, int tile_rows,
+                                                                   int32_t* __restrict__ wsum,
+                                                                   int32_t* __restrict__ offsets,
+                                                                   int32_t* __restrict__ tiles,
+                                                                   int32_t* __restrict__ n_tiles) {
+  scan_experts(
+      E, tile_rows,
+      [&](int e) {
+        int tot = 0;
+#pragma unroll 8
+        for (int b = 0; b < NB; ++b) tot += wsum[(int64_t)b * E + e];
+        return tot;
+      },
+      [&](int e, int first) {
+        int cur = first;
+        for (int b = 0; b < NB; ++b) {
+          const int c = wsum[(int64_t)b * E + e];
+          wsum[(int64_t)b * E + e] = cur;
+          cur += c;
         }
-      }
-      off = cur;
-    }
-    if (tid == kRouteThreads - 1) {
-      offsets[E] = rbase + rows_incl;
-      if (n_tiles) *n_tiles = tbase + tl_incl;
-    }
-  }
+        return cur - first;
+      },
+      offsets, tiles, n_tiles);
+}
+
+__global__ __launch_bounds__(kRouteThreads) void route_scatter_kernel(
+    const int32_t* __restrict__ ids, int S, int E, int eb, int P, int chunk, int C,
+    const int32_t* __restrict__ wsum, int32_t* __restrict__ perm, int32_t* __restrict__ inv) {
+  extern __shared__ int32_t cnt[];      // [P][E]
+  const int s0 = (int)blockIdx.x * C, s1 = min(S, s0 + C);
+  const int bits = id_bits(E);
+  range_hist(ids, s0, s1, E, eb, P, chunk, bits, cnt);
+  for (int e = threadIdx.x; e < E; e += kRouteThreads)
+    counts_to_cursors(cnt, P, E, e, wsum[(int64_t)blockIdx.x * E + e]);
   __syncthreads();
-  // 3. stable scatter, one wave per slot range
-  if (wave < P) {
-    const int s_begin = wave * chunk, s_end = min(S, s_begin + chunk);
-    for (int base = s_begin; base < s_end; base += 64) {
-      const int s = base + lane;
-      int e = -1;
-      if (s < s_end) {
-        e = ids[s] - eb;
-        if (e < 0 || e >= E) e = -1;
-      }
-      const uint64_t m = match_lanes(e, bits);
-      const int rank = __builtin_popcountll(m & below), tot = __builtin_popcountll(m);
-      if (e >= 0) {
-        const int pos = cnt[wave * E + e] + rank;
-        perm[pos] = s;
-        if (inv) inv[s] = pos;
-      } else if (s < s_end && inv) {
-        inv[s] = -1;
-      }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      if (e >= 0 && rank == tot - 1) cnt[wave * E + e] += tot;
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-    }
-  }
+  range_scatter(ids, s0, s1, E, eb, P, chunk, bits, cnt, perm, inv);
+}
+
+namespace {
+// ranges per workgroup (one wave each) and their length for a window of n slots
+void route_ranges(int64_t n, int E, int& P, int64_t& chunk) {
+  P = kRouteLdsInts / E;
+  if (P > kRouteWaves) P = kRouteWaves;
+  if (P < 1) P = 1;
+  chunk = (n + P - 1) / P;
+  chunk = ((chunk + 63) / 64) * 64;
+  if (chunk < 64) chunk = 64;
+}
+
+// window of the multi-workgroup form: >= kRouteWindow slots, at most kRouteMaxWgs workgroups
+constexpr int64_t kRouteSingleMax = 4096;   // slots one workgroup routes
+constexpr int64_t kRouteWindow = 2048;
+constexpr int64_t kRouteMaxWgs = 64;
+int64_t route_window(int64_t S) {
+  int64_t C = (S + kRouteMaxWgs - 1) / kRouteMaxWgs;
+  C = ((C + 63) / 64) * 64;
+  return C < kRouteWindow ? kRouteWindow : C;
+}
+}  // namespace
+
+size_t route_scratch_bytes(int64_t S, int E) {
+  if (S <= kRouteSingleMax) return 0;
+  const int64_t NB = (S + route_window(S) - 1) / route_window(S);
+  return sizeof(int32_t) * (size_t)NB * (size_t)E;
 }
 
 hipError_t launch_route(const int32_t* ids, int64_t S, int E, int eb, int tile_rows, int32_t* offsets,
                         int32_t* perm, int32_t* inv, int32_t* tiles, int32_t* n_tiles,
-                        const RoutePrep& prep, hipStream_t s) {
-  int P = kRouteLdsInts / E;
-  if (P > kRouteWaves) P = kRouteWaves;
-  if (P < 1) P = 1;
-  int64_t chunk = (S + P - 1) / P;
-  chunk = ((chunk + 63) / 64) * 64;
-  if (chunk < 64) chunk = 64;
+                        const RoutePrep& prep, hipStream_t s, int32_t* scratch, size_t scratch_bytes) {
+  // rows per prep workgroup: one while that still leaves <= 256 workgroups, up to 16
+  RoutePrep pp = prep;
+  pp.rpb = (int)std::min<int64_t>(kRouteWaves, std::max<int64_t>(1, prep.T / 256));
+  const int64_t prep_wgs = prep.x16 ? (prep.T + pp.rpb - 1) / pp.rpb : 0;
+  const size_t need = route_scratch_bytes(S, E);
+  if (need > 0 && scratch && scratch_bytes >= need) {
+    const int64_t C = route_window(S), NB = (S + C - 1) / C;
+    int P;
+    int64_t chunk;
+    route_ranges(C, E, P, chunk);
+    const size_t lds = (size_t)P * E * sizeof(int32_t);
+    hipLaunchKernelGGL(route_count_kernel, dim3((unsigned)(NB + prep_wgs)), dim3(kRouteThreads), lds, s, ids,
+                       (int)S, E, eb, P, (int)chunk, (int)C, (int)NB, scratch, pp);
+    hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(kRouteThreads), 0, s, E, (int)NB, tile_rows, scratch,
+                       offsets, tiles, n_tiles);
+    hipLaunchKernelGGL(route_scatter_kernel, dim3((unsigned)NB), dim3(kRouteThreads), lds, s, ids, (int)S, E,
+                       eb, P, (int)chunk, (int)C, scratch, perm, inv);
+    return hipGetLastError();
+  }
+  int P;
+  int64_t chunk;
+  route_ranges(S, E, P, chunk);
   const size_t lds = (size_t)P * E * sizeof(int32_t);
-  const unsigned grid = 1 + (prep.x16 ? (unsigned)prep.T : 0u);
-  hipLaunchKernelGGL(route_kernel, dim3(grid), dim3(kRouteThreads), lds, s, ids, (int)S, E, eb, P,
-                     (int)chunk, tile_rows, offsets, perm, inv, tiles, n_tiles, prep);
+  hipLaunchKernelGGL(route_kernel, dim3((unsigned)(1 + prep_wgs)), dim3(kRouteThreads), lds, s, ids, (int)S, E,
+                     eb, P, (int)chunk, tile_rows, offsets, perm, inv, tiles, n_tiles, pp);
   return hipGetLastError();
 }
 

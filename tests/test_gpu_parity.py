@@ -136,6 +136,12 @@ def _route_cases():
     cases.append(("all_skipped", r.integers(0, 16, (9, 4)).astype(np.int32), 16, 1000))
     cases.append(("ragged_S", r.integers(0, 3, (67, 1)).astype(np.int32), 3, 0))
     cases.append(("negative_ids", r.integers(-5, 5, (20, 2)).astype(np.int32), 5, 0))
+    # prefill-sized batches with uniform ids, one of them ragged and with skipped ids
+    cases.append(("uniform_4096", r.integers(0, 288, (4096, 8)).astype(np.int32), 288, 0))
+    cases.append(("uniform_4097_skips", r.integers(0, 300, (4097, 8)).astype(np.int32), 288, 6))
+    # 4096 experts over several windows; 64 windows of more than 2048 slots
+    cases.append(("many_experts_large", r.integers(0, 4096, (1000, 8)).astype(np.int32), 4096, 0))
+    cases.append(("windows_64", r.integers(-3, 290, (16500, 8)).astype(np.int32), 288, 0))
     return cases
 
 
@@ -149,6 +155,34 @@ def test_route_bit_exact(ci):
     assert np.array_equal(off.cpu().numpy(), roff)
     V = int(roff[-1])
     assert np.array_equal(perm.cpu().numpy()[:V], rperm)
+    assert np.array_equal(inv.cpu().numpy(), rinv)
+
+
+@pytest.mark.parametrize("name", ["prefill_zipf", "uniform_4097_skips", "many_experts_large", "windows_64"])
+def test_route_one_workgroup_large_batch(name):
+    # without scratch one workgroup routes a batch the scratch path spreads over windows
+    _, ids, E, eb = next(c for c in _route_cases() if c[0] == name)
+    note(f"route (no scratch) {name} ids{ids.shape} E={E} eb={eb}")
+    assert nv.load_library().nvfp4_moe_route_workspace_size(ids.shape[0], ids.shape[1], E) > 0
+    off, perm, inv = nv.moe_route(torch.from_numpy(ids).to(DEV), E, eb, scratch=False)
+    torch.cuda.synchronize()
+    counts, roff, rperm, rinv = OM.route(ids, E, eb)
+    assert np.array_equal(off.cpu().numpy(), roff)
+    assert np.array_equal(perm.cpu().numpy()[:int(roff[-1])], rperm)
+    assert np.array_equal(inv.cpu().numpy(), rinv)
+
+
+def test_route_unaligned_ids():
+    # ids that do not start on a 16-byte boundary
+    r = np.random.default_rng(11)
+    ids = r.integers(0, 40, (1 + 33 * 5,)).astype(np.int32)
+    dev = torch.from_numpy(ids).to(DEV)[1:].view(33, 5)
+    assert dev.data_ptr() % 16 != 0
+    off, perm, inv = nv.moe_route(dev, 40, 0)
+    torch.cuda.synchronize()
+    counts, roff, rperm, rinv = OM.route(ids[1:].reshape(33, 5), 40, 0)
+    assert np.array_equal(off.cpu().numpy(), roff)
+    assert np.array_equal(perm.cpu().numpy()[:int(roff[-1])], rperm)
     assert np.array_equal(inv.cpu().numpy(), rinv)
 
 
