@@ -76,26 +76,32 @@ __device__ __forceinline__ u32x4 to_f16_scaled(const u32x4& v, float sc) {
   return o;
 }
 
+// W4A4: the row's static NVFP4 quantization (threads 2j, 2j+1 hold one 16-block),
+// stored as its unscaled values e2m1 * e4m3 in fp16 (exact); input_scale is
+// applied in the GEMM epilogue, so the row exponent is 0. Thread `first` of
+// `stride` (a multiple of 64).
+__device__ void w4a4_row(const RoutePrep& pr, int64_t t, int first, int stride) {
+  const uint16_t* xr = pr.x + t * pr.H;
+  const float gs = *pr.act_scale;
+  for (int64_t i = (int64_t)first * 8; i < pr.H; i += (int64_t)stride * 8) {
+    const u32x4 v = ld16(xr + i);
+    uint32_t am = absmax8(v);
+    am = max(am, (uint32_t)__shfl_xor((int)am, 1));
+    float s_eff;
+    const uint32_t byte = block_byte(am, gs, s_eff);
+    const _Float16 sv = (_Float16)e4m3_to_f32(byte);
+    st16(pr.x16 + t * pr.H + i, __builtin_bit_cast(u32x4, dequant8_f16(quant8(v, s_eff), f16x2{sv, sv})));
+  }
+  if (first == 0) pr.xexp[t] = 0;
+  for (int j = first; j < pr.k; j += stride) pr.hmax[t * pr.k + j] = 0u;
+}
+
 __device__ void prep_row(const RoutePrep& pr, int64_t t) {
   const int lane = threadIdx.x & 63;
   const uint16_t* xr = pr.x + t * pr.H;
   uint16_t* orow = pr.x16 + t * pr.H;
   if (pr.act_scale) {
-    // W4A4: the row's static NVFP4 quantization (lanes 2j, 2j+1 hold one 16-block),
-    // stored as its unscaled values e2m1 * e4m3 in fp16 (exact); input_scale is
-    // applied in the GEMM epilogue, so the row exponent is 0
-    const float gs = *pr.act_scale;
-    for (int64_t i = (int64_t)lane * 8; i < pr.H; i += 64 * 8) {
-      const u32x4 v = ld16(xr + i);
-      uint32_t am = absmax8(v);
-      am = max(am, (uint32_t)__shfl_xor((int)am, 1));
-      float s_eff;
-      const uint32_t byte = block_byte(am, gs, s_eff);
-      const _Float16 sv = (_Float16)e4m3_to_f32(byte);
-      st16(orow + i, __builtin_bit_cast(u32x4, dequant8_f16(quant8(v, s_eff), f16x2{sv, sv})));
-    }
-    if (lane == 0) pr.xexp[t] = 0;
-    for (int j = lane; j < pr.k; j += 64) pr.hmax[t * pr.k + j] = 0u;
+    w4a4_row(pr, t, lane, 64);
     return;
   }
   const bool in_regs = pr.H <= 512 * kPrepRegChunks;
@@ -255,8 +261,48 @@ __device__ __forceinline__ int id_bits(int E) {
   return bits;
 }
 
+// Small batches (rpb == 1): the whole workgroup converts one row, two passes (max,
+// then convert) with a workgroup reduction between them; its loads spread over 16
+// waves rather than queueing in one (a one-wave row cost ~1 us more per route).
+__device__ void prep_row_wg(const RoutePrep& pr, int64_t t) {
+  __shared__ uint32_t red[kRouteWaves];
+  __shared__ int pexp;
+  const int tid = threadIdx.x;
+  if (pr.act_scale) {
+    w4a4_row(pr, t, tid, kRouteThreads);
+    return;
+  }
+  const uint16_t* xr = pr.x + t * pr.H;
+  uint32_t m = 0;
+  for (int64_t i = (int64_t)tid * 8; i < pr.H; i += kRouteThreads * 8) m = max(m, absmax_bf16x8(ld16(xr + i)));
+  for (int off = 32; off >= 1; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
+  if ((tid & 63) == 0) red[tid >> 6] = m;
+  __syncthreads();
+  if (tid == 0) {
+    uint32_t r = 0;
+    for (int i = 0; i < kRouteWaves; ++i) r = max(r, red[i]);
+    int p = 0;
+    if (r != 0) {
+      const int e = (int)((r >> 7) & 0xFF) - 127;   // bf16 exponent of the row max
+      p = 14 - e;
+      p = p > 126 ? 126 : (p < -126 ? -126 : p);
+    }
+    pexp = p;
+    pr.xexp[t] = p;
+  }
+  __syncthreads();
+  const float sc = ldexpf(1.0f, pexp);
+  for (int64_t i = (int64_t)tid * 8; i < pr.H; i += kRouteThreads * 8)
+    st16(pr.x16 + t * pr.H + i, to_f16_scaled(ld16(xr + i), sc));
+  for (int j = tid; j < pr.k; j += kRouteThreads) pr.hmax[t * pr.k + j] = 0u;
+}
+
 __device__ __forceinline__ bool prep_block(const RoutePrep& prep, int64_t pb) {
   if (pb < 0) return false;
+  if (prep.rpb == 1) {
+    prep_row_wg(prep, pb);
+    return true;
+  }
   const int w = threadIdx.x >> 6;
   const int64_t t = pb * prep.rpb + w;
   if (w < prep.rpb && t < prep.T) prep_row(prep, t);
