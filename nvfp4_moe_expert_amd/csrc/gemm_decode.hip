@@ -386,9 +386,15 @@ __device__ __forceinline__ void res_item(const GemmArgs& a, const F16Args& d, ui
   const int tid = opaque_tid(), lane = tid & 63, wave = tid >> 6, lr = lane & 15, q = lane >> 4;
   const int64_t N = a.N;
 
+  // The item's own loads are issued in the order they are needed and none sits
+  // behind a branch, so no wait covers more than it must: the tile entry, then
+  // the activation tile, each lane's row maximum and output row, then the
+  // weights. (An item used to end its prologue on a chain of dependent loads: the
+  // tile entry, then the weights, then one staging load after another, then the
+  // epilogue's row maximum and output row.)
   int e = 0, rb, rows;
   if (kMoe) {
-    const int32_t* t = a.tiles + 4 * (int64_t)tile;
+    const int32_t* t = a.tiles + 4 * (int64_t)__builtin_amdgcn_readfirstlane(tile);
     e = t[0];
     rb = t[1];
     rows = t[2];
@@ -396,6 +402,24 @@ __device__ __forceinline__ void res_item(const GemmArgs& a, const F16Args& d, ui
     rb = tile * 16;
     rows = (int)min((int64_t)16, a.M - rb);
   }
+  // the activation tile first: it comes from the cache (the previous kernel wrote
+  // it) and is converted and staged while the weights are still on their way
+  const __amdgpu_buffer_rsrc_t xrs = rsrc(a.x, a.x_rows * KT * 2);
+  u32x4 hv[XU];
+#pragma unroll
+  for (int i = 0; i < XU; ++i) {
+    const int u = i * kThreads + tid, r = u / (KT / 8), c = u % (KT / 8);
+    const uint32_t off = r < rows ? (uint32_t)((rb + r) * (KT * 2) + 16 * c) : 0x80000000u;
+    hv[i] = __builtin_amdgcn_raw_buffer_load_b128(xrs, off, 0, 0);
+  }
+  const bool live = lr < rows;
+  const int64_t p = rb + lr;
+  const int64_t pc = rb + min(lr, rows - 1);   // a valid row for every lane
+  uint32_t hm = 0;
+  if constexpr (F16) hm = d.hmax[pc];
+  const int32_t orow_v = kMoe ? a.perm[pc] : 0;
+  const float s2e = a.w0.scale_2[e];
+  const float act = a.act_scale ? *a.act_scale : 1.0f;   // W4A4: the activations' input_scale
 
   // block j of this wave: rows nrow + 64j; in both layouts 64 rows are 32*K code
   // bytes and 4*K scale bytes further on
@@ -423,29 +447,23 @@ __device__ __forceinline__ void res_item(const GemmArgs& a, const F16Args& d, ui
 #pragma unroll
   for (int g = 0; g < G; ++g)
     sc[g] = *reinterpret_cast<const u32x2*>(s0 + (int64_t)(g / NST) * 4 * KT + (g % NST) * SSTEP);
+  // nothing below may be scheduled above the weight loads (the conversion's first
+  // use of a row maximum would make them wait for it)
+  __builtin_amdgcn_sched_barrier(0);
 
   // ---- the activation tile, converted to fp16 * 2^p per row in the fp16 form
+  // (units of rows past the tile's read zeros without a memory access)
   {
-    u32x4 hv[XU];
-    float hs[XU];
-#pragma unroll
-    for (int i = 0; i < XU; ++i) {
-      const int u = i * kThreads + tid, r = u / (KT / 8), c = u % (KT / 8);
-      hv[i] = u32x4{0, 0, 0, 0};
-      hs[i] = 1.0f;
-      if (r < rows) {
-        hv[i] = ld16(a.x + (int64_t)(rb + r) * KT + 8 * c);
-        if constexpr (F16) hs[i] = ldexpf(1.0f, row_exponent(d.hmax[rb + r]));
-      }
-    }
 #pragma unroll
     for (int i = 0; i < XU; ++i) {
       const int u = i * kThreads + tid, r = u / (KT / 8), c = u % (KT / 8);
       u32x4 o = hv[i];
       if constexpr (F16) {
+        // row r's maximum sits in lane r (r is the same across the wave: KT / 8 is a multiple of 64)
+        const float hs = ldexpf(1.0f, row_exponent(__builtin_amdgcn_readlane(hm, __builtin_amdgcn_readfirstlane(r & 15))));
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const f16x2 h2 = {(_Float16)(bf16_lo(hv[i][j]) * hs[i]), (_Float16)(bf16_hi(hv[i][j]) * hs[i])};
+          const f16x2 h2 = {(_Float16)(bf16_lo(hv[i][j]) * hs), (_Float16)(bf16_hi(hv[i][j]) * hs)};
           o[j] = __builtin_bit_cast(uint32_t, h2);
         }
       }
@@ -454,14 +472,12 @@ __device__ __forceinline__ void res_item(const GemmArgs& a, const F16Args& d, ui
   }
   __syncthreads();
 
-  const bool live = lr < rows;
-  const int64_t p = rb + lr;
-  float s2 = a.w0.scale_2[e];
+  float s2 = s2e;
   if constexpr (F16) {
-    if (live) s2 *= ldexpf(1.0f, -row_exponent(d.hmax[p]));
+    if (live) s2 *= ldexpf(1.0f, -row_exponent(hm));
   }
-  if (a.act_scale) s2 *= *a.act_scale;   // W4A4: the activations' input_scale
-  const int64_t orow = kMoe ? (live ? (int64_t)a.perm[p] : 0) : p;
+  if (a.act_scale) s2 *= act;
+  const int64_t orow = kMoe ? (live ? (int64_t)orow_v : 0) : p;
 
   f32x4 acc = {0, 0, 0, 0};
 #pragma unroll
@@ -542,9 +558,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(PER ? 
 constexpr int kSmallRows = 4;
 constexpr int kSmallMaxK = 4096;
 
-template <int MODE, bool TL>
+// FULL (K = 4096): every wave takes exactly two stages, so no load sits behind a
+// branch and the waits before the first stage's MFMAs do not also wait for the
+// second stage's loads (a load issued under a branch makes those waits drain).
+template <int MODE, bool TL, bool FULL>
 __global__ __launch_bounds__(kThreads) void gemm_decode_ks_kernel(GemmArgs a, F16Args d) {
-  static_assert(MODE == kGateUp || MODE == kDown, "routed modes");
+  static_assert(MODE == kGateUp, "gate/up: down has few stages and keeps the decode kernels");
   constexpr bool kTwo = MODE == kGateUp;
   constexpr int U = 4, KC = 128 * U;
   __shared__ __attribute__((aligned(16))) uint16_t xs[kSmallRows][kSmallMaxK + 8];
@@ -585,28 +604,46 @@ __global__ __launch_bounds__(kThreads) void gemm_decode_ks_kernel(GemmArgs a, F1
       su[b] = *reinterpret_cast<const u32x2*>(s1 + st * SSTEP);
     }
   };
-  if (wave < nst) load(0, wave);
-
-  // activation rows in fp16: gate/up reads the prep's x16 row of the slot's token,
-  // down converts its bf16 H row with the row's power of two
-  for (int64_t u = tid; u < kSmallRows * (K / 8); u += kThreads) {
-    const int r = (int)(u / (K / 8));
-    const int64_t c = u % (K / 8);
-    u32x4 o = {0, 0, 0, 0};
-    if (r < rows) {
-      if constexpr (kTwo) {
-        o = ld16(d.x16 + (int64_t)(a.perm[rb + r] / a.topk) * K + 8 * c);
-      } else {
-        const u32x4 v = ld16(a.x + (int64_t)(rb + r) * K + 8 * c);
-        const float sc = ldexpf(1.0f, row_exponent(d.hmax[rb + r]));
+  // The tile's token rows and their exponents (gate/up) through scalar loads: they
+  // neither queue behind the weight loads nor wait for them, and the epilogue
+  // finds its scales ready instead of ending on two dependent loads.
+  // (rows past the tile's last repeat its last row: no branches between the loads)
+  if (FULL || wave < nst) load(0, wave);
+  int tok[kSmallRows], xe[kSmallRows];
+  if constexpr (kTwo) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const f16x2 h2 = {(_Float16)(bf16_lo(v[j]) * sc), (_Float16)(bf16_hi(v[j]) * sc)};
-          o[j] = __builtin_bit_cast(uint32_t, h2);
-        }
-      }
+    for (int r = 0; r < kSmallRows; ++r) tok[r] = __builtin_amdgcn_readfirstlane(a.perm[rb + min(r, rows - 1)]);
+#pragma unroll
+    for (int r = 0; r < kSmallRows; ++r) tok[r] /= a.topk;
+#pragma unroll
+    for (int r = 0; r < kSmallRows; ++r) xe[r] = __builtin_amdgcn_readfirstlane(d.xexp[tok[r]]);
+  }
+  const float s2g = a.w0.scale_2[e];
+  const float s2u = kTwo ? a.w1.scale_2[e] : 0.0f;
+
+  // activation rows: the prep's x16 row of each slot's token. Buffer loads, all
+  // issued before any is waited for; a unit past the tile's rows reads out of
+  // the descriptor's range and gets zeros without a memory access.
+  {
+    constexpr int NU = kSmallRows * (kSmallMaxK / 8) / kThreads;
+    const __amdgpu_buffer_rsrc_t xrs = rsrc(d.x16, a.x_rows * K * 2);
+    u32x4 xv[NU];
+#pragma unroll
+    for (int i = 0; i < NU; ++i) {
+      const int u = i * kThreads + tid;
+      const int r = u / (int)(K / 8), c = u % (int)(K / 8);   // r is the same across a wave (K >= 512)
+      const int tr = r == 0 ? tok[0] : r == 1 ? tok[1] : r == 2 ? tok[2] : tok[3];
+      const uint32_t off = r < rows ? (uint32_t)(tr * (int)K * 2 + 16 * c) : 0x80000000u;
+      xv[i] = __builtin_amdgcn_raw_buffer_load_b128(xrs, off, 0, 0);
     }
-    st16(&xs[r][8 * c], o);
+    // K = 4096: the second stage goes out now, behind the activations; waiting
+    // for those then counts the second stage's loads as still in flight
+    if (FULL) load(1, wave + 4);
+#pragma unroll
+    for (int i = 0; i < NU; ++i) {
+      const int u = i * kThreads + tid;
+      if (FULL || u < kSmallRows * (int)(K / 8)) st16(&xs[u / (int)(K / 8)][8 * (u % (int)(K / 8))], xv[i]);
+    }
   }
   __syncthreads();
 
@@ -614,7 +651,7 @@ __global__ __launch_bounds__(kThreads) void gemm_decode_ks_kernel(GemmArgs a, F1
   const f16x8 zero8 = {};
   // stage st from register set b (a literal at each call, so the sets stay in registers)
   auto step = [&](const int b, int st) {
-    if (st + 4 < nst) load(b ^ 1, st + 4);
+    if (!FULL && st + 4 < nst) load(b ^ 1, st + 4);
     const int64_t kb = (int64_t)st * KC;
 #pragma unroll
     for (int i = 0; i < U; ++i) {
@@ -635,9 +672,14 @@ __global__ __launch_bounds__(kThreads) void gemm_decode_ks_kernel(GemmArgs a, F1
       }
     }
   };
-  for (int st = wave; st < nst; st += 8) {
-    step(0, st);
-    if (st + 4 < nst) step(1, st + 4);
+  if (FULL) {
+    step(0, wave);
+    step(1, wave + 4);
+  } else {
+    for (int st = wave; st < nst; st += 8) {
+      step(0, st);
+      if (st + 4 < nst) step(1, st + 4);
+    }
   }
 
   // partial sums of waves 1..3 to wave 0, added in wave order
@@ -663,10 +705,11 @@ __global__ __launch_bounds__(kThreads) void gemm_decode_ks_kernel(GemmArgs a, F1
   if (lr >= rows) return;
   const int64_t p = rb + lr;
   const int64_t n0 = (int64_t)blockIdx.y * 16 + 4 * q;
-  float unscale = kTwo ? ldexpf(1.0f, -d.xexp[a.perm[p] / a.topk]) : ldexpf(1.0f, -row_exponent(d.hmax[p]));
+  const int xl = lr == 0 ? xe[0] : lr == 1 ? xe[1] : lr == 2 ? xe[2] : xe[3];
+  float unscale = ldexpf(1.0f, -xl);
   if (a.act_scale) unscale *= *a.act_scale;   // W4A4: the activations' input_scale
-  const float s2a = a.w0.scale_2[e] * unscale;
-  const float s2b = kTwo ? a.w1.scale_2[e] * unscale : 0.0f;
+  const float s2a = s2g * unscale;
+  const float s2b = s2u * unscale;
   float v[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) v[r] = kTwo ? silu(s2a * acc0[r]) * (s2b * acc1[r]) : s2a * acc0[r];
@@ -699,8 +742,11 @@ hipError_t launch_decode_small(GemmMode mode, const GemmArgs& a, const F16Args& 
   const bool tl = a.w0.tiled;
   // gate/up only: down has few stages (K = I) and keeps the decode kernels
   if (mode != kGateUp) return hipErrorInvalidValue;
-  if (tl) hipLaunchKernelGGL((gemm_decode_ks_kernel<kGateUp, true>), grid, dim3(kThreads), 0, s, a, d);
-  else hipLaunchKernelGGL((gemm_decode_ks_kernel<kGateUp, false>), grid, dim3(kThreads), 0, s, a, d);
+  const bool full = a.K == kSmallMaxK;
+  if (tl && full) hipLaunchKernelGGL((gemm_decode_ks_kernel<kGateUp, true, true>), grid, dim3(kThreads), 0, s, a, d);
+  else if (tl) hipLaunchKernelGGL((gemm_decode_ks_kernel<kGateUp, true, false>), grid, dim3(kThreads), 0, s, a, d);
+  else if (full) hipLaunchKernelGGL((gemm_decode_ks_kernel<kGateUp, false, true>), grid, dim3(kThreads), 0, s, a, d);
+  else hipLaunchKernelGGL((gemm_decode_ks_kernel<kGateUp, false, false>), grid, dim3(kThreads), 0, s, a, d);
   return hipGetLastError();
 }
 
@@ -746,7 +792,8 @@ template <int MODE, bool F16, bool TL>
 static hipError_t launch_dec(const GemmArgs& a, const F16Args& d, int64_t grid_tiles, hipStream_t s) {
   constexpr int NS = 8;   // up to 8 stages: scales up front
   if constexpr (MODE == kDown && F16) {   // the bf16 form needs too many registers here
-    if (a.K % 512 == 0 && a.K <= 2048 && a.N % (kBlockN * 4) == 0) {
+    // (the activation tile is read through a buffer descriptor: 32-bit offsets)
+    if (a.K % 512 == 0 && a.K <= 2048 && a.N % (kBlockN * 4) == 0 && a.x_rows * a.K * 2 < ((int64_t)1 << 31)) {
       // 64-row blocks per wave stream: as many as keep >= 4 workgroups per CU
       const int64_t want = 4 * (int64_t)cu_count();
       const int nb = grid_tiles * (a.N / (kBlockN * 4)) >= want ? 4 : grid_tiles * (a.N / (kBlockN * 2)) >= want ? 2 : 1;

@@ -52,17 +52,11 @@ constexpr int RSB = 16 * RSU;       // tile row stride in bytes
 constexpr int XI = ((MT * RSU + 63) / 64 + kWaves - 1) / kWaves * kWaves;  // 1 KB direct-to-LDS loads per stage
 constexpr int XPW = XI / kWaves;    // of them per wave
 constexpr int XBUF = XI * 1024;     // bytes per buffer
-// Buffer descriptor word 3 for raw (untyped) buffer access on gfx9-family parts.
-constexpr int kRsrcWord3 = 0x00020000;
-
 template <int SEL>
 __device__ __forceinline__ float sc(uint32_t w) {
   return __builtin_amdgcn_cvt_f32_fp8(w, SEL);
 }
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int64_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRsrcWord3);
-}
 
 // MFMA operand type of the bf16 and fp16 forms
 template <bool F16> struct Op { typedef bf16x8 T; };
