@@ -241,7 +241,12 @@ __device__ __forceinline__ void prefill_body(const GemmArgs& a, const F16Args& d
       } else {
         if (s % 4 == 3) load_codes(0, s / 4, kn);   // piece s/4 was last used just above
       }
+      // the wave issuing its MFMAs takes the SIMD's issue priority while it does, so
+      // the other wave's dequant and loads fill the gaps instead of delaying them
+      // (dense MLP 958 -> 1036 TFLOP/s)
+      __builtin_amdgcn_s_setprio(3);
       mma(A, B, 0, W * NB);
+      __builtin_amdgcn_s_setprio(0);
       // LDS reads and dequant first, then the MFMAs (the other wave of the SIMD
       // fills the gaps)
 #pragma unroll
