@@ -137,15 +137,44 @@ __device__ __forceinline__ uint32_t block_byte(uint32_t amax16, float gs, float&
 }
 
 // Codes of 8 bf16 values (one u32x4) -> one dword, element 2j in the low nibble of byte j.
-__device__ __forceinline__ uint32_t quant8(u32x4 v, float s_eff) {
+// code = e2m1_rne(q) with q the correctly rounded w / s_eff. The e2m1 code comes
+// from the packed fp4 convert with a unit scale, which equals e2m1_rne bit for bit
+// on every non-NaN fp32 input (checked exhaustively on the device, both signs:
+// nearest even, saturation at 6, sign bit kept).
+// Fast path without a division per element: with r = 1/s_eff rounded, and
+// r_lo = r(1 - 2^-20), r_hi = r(1 + 2^-20) rounded, every |w * r_lo| <= |q| <=
+// |w * r_hi| (the roundings move each product by at most 3 * 2^-24 relative, q by
+// 2^-24), all with the sign of w. The convert is monotone in |q|, so where the
+// codes of w * r_lo and w * r_hi agree they are the code of q; only a word with
+// a value that close to a rounding boundary (a tie, for instance) takes the
+// exact division.
+__device__ __forceinline__ uint32_t quant8_exact(u32x4 v, float s_eff) {
   uint32_t word = 0;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t lo = (s_eff != 0.0f) ? e2m1_rne(bf16_lo(v[i]) / s_eff) : 0u;
-    const uint32_t hi = (s_eff != 0.0f) ? e2m1_rne(bf16_hi(v[i]) / s_eff) : 0u;
-    word |= (lo | (hi << 4)) << (8 * i);
-  }
+  word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, bf16_lo(v[0]) / s_eff, bf16_hi(v[0]) / s_eff, 1.0f, 0);
+  word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, bf16_lo(v[1]) / s_eff, bf16_hi(v[1]) / s_eff, 1.0f, 1);
+  word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, bf16_lo(v[2]) / s_eff, bf16_hi(v[2]) / s_eff, 1.0f, 2);
+  word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, bf16_lo(v[3]) / s_eff, bf16_hi(v[3]) / s_eff, 1.0f, 3);
   return word;
+}
+
+__device__ __forceinline__ uint32_t quant8_scaled(u32x4 v, float r) {
+  uint32_t word = 0;
+  word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, bf16_lo(v[0]) * r, bf16_hi(v[0]) * r, 1.0f, 0);
+  word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, bf16_lo(v[1]) * r, bf16_hi(v[1]) * r, 1.0f, 1);
+  word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, bf16_lo(v[2]) * r, bf16_hi(v[2]) * r, 1.0f, 2);
+  word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, bf16_lo(v[3]) * r, bf16_hi(v[3]) * r, 1.0f, 3);
+  return word;
+}
+
+__device__ __forceinline__ uint32_t quant8(u32x4 v, float s_eff) {
+  if (s_eff == 0.0f) return 0u;
+  const float r = 1.0f / s_eff;
+  const float r_lo = r * (1.0f - 0x1p-20f), r_hi = r * (1.0f + 0x1p-20f);
+  if (r_hi <= 3.0e38f) {   // finite (an s_eff near the bottom of the fp32 range takes the exact path)
+    const uint32_t lo = quant8_scaled(v, r_lo), hi = quant8_scaled(v, r_hi);
+    if (lo == hi) return lo;
+  }
+  return quant8_exact(v, s_eff);
 }
 
 // Power-of-two exponent p that puts a row maximum m (> 0, given by its fp32 bits)

@@ -81,6 +81,63 @@ __global__ __launch_bounds__(kPackThreads) void pack_quant_kernel(
       (uint16_t)sbytes;
 }
 
+// Tiled output layout: one wave per 32 rows x 256 inputs, lane (r, h) = row r of
+// the block, inputs 128h .. 128h + 127 of the chunk (8 16-blocks). Each store
+// instruction then writes whole 512-byte runs: code piece j of the 64 lanes is
+// the 16-byte piece (row r, inputs 128h + 32j ..) of two runs, and the 8 scale
+// bytes of the lanes fill the chunk's 512-byte scale run. (With one thread per
+// 32 inputs of a row in row order, every 16-byte code store and 2-byte scale
+// store landed in a different run: 1.28 ms per 288-tensor batch against 0.88 for
+// the row-major layout.) Same arithmetic per block as pack_quant_kernel.
+__global__ __launch_bounds__(kPackThreads) void pack_quant_tiled_kernel(
+    const uint16_t* __restrict__ w, int64_t n, int64_t k, int nblk, const uint32_t* __restrict__ partial,
+    uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, float* __restrict__ scale_2) {
+  const int g = blockIdx.y;
+  __shared__ float s_scale2;
+  if (threadIdx.x < 64) {
+    uint32_t m = 0;
+    for (int i = threadIdx.x; i < nblk; i += 64) m = max(m, partial[(int64_t)g * nblk + i]);
+    for (int off = 32; off >= 1; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
+    if (threadIdx.x == 0) {
+      float amax = __builtin_bit_cast(float, m << 16);
+      float s2 = amax / 2688.0f;
+      s_scale2 = s2;
+      if (blockIdx.x == 0) scale_2[g] = s2;
+    }
+  }
+  __syncthreads();
+  const float s2 = s_scale2;
+  const int64_t chunks = k / 256;
+  const int64_t item = (int64_t)blockIdx.x * (kPackThreads / 64) + (threadIdx.x >> 6);
+  if (item >= (n / 32) * chunks) return;
+  const int lane = threadIdx.x & 63, r = lane & 31, h = lane >> 5;
+  const int64_t R = item / chunks, c = item % chunks;
+  const int64_t row = 32 * R + r;
+  const uint16_t* src = w + (int64_t)g * n * k + row * k + 256 * c + 128 * h;
+  u32x4 v[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) v[i] = ld16(src + 8 * i);
+  uint8_t* cg = codes + (int64_t)g * n * (k / 2);
+  uint32_t sb[2] = {0, 0};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {   // code piece j: 16-blocks 2j, 2j + 1 of the lane's 8
+    u32x4 out;
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const u32x4 a = v[4 * j + 2 * b], bb = v[4 * j + 2 * b + 1];
+      float s_eff;
+      const uint32_t byte = block_byte(max(absmax8(a), absmax8(bb)), s2, s_eff);
+      out[2 * b] = quant8(a, s_eff);
+      out[2 * b + 1] = quant8(bb, s_eff);
+      const int blk = 2 * j + b;
+      sb[blk / 4] |= byte << (8 * (blk % 4));
+    }
+    st16(cg + code_piece_off(true, row, 8 * c + 4 * h + j, k), out);
+  }
+  *reinterpret_cast<u32x2*>(scales + (int64_t)g * n * (k / 16) + scale_off(true, row, 16 * c + 8 * h, k)) =
+      u32x2{sb[0], sb[1]};
+}
+
 // Static activation quantization (the W4A4 form): the block steps of the pack
 // with a calibrated input_scale (one fp32 in device memory) in place of scale_2.
 // One thread: 32 consecutive elements of a row -> 16 code bytes, 2 scale bytes
@@ -189,6 +246,13 @@ hipError_t launch_pack(const uint16_t* w, int batch, int64_t n, int64_t k, uint8
                      nblk, partial);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (tiled && n % 32 == 0 && k % 256 == 0) {
+    const int64_t items = (n / 32) * (k / 256);
+    const int64_t gx = (items + kPackThreads / 64 - 1) / (kPackThreads / 64);
+    hipLaunchKernelGGL(pack_quant_tiled_kernel, dim3((unsigned)gx, batch), dim3(kPackThreads), 0, s, w, n, k,
+                       nblk, partial, codes, scales, scale_2);
+    return hipGetLastError();
+  }
   const int64_t units = n * (k / 32);
   const int64_t gx = (units + kPackThreads - 1) / kPackThreads;
   hipLaunchKernelGGL(pack_quant_kernel, dim3((unsigned)gx, batch), dim3(kPackThreads), 0, s, w, n, k,
