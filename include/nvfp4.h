@@ -70,7 +70,7 @@
 extern "C" {
 #endif
 
-#define NVFP4_ABI_VERSION 5
+#define NVFP4_ABI_VERSION 6
 
 #define NVFP4_LAYOUT_ROWS 0
 #define NVFP4_LAYOUT_TILED32 1
@@ -144,6 +144,19 @@ nvfp4_status nvfp4_relayout(const nvfp4_weight_t* src, const nvfp4_weight_t* dst
  */
 nvfp4_status nvfp4_dequant(const nvfp4_weight_t* w, uint16_t* wq_unscaled, float* wq_scaled,
                            void* stream);
+
+/*
+ * nvfp4_selftest_fp4_convert - debug export behind the pack's e2m1 encoding.
+ * Passage: issue #308 "The checkpoint" (e2m1 codes). The pack, the activation
+ * quantization of W4A4 and their exports encode e2m1 codes with the device's
+ * packed fp4 convert (unit scale) instead of comparisons against the rounding
+ * midpoints. This runs both on every non-NaN fp32 bit pattern and its negation
+ * (2^32 inputs, one launch) and counts the ones where the convert's code differs
+ * from the reading of the pages (nearest, ties to the even code, saturation at
+ * 6, sign bit of the input kept).
+ * mismatches: device uint64, overwritten with the count (0 expected).
+ */
+nvfp4_status nvfp4_selftest_fp4_convert(unsigned long long* mismatches, void* stream);
 
 /*
  * nvfp4_linear - dense Fp4Linear: y[m, n] = bf16(scale_2 * sum_k x[m,k] * W[n,k]).

@@ -23,12 +23,12 @@ import torch
 
 __all__ = [
     "Nvfp4Error", "NVFP4Weight", "load_library", "library_path", "abi_version", "ABI_VERSION",
-    "pack", "relayout", "dequant", "linear", "linear_gated", "moe_route", "moe_grouped",
+    "pack", "relayout", "dequant", "selftest_fp4_convert", "linear", "linear_gated", "moe_route", "moe_grouped",
     "moe_workspace_size", "pack_workspace_size", "LAYOUT_ROWS", "LAYOUT_TILED32",
 ]
 
 # interface version this binding was written against (NVFP4_ABI_VERSION in include/nvfp4.h)
-ABI_VERSION = 5
+ABI_VERSION = 6
 
 LAYOUT_ROWS = 0       # the checkpoint's row-major codes and scales
 LAYOUT_TILED32 = 1    # blocks of 32 rows (n % 32 == 0, k % 256 == 0)
@@ -64,6 +64,7 @@ _SIGNATURES = {
     "nvfp4_pack": (ctypes.c_int, [_P, _I32, _I64, _I64, _P, _P, _P, _P, _SZ, _I32, _P]),
     "nvfp4_relayout": (ctypes.c_int, [_WP, _WP, _P]),
     "nvfp4_dequant": (ctypes.c_int, [_WP, _P, _P, _P]),
+    "nvfp4_selftest_fp4_convert": (ctypes.c_int, [_P, _P]),
     "nvfp4_linear": (ctypes.c_int, [_P, _I64, _WP, _P, _P]),
     "nvfp4_linear_gated": (ctypes.c_int, [_P, _I64, _WP, _WP, _P, _P]),
     "nvfp4_moe_route_workspace_size": (_SZ, [_I64, _I32, _I32]),
@@ -256,6 +257,15 @@ def linear_gated(x: torch.Tensor, w_gate: NVFP4Weight, w_up: NVFP4Weight,
     _check(lib.nvfp4_linear_gated(_ptr(x), x.shape[0], ctypes.byref(g), ctypes.byref(u), _ptr(out), _stream()),
            "nvfp4_linear_gated")
     return out
+
+
+def selftest_fp4_convert(device="cuda") -> int:
+    """Inputs (of all 2^32 fp32 patterns, NaNs skipped, with their negations) whose
+    device fp4 convert differs from the e2m1 rounding the pack uses; 0 expected."""
+    lib = load_library()
+    out = torch.empty((1,), dtype=torch.int64, device=device)
+    _check(lib.nvfp4_selftest_fp4_convert(_ptr(out), _stream()), "nvfp4_selftest_fp4_convert")
+    return int(out.item())
 
 
 def moe_route(topk_ids: torch.Tensor, n_experts: int, expert_begin: int = 0, scratch: bool = True):

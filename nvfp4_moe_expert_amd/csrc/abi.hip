@@ -327,6 +327,12 @@ nvfp4_status nvfp4_relayout(const nvfp4_weight_t* src, const nvfp4_weight_t* dst
                                   const_cast<uint8_t*>(dst->scales), static_cast<hipStream_t>(stream)));
 }
 
+nvfp4_status nvfp4_selftest_fp4_convert(unsigned long long* mismatches, void* stream) {
+  if (!mismatches) return NVFP4_ERR_NULL;
+  if (reinterpret_cast<uintptr_t>(mismatches) % 8 != 0) return NVFP4_ERR_ALIGN;
+  return from_hip(launch_fp4_convert_check(mismatches, static_cast<hipStream_t>(stream)));
+}
+
 nvfp4_status nvfp4_dequant(const nvfp4_weight_t* w, uint16_t* wq_unscaled, float* wq_scaled,
                            void* stream) {
   nvfp4_status st = check_weight(w);

@@ -109,6 +109,9 @@ struct RoutePrep {
   const float* act_scale;   // W4A4: x16 holds the NVFP4-quantized rows (unscaled values), xexp 0
   int rpb;                  // rows per prep workgroup (set by launch_route)
 };
+// Counts the fp32 inputs whose packed fp4 convert differs from e2m1_rne (into *bad).
+hipError_t launch_fp4_convert_check(unsigned long long* bad, hipStream_t s);
+
 hipError_t launch_route(const int32_t* ids, int64_t S, int E, int expert_begin, int tile_rows,
                         int32_t* offsets, int32_t* perm, int32_t* inv, int32_t* tiles,
                         int32_t* n_tiles, const RoutePrep& prep, hipStream_t s,

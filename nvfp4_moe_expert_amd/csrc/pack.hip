@@ -229,6 +229,31 @@ __global__ __launch_bounds__(kPackThreads) void dequant_kernel(
   }
 }
 
+__global__ void fill_u64_kernel(unsigned long long* p) {
+  if (threadIdx.x == 0) *p = 0ull;
+}
+
+// Every non-NaN fp32 bit pattern b (and -b): the packed fp4 convert's code
+// against e2m1_rne. Thread t of the grid takes patterns t, t + stride, ... in
+// 32 bits; the count is added only on a mismatch.
+__global__ __launch_bounds__(kPackThreads) void fp4_convert_check_kernel(unsigned long long* __restrict__ bad) {
+  const uint32_t stride = gridDim.x * kPackThreads;
+  uint32_t local = 0;
+  for (uint64_t b = (uint64_t)blockIdx.x * kPackThreads + threadIdx.x; b < ((uint64_t)1 << 32); b += stride) {
+    const float q = __builtin_bit_cast(float, (uint32_t)b);
+    if (q != q) continue;
+    const uint32_t hw = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, q, -q, 1.0f, 0);
+    local += hw != (e2m1_rne(q) | (e2m1_rne(-q) << 4));
+  }
+  if (local) atomicAdd(bad, (unsigned long long)local);
+}
+
+hipError_t launch_fp4_convert_check(unsigned long long* bad, hipStream_t s) {
+  hipLaunchKernelGGL(fill_u64_kernel, dim3(1), dim3(64), 0, s, bad);
+  hipLaunchKernelGGL(fp4_convert_check_kernel, dim3(65536), dim3(kPackThreads), 0, s, bad);
+  return hipGetLastError();
+}
+
 // ------------------------------------------------------------------ launchers
 int pack_nblk(int64_t per_tensor) {
   int64_t per_block = (int64_t)kPackThreads * 8 * 16;   // 16 loads per thread per block

@@ -108,6 +108,13 @@ def test_pack_bit_exact(name):
     assert np.array_equal(g.scale_2.cpu().numpy().view(np.uint32), s2.view(np.uint32))
 
 
+def test_fp4_convert_equals_e2m1_rounding_everywhere():
+    # the pack encodes e2m1 with the device's fp4 convert: it must round every fp32
+    # input (both signs, 2^32 patterns, NaNs skipped) as the nearest-even reading does
+    note("fp4 convert self-test over all fp32 bit patterns")
+    assert nv.selftest_fp4_convert(DEV) == 0
+
+
 def test_pack_2d_input_and_repeat_determinism():
     w = synth.bf16_normal((48, 128), 0.02, 36)
     a = nv.pack(bf16_dev(w))
