@@ -564,7 +564,6 @@ constexpr int kSmallMaxK = 4096;
 template <int MODE, bool TL, bool FULL>
 __global__ __launch_bounds__(kThreads) void gemm_decode_ks_kernel(GemmArgs a, F16Args d) {
   static_assert(MODE == kGateUp, "gate/up: down has few stages and keeps the decode kernels");
-  constexpr bool kTwo = MODE == kGateUp;
   constexpr int U = 4, KC = 128 * U;
   __shared__ __attribute__((aligned(16))) uint16_t xs[kSmallRows][kSmallMaxK + 8];
   __shared__ f32x4 red[3][2][64];
@@ -588,8 +587,8 @@ __global__ __launch_bounds__(kThreads) void gemm_decode_ks_kernel(GemmArgs a, F1
   }
   const uint8_t* c0 = a.w0.codes + coff;
   const uint8_t* s0 = a.w0.scales + soff;
-  const uint8_t* c1 = kTwo ? a.w1.codes + coff : nullptr;
-  const uint8_t* s1 = kTwo ? a.w1.scales + soff : nullptr;
+  const uint8_t* c1 = a.w1.codes + coff;
+  const uint8_t* s1 = a.w1.scales + soff;
   const int64_t SSTEP = TL ? 2 * KC : KC / 16;
   const int nst = (int)(K / KC);
 
@@ -599,10 +598,8 @@ __global__ __launch_bounds__(kThreads) void gemm_decode_ks_kernel(GemmArgs a, F1
   auto load = [&](int b, int st) {
     load_codes<U, TL>(Cg[b], c0, (int64_t)st * KC);
     sg[b] = *reinterpret_cast<const u32x2*>(s0 + st * SSTEP);
-    if constexpr (kTwo) {
-      load_codes<U, TL>(Cu[b], c1, (int64_t)st * KC);
-      su[b] = *reinterpret_cast<const u32x2*>(s1 + st * SSTEP);
-    }
+    load_codes<U, TL>(Cu[b], c1, (int64_t)st * KC);
+    su[b] = *reinterpret_cast<const u32x2*>(s1 + st * SSTEP);
   };
   // The tile's token rows and their exponents (gate/up) through scalar loads: they
   // neither queue behind the weight loads nor wait for them, and the epilogue
@@ -610,16 +607,14 @@ __global__ __launch_bounds__(kThreads) void gemm_decode_ks_kernel(GemmArgs a, F1
   // (rows past the tile's last repeat its last row: no branches between the loads)
   if (FULL || wave < nst) load(0, wave);
   int tok[kSmallRows], xe[kSmallRows];
-  if constexpr (kTwo) {
 #pragma unroll
-    for (int r = 0; r < kSmallRows; ++r) tok[r] = __builtin_amdgcn_readfirstlane(a.perm[rb + min(r, rows - 1)]);
+  for (int r = 0; r < kSmallRows; ++r) tok[r] = __builtin_amdgcn_readfirstlane(a.perm[rb + min(r, rows - 1)]);
 #pragma unroll
-    for (int r = 0; r < kSmallRows; ++r) tok[r] /= a.topk;
+  for (int r = 0; r < kSmallRows; ++r) tok[r] /= a.topk;
 #pragma unroll
-    for (int r = 0; r < kSmallRows; ++r) xe[r] = __builtin_amdgcn_readfirstlane(d.xexp[tok[r]]);
-  }
+  for (int r = 0; r < kSmallRows; ++r) xe[r] = __builtin_amdgcn_readfirstlane(d.xexp[tok[r]]);
   const float s2g = a.w0.scale_2[e];
-  const float s2u = kTwo ? a.w1.scale_2[e] : 0.0f;
+  const float s2u = a.w1.scale_2[e];
 
   // activation rows: the prep's x16 row of each slot's token. Buffer loads, all
   // issued before any is waited for; a unit past the tile's rows reads out of
@@ -656,8 +651,7 @@ __global__ __launch_bounds__(kThreads) void gemm_decode_ks_kernel(GemmArgs a, F1
 #pragma unroll
     for (int i = 0; i < U; ++i) {
       const f16x2 sgf = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sg[b][i / 2] >> (16 * (i & 1)), 1.0f, false);
-      f16x2 suf = {};
-      if constexpr (kTwo) suf = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(su[b][i / 2] >> (16 * (i & 1)), 1.0f, false);
+      const f16x2 suf = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(su[b][i / 2] >> (16 * (i & 1)), 1.0f, false);
 #pragma unroll
       for (int sst = 0; sst < 4; ++sst) {
         const f16x8 B = lr < kSmallRows
@@ -665,10 +659,8 @@ __global__ __launch_bounds__(kThreads) void gemm_decode_ks_kernel(GemmArgs a, F1
                             : zero8;
         const f16x2 gs = (sst < 2) ? f16x2{sgf[0], sgf[0]} : f16x2{sgf[1], sgf[1]};
         acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(dequant8_f16(Cg[b].c[i][sst], gs), B, acc0, 0, 0, 0);
-        if constexpr (kTwo) {
-          const f16x2 us = (sst < 2) ? f16x2{suf[0], suf[0]} : f16x2{suf[1], suf[1]};
-          acc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(dequant8_f16(Cu[b].c[i][sst], us), B, acc1, 0, 0, 0);
-        }
+        const f16x2 us = (sst < 2) ? f16x2{suf[0], suf[0]} : f16x2{suf[1], suf[1]};
+        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(dequant8_f16(Cu[b].c[i][sst], us), B, acc1, 0, 0, 0);
       }
     }
   };
@@ -685,19 +677,17 @@ __global__ __launch_bounds__(kThreads) void gemm_decode_ks_kernel(GemmArgs a, F1
   // partial sums of waves 1..3 to wave 0, added in wave order
   if (wave > 0) {
     red[wave - 1][0][lane] = acc0;
-    if constexpr (kTwo) red[wave - 1][1][lane] = acc1;
+    red[wave - 1][1][lane] = acc1;
   }
   __syncthreads();
   if (wave > 0) return;
 #pragma unroll
   for (int w = 0; w < 3; ++w) {
-    const f32x4 p0 = red[w][0][lane];
+    const f32x4 p0 = red[w][0][lane], p1 = red[w][1][lane];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) acc0[r] += p0[r];
-    if constexpr (kTwo) {
-      const f32x4 p1 = red[w][1][lane];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) acc1[r] += p1[r];
+    for (int r = 0; r < 4; ++r) {
+      acc0[r] += p0[r];
+      acc1[r] += p1[r];
     }
   }
 
@@ -712,23 +702,18 @@ __global__ __launch_bounds__(kThreads) void gemm_decode_ks_kernel(GemmArgs a, F1
   const float s2b = s2u * unscale;
   float v[4];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) v[r] = kTwo ? silu(s2a * acc0[r]) * (s2b * acc1[r]) : s2a * acc0[r];
-  if constexpr (MODE == kDown) {
-    *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.out) + (int64_t)a.perm[p] * N + n0) =
-        f32x4{v[0], v[1], v[2], v[3]};
-  } else {
-    u32x2 o;
-    o[0] = pack_bf16x2(v[0], v[1]);
-    o[1] = pack_bf16x2(v[2], v[3]);
-    *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(a.out) + p * N + n0) = o;
-    // row maximum of |H| as stored, for the down projection's fp16 scaling (order-free)
-    float m = 0.0f;
+  for (int r = 0; r < 4; ++r) v[r] = silu(s2a * acc0[r]) * (s2b * acc1[r]);
+  u32x2 o;
+  o[0] = pack_bf16x2(v[0], v[1]);
+  o[1] = pack_bf16x2(v[2], v[3]);
+  *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(a.out) + p * N + n0) = o;
+  // row maximum of |H| as stored, for the down projection's fp16 scaling (order-free)
+  float m = 0.0f;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) m = fmaxf(m, fabsf((float)(__bf16)v[r]));
-    m = fmaxf(m, __shfl_xor(m, 16));
-    m = fmaxf(m, __shfl_xor(m, 32));
-    if (q == 0) atomicMax(reinterpret_cast<unsigned int*>(d.hmax + p), __builtin_bit_cast(unsigned int, m));
-  }
+  for (int r = 0; r < 4; ++r) m = fmaxf(m, fabsf((float)(__bf16)v[r]));
+  m = fmaxf(m, __shfl_xor(m, 16));
+  m = fmaxf(m, __shfl_xor(m, 32));
+  if (q == 0) atomicMax(reinterpret_cast<unsigned int*>(d.hmax + p), __builtin_bit_cast(unsigned int, m));
 }
 
 bool decode_small_supported(int64_t K, int64_t N) {
