@@ -395,6 +395,10 @@ namespace {
 void route_ranges(int64_t n, int E, int& P, int64_t& chunk) {
   P = kRouteLdsInts / E;
   if (P > kRouteWaves) P = kRouteWaves;
+  // no more ranges than 64-slot steps: every range costs a row of counters to
+  // clear and a term in each expert's cursor sum
+  const int64_t steps = (n + 63) / 64;
+  if (P > steps) P = (int)steps;
   if (P < 1) P = 1;
   chunk = (n + P - 1) / P;
   chunk = ((chunk + 63) / 64) * 64;
