@@ -468,19 +468,18 @@ __global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict_
   const int64_t t = u / per_tok, c8 = u % per_tok;
   float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   if constexpr (KM > 0) {
-    bool ok[KM];
+    // the partial rows are loaded before the ids are known (a skipped slot's row is
+    // workspace of no meaning: it is loaded, then left out of the sum by a select),
+    // so the two loads overlap instead of the partials waiting for the ids
+    int id[KM];
     float wt[KM];
     f32x4 a[KM], b[KM];
 #pragma unroll
     for (int j = 0; j < KM; ++j) {
-      const int e = (j < k) ? ids[t * k + j] - eb : -1;
-      ok[j] = e >= 0 && e < E;
-      wt[j] = ok[j] ? w[t * k + j] : 0.0f;
-    }
-#pragma unroll
-    for (int j = 0; j < KM; ++j) {
+      id[j] = (j < k) ? ids[t * k + j] : eb - 1;
+      wt[j] = (j < k) ? w[t * k + j] : 0.0f;
       a[j] = b[j] = f32x4{0, 0, 0, 0};
-      if (ok[j]) {
+      if (j < k) {
         const f32x4* src = reinterpret_cast<const f32x4*>(ypart + (t * k + j) * H + c8 * 8);
         a[j] = src[0];
         b[j] = src[1];
@@ -488,7 +487,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict_
     }
 #pragma unroll
     for (int j = 0; j < KM; ++j) {
-      if (!ok[j]) continue;
+      const int e = id[j] - eb;
+      if (e < 0 || e >= E) continue;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         acc[i] += wt[j] * a[j][i];
