@@ -222,6 +222,25 @@ def test_workspace_sizes_monotone_and_cover_buffers():
     assert lib.nvfp4_moe_workspace_size(4, 0, 288, 4096, 1536) == 0
 
 
+def test_route_workspace_size():
+    # no scratch up to 4096 slots (one workgroup routes them); beyond, one row of
+    # per-expert counts per window of >= 2048 slots, at most 64 windows; the routed
+    # MLP keeps them in its fp32 partials, which are always large enough
+    lib = nv.load_library()
+    f = lib.nvfp4_moe_route_workspace_size
+    assert f(512, 8, 288) == 0
+    assert f(4096 // 8, 8, 288) == 0
+    assert f(4096 // 8 + 1, 8, 288) == 3 * 288 * 4          # 4104 slots: 3 windows of 2048
+    assert f(4096, 8, 288) == 16 * 288 * 4                  # 32768 slots: 16 windows
+    assert f(16500, 8, 288) == 63 * 288 * 4                 # 132000 slots: 63 windows of 2112
+    assert f(1 << 20, 8, 4096) == 64 * 4096 * 4
+    assert f(-1, 8, 288) == 0 and f(4, 0, 288) == 0 and f(4, 8, 0) == 0
+    for T in (513, 4096, 16500, 1 << 20):
+        for E in (1, 288, 4096):
+            if f(T, 8, E):
+                assert f(T, 8, E) <= T * 8 * 32 * 4           # the smallest Ypart (H = 32) holds them
+
+
 def test_block_validation():
     lib = nv.load_library()
     r = lambda T=4, H=256, E=16, k=2, ws=B, wsb=None, x=A, ids=B, w=B + 4096: lib.nvfp4_router_topk(

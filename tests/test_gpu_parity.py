@@ -146,9 +146,9 @@ def _route_cases():
     # prefill-sized batches with uniform ids, one of them ragged and with skipped ids
     cases.append(("uniform_4096", r.integers(0, 288, (4096, 8)).astype(np.int32), 288, 0))
     cases.append(("uniform_4097_skips", r.integers(0, 300, (4097, 8)).astype(np.int32), 288, 6))
-    # 4096 experts over several windows; 64 windows of more than 2048 slots
+    # 4096 experts over several windows; 63 windows of 2112 slots (the most windows: 64)
     cases.append(("many_experts_large", r.integers(0, 4096, (1000, 8)).astype(np.int32), 4096, 0))
-    cases.append(("windows_64", r.integers(-3, 290, (16500, 8)).astype(np.int32), 288, 0))
+    cases.append(("windows_63", r.integers(-3, 290, (16500, 8)).astype(np.int32), 288, 0))
     return cases
 
 
@@ -165,7 +165,7 @@ def test_route_bit_exact(ci):
     assert np.array_equal(inv.cpu().numpy(), rinv)
 
 
-@pytest.mark.parametrize("name", ["prefill_zipf", "uniform_4097_skips", "many_experts_large", "windows_64"])
+@pytest.mark.parametrize("name", ["prefill_zipf", "uniform_4097_skips", "many_experts_large", "windows_63"])
 def test_route_one_workgroup_large_batch(name):
     # without scratch one workgroup routes a batch the scratch path spreads over windows
     _, ids, E, eb = next(c for c in _route_cases() if c[0] == name)
@@ -279,6 +279,8 @@ def _run_moe(x, ids, w, gate, up, down, eb=0):
     (64, 8, 20, 256, 160, 63),
     (300, 4, 6, 512, 256, 74),     # prefill tiles in the fp16 form, 2 tiles per expert (full + ragged)
     (150, 8, 40, 256, 512, 75),    # prefill fp16 form, 30 rows per expert on average (1-row-block tiles)
+    (600, 2, 8, 512, 256, 76),     # two activation rows per prep workgroup (ragged last one)
+    (600, 8, 16, 256, 256, 77),    # 4800 slots: the route's three windows, prep rows in pairs
 ])
 def test_moe_vs_oracle(T, k, E, H, I, seed):
     note(f"moe T={T} k={k} E={E} H={H} I={I}")
