@@ -332,6 +332,42 @@ def test_moe_token_permutation_and_repeat_bitwise(T, k, E, H, I):
     assert np.array_equal(yp, y1[p])
 
 
+@pytest.mark.parametrize("T,k,E,H,I", [(1, 8, 12, 4096, 512),     # one token: K-split gate/up
+                                       (8, 4, 16, 2048, 512),     # decode tiles
+                                       (300, 4, 6, 512, 256),     # prefill tiles, fp16 form
+                                       (600, 8, 16, 256, 256)])   # 4800 slots: three-launch route
+def test_moe_graph_capture_replays_equal_eager(T, k, E, H, I):
+    # the library allocates, synchronizes and clears nothing on the host side, so a
+    # captured call replays; every replay, with eager work and synchronizations in
+    # between, must give the eager result bit for bit
+    note(f"moe graph capture T={T} k={k} E={E} H={H} I={I}")
+    x, ids, w, gate, up, down = _moe_problem(T, k, E, H, I, 78, sigma=0.05)
+    xd, idd, wd = bf16_dev(x), torch.from_numpy(ids).to(DEV), torch.from_numpy(w).to(DEV)
+    gw, uw, dw = weight_dev(gate), weight_dev(up), weight_dev(down)
+    ws = torch.empty((nv.moe_workspace_size(T, k, E, H, I),), dtype=torch.uint8, device=DEV)
+    out = torch.empty((T, H), dtype=torch.bfloat16, device=DEV)
+    nv.moe_grouped(xd, idd, wd, gw, uw, dw, workspace=ws, out=out)
+    torch.cuda.synchronize()
+    eager = out.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        nv.moe_grouped(xd, idd, wd, gw, uw, dw, workspace=ws, out=out)   # warm-up on the side stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        nv.moe_grouped(xd, idd, wd, gw, uw, dw, workspace=ws, out=out)
+    for rep in range(3):
+        out.zero_()
+        ws.fill_(0x5A)                                                     # stale workspace contents
+        _ = _run_moe(x[::-1].copy(), ids[::-1].copy(), w[::-1].copy(), gate, up, down)   # eager work between
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), eager.view(torch.int16)), f"replay {rep}"
+
+
 @pytest.mark.parametrize("T,I", [(24, 128), (200, 256)])
 def test_moe_k1_matches_dense_mlp_path(T, I):
     # one expert per token with weight 1: the grouped path equals linear_gated then
