@@ -368,6 +368,51 @@ def test_moe_graph_capture_replays_equal_eager(T, k, E, H, I):
         assert torch.equal(out.view(torch.int16), eager.view(torch.int16)), f"replay {rep}"
 
 
+def test_pack_and_linear_graph_capture_replays_equal_eager():
+    # pack (both quantize kernels' layouts) and the dense linear paths captured in one graph
+    note("pack + linear graph capture")
+    wb = synth.bf16_normal((3, 256, 512), 0.02, 79)
+    wd = torch.from_numpy(wb.view(np.int16)).view(torch.bfloat16).to(DEV)
+    xs = [bf16_dev(synth.bf16_normal((m, 512), 1.0, 80, m)) for m in (4, 300)]
+    lin = ONV.pack(wb[0])
+    lw = weight_dev((lin[0][None], lin[1][None], np.float32(lin[2])))
+    outs = [torch.empty((x.shape[0], 256), dtype=torch.bfloat16, device=DEV) for x in xs]
+
+    def work():
+        p = [nv.pack(wd, layout=nv.LAYOUT_TILED32), nv.pack(wd, layout=nv.LAYOUT_ROWS)]
+        for x, o in zip(xs, outs):
+            nv.linear(x, lw, out=o)
+        return p
+
+    eager_p = work()
+    torch.cuda.synchronize()
+    eager_o = [o.clone() for o in outs]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        work()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        cap_p = work()
+    for rep in range(3):
+        for o in outs:
+            o.zero_()
+        for pk in cap_p:
+            pk.codes.zero_()
+            pk.scales.zero_()
+        work()                                                             # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(cap_p, eager_p):
+            assert torch.equal(a.codes, b.codes) and torch.equal(a.scales, b.scales), f"pack, replay {rep}"
+            assert torch.equal(a.scale_2, b.scale_2), f"scale_2, replay {rep}"
+        for a, b in zip(outs, eager_o):
+            assert torch.equal(a.view(torch.int16), b.view(torch.int16)), f"linear, replay {rep}"
+
+
 @pytest.mark.parametrize("T,I", [(24, 128), (200, 256)])
 def test_moe_k1_matches_dense_mlp_path(T, I):
     # one expert per token with weight 1: the grouped path equals linear_gated then
