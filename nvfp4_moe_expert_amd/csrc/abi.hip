@@ -550,13 +550,16 @@ nvfp4_status nvfp4_moe_grouped_bf16(const uint16_t* x, int64_t T, int64_t H, con
   uint16_t* h = reinterpret_cast<uint16_t*>(p);
   p += round_up(sizeof(uint16_t) * (size_t)(S * I));
   float* ypart = reinterpret_cast<float*>(p);
+  // tiles of 64 or 128 rows (the tile list above is sized for 64)
+  const int tr = bf16_grouped_tile_rows(S, n_experts);
+  const int64_t grid_tiles = S / tr + (S < n_experts ? S : n_experts);
   // Ypart is not written before down: it holds the route's scratch meanwhile
-  hipError_t e = launch_route(topk_ids, S, n_experts, expert_begin, 64, offsets, perm, nullptr, tiles, n_tiles,
+  hipError_t e = launch_route(topk_ids, S, n_experts, expert_begin, tr, offsets, perm, nullptr, tiles, n_tiles,
                               RoutePrep{}, s, reinterpret_cast<int32_t*>(ypart), sizeof(float) * (size_t)(S * H));
   if (e == hipSuccess)
-    e = launch_bf16_grouped(true, x, w_gate, w_up, tiles, n_tiles, max_tiles, perm, k, I, H, h, s);
+    e = launch_bf16_grouped(true, x, w_gate, w_up, tiles, n_tiles, grid_tiles, perm, k, I, H, h, s, tr);
   if (e == hipSuccess)
-    e = launch_bf16_grouped(false, h, w_down, nullptr, tiles, n_tiles, max_tiles, perm, 0, H, I, ypart, s);
+    e = launch_bf16_grouped(false, h, w_down, nullptr, tiles, n_tiles, grid_tiles, perm, 0, H, I, ypart, s, tr);
   if (e == hipSuccess) e = launch_combine(topk_ids, topk_w, ypart, T, k, H, n_experts, expert_begin, nullptr, 1, y, s);
   return from_hip(e);
 }

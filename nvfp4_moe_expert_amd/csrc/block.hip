@@ -61,18 +61,23 @@ struct Bf16Group {
   int64_t w_stride;        // elements of one expert's weight
 };
 
-template <int MODE, bool GROUPED>
+// TM: 32-row activation blocks per wave (1: 64-row workgroup tiles; 2: 128-row
+// tiles, for grouped calls whose experts average at least 64 rows: every weight
+// row loaded then serves twice the activation rows, and a tile of a large expert
+// re-reads its weights half as often).
+template <int MODE, bool GROUPED, int TM>
 __global__ __launch_bounds__(kThreads) void bf16_gemm_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w0,
                                                              const uint16_t* __restrict__ w1, int64_t M, int64_t N,
                                                              int64_t K, int64_t k_per_split, void* __restrict__ out,
                                                              float* __restrict__ partial, Bf16Group grp) {
   constexpr int NW = MODE == kBf16Gated ? 2 : 1;
-  __shared__ __attribute__((aligned(16))) uint16_t xs[2][BM][LDW];
+  constexpr int TBM = BM * TM;   // activation rows per workgroup
+  __shared__ __attribute__((aligned(16))) uint16_t xs[2][TBM][LDW];
   __shared__ __attribute__((aligned(16))) uint16_t ws[2][NW * BN][LDW];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wt = wave >> 1, wn = wave & 1;
-  int64_t m0 = (int64_t)blockIdx.x * BM, rb = 0;
+  int64_t m0 = (int64_t)blockIdx.x * TBM, rb = 0;
   if constexpr (GROUPED) {
     const int tile = (int)blockIdx.x;
     if (tile >= *grp.n_tiles) return;
@@ -91,12 +96,18 @@ __global__ __launch_bounds__(kThreads) void bf16_gemm_kernel(const uint16_t* __r
   // global -> LDS: load i of thread tid moves 16 bytes (8 inputs) of row tid / 4,
   // inputs 8 * (tid % 4) + 32 * i of the stage
   const int lr = tid >> 2, lc = (tid & 3) * 8;
-  const bool xok = m0 + lr < M;
-  int64_t xrow = m0 + lr;
-  if constexpr (GROUPED) {
-    if (xok) xrow = grp.topk > 0 ? grp.perm[rb + lr] / grp.topk : rb + lr;
+  bool xok[TM];
+  const uint16_t* xp[TM];
+#pragma unroll
+  for (int u = 0; u < TM; ++u) {   // activation rows lr and, with TM = 2, lr + 64
+    const int r = lr + BM * u;
+    xok[u] = m0 + r < M;
+    int64_t xrow = m0 + r;
+    if constexpr (GROUPED) {
+      if (xok[u]) xrow = grp.topk > 0 ? grp.perm[rb + r] / grp.topk : rb + r;
+    }
+    xp[u] = x + (xok[u] ? xrow * K : 0) + lc;
   }
-  const uint16_t* xp = x + (xok ? xrow * K : 0) + lc;
   const uint16_t* wp[NW];
   bool wok[NW];
 #pragma unroll
@@ -104,11 +115,12 @@ __global__ __launch_bounds__(kThreads) void bf16_gemm_kernel(const uint16_t* __r
     wok[j] = n0 + lr < N;
     wp[j] = (j == 0 ? w0 : w1) + (wok[j] ? (n0 + lr) * K : 0) + lc;
   }
-  u32x4 rx[LPR], rw[NW][LPR];
+  u32x4 rx[TM][LPR], rw[NW][LPR];
   auto load = [&](int64_t kb) {
 #pragma unroll
     for (int i = 0; i < LPR; ++i) {
-      rx[i] = ld16_guard(xp + kb + 32 * i, xok);
+#pragma unroll
+      for (int u = 0; u < TM; ++u) rx[u][i] = ld16_guard(xp[u] + kb + 32 * i, xok[u]);
 #pragma unroll
       for (int j = 0; j < NW; ++j) rw[j][i] = ld16_guard(wp[j] + kb + 32 * i, wok[j]);
     }
@@ -116,15 +128,18 @@ __global__ __launch_bounds__(kThreads) void bf16_gemm_kernel(const uint16_t* __r
   auto store = [&](int b) {
 #pragma unroll
     for (int i = 0; i < LPR; ++i) {
-      st16(&xs[b][lr][lc + 32 * i], rx[i]);
+#pragma unroll
+      for (int u = 0; u < TM; ++u) st16(&xs[b][lr + BM * u][lc + 32 * i], rx[u][i]);
 #pragma unroll
       for (int j = 0; j < NW; ++j) st16(&ws[b][j * BN + lr][lc + 32 * i], rw[j][i]);
     }
   };
 
-  f32x16 acc[NW];
+  f32x16 acc[NW][TM];
 #pragma unroll
-  for (int j = 0; j < NW; ++j) acc[j] = f32x16{};
+  for (int j = 0; j < NW; ++j)
+#pragma unroll
+    for (int t = 0; t < TM; ++t) acc[j][t] = f32x16{};
 
   if (nst > 0) {
     load(kb0);
@@ -137,43 +152,51 @@ __global__ __launch_bounds__(kThreads) void bf16_gemm_kernel(const uint16_t* __r
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
       const int kk = 16 * ks + 8 * (lane >> 5);
-      const bf16x8 B = *reinterpret_cast<const bf16x8*>(&xs[b][32 * wt + (lane & 31)][kk]);
+      bf16x8 B[TM];
+#pragma unroll
+      for (int t = 0; t < TM; ++t)
+        B[t] = *reinterpret_cast<const bf16x8*>(&xs[b][32 * (TM * wt + t) + (lane & 31)][kk]);
 #pragma unroll
       for (int j = 0; j < NW; ++j) {
         const bf16x8 A = *reinterpret_cast<const bf16x8*>(&ws[b][j * BN + 32 * wn + (lane & 31)][kk]);
-        acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, B, acc[j], 0, 0, 0);
+#pragma unroll
+        for (int t = 0; t < TM; ++t) acc[j][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, B[t], acc[j][t], 0, 0, 0);
       }
     }
     if (st + 1 < nst) store(b ^ 1);
     __syncthreads();
   }
 
-  // lane holds C[token m0 + 32wt + lane%32][weight row n0 + 32wn + 8(r/4) + 4(lane/32) + r%4]
-  int64_t m = m0 + 32 * wt + (lane & 31);
-  if (m >= M) return;
-  if constexpr (GROUPED) m = (MODE == kBf16F32) ? grp.perm[rb + m] : rb + m;   // output row
+  // lane holds C[token m0 + 32(TM wt + t) + lane%32][weight row n0 + 32wn + 8(r/4) + 4(lane/32) + r%4]
   const bool split = !GROUPED && partial != nullptr;
 #pragma unroll
-  for (int g = 0; g < 4; ++g) {
-    const int64_t n = n0 + 32 * wn + 8 * g + 4 * (lane >> 5);
-    if (n >= N) continue;   // N % 4 == 0: the 4 rows are all in or all out
-    if (split) {
+  for (int t = 0; t < TM; ++t) {
+    int64_t m = m0 + 32 * (TM * wt + t) + (lane & 31);
+    if (m >= M) continue;
+    if constexpr (GROUPED) m = (MODE == kBf16F32) ? grp.perm[rb + m] : rb + m;   // output row
 #pragma unroll
-      for (int j = 0; j < NW; ++j) {
-        float* dst = partial + ((int64_t)blockIdx.z * NW + j) * M * N + m * N + n;
-        *reinterpret_cast<f32x4*>(dst) = f32x4{acc[j][4 * g], acc[j][4 * g + 1], acc[j][4 * g + 2], acc[j][4 * g + 3]};
+    for (int g = 0; g < 4; ++g) {
+      const int64_t n = n0 + 32 * wn + 8 * g + 4 * (lane >> 5);
+      if (n >= N) continue;   // N % 4 == 0: the 4 rows are all in or all out
+      if (split) {
+#pragma unroll
+        for (int j = 0; j < NW; ++j) {
+          float* dst = partial + ((int64_t)blockIdx.z * NW + j) * M * N + m * N + n;
+          *reinterpret_cast<f32x4*>(dst) =
+              f32x4{acc[j][t][4 * g], acc[j][t][4 * g + 1], acc[j][t][4 * g + 2], acc[j][t][4 * g + 3]};
+        }
+      } else if constexpr (MODE == kBf16F32) {
+        *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) + m * N + n) =
+            f32x4{acc[0][t][4 * g], acc[0][t][4 * g + 1], acc[0][t][4 * g + 2], acc[0][t][4 * g + 3]};
+      } else {
+        float h[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) h[r] = silu(acc[0][t][4 * g + r]) * acc[NW - 1][t][4 * g + r];
+        u32x2 o;
+        o[0] = pack_bf16x2(h[0], h[1]);
+        o[1] = pack_bf16x2(h[2], h[3]);
+        *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(out) + m * N + n) = o;
       }
-    } else if constexpr (MODE == kBf16F32) {
-      *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) + m * N + n) =
-          f32x4{acc[0][4 * g], acc[0][4 * g + 1], acc[0][4 * g + 2], acc[0][4 * g + 3]};
-    } else {
-      float h[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) h[r] = silu(acc[0][4 * g + r]) * acc[NW - 1][4 * g + r];
-      u32x2 o;
-      o[0] = pack_bf16x2(h[0], h[1]);
-      o[1] = pack_bf16x2(h[2], h[3]);
-      *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(out) + m * N + n) = o;
     }
   }
 }
@@ -285,18 +308,29 @@ size_t bf16_gemm_partial_bytes(int64_t M, int64_t N, int64_t K, bool gated) {
   return s > 1 ? (size_t)s * (gated ? 2 : 1) * (size_t)M * (size_t)N * sizeof(float) : 0;
 }
 
+int bf16_grouped_tile_rows(int64_t S, int64_t E) {
+  const int64_t busy = S < E ? S : E;
+  return (busy > 0 && S >= BM * busy) ? 2 * BM : BM;
+}
+
 hipError_t launch_bf16_grouped(bool gated, const uint16_t* x, const uint16_t* w0, const uint16_t* w1,
                                const int32_t* tiles, const int32_t* n_tiles, int64_t max_tiles, const int32_t* perm,
-                               int topk, int64_t N, int64_t K, void* out, hipStream_t s) {
+                               int topk, int64_t N, int64_t K, void* out, hipStream_t s, int tile_rows) {
   if (max_tiles <= 0) return hipSuccess;
+  if (tile_rows != BM && tile_rows != 2 * BM) return hipErrorInvalidValue;
   const Bf16Group grp{tiles, n_tiles, perm, topk, N * K};
   const dim3 grid((unsigned)max_tiles, (unsigned)((N + BN - 1) / BN), 1u);
-  if (gated)
-    hipLaunchKernelGGL((bf16_gemm_kernel<kBf16Gated, true>), grid, dim3(kThreads), 0, s, x, w0, w1, (int64_t)0, N, K,
-                       K, out, nullptr, grp);
-  else
-    hipLaunchKernelGGL((bf16_gemm_kernel<kBf16F32, true>), grid, dim3(kThreads), 0, s, x, w0, w1, (int64_t)0, N, K,
-                       K, out, nullptr, grp);
+#define NVFP4_BF16G(MODE_, TM_)                                                                                   \
+  hipLaunchKernelGGL((bf16_gemm_kernel<MODE_, true, TM_>), grid, dim3(kThreads), 0, s, x, w0, w1, (int64_t)0, N, K, \
+                     K, out, nullptr, grp)
+  if (tile_rows == 2 * BM) {
+    if (gated) NVFP4_BF16G(kBf16Gated, 2);
+    else NVFP4_BF16G(kBf16F32, 2);
+  } else {
+    if (gated) NVFP4_BF16G(kBf16Gated, 1);
+    else NVFP4_BF16G(kBf16F32, 1);
+  }
+#undef NVFP4_BF16G
   return hipGetLastError();
 }
 
@@ -312,10 +346,10 @@ hipError_t launch_bf16_gemm(bool gated, const uint16_t* x, const uint16_t* w0, c
   const dim3 grid((unsigned)gm, (unsigned)gn, (unsigned)gz);
   const Bf16Group none{};
   if (gated)
-    hipLaunchKernelGGL((bf16_gemm_kernel<kBf16Gated, false>), grid, dim3(kThreads), 0, s, x, w0, w1, M, N, K, kps, out,
+    hipLaunchKernelGGL((bf16_gemm_kernel<kBf16Gated, false, 1>), grid, dim3(kThreads), 0, s, x, w0, w1, M, N, K, kps, out,
                        part, none);
   else
-    hipLaunchKernelGGL((bf16_gemm_kernel<kBf16F32, false>), grid, dim3(kThreads), 0, s, x, w0, w1, M, N, K, kps, out,
+    hipLaunchKernelGGL((bf16_gemm_kernel<kBf16F32, false, 1>), grid, dim3(kThreads), 0, s, x, w0, w1, M, N, K, kps, out,
                        part, none);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || gz == 1) return e;

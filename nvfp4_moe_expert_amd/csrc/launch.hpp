@@ -136,12 +136,14 @@ size_t bf16_gemm_partial_bytes(int64_t M, int64_t N, int64_t K, bool gated);
 hipError_t launch_bf16_gemm(bool gated, const uint16_t* x, const uint16_t* w0, const uint16_t* w1, int64_t M,
                             int64_t N, int64_t K, void* out, float* partial, hipStream_t s,
                             int* splits_left = nullptr);
-// Grouped bf16 GEMM over the route's tile list (tiles of <= 64 rows): gated (gate/up,
-// x rows gathered through perm / topk, H written in permuted order) or fp32 (down,
-// topk 0: H rows in permuted order, written to Ypart at slot perm[p]).
+// Grouped bf16 GEMM over the route's tile list (tiles of <= tile_rows rows, 64 or
+// 128): gated (gate/up, x rows gathered through perm / topk, H written in permuted
+// order) or fp32 (down, topk 0: H rows in permuted order, written to Ypart at slot
+// perm[p]). bf16_grouped_tile_rows picks the tile rows for S slots over E experts.
+int bf16_grouped_tile_rows(int64_t S, int64_t E);
 hipError_t launch_bf16_grouped(bool gated, const uint16_t* x, const uint16_t* w0, const uint16_t* w1,
                                const int32_t* tiles, const int32_t* n_tiles, int64_t max_tiles, const int32_t* perm,
-                               int topk, int64_t N, int64_t K, void* out, hipStream_t s);
+                               int topk, int64_t N, int64_t K, void* out, hipStream_t s, int tile_rows);
 // Per row of fp32 logits ([splits][T][E], summed in split order): the k largest
 // (ties to the lower index) and their softmax.
 hipError_t launch_topk_softmax(const float* logits, int splits, int64_t T, int E, int k, int32_t* ids, float* w,

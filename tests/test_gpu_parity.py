@@ -718,7 +718,9 @@ def test_moe_block_single_token():
 # ------------------------------------------------------------------ BF16 routed experts
 @pytest.mark.parametrize("T,k,E,H,I,seed,eb", [
     (8, 4, 16, 2048, 512, 114, 0),      # decode-like: ~2 rows per expert
-    (300, 4, 6, 512, 256, 115, 0),      # 200 rows per expert: 4 tiles of 64, the last ragged
+    (300, 4, 6, 512, 256, 115, 0),      # 200 rows per expert: 128-row tiles, the second ragged
+    (600, 8, 5, 256, 128, 118, 0),      # 4800 slots: windowed route, 128-row tiles
+    (40, 4, 16, 256, 128, 119, 0),      # 10 rows per expert: 64-row tiles
     (1, 8, 12, 256, 128, 116, 0),       # one token
     (30, 4, 4, 256, 128, 117, 4),       # expert-parallel slice (ids 0..11, local 4..7), duplicates
 ])
