@@ -338,7 +338,21 @@ hipError_t launch_bf16_gemm(bool gated, const uint16_t* x, const uint16_t* w0, c
                             int64_t N, int64_t K, void* out, float* partial, hipStream_t s, int* splits_left) {
   if (splits_left) *splits_left = 1;
   if (M <= 0) return hipSuccess;
-  const int64_t gm = (M + BM - 1) / BM, gn = (N + BN - 1) / BN;
+  const int64_t gn = (N + BN - 1) / BN;
+  // 128-row tiles where they still give one K split (at least two workgroups per CU)
+  const int64_t gm2 = (M + 2 * BM - 1) / (2 * BM);
+  if (M >= 4 * BM && splits_for(gm2 * gn, K) == 1) {
+    const dim3 grid2((unsigned)gm2, (unsigned)gn, 1u);
+    const Bf16Group none{};
+    if (gated)
+      hipLaunchKernelGGL((bf16_gemm_kernel<kBf16Gated, false, 2>), grid2, dim3(kThreads), 0, s, x, w0, w1, M, N, K, K,
+                         out, nullptr, none);
+    else
+      hipLaunchKernelGGL((bf16_gemm_kernel<kBf16F32, false, 2>), grid2, dim3(kThreads), 0, s, x, w0, w1, M, N, K, K,
+                         out, nullptr, none);
+    return hipGetLastError();
+  }
+  const int64_t gm = (M + BM - 1) / BM;
   const int splits = splits_for(gm * gn, K);
   int64_t kps = (K / splits + BK - 1) / BK * BK;
   const int gz = (int)((K + kps - 1) / kps);

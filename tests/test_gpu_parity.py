@@ -621,7 +621,8 @@ def test_router_topk_vs_oracle(T, E, H, k, seed):
 
 
 @pytest.mark.parametrize("M,H,Is,seed", [(1, 4096, 1536, 103), (64, 4096, 1536, 104), (300, 2048, 512, 105),
-                                         (1024, 1024, 2048, 106)])
+                                         (1024, 1024, 2048, 106),
+                                         (4096, 2048, 2048, 109)])   # both products on 128-row tiles
 def test_bf16_mlp_vs_oracle(M, H, Is, seed):
     note(f"bf16 mlp M={M} H={H} Is={Is}")
     x = synth.bf16_normal((M, H), 1.0, seed, synth.S_X)
