@@ -148,6 +148,9 @@ def main():
             "gateup_gbs": gateup_bytes / (stage[:, 1].sum() * 1e-3) / 1e9,
             "down_gbs": down_bytes / (stage[:, 2].sum() * 1e-3) / 1e9,
             "gateup_bytes_per_launch": gateup_bytes / steps,
+            # per-step times of the event pass (first to last event of each call)
+            "step_ms_event": {q: float(np.percentile(stage.sum(axis=1), p))
+                              for q, p in (("min", 0), ("p50", 50), ("p90", 90))},
         }
 
     def w4a4_scales():
@@ -415,6 +418,7 @@ def main():
                      "algorithmic_bytes_per_launch": round(head["gateup_bytes_per_launch"]),
                      "avg_launch_ms": round(head["stage_ms_mean"]["gate_up"], 5)},
         "stages_ms": {k: round(v, 5) for k, v in head["stage_ms_mean"].items()},
+        "step_ms_event_pass": {k: round(v, 5) for k, v in head["step_ms_event"].items()},
         "experts_touched_mean": head["experts_touched_mean"],
         "down_kernel_gbs": round(head["down_gbs"], 1),
     }
