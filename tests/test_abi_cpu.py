@@ -222,6 +222,13 @@ def test_workspace_sizes_monotone_and_cover_buffers():
     assert lib.nvfp4_moe_workspace_size(4, 0, 288, 4096, 1536) == 0
 
 
+def test_selftest_fp4_convert_validation():
+    # argument errors return before any launch (no device needed)
+    lib = nv.load_library()
+    assert lib.nvfp4_selftest_fp4_convert(None, None) == ENULL
+    assert lib.nvfp4_selftest_fp4_convert(P(A + 4), None) == EALIGN
+
+
 def test_route_workspace_size():
     # no scratch up to 4096 slots (one workgroup routes them); beyond, one row of
     # per-expert counts per window of >= 2048 slots, at most 64 windows; the routed
