@@ -185,9 +185,6 @@ nvfp4_status moe_impl(const uint16_t* x, int64_t T, int64_t H, const int32_t* id
   }
   // W4A4: H quantized in place (its row maxima replace the ones gate/up recorded)
   if (e == hipSuccess && w4a4) e = launch_act_fakequant_rows(hbuf, dx.hmax, S, I, in_d, s);
-  // the prefill kernel's fp16 form of down reads H converted in place; the decode
-  // kernel converts while staging
-  if (e == hipSuccess && f16 && kd == kKPre) e = launch_h_to_f16(hbuf, dx.hmax, S, I, s);
   if (e == hipSuccess) e = mark(2);
   if (e == hipSuccess) {
     g.x = hbuf;
@@ -200,7 +197,10 @@ nvfp4_status moe_impl(const uint16_t* x, int64_t T, int64_t H, const int32_t* id
     g.act_scale = in_d;
     e = kd == kKDecS  ? launch_decode_small(kDown, g, dx, L.max_tiles, s)
         : kd == kKDec ? launch_decode(kDown, f16, g, dx, L.max_tiles, s)
-        : kd == kKPre ? launch_prefill(kDown, f16, g, dx, L.max_tiles, s)
+        // prefill down takes H in bf16: its fp16 form would need H converted in place
+        // first, a pass over H that costs more than the fp16 operands save (the
+        // decode kernels convert while staging)
+        : kd == kKPre ? launch_prefill(kDown, false, g, dx, L.max_tiles, s)
                       : launch_gemm(kDown, v, g, L.max_tiles, s);
   }
   if (e == hipSuccess) e = mark(3);

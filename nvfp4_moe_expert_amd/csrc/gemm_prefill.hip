@@ -275,7 +275,8 @@ __device__ __forceinline__ void prefill_body(const GemmArgs& a, const F16Args& d
   // and weight rows 8*(j/4) + 4*(l/32) + j%4, j = 0..15.
   // fp16 form: the activation row was scaled by 2^p; the results are scaled back
   // here (exactly: a power of two). Routed gate/up also records max |H| of each
-  // row as stored (order-free max, so deterministic) for the fp16 form of down.
+  // row as stored (order-free max, so deterministic) for the fp16 form of a
+  // decode-tile down.
   const float act = a.act_scale ? *a.act_scale : 1.0f;   // W4A4: the activations' input_scale
   const float s2a0 = a.w0.scale_2[e] * act;
   const float s2b0 = kTwo ? a.w1.scale_2[e] * act : 0.0f;
@@ -286,7 +287,6 @@ __device__ __forceinline__ void prefill_body(const GemmArgs& a, const F16Args& d
     const int64_t p = rb + tok;
     float unscale = 1.0f;
     if constexpr (F16 && MODE == kGateUp) unscale = ldexpf(1.0f, -d.xexp[a.perm[p] / a.topk]);
-    if constexpr (F16 && MODE == kDown) unscale = ldexpf(1.0f, -row_exponent(d.hmax[p]));
     const float s2a = s2a0 * unscale, s2b = s2b0 * unscale;
     float hm = 0.0f;
 #pragma unroll
@@ -420,38 +420,14 @@ hipError_t launch_prefill(GemmMode mode, bool f16, const GemmArgs& a, const F16A
       else launch_pf<kGateUp, false, 2>(a, d, grid_tiles, s);
       break;
     case kDown:
-      if (f16) narrow ? launch_pf<kDown, true, 1>(a, d, grid_tiles, s) : launch_pf<kDown, true, 2>(a, d, grid_tiles, s);
-      else narrow ? launch_pf<kDown, false, 1>(a, d, grid_tiles, s) : launch_pf<kDown, false, 2>(a, d, grid_tiles, s);
+      if (f16) return hipErrorInvalidValue;   // the fp16 form is gate/up's only
+      narrow ? launch_pf<kDown, false, 1>(a, d, grid_tiles, s) : launch_pf<kDown, false, 2>(a, d, grid_tiles, s);
       break;
     case kLinear:
       narrow ? launch_pf<kLinear, false, 1>(a, d, grid_tiles, s) : launch_pf<kLinear, false, 2>(a, d, grid_tiles, s);
       break;
     case kGated: launch_pf<kGated, false, 2>(a, d, grid_tiles, s); break;
   }
-  return hipGetLastError();
-}
-
-// H rows (bf16, in place) -> fp16 times 2^p, p from the row's recorded max |H|:
-// the input of the fp16 form of the routed down projection. 8 elements per thread.
-__global__ __launch_bounds__(256) void h_to_f16_kernel(uint16_t* h, const uint32_t* hmax, int64_t S, int64_t I) {
-  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
-  if (i >= S * I) return;
-  const int64_t p = i / I;
-  const float sc = ldexpf(1.0f, row_exponent(hmax[p]));
-  const u32x4 v = ld16(h + i);
-  u32x4 o;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const f16x2 q = {(_Float16)(bf16_lo(v[j]) * sc), (_Float16)(bf16_hi(v[j]) * sc)};
-    o[j] = __builtin_bit_cast(uint32_t, q);
-  }
-  st16(h + i, o);
-}
-
-hipError_t launch_h_to_f16(uint16_t* h, const uint32_t* hmax, int64_t S, int64_t I, hipStream_t s) {
-  if (S * I == 0) return hipSuccess;
-  const int64_t blocks = (S * I / 8 + 255) / 256;
-  hipLaunchKernelGGL(h_to_f16_kernel, dim3((unsigned)blocks), dim3(256), 0, s, h, hmax, S, I);
   return hipGetLastError();
 }
 
