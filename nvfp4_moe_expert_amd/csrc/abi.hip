@@ -129,6 +129,9 @@ nvfp4_status moe_impl(const uint16_t* x, int64_t T, int64_t H, const int32_t* id
   const Kern kg = pick(kGateUp, v, gate->layout == NVFP4_LAYOUT_TILED32, T, H, I);
   const Kern kd = pick(kDown, v, down->layout == NVFP4_LAYOUT_TILED32, S, I, H);
   if (T > 0 && (kg == kKNone || kd == kKNone)) return NVFP4_ERR_SHAPE;
+  // a prefill-tile gate/up records no row maxima of H, which a decode-tile down
+  // (fp16 form) needs; pick() never pairs the two (their shape conditions exclude it)
+  if (T > 0 && kg == kKPre && (kd == kKDec || kd == kKDecS)) return NVFP4_ERR_UNSUPPORTED;
   // W4A4 runs on the fp16 form (quantized activations are exact in fp16), which
   // the decode and prefill kernels provide
   if (w4a4 && T > 0 && (kg == kKV1 || kd == kKV1)) return NVFP4_ERR_UNSUPPORTED;

@@ -274,9 +274,9 @@ __device__ __forceinline__ void prefill_body(const GemmArgs& a, const F16Args& d
   // ---- epilogue. 32x32 result layout: lane l holds column (row of the tile) l % 32
   // and weight rows 8*(j/4) + 4*(l/32) + j%4, j = 0..15.
   // fp16 form: the activation row was scaled by 2^p; the results are scaled back
-  // here (exactly: a power of two). Routed gate/up also records max |H| of each
-  // row as stored (order-free max, so deterministic) for the fp16 form of a
-  // decode-tile down.
+  // here (exactly: a power of two). No row maxima of H are recorded: the down
+  // projection after a prefill-tile gate/up is a prefill-tile one too (both take
+  // K and N multiples of 256 and 32), and it reads H in bf16.
   const float act = a.act_scale ? *a.act_scale : 1.0f;   // W4A4: the activations' input_scale
   const float s2a0 = a.w0.scale_2[e] * act;
   const float s2b0 = kTwo ? a.w1.scale_2[e] * act : 0.0f;
@@ -288,7 +288,6 @@ __device__ __forceinline__ void prefill_body(const GemmArgs& a, const F16Args& d
     float unscale = 1.0f;
     if constexpr (F16 && MODE == kGateUp) unscale = ldexpf(1.0f, -d.xexp[a.perm[p] / a.topk]);
     const float s2a = s2a0 * unscale, s2b = s2b0 * unscale;
-    float hm = 0.0f;
 #pragma unroll
     for (int g = 0; g < 4; ++g) {               // 4 groups of 4 consecutive weight rows
       float v0[4], v1[4];
@@ -309,10 +308,6 @@ __device__ __forceinline__ void prefill_body(const GemmArgs& a, const F16Args& d
           o[0] = pack_bf16x2(v[0], v[1]);
           o[1] = pack_bf16x2(v[2], v[3]);
           *reinterpret_cast<u32x2*>(dst) = o;
-          if constexpr (F16 && MODE == kGateUp) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) hm = fmaxf(hm, fabsf(bf16_lo(j & 1 ? o[j / 2] >> 16 : o[j / 2])));
-          }
         }
       } else {
 #pragma unroll
@@ -332,10 +327,6 @@ __device__ __forceinline__ void prefill_body(const GemmArgs& a, const F16Args& d
           }
         }
       }
-    }
-    if constexpr (F16 && MODE == kGateUp) {
-      hm = fmaxf(hm, __shfl_xor(hm, 32));
-      if (h == 0) atomicMax(reinterpret_cast<unsigned int*>(d.hmax + p), __builtin_bit_cast(unsigned int, hm));
     }
   }
 }

@@ -68,7 +68,7 @@ hipError_t launch_decode_small(GemmMode mode, const GemmArgs& a, const F16Args& 
 // Prefill-tile (<= 128 rows) matrix-core GEMM; the tiled kernel covers other shapes.
 bool prefill_supported(GemmMode mode, int64_t x_rows, int64_t K, int64_t N);
 // The fp16 form (routed gate/up only; down takes bf16 H) reads the prep kernel's
-// x16 (as GemmArgs::x) and xexp, and records hmax for a decode-tile down.
+// x16 (as GemmArgs::x) and xexp.
 hipError_t launch_prefill(GemmMode mode, bool f16, const GemmArgs& a, const F16Args& d, int64_t grid_tiles,
                           hipStream_t s);
 hipError_t launch_decode(GemmMode mode, bool f16, const GemmArgs& a, const F16Args& d, int64_t grid_tiles,
