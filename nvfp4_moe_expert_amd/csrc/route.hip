@@ -465,7 +465,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict_
                                                       const float* __restrict__ ypart, int64_t T, int k,
                                                       int64_t H, int E, int eb, const float* __restrict__ extra,
                                                       int extra_splits, uint16_t* __restrict__ y) {
-  const int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t per_tok = H / 8;
   if (u >= T * per_tok) return;
   const int64_t t = u / per_tok, c8 = u % per_tok;
@@ -546,16 +546,19 @@ hipError_t launch_combine(const int32_t* ids, const float* w, const float* ypart
                           int64_t H, int E, int eb, const float* extra, int extra_splits, uint16_t* y,
                           hipStream_t s) {
   const int64_t n = T * (H / 8);
-  const int64_t gx = (n + 255) / 256;
+  // small batches: one-wave workgroups, so the partials stream through the load
+  // pipes of as many CUs as possible (one token: 8 CUs instead of 2)
+  const int bs = n < 256 * 256 ? 64 : 256;
+  const int64_t gx = (n + bs - 1) / bs;
   const bool nt = T * k * H * (int64_t)sizeof(float) > ((int64_t)128 << 20);   // partials beyond 128 MB
   if (k <= 8 && nt)
-    hipLaunchKernelGGL((combine_kernel<8, true>), dim3((unsigned)gx), dim3(256), 0, s, ids, w, ypart, T, k, H, E, eb,
+    hipLaunchKernelGGL((combine_kernel<8, true>), dim3((unsigned)gx), dim3(bs), 0, s, ids, w, ypart, T, k, H, E, eb,
                        extra, extra_splits, y);
   else if (k <= 8)
-    hipLaunchKernelGGL((combine_kernel<8, false>), dim3((unsigned)gx), dim3(256), 0, s, ids, w, ypart, T, k, H, E, eb,
+    hipLaunchKernelGGL((combine_kernel<8, false>), dim3((unsigned)gx), dim3(bs), 0, s, ids, w, ypart, T, k, H, E, eb,
                        extra, extra_splits, y);
   else
-    hipLaunchKernelGGL((combine_kernel<0, false>), dim3((unsigned)gx), dim3(256), 0, s, ids, w, ypart, T, k, H, E, eb,
+    hipLaunchKernelGGL((combine_kernel<0, false>), dim3((unsigned)gx), dim3(bs), 0, s, ids, w, ypart, T, k, H, E, eb,
                        extra, extra_splits, y);
   return hipGetLastError();
 }
