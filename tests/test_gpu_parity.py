@@ -506,6 +506,28 @@ def test_moe_tiled_vs_oracle_and_rows(T, k, E, H, I, seed):
     assert np.array_equal(bf16_host_bits(yt), bf16_host_bits(yr))
 
 
+@pytest.mark.gpu
+@pytest.mark.parametrize("T,k,E,H,I,seed", [
+    (8, 4, 16, 2048, 512, 86),      # decode tiles
+    (300, 4, 6, 512, 256, 87),      # prefill tiles, full and ragged
+])
+def test_moe_mixed_layouts_bitwise(T, k, E, H, I, seed):
+    """gate and up share a layout; down may hold the other one. Each projection's
+    kernel reads its own layout, so the output is bitwise that of all-tiled weights.
+    A gate/up pair in two layouts is refused."""
+    note(f"moe mixed layouts T={T} k={k} E={E} H={H} I={I}")
+    x, ids, w, gate, up, down = _moe_problem(T, k, E, H, I, seed, sigma=0.05)
+    args = (bf16_dev(x), torch.from_numpy(ids).to(DEV), torch.from_numpy(w).to(DEV))
+    gt, ut, dt = weight_dev(gate, TILED), weight_dev(up, TILED), weight_dev(down, TILED)
+    gr, ur, dr = weight_dev(gate), weight_dev(up), weight_dev(down)
+    ref = bf16_host_bits(nv.moe_grouped(*args, gt, ut, dt))
+    for g_, u_, d_ in ((gt, ut, dr), (gr, ur, dt)):
+        y = nv.moe_grouped(*args, g_, u_, d_)
+        torch.cuda.synchronize()
+        assert np.array_equal(bf16_host_bits(y), ref)
+    with pytest.raises(RuntimeError):
+        nv.moe_grouped(*args, gt, ur, dt)
+
 # ------------------------------------------------------------------ W4A4 activations
 def _scale_dev(*v):
     return torch.tensor([np.float32(a) for a in v], dtype=torch.float32, device=DEV)
