@@ -19,8 +19,11 @@
  * Memory.   Every tensor argument is a DEVICE pointer to contiguous row-major
  *           memory owned by the caller. The library never allocates, frees,
  *           copies to the host or synchronizes; all work is enqueued on
- *           `stream` (a hipStream_t; NULL is the default stream). It keeps no
- *           mutable global state and does not change the current device.
+ *           `stream` (a hipStream_t; NULL is the default stream). It does not
+ *           change the current device. Between calls it keeps only per-device
+ *           caches of device properties (compute-unit count, resident
+ *           workgroups per kernel), filled on first use and safe to fill from
+ *           several threads.
  * bf16.     bf16 tensors are passed as uint16_t bit patterns.
  * Weights.  A weight [n, k] (out x in) is described by nvfp4_weight_t:
  *             codes   [groups, n, k/2]  uint8: element 2j of a row in the LOW
@@ -51,14 +54,23 @@
  * Errors.   Argument errors are detected on the host before anything is
  *           enqueued; on error nothing is written. A failed launch returns
  *           NVFP4_ERR_HIP. No C++ exception crosses this interface.
- * Numerics. Products use bf16 matrix cores with fp32 accumulation over exactly
+ * Numerics. Products run on matrix cores with fp32 accumulation over exactly
  *           dequantized weights; scale_2 multiplies the fp32 accumulator. The
- *           summation order of an output element is fixed by the shapes and by
- *           the call's class (decode-shaped: at most 16 rows per local expert on
- *           average, or at most 16 rows for the dense entry points; otherwise
- *           prefill-shaped). It never depends on the values, on the other rows or
- *           on the tile a row lands in, so results are bitwise reproducible and
- *           permuting the tokens permutes the outputs bit for bit.
+ *           dense entry points feed bf16 operands. The routed kernels feed fp16
+ *           operands: a dequantized weight (at most 6 significant bits, within
+ *           [2^-10, 2688]) is exact in fp16, and each activation row is first
+ *           scaled by a power of two that puts its largest |value| in
+ *           [2^14, 2^15), so every bf16 value down to 2^-28 of the row maximum
+ *           converts exactly (smaller ones round, far below the output's bf16
+ *           rounding); the scaling is undone exactly in fp32 afterwards.
+ *           The summation order of an output element is fixed by the shapes and
+ *           by the kernel class of the call (see nvfp4_moe_grouped_class). Some
+ *           classes split K over the waves of a workgroup and add the partial
+ *           sums in a fixed wave order; none uses atomics on outputs. So the
+ *           order never depends on the values, on the other rows or on the tile a
+ *           row lands in: within one class results are bitwise reproducible,
+ *           permuting the tokens permutes the outputs bit for bit, and a batch
+ *           split into chunks gives the same bits as the whole batch.
  */
 #ifndef NVFP4_MOE_EXPERT_AMD_NVFP4_H
 #define NVFP4_MOE_EXPERT_AMD_NVFP4_H
@@ -70,7 +82,7 @@
 extern "C" {
 #endif
 
-#define NVFP4_ABI_VERSION 6
+#define NVFP4_ABI_VERSION 7
 
 #define NVFP4_LAYOUT_ROWS 0
 #define NVFP4_LAYOUT_TILED32 1
@@ -103,8 +115,9 @@ const char* nvfp4_status_string(int status);
 
 /*
  * nvfp4_pack - load-time BF16 -> NVFP4 pack of `batch` independent tensors.
- * Passage: issue #308 "What the branch does" (the MTP layer's BF16 experts are
- * packed to NVFP4 by ModelOpt's recipe at load, a projection at a time).
+ * Passage: issue #308 "What the branch does" (at load the MTP layer's BF16
+ * experts are quantized to NVFP4 with ModelOpt's recipe, one projection after
+ * another).
  * Recipe, per tensor, in fp32 with correctly rounded division:
  *   scale_2 = amax / 2688  (6 * 448);
  *   per 16-block along k: byte = e4m3(block_amax / 6 / scale_2), nearest-even,
@@ -225,6 +238,72 @@ nvfp4_status nvfp4_moe_grouped(const uint16_t* x, int64_t T, int64_t H, const in
                                const nvfp4_weight_t* gate, const nvfp4_weight_t* up,
                                const nvfp4_weight_t* down, void* ws, size_t ws_bytes,
                                uint16_t* y, void* stream);
+
+/*
+ * Kernel classes of the routed GEMMs. A class fixes the tile shape of both
+ * projections and with it the summation order of every output element, which
+ * then depends on the shapes alone (never on the batch size, the routing, the
+ * other rows or the tile a row lands in):
+ *   NVFP4_CLASS_DECODE  - tiles of at most 16 rows, weights streamed through
+ *                         registers (decode-shaped calls);
+ *   NVFP4_CLASS_PREFILL - tiles of at most 128 rows on the 32x32 matrix-core
+ *                         kernel (prompt-shaped calls);
+ *   NVFP4_CLASS_AUTO    - what nvfp4_moe_grouped runs: at most 32 slots take
+ *                         4-row tiles whose gate/up splits K over four waves
+ *                         (partials added in wave order); otherwise DECODE when
+ *                         the average local expert gets at most 16 rows
+ *                         (T*k <= 16 * min(T*k, n_experts)), else PREFILL. The
+ *                         class, and so the bits, can change with the batch size.
+ * Shapes that a class's kernel does not cover fall back the same way for every
+ * batch (tiled weights to the prefill kernel, row-major ones to the tiled
+ * fallback GEMM), so a pinned class stays bitwise chunk-invariant.
+ */
+#define NVFP4_CLASS_AUTO 0
+#define NVFP4_CLASS_DECODE 1
+#define NVFP4_CLASS_PREFILL 2
+
+/*
+ * nvfp4_moe_grouped_class - nvfp4_moe_grouped with the kernel class pinned.
+ * Passage: TensorFold issue #308, "Questions", item 4 (a prompt-shaped expert
+ * kernel whose sums do not change with the chunking). A prompt processed in
+ * chunks with NVFP4_CLASS_PREFILL (or any pinned class) gives every token the
+ * bits it gets when the whole prompt goes in one call. Same arguments, workspace
+ * (nvfp4_moe_workspace_size covers every class), ownership and errors as
+ * nvfp4_moe_grouped; an unknown class is NVFP4_ERR_UNSUPPORTED.
+ */
+nvfp4_status nvfp4_moe_grouped_class(const uint16_t* x, int64_t T, int64_t H, const int32_t* topk_ids,
+                                     const float* topk_w, int32_t k, int32_t expert_begin,
+                                     const nvfp4_weight_t* gate, const nvfp4_weight_t* up,
+                                     const nvfp4_weight_t* down, int32_t kernel_class, void* ws, size_t ws_bytes,
+                                     uint16_t* y, void* stream);
+
+/* Kernels named by nvfp4_moe_plan. */
+#define NVFP4_KERNEL_NONE 0
+#define NVFP4_KERNEL_DECODE_KSPLIT 1   /* gate/up on 4-row tiles, K split over 4 waves */
+#define NVFP4_KERNEL_DECODE 2          /* decode tiles, weights streamed, activations staged per stage */
+#define NVFP4_KERNEL_DECODE_RESIDENT 3 /* down on decode tiles: whole H tile in LDS, 1/2/4 weight blocks per wave */
+#define NVFP4_KERNEL_PREFILL 4         /* prefill tiles, 32x32 matrix-core kernel */
+#define NVFP4_KERNEL_FALLBACK 5        /* tiled fallback GEMM (row-major weights of other shapes) */
+
+/*
+ * nvfp4_moe_plan - which kernels a routed call of these shapes runs (host only:
+ * nothing is enqueued; it reads the device's compute-unit count). Passage: as
+ * nvfp4_moe_grouped_class. For T tokens (T = 0 is planned as one token), top-k,
+ * n_experts local experts, hidden H, intermediate I, the gate/up and down
+ * layouts and a kernel class, plan[5] receives:
+ *   plan[0] rows per tile (4, 16 or 128);
+ *   plan[1] the gate/up kernel (NVFP4_KERNEL_*);
+ *   plan[2] the down kernel;
+ *   plan[3] the down kernel's width: 64-row weight blocks per wave stream for
+ *           NVFP4_KERNEL_DECODE_RESIDENT, 32-row weight blocks per wave for
+ *           NVFP4_KERNEL_PREFILL, else 0;
+ *   plan[4] 1 if the routed GEMMs run on fp16 operands (see Numerics), else 0.
+ * The W4A16 and W4A4 entry points run the same kernels (W4A4 refuses plans
+ * with the fallback GEMM). Errors: NVFP4_ERR_NULL, NVFP4_ERR_SHAPE, and those
+ * of nvfp4_moe_grouped_class for the shapes and class.
+ */
+nvfp4_status nvfp4_moe_plan(int64_t T, int32_t k, int32_t n_experts, int64_t H, int64_t I, int32_t gate_layout,
+                            int32_t down_layout, int32_t kernel_class, int32_t* plan);
 
 /*
  * nvfp4_moe_grouped_timed - nvfp4_moe_grouped with a hipEvent_t recorded on

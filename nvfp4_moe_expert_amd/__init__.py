@@ -24,14 +24,22 @@ import torch
 __all__ = [
     "Nvfp4Error", "NVFP4Weight", "load_library", "library_path", "abi_version", "ABI_VERSION",
     "pack", "relayout", "dequant", "selftest_fp4_convert", "linear", "linear_gated", "moe_route", "moe_grouped",
-    "moe_workspace_size", "pack_workspace_size", "LAYOUT_ROWS", "LAYOUT_TILED32",
+    "moe_workspace_size", "pack_workspace_size", "moe_plan", "LAYOUT_ROWS", "LAYOUT_TILED32",
+    "CLASS_AUTO", "CLASS_DECODE", "CLASS_PREFILL", "KERNEL_NAMES",
 ]
 
 # interface version this binding was written against (NVFP4_ABI_VERSION in include/nvfp4.h)
-ABI_VERSION = 6
+ABI_VERSION = 7
 
 LAYOUT_ROWS = 0       # the checkpoint's row-major codes and scales
 LAYOUT_TILED32 = 1    # blocks of 32 rows (n % 32 == 0, k % 256 == 0)
+
+# kernel classes of the routed GEMMs (NVFP4_CLASS_* in include/nvfp4.h)
+CLASS_AUTO = 0
+CLASS_DECODE = 1
+CLASS_PREFILL = 2
+# kernels named by moe_plan (NVFP4_KERNEL_*)
+KERNEL_NAMES = {0: "none", 1: "decode_ksplit", 2: "decode", 3: "decode_resident", 4: "prefill", 5: "fallback"}
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libnvfp4.so")
@@ -71,6 +79,9 @@ _SIGNATURES = {
     "nvfp4_moe_route": (ctypes.c_int, [_P, _I64, _I32, _I32, _I32, _P, _P, _P, _P, _SZ, _P]),
     "nvfp4_moe_workspace_size": (_SZ, [_I64, _I32, _I32, _I64, _I64]),
     "nvfp4_moe_grouped": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _I32, _I32, _WP, _WP, _WP, _P, _SZ, _P, _P]),
+    "nvfp4_moe_grouped_class": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _I32, _I32, _WP, _WP, _WP, _I32, _P, _SZ,
+                                               _P, _P]),
+    "nvfp4_moe_plan": (ctypes.c_int, [_I64, _I32, _I32, _I64, _I64, _I32, _I32, _I32, ctypes.POINTER(_I32)]),
     "nvfp4_moe_grouped_timed": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _I32, _I32, _WP, _WP, _WP, _P, _SZ, _P,
                                                _P, ctypes.POINTER(_P)]),
     "nvfp4_moe_grouped_w4a4": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _I32, _I32, _WP, _WP, _WP, _P, _P, _P, _SZ,
@@ -290,9 +301,20 @@ def moe_workspace_size(T: int, k: int, n_experts: int, H: int, I: int) -> int:
     return load_library().nvfp4_moe_workspace_size(T, k, n_experts, H, I)
 
 
+def moe_plan(T: int, k: int, n_experts: int, H: int, I: int, gate_layout: int = LAYOUT_ROWS,
+             down_layout: int = LAYOUT_ROWS, kernel_class: int = CLASS_AUTO) -> dict:
+    """The kernels a routed call of these shapes runs (nvfp4_moe_plan; host only)."""
+    lib = load_library()
+    plan = (_I32 * 5)()
+    _check(lib.nvfp4_moe_plan(T, k, n_experts, H, I, gate_layout, down_layout, kernel_class, plan), "nvfp4_moe_plan")
+    return {"tile_rows": plan[0], "gate_up": KERNEL_NAMES[plan[1]], "down": KERNEL_NAMES[plan[2]],
+            "down_width": plan[3], "fp16": bool(plan[4])}
+
+
 def moe_grouped(x: torch.Tensor, topk_ids: torch.Tensor, topk_w: torch.Tensor, gate: NVFP4Weight,
                 up: NVFP4Weight, down: NVFP4Weight, expert_begin: int = 0, workspace: torch.Tensor | None = None,
-                out: torch.Tensor | None = None, events=None, input_scales=None) -> torch.Tensor:
+                out: torch.Tensor | None = None, events=None, input_scales=None,
+                kernel_class: int | None = None) -> torch.Tensor:
     """Routed expert MLP of one MoE layer: y[T, H] bf16.
 
     events: optional sequence of 5 torch.cuda.Event; the library records them on the
@@ -300,8 +322,12 @@ def moe_grouped(x: torch.Tensor, topk_ids: torch.Tensor, topk_w: torch.Tensor, g
     combine stages.
     input_scales: None (W4A16), or a float32 device tensor [2] holding the
     calibrated activation scales (gate/up input, down input) for W4A4
-    (nvfp4_moe_grouped_w4a4; not combined with events)."""
+    (nvfp4_moe_grouped_w4a4; not combined with events).
+    kernel_class: None (nvfp4_moe_grouped), or CLASS_AUTO / CLASS_DECODE /
+    CLASS_PREFILL to pin the class (nvfp4_moe_grouped_class; W4A16 only, no events)."""
     lib = load_library()
+    if kernel_class is not None and (input_scales is not None or events is not None):
+        raise ValueError("kernel_class is taken by the W4A16 entry point without events")
     if input_scales is not None:
         _need(input_scales, torch.float32, "input_scales", 1)
         if input_scales.numel() != 2:
@@ -329,6 +355,9 @@ def moe_grouped(x: torch.Tensor, topk_ids: torch.Tensor, topk_w: torch.Tensor, g
     if input_scales is not None:
         st = lib.nvfp4_moe_grouped_w4a4(*args[:10], _ptr(input_scales), _ptr(input_scales[1:]), *args[10:])
         _check(st, "nvfp4_moe_grouped_w4a4")
+        return out
+    if kernel_class is not None:
+        _check(lib.nvfp4_moe_grouped_class(*args[:10], kernel_class, *args[10:]), "nvfp4_moe_grouped_class")
         return out
     if events is None:
         st = lib.nvfp4_moe_grouped(*args)

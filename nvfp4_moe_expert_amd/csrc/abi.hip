@@ -55,32 +55,38 @@ Kern pick(GemmMode mode, GemmVariant v, bool tiled, int64_t x_rows, int64_t K, i
 
 nvfp4_status from_hip(hipError_t e) { return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP; }
 
-// Workspace of nvfp4_moe_grouped, in order: offsets[E+1], perm[S], tiles[max_tiles][4],
+// Workspace of nvfp4_moe_grouped, in order: offsets[E+1], perm[S], tiles[tile_cap][4],
 // n_tiles, H[S][I] bf16, Ypart[S][H] fp32, x16[T][H] fp16, xexp[T], hmax[S].
 // Each region starts on a 256-byte boundary.
 struct MoeLayout {
   size_t offsets, perm, tiles, n_tiles, h, ypart, x16, xexp, hmax, total;
-  int64_t max_tiles;
 };
 
-// Decode tiles (16 rows) when the average local expert gets at most 16 rows, else prefill tiles;
-// for at most 32 slots, 4-row tiles with gate/up's K split over the waves (when the shapes fit).
-GemmVariant moe_variant(int64_t S, int64_t E, int64_t H, int64_t I) {
+// Kernel class of the routed GEMMs, which fixes the tile shape and with it the
+// summation order of every output. NVFP4_CLASS_AUTO: decode tiles (16 rows) when the
+// average local expert gets at most 16 rows, else prefill tiles; for at most 32
+// slots, 4-row tiles with gate/up's K split over the waves (when the shapes fit).
+GemmVariant moe_variant(int64_t S, int64_t E, int64_t H, int64_t I, int cls) {
+  if (cls == NVFP4_CLASS_DECODE) return kDecode;
+  if (cls == NVFP4_CLASS_PREFILL) return kPrefill;
   const int64_t busy = S < E ? S : E;
   if (S <= 32 && decode_small_supported(H, I) && decode_supported(kDown, I, H)) return kDecodeSmall;
   return (busy > 0 && S <= 16 * busy) ? kDecode : kPrefill;
 }
 
+// Tiles of at most tr rows over S slots and E experts: sum over experts of
+// ceil(rows/tr) <= floor(S/tr) + (number of non-empty experts).
+int64_t tile_bound(int64_t S, int64_t E, int64_t tr) { return S / tr + (S < E ? S : E); }
+
 MoeLayout moe_layout(int64_t T, int k, int64_t E, int64_t H, int64_t I) {
   MoeLayout L{};
   const int64_t S = T * k;
-  const int64_t tr = variant_tile_rows(moe_variant(S, E, H, I));
-  // sum over experts of ceil(rows/tr) <= floor(S/tr) + (number of non-empty experts)
-  L.max_tiles = S / tr + (S < E ? S : E);
+  // room for the smallest tiles (4 rows), so the same workspace serves every class
+  const int64_t cap = tile_bound(S, E, variant_tile_rows(kDecodeSmall));
   size_t off = 0;
   L.offsets = off; off += round_up(sizeof(int32_t) * (size_t)(E + 1));
   L.perm = off;    off += round_up(sizeof(int32_t) * (size_t)(S > 0 ? S : 1));
-  L.tiles = off;   off += round_up(sizeof(int32_t) * 4 * (size_t)(L.max_tiles > 0 ? L.max_tiles : 1));
+  L.tiles = off;   off += round_up(sizeof(int32_t) * 4 * (size_t)(cap > 0 ? cap : 1));
   L.n_tiles = off; off += 256;
   L.h = off;       off += round_up(sizeof(uint16_t) * (size_t)S * (size_t)I);
   L.ypart = off;   off += round_up(sizeof(float) * (size_t)S * (size_t)H);
@@ -96,51 +102,83 @@ T* at(void* base, size_t off) {
   return reinterpret_cast<T*>(reinterpret_cast<char*>(base) + off);
 }
 
-// in_gu / in_d: null for W4A16; for W4A4 the device pointers of the two calibrated
-// activation input scales (gate/up input x, down input H).
-nvfp4_status moe_impl(const uint16_t* x, int64_t T, int64_t H, const int32_t* ids, const float* tw,
-                      int32_t k, int32_t eb, const nvfp4_weight_t* gate, const nvfp4_weight_t* up,
-                      const nvfp4_weight_t* down, void* ws, size_t ws_bytes, uint16_t* y,
-                      hipStream_t s, void* const* events, const float* in_gu = nullptr,
-                      const float* in_d = nullptr, const float* extra = nullptr, int extra_splits = 1) {
-  const bool w4a4 = in_gu || in_d;
-  if (w4a4 && !(in_gu && in_d)) return NVFP4_ERR_NULL;
+// The kernels one routed call runs, decided on the host from the shapes alone.
+struct MoePlan {
+  GemmVariant v;
+  Kern kg, kd;             // gate/up and down kernels
+  bool f16;                // fp16 form of the routed GEMMs
+  int64_t S, E, I;
+  int64_t grid_tiles;      // tile-list bound of the class's tile rows
+  MoeLayout L;
+};
+
+// Shapes and kernel choice of a routed call (no pointers looked at).
+nvfp4_status moe_shape_plan(int64_t T, int64_t H, int32_t k, int64_t E, int64_t I, bool gate_tiled, bool down_tiled,
+                            bool w4a4, int cls, MoePlan& P) {
+  if (T < 0 || k < 1 || k > kMaxTopk || E < 1 || E > kMaxExperts) return NVFP4_ERR_SHAPE;
+  if (cls != NVFP4_CLASS_AUTO && cls != NVFP4_CLASS_DECODE && cls != NVFP4_CLASS_PREFILL) return NVFP4_ERR_UNSUPPORTED;
+  if (T * (int64_t)k > kMaxSlots) return NVFP4_ERR_SHAPE;
+  P.S = T * k;
+  P.E = E;
+  P.I = I;
+  P.v = moe_variant(P.S, E, H, I, cls);
+  P.kg = pick(kGateUp, P.v, gate_tiled, T, H, I);
+  P.kd = pick(kDown, P.v, down_tiled, P.S, I, H);
+  if (T > 0 && (P.kg == kKNone || P.kd == kKNone)) return NVFP4_ERR_SHAPE;
+  // a prefill-tile gate/up records no row maxima of H, which a decode-tile down
+  // (fp16 form) needs; the class rules never pair the two (their shape conditions exclude it)
+  if (T > 0 && P.kg == kKPre && (P.kd == kKDec || P.kd == kKDecS)) return NVFP4_ERR_UNSUPPORTED;
+  // W4A4 runs on the fp16 form (quantized activations are exact in fp16), which
+  // the decode and prefill kernels provide
+  if (w4a4 && T > 0 && (P.kg == kKV1 || P.kd == kKV1)) return NVFP4_ERR_UNSUPPORTED;
+  // fp16 form of the routed GEMMs (x16 and H rows scaled per row by a power of two)
+  // when the decode or prefill kernels run both projections
+  P.f16 = P.kg != kKV1 && P.kd != kKV1;
+  P.grid_tiles = tile_bound(P.S, E, variant_tile_rows(P.v));
+  P.L = moe_layout(T, k, E, H, I);
+  return NVFP4_OK;
+}
+
+// Every argument check of a routed call, before anything is enqueued.
+nvfp4_status moe_check(const uint16_t* x, int64_t T, int64_t H, const int32_t* ids, const float* tw, int32_t k,
+                       const nvfp4_weight_t* gate, const nvfp4_weight_t* up, const nvfp4_weight_t* down,
+                       const uint16_t* y, const void* ws, size_t ws_bytes, bool w4a4, int cls, MoePlan& P) {
   nvfp4_status st;
   if ((st = check_weight(gate)) != NVFP4_OK) return st;
   if ((st = check_weight(up)) != NVFP4_OK) return st;
   if ((st = check_weight(down)) != NVFP4_OK) return st;
-  if (T < 0 || k < 1 || k > kMaxTopk) return NVFP4_ERR_SHAPE;
   const int64_t E = gate->groups, I = gate->n;
-  if (E > kMaxExperts) return NVFP4_ERR_SHAPE;
   if (gate->k != H || up->k != H || up->n != I || up->groups != E) return NVFP4_ERR_SHAPE;
   if (down->groups != E || down->n != H || down->k != I) return NVFP4_ERR_SHAPE;
   if (gate->layout != up->layout) return NVFP4_ERR_SHAPE;
-  if (T * (int64_t)k > kMaxSlots) return NVFP4_ERR_SHAPE;
+  if (T < 0 || k < 1 || k > kMaxTopk || E > kMaxExperts || T * (int64_t)k > kMaxSlots) return NVFP4_ERR_SHAPE;
   if (T > 0 && (!x || !ids || !tw || !y)) return NVFP4_ERR_NULL;
   if (T > 0 && (!aligned16(x) || !aligned16(y))) return NVFP4_ERR_ALIGN;
-  const MoeLayout L = moe_layout(T, k, E, H, I);
   if (T > 0) {
     if (!ws) return NVFP4_ERR_WORKSPACE;
     if (!aligned16(ws)) return NVFP4_ERR_ALIGN;
-    if (ws_bytes < L.total) return NVFP4_ERR_WORKSPACE;
+    if (ws_bytes < moe_layout(T, k, E, H, I).total) return NVFP4_ERR_WORKSPACE;
   }
-  const int64_t S = T * k;
-  const GemmVariant v = moe_variant(S, E, H, I);
-  const Kern kg = pick(kGateUp, v, gate->layout == NVFP4_LAYOUT_TILED32, T, H, I);
-  const Kern kd = pick(kDown, v, down->layout == NVFP4_LAYOUT_TILED32, S, I, H);
-  if (T > 0 && (kg == kKNone || kd == kKNone)) return NVFP4_ERR_SHAPE;
-  // a prefill-tile gate/up records no row maxima of H, which a decode-tile down
-  // (fp16 form) needs; pick() never pairs the two (their shape conditions exclude it)
-  if (T > 0 && kg == kKPre && (kd == kKDec || kd == kKDecS)) return NVFP4_ERR_UNSUPPORTED;
-  // W4A4 runs on the fp16 form (quantized activations are exact in fp16), which
-  // the decode and prefill kernels provide
-  if (w4a4 && T > 0 && (kg == kKV1 || kd == kKV1)) return NVFP4_ERR_UNSUPPORTED;
+  return moe_shape_plan(T, H, k, E, I, gate->layout == NVFP4_LAYOUT_TILED32, down->layout == NVFP4_LAYOUT_TILED32,
+                        w4a4, cls, P);
+}
+
+// The launches of a checked routed call. in_gu / in_d: null for W4A16; for W4A4 the
+// device pointers of the two calibrated activation input scales (gate/up input x,
+// down input H). extra: fp32 terms added by the combine after the k slots.
+nvfp4_status moe_run(const MoePlan& P, const uint16_t* x, int64_t T, int64_t H, const int32_t* ids, const float* tw,
+                     int32_t k, int32_t eb, const nvfp4_weight_t* gate, const nvfp4_weight_t* up,
+                     const nvfp4_weight_t* down, void* ws, uint16_t* y, hipStream_t s, void* const* events,
+                     const float* in_gu = nullptr, const float* in_d = nullptr, const float* extra = nullptr,
+                     int extra_splits = 1) {
+  const bool w4a4 = in_gu || in_d;
+  const MoeLayout& L = P.L;
+  const int64_t S = P.S, E = P.E, I = P.I;
+  const Kern kg = P.kg, kd = P.kd;
+  const GemmVariant v = P.v;
   hipEvent_t ev[5] = {};
   if (events)
-    for (int i = 0; i < 5; ++i) {
-      if (!events[i]) return NVFP4_ERR_NULL;
-      ev[i] = reinterpret_cast<hipEvent_t>(events[i]);
-    }
+    for (int i = 0; i < 5; ++i) ev[i] = reinterpret_cast<hipEvent_t>(events[i]);
   auto mark = [&](int i) -> hipError_t { return events ? hipEventRecord(ev[i], s) : hipSuccess; };
   hipError_t e = mark(0);
   if (T == 0) {
@@ -153,9 +191,7 @@ nvfp4_status moe_impl(const uint16_t* x, int64_t T, int64_t H, const int32_t* id
   int32_t* n_tiles = at<int32_t>(ws, L.n_tiles);
   uint16_t* hbuf = at<uint16_t>(ws, L.h);
   float* ypart = at<float>(ws, L.ypart);
-  // fp16 form of the routed GEMMs (x16 and H rows scaled per row by a power of two)
-  // when the decode or prefill kernels run both projections
-  const bool f16 = kg != kKV1 && kd != kKV1;
+  const bool f16 = P.f16;
   F16Args dx{at<uint16_t>(ws, L.x16), at<int32_t>(ws, L.xexp), at<uint32_t>(ws, L.hmax)};
   RoutePrep prep{};
   if (f16)
@@ -181,10 +217,10 @@ nvfp4_status moe_impl(const uint16_t* x, int64_t T, int64_t H, const int32_t* id
     g.K = H;
     g.out = hbuf;
     g.act_scale = in_gu;
-    e = kg == kKDecS  ? launch_decode_small(kGateUp, g, dx, L.max_tiles, s)
-        : kg == kKDec ? launch_decode(kGateUp, f16, g, dx, L.max_tiles, s)
-        : kg == kKPre ? launch_prefill(kGateUp, f16, g, dx, L.max_tiles, s)
-                      : launch_gemm(kGateUp, v, g, L.max_tiles, s);
+    e = kg == kKDecS  ? launch_decode_small(kGateUp, g, dx, P.grid_tiles, s)
+        : kg == kKDec ? launch_decode(kGateUp, f16, g, dx, P.grid_tiles, s)
+        : kg == kKPre ? launch_prefill(kGateUp, f16, g, dx, P.grid_tiles, s)
+                      : launch_gemm(kGateUp, v, g, P.grid_tiles, s);
   }
   // W4A4: H quantized in place (its row maxima replace the ones gate/up recorded)
   if (e == hipSuccess && w4a4) e = launch_act_fakequant_rows(hbuf, dx.hmax, S, I, in_d, s);
@@ -198,18 +234,56 @@ nvfp4_status moe_impl(const uint16_t* x, int64_t T, int64_t H, const int32_t* id
     g.K = I;
     g.out = ypart;
     g.act_scale = in_d;
-    e = kd == kKDecS  ? launch_decode_small(kDown, g, dx, L.max_tiles, s)
-        : kd == kKDec ? launch_decode(kDown, f16, g, dx, L.max_tiles, s)
+    e = kd == kKDecS  ? launch_decode_small(kDown, g, dx, P.grid_tiles, s)
+        : kd == kKDec ? launch_decode(kDown, f16, g, dx, P.grid_tiles, s)
         // prefill down takes H in bf16: its fp16 form would need H converted in place
         // first, a pass over H that costs more than the fp16 operands save (the
         // decode kernels convert while staging)
-        : kd == kKPre ? launch_prefill(kDown, false, g, dx, L.max_tiles, s)
-                      : launch_gemm(kDown, v, g, L.max_tiles, s);
+        : kd == kKPre ? launch_prefill(kDown, false, g, dx, P.grid_tiles, s)
+                      : launch_gemm(kDown, v, g, P.grid_tiles, s);
   }
   if (e == hipSuccess) e = mark(3);
   if (e == hipSuccess) e = launch_combine(ids, tw, ypart, T, k, H, (int)E, eb, extra, extra_splits, y, s);
   if (e == hipSuccess) e = mark(4);
   return from_hip(e);
+}
+
+// A whole routed call: checks, then launches.
+nvfp4_status moe_impl(const uint16_t* x, int64_t T, int64_t H, const int32_t* ids, const float* tw, int32_t k,
+                      int32_t eb, const nvfp4_weight_t* gate, const nvfp4_weight_t* up, const nvfp4_weight_t* down,
+                      void* ws, size_t ws_bytes, uint16_t* y, hipStream_t s, void* const* events,
+                      const float* in_gu, const float* in_d, int cls) {
+  const bool w4a4 = in_gu || in_d;
+  if (w4a4 && !(in_gu && in_d)) return NVFP4_ERR_NULL;
+  MoePlan P{};
+  const nvfp4_status st = moe_check(x, T, H, ids, tw, k, gate, up, down, y, ws, ws_bytes, w4a4, cls, P);
+  if (st != NVFP4_OK) return st;
+  if (events)
+    for (int i = 0; i < 5; ++i)
+      if (!events[i]) return NVFP4_ERR_NULL;
+  return moe_run(P, x, T, H, ids, tw, k, eb, gate, up, down, ws, y, s, events, in_gu, in_d);
+}
+
+// Plan entries (include/nvfp4.h, nvfp4_moe_plan) of a gate/up or down kernel.
+int32_t kernel_id(Kern kn, bool down, const MoePlan& P, int64_t H, int32_t* detail) {
+  *detail = 0;
+  switch (kn) {
+    case kKDecS: return NVFP4_KERNEL_DECODE_KSPLIT;
+    case kKDec:
+      if (down) {
+        if (const int nb = decode_down_streams(P.f16, P.S, P.I, H, P.grid_tiles)) {
+          *detail = nb;
+          return NVFP4_KERNEL_DECODE_RESIDENT;
+        }
+      }
+      return NVFP4_KERNEL_DECODE;
+    case kKPre:
+      *detail = prefill_weight_blocks(down ? kDown : kGateUp, down ? H : P.I, P.grid_tiles);
+      return NVFP4_KERNEL_PREFILL;
+    case kKV1: return NVFP4_KERNEL_FALLBACK;
+    case kKNone: break;
+  }
+  return NVFP4_KERNEL_NONE;
 }
 
 // ---- BF16 steps either side of the routed experts
@@ -283,7 +357,7 @@ const char* nvfp4_status_string(int status) {
     case NVFP4_ERR_SHAPE: return "inconsistent or unsupported sizes";
     case NVFP4_ERR_ALIGN: return "a pointer is not 16-byte aligned";
     case NVFP4_ERR_WORKSPACE: return "workspace missing or too small";
-    case NVFP4_ERR_UNSUPPORTED: return "unsupported request (the library is W4A16: bf16 activations only)";
+    case NVFP4_ERR_UNSUPPORTED: return "unsupported request (a kernel class, or a W4A4 call on shapes only the fallback GEMM covers)";
     case NVFP4_ERR_HIP: return "HIP runtime error while enqueueing";
   }
   return "unknown status";
@@ -387,7 +461,39 @@ nvfp4_status nvfp4_moe_grouped(const uint16_t* x, int64_t T, int64_t H, const in
                                const nvfp4_weight_t* down, void* ws, size_t ws_bytes, uint16_t* y,
                                void* stream) {
   return moe_impl(x, T, H, topk_ids, topk_w, k, expert_begin, gate, up, down, ws, ws_bytes, y,
-                  static_cast<hipStream_t>(stream), nullptr);
+                  static_cast<hipStream_t>(stream), nullptr, nullptr, nullptr, NVFP4_CLASS_AUTO);
+}
+
+nvfp4_status nvfp4_moe_grouped_class(const uint16_t* x, int64_t T, int64_t H, const int32_t* topk_ids,
+                                     const float* topk_w, int32_t k, int32_t expert_begin,
+                                     const nvfp4_weight_t* gate, const nvfp4_weight_t* up,
+                                     const nvfp4_weight_t* down, int32_t kernel_class, void* ws, size_t ws_bytes,
+                                     uint16_t* y, void* stream) {
+  return moe_impl(x, T, H, topk_ids, topk_w, k, expert_begin, gate, up, down, ws, ws_bytes, y,
+                  static_cast<hipStream_t>(stream), nullptr, nullptr, nullptr, kernel_class);
+}
+
+nvfp4_status nvfp4_moe_plan(int64_t T, int32_t k, int32_t n_experts, int64_t H, int64_t I, int32_t gate_layout,
+                            int32_t down_layout, int32_t kernel_class, int32_t* plan) {
+  if (!plan) return NVFP4_ERR_NULL;
+  for (int i = 0; i < 5; ++i) plan[i] = 0;
+  if (H < 32 || H % 32 != 0 || I < 32 || I % 32 != 0) return NVFP4_ERR_SHAPE;
+  for (int32_t lay : {gate_layout, down_layout})
+    if (lay != NVFP4_LAYOUT_ROWS && lay != NVFP4_LAYOUT_TILED32) return NVFP4_ERR_SHAPE;
+  if (gate_layout == NVFP4_LAYOUT_TILED32 && (I % 32 != 0 || H % 256 != 0)) return NVFP4_ERR_SHAPE;
+  if (down_layout == NVFP4_LAYOUT_TILED32 && (H % 32 != 0 || I % 256 != 0)) return NVFP4_ERR_SHAPE;
+  MoePlan P{};
+  // at least one row, so the plan names the kernels a non-empty call of this class runs
+  const nvfp4_status st = moe_shape_plan(T > 0 ? T : 1, H, k, n_experts, I, gate_layout == NVFP4_LAYOUT_TILED32,
+                                         down_layout == NVFP4_LAYOUT_TILED32, false, kernel_class, P);
+  if (st != NVFP4_OK) return st;
+  int32_t gate_detail = 0, down_detail = 0;
+  plan[0] = variant_tile_rows(P.v);
+  plan[1] = kernel_id(P.kg, false, P, H, &gate_detail);
+  plan[2] = kernel_id(P.kd, true, P, H, &down_detail);
+  plan[3] = down_detail;
+  plan[4] = P.f16 ? 1 : 0;
+  return NVFP4_OK;
 }
 
 nvfp4_status nvfp4_moe_grouped_timed(const uint16_t* x, int64_t T, int64_t H,
@@ -398,7 +504,7 @@ nvfp4_status nvfp4_moe_grouped_timed(const uint16_t* x, int64_t T, int64_t H,
                                      void* const* events) {
   if (!events) return NVFP4_ERR_NULL;
   return moe_impl(x, T, H, topk_ids, topk_w, k, expert_begin, gate, up, down, ws, ws_bytes, y,
-                  static_cast<hipStream_t>(stream), events);
+                  static_cast<hipStream_t>(stream), events, nullptr, nullptr, NVFP4_CLASS_AUTO);
 }
 
 nvfp4_status nvfp4_moe_grouped_w4a4(const uint16_t* x, int64_t T, int64_t H, const int32_t* topk_ids,
@@ -409,7 +515,8 @@ nvfp4_status nvfp4_moe_grouped_w4a4(const uint16_t* x, int64_t T, int64_t H, con
                                     void* stream) {
   if (!input_scale_gate_up || !input_scale_down) return NVFP4_ERR_NULL;
   return moe_impl(x, T, H, topk_ids, topk_w, k, expert_begin, gate, up, down, ws, ws_bytes, y,
-                  static_cast<hipStream_t>(stream), nullptr, input_scale_gate_up, input_scale_down);
+                  static_cast<hipStream_t>(stream), nullptr, input_scale_gate_up, input_scale_down,
+                  NVFP4_CLASS_AUTO);
 }
 
 nvfp4_status nvfp4_quantize_act(const uint16_t* x, int64_t rows, int64_t k, const float* input_scale,
@@ -489,13 +596,22 @@ nvfp4_status nvfp4_moe_block(const uint16_t* x, int64_t T, int64_t H, const uint
   if (T < 0 || k < 1 || k > kMaxTopk || k > E || E > kMaxExperts || !bf16_shape_ok(E, H) ||
       !bf16_shape_ok(Is, H) || !bf16_shape_ok(H, Is))
     return NVFP4_ERR_SHAPE;
-  if (T == 0) return NVFP4_OK;
-  if (!x || !w_router || !shared_gate || !shared_up || !shared_down || !ws || !y) return NVFP4_ERR_NULL;
-  if (!aligned16(x) || !aligned16(w_router) || !aligned16(shared_gate) || !aligned16(shared_up) ||
-      !aligned16(shared_down) || !aligned16(ws) || !aligned16(y))
+  if (T > 0 && (!x || !w_router || !shared_gate || !shared_up || !shared_down || !ws || !y)) return NVFP4_ERR_NULL;
+  if (T > 0 && (!aligned16(x) || !aligned16(w_router) || !aligned16(shared_gate) || !aligned16(shared_up) ||
+                !aligned16(shared_down) || !aligned16(ws) || !aligned16(y)))
     return NVFP4_ERR_ALIGN;
   const BlockLayout L = block_layout(T, k, E, H, I, Is);
-  if (ws_bytes < L.total) return NVFP4_ERR_WORKSPACE;
+  if (T > 0 && ws_bytes < L.total) return NVFP4_ERR_WORKSPACE;
+  // the routed part's checks (weights, layouts, kernel cover) before the first launch;
+  // its ids, weights and workspace lie inside ws (valid pointers when T > 0)
+  void* moe_ws = T > 0 ? at<void>(ws, L.moe) : nullptr;
+  const int32_t* ids_c = T > 0 ? at<int32_t>(ws, L.ids) : nullptr;
+  const float* tw_c = T > 0 ? at<float>(ws, L.w) : nullptr;
+  MoePlan P{};
+  if ((st = moe_check(x, T, H, ids_c, tw_c, k, gate, up, down, y, moe_ws, T > 0 ? ws_bytes - L.moe : 0, false,
+                      NVFP4_CLASS_AUTO, P)) != NVFP4_OK)
+    return st;
+  if (T == 0) return NVFP4_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
   float* logits = at<float>(ws, L.logits);
   int32_t* ids = at<int32_t>(ws, L.ids);
@@ -513,8 +629,8 @@ nvfp4_status nvfp4_moe_block(const uint16_t* x, int64_t T, int64_t H, const uint
   if (e == hipSuccess) e = launch_bf16_gemm(true, x, shared_gate, shared_up, T, Is, H, hs, part, s);
   if (e == hipSuccess) e = launch_bf16_gemm(false, hs, shared_down, nullptr, T, H, Is, ys, part, s, &ds);
   if (e != hipSuccess) return from_hip(e);
-  return moe_impl(x, T, H, ids, tw, k, 0, gate, up, down, at<void>(ws, L.moe), ws_bytes - L.moe, y, s, nullptr,
-                  nullptr, nullptr, ds > 1 ? part : ys, ds);
+  return moe_run(P, x, T, H, ids, tw, k, 0, gate, up, down, moe_ws, y, s, nullptr, nullptr, nullptr,
+                 ds > 1 ? part : ys, ds);
 }
 
 size_t nvfp4_moe_grouped_bf16_workspace_size(int64_t T, int32_t k, int32_t n_experts, int64_t H, int64_t I) {

@@ -773,15 +773,20 @@ static void launch_items(const void* one_shot, const void* persistent, int64_t g
   }
 }
 
+int decode_down_streams(bool f16, int64_t x_rows, int64_t K, int64_t N, int64_t grid_tiles) {
+  // the fp16 form only (the bf16 form needs too many registers here); the
+  // activation tile is read through a buffer descriptor: 32-bit offsets
+  if (!f16 || K % 512 != 0 || K > 2048 || N % (kBlockN * 4) != 0 || x_rows * K * 2 >= ((int64_t)1 << 31)) return 0;
+  // 64-row blocks per wave stream: as many as keep >= 4 workgroups per CU
+  const int64_t want = 4 * (int64_t)cu_count();
+  return grid_tiles * (N / (kBlockN * 4)) >= want ? 4 : grid_tiles * (N / (kBlockN * 2)) >= want ? 2 : 1;
+}
+
 template <int MODE, bool F16, bool TL>
 static hipError_t launch_dec(const GemmArgs& a, const F16Args& d, int64_t grid_tiles, hipStream_t s) {
   constexpr int NS = 8;   // up to 8 stages: scales up front
-  if constexpr (MODE == kDown && F16) {   // the bf16 form needs too many registers here
-    // (the activation tile is read through a buffer descriptor: 32-bit offsets)
-    if (a.K % 512 == 0 && a.K <= 2048 && a.N % (kBlockN * 4) == 0 && a.x_rows * a.K * 2 < ((int64_t)1 << 31)) {
-      // 64-row blocks per wave stream: as many as keep >= 4 workgroups per CU
-      const int64_t want = 4 * (int64_t)cu_count();
-      const int nb = grid_tiles * (a.N / (kBlockN * 4)) >= want ? 4 : grid_tiles * (a.N / (kBlockN * 2)) >= want ? 2 : 1;
+  if constexpr (MODE == kDown && F16) {
+    if (const int nb = decode_down_streams(true, a.x_rows, a.K, a.N, grid_tiles)) {
       switch (nb * 8 + (int)(a.K / 512)) {
 #define NVFP4_RES(NB_, NST_)                                                                          \
   case NB_ * 8 + NST_:                                                                                 \

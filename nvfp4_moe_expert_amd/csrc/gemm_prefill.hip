@@ -31,6 +31,8 @@
 //
 // Summation order of an output element: stages in increasing k, within a stage
 // MFMA steps s = 0..15, each over its 16 k. It depends only on K.
+#include <atomic>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -376,15 +378,16 @@ bool prefill_supported(GemmMode mode, int64_t x_rows, int64_t K, int64_t N) {
 }
 
 int cu_count() {
-  static int cached[64] = {};
+  // one cached count per device; threads that race on a first query store the same value
+  static std::atomic<int> cached[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
-    int n = 0;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cached[dev] = n;
+    cached[dev].store(n, std::memory_order_relaxed);
   }
-  return cached[dev];
+  return n;
 }
 
 template <int MODE, bool F16, int WB>
@@ -400,11 +403,16 @@ static void launch_pf(const GemmArgs& a, const F16Args& d, int64_t grid_tiles, h
   else hipLaunchKernelGGL((gemm_prefill_kernel<MODE, F16, WB, false>), grid, dim3(kThreads), 0, s, a, d);
 }
 
+int prefill_weight_blocks(GemmMode mode, int64_t N, int64_t grid_tiles) {
+  if (mode == kGateUp || mode == kGated) return 2;   // 32 rows of each of the two weights per wave
+  // one-weight modes: half-width workgroups when full-width ones would leave CUs idle
+  return grid_tiles * ((N + 32 * 2 * kWaves - 1) / (32 * 2 * kWaves)) < 2 * (int64_t)cu_count() ? 1 : 2;
+}
+
 hipError_t launch_prefill(GemmMode mode, bool f16, const GemmArgs& a, const F16Args& d, int64_t grid_tiles,
                           hipStream_t s) {
   if (grid_tiles <= 0) return hipSuccess;
-  // one-weight modes: half-width workgroups when full-width ones would leave CUs idle
-  const bool narrow = grid_tiles * ((a.N + 32 * 2 * kWaves - 1) / (32 * 2 * kWaves)) < 2 * (int64_t)cu_count();
+  const bool narrow = prefill_weight_blocks(mode, a.N, grid_tiles) == 1;
   switch (mode) {
     case kGateUp:
       if (f16) launch_pf<kGateUp, true, 2>(a, d, grid_tiles, s);

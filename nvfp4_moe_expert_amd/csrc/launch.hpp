@@ -73,6 +73,11 @@ hipError_t launch_prefill(GemmMode mode, bool f16, const GemmArgs& a, const F16A
                           hipStream_t s);
 hipError_t launch_decode(GemmMode mode, bool f16, const GemmArgs& a, const F16Args& d, int64_t grid_tiles,
                          hipStream_t s);
+// Routed down projection on decode tiles: 64-row weight blocks per wave stream of
+// the resident-activation kernel (1, 2 or 4), or 0 when the streaming kernel runs.
+int decode_down_streams(bool f16, int64_t x_rows, int64_t K, int64_t N, int64_t grid_tiles);
+// Prefill tiles: 32-row weight blocks per wave (1: 256 weight rows per workgroup, 2: 512).
+int prefill_weight_blocks(GemmMode mode, int64_t N, int64_t grid_tiles);
 
 hipError_t launch_pack(const uint16_t* w, int batch, int64_t n, int64_t k, uint8_t* codes,
                        uint8_t* scales, float* scale_2, uint32_t* partial, bool tiled, hipStream_t s);

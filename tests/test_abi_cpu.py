@@ -16,7 +16,7 @@ import nvfp4_moe_expert_amd as nv
 HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "nvfp4.h")
 A = 0x100000          # 16-byte aligned dummy device address
 B = 0x200000
-OK, ENULL, ESHAPE, EALIGN, EWS = 0, 1, 2, 3, 4
+OK, ENULL, ESHAPE, EALIGN, EWS, EUNSUP = 0, 1, 2, 3, 4, 5
 
 
 def declared_symbols():
@@ -281,6 +281,73 @@ def test_block_validation():
     assert blk(sg=0) == ENULL
     assert blk(wsb=64) == EWS
     assert blk(T=0) == OK
+
+
+@pytest.mark.parametrize("gate,up,down", [
+    (dict(n=128, k=256), dict(n=64, k=256), dict(n=256, k=128)),      # up n != I
+    (dict(n=128, k=256), dict(n=128, k=256), dict(n=256, k=64)),      # down k != I
+    (dict(n=128, k=256), dict(n=128, k=256), dict(n=128, k=128)),     # down n != H
+    (dict(n=256, k=256), dict(n=256, k=256, layout=1), dict(n=256, k=256)),   # gate and up layouts differ
+    (dict(n=128, k=256), dict(n=128, k=256, groups=8), dict(n=256, k=128)),   # expert counts differ
+])
+def test_block_rejects_bad_routed_weights_before_any_launch(gate, up, down):
+    # the routed part's checks run before the router is enqueued: with no GPU here, a
+    # launch would come back as NVFP4_ERR_HIP instead of the shape error
+    lib = nv.load_library()
+    g = _w(**{"groups": 16, **gate})
+    u = _w(**{"groups": 16, **up})
+    d = _w(**{"groups": 16, **down})
+    I = gate["n"]
+    wsb = lib.nvfp4_moe_block_workspace_size(8, 4, 16, 256, I, 128)
+    st = lib.nvfp4_moe_block(P(A), 8, 256, P(A), 4, ctypes.byref(g), ctypes.byref(u), ctypes.byref(d), P(A), P(A),
+                             P(A), 128, P(B), wsb, P(B), None)
+    assert st == ESHAPE
+
+
+def _moe_class(lib, cls, T=8, H=256, k=4, E=16, I=128, **kw):
+    g, u, d = _w(n=I, k=H, groups=E), _w(n=I, k=H, groups=E), _w(n=H, k=I, groups=E)
+    wsb = kw.get("wsb", lib.nvfp4_moe_workspace_size(T, k, E, H, I))
+    return lib.nvfp4_moe_grouped_class(P(kw.get("x", A)), T, H, P(A), P(A), k, 0, ctypes.byref(g), ctypes.byref(u),
+                                       ctypes.byref(d), cls, P(kw.get("ws", B)), wsb, P(B), None)
+
+
+def test_moe_class_validation():
+    lib = nv.load_library()
+    assert _moe_class(lib, 3) == EUNSUP
+    assert _moe_class(lib, -1) == EUNSUP
+    for cls in (0, 1, 2):
+        assert _moe_class(lib, cls, x=0) == ENULL
+        assert _moe_class(lib, cls, ws=0) == EWS
+        assert _moe_class(lib, cls, T=0, wsb=0) == OK
+
+
+def _plan(lib, T, k, E, H, I, gl=1, dl=1, cls=0):
+    out = (ctypes.c_int32 * 5)()
+    st = lib.nvfp4_moe_plan(T, k, E, H, I, gl, dl, cls, out)
+    return st, tuple(out)
+
+
+DEC_K, DEC, RES, PRE, FB = 1, 2, 3, 4, 5
+
+
+def test_moe_plan_names_the_kernels():
+    # without a GPU the library takes 256 compute units, the MI355X's count
+    lib = nv.load_library()
+    layer = (8, 288, 4096, 1536)
+    assert _plan(lib, 1, *layer) == (OK, (4, DEC_K, RES, 1, 1))
+    assert _plan(lib, 16, *layer) == (OK, (16, DEC, RES, 4, 1))
+    assert _plan(lib, 64, *layer) == (OK, (16, DEC, RES, 4, 1))
+    assert _plan(lib, 4096, *layer) == (OK, (128, PRE, PRE, 2, 1))
+    # a pinned class overrides the batch-size rule
+    assert _plan(lib, 1, *layer, cls=2) == (OK, (128, PRE, PRE, 1, 1))
+    assert _plan(lib, 4096, *layer, cls=1) == (OK, (16, DEC, RES, 4, 1))
+    assert _plan(lib, 1, *layer, cls=1) == (OK, (16, DEC, RES, 1, 1))
+    # row-major weights of shapes the fast kernels do not cover: the fallback, bf16 operands
+    assert _plan(lib, 9, 2, 3, 96, 64, 0, 0) == (OK, (16, FB, FB, 0, 0))
+    # tiled weights must have shapes the tiled layout allows
+    assert _plan(lib, 9, 2, 3, 96, 64)[0] == ESHAPE
+    assert _plan(lib, 9, 2, 3, 96, 64, 0, 0, cls=7)[0] == EUNSUP
+    assert lib.nvfp4_moe_plan(8, 2, 3, 256, 256, 0, 0, 0, None) == ENULL
 
 
 def test_moe_grouped_bf16_validation():

@@ -4,6 +4,7 @@ finishes in seconds (several tiles and ragged tails), plus the edge cases.
 Bit-exact: dequantized weights, packed codes/scales/scale_2, the permutation,
 and the integer-exact linear. Within max|diff| <= 1e-2*max|ref| and cosine >=
 0.9999: every bf16 output of a contraction."""
+import concurrent.futures as cf
 import json
 import os
 
@@ -203,7 +204,8 @@ def test_route_empty_batch():
 # ------------------------------------------------------------------ linear
 @pytest.mark.parametrize("M,N,K,seed", [
     (4, 256, 512, 1),        # single NVFP4 linear workload: X[4,512], W[256,512]
-    (16, 80, 4096, 49), (7, 64, 2048, 50), (3, 48, 1536, 51),   # streaming kernel, N % 64 != 0
+    (16, 80, 4096, 49), (3, 48, 1536, 51),   # N % 64 != 0, row-major: the fallback GEMM
+    (7, 64, 2048, 50),                        # at most 16 rows: the decode kernel
     (1, 64, 32, 40), (16, 128, 256, 41), (17, 100, 96, 42), (130, 48, 160, 43),
     (300, 256, 1024, 44), (129, 200, 544, 45),
     (4000, 8192, 256, 46),   # prefill tiles, full-width workgroups (grid of 32 x 16), ragged last tile
@@ -252,42 +254,92 @@ def test_linear_gated_vs_oracle(M, N, K):
 
 
 # ------------------------------------------------------------------ moe
+def _pack_experts(E, N, K, sigma, seed, stream):
+    """Oracle packs of E seeded bf16 experts [N, K], packed on threads (numpy releases
+    the GIL); the same result as ONV.pack_batch."""
+    wb = synth.expert_weights(E, N, K, sigma, seed, stream)
+    with cf.ThreadPoolExecutor(max_workers=8) as ex:
+        outs = list(ex.map(ONV.pack, wb))
+    return (np.stack([o[0] for o in outs]), np.stack([o[1] for o in outs]),
+            np.array([o[2] for o in outs], dtype=np.float32))
+
+
 def _moe_problem(T, k, E, H, I, seed, sigma=0.02, ids=None, weights=None):
     x = synth.bf16_normal((T, H), 1.0, seed, synth.S_X)
     if ids is None:
         ids, weights = synth.topk_softmax_routing(T, E, k, seed, synth.S_ROUTE)
-    gate = ONV.pack_batch(synth.expert_weights(E, I, H, sigma, seed, synth.S_GATE))
-    up = ONV.pack_batch(synth.expert_weights(E, I, H, sigma, seed, synth.S_UP))
-    down = ONV.pack_batch(synth.expert_weights(E, H, I, sigma, seed, synth.S_DOWN))
+    gate = _pack_experts(E, I, H, sigma, seed, synth.S_GATE)
+    up = _pack_experts(E, I, H, sigma, seed, synth.S_UP)
+    down = _pack_experts(E, H, I, sigma, seed, synth.S_DOWN)
     return x, ids.astype(np.int32), weights.astype(np.float32), gate, up, down
 
 
-def _run_moe(x, ids, w, gate, up, down, eb=0):
+def _run_moe(x, ids, w, gate, up, down, eb=0, layout=nv.LAYOUT_ROWS, kernel_class=None):
     return nv.moe_grouped(bf16_dev(x), torch.from_numpy(ids).to(DEV), torch.from_numpy(w).to(DEV),
-                          weight_dev(gate), weight_dev(up), weight_dev(down), expert_begin=eb)
+                          weight_dev(gate, layout), weight_dev(up, layout), weight_dev(down, layout), expert_begin=eb,
+                          kernel_class=kernel_class)
 
 
-@pytest.mark.parametrize("T,k,E,H,I,seed", [
-    (8, 4, 16, 2048, 512, 2),      # grouped decode MoE workload: 16 experts, top-4, 8 tokens
-    (6, 2, 4, 2048, 1536, 70),     # streaming kernel: gate/up K=2048, down K=1536
-    (3, 2, 2, 4096, 512, 71),      # streaming kernel: gate/up K=4096, down K=512
-    (32, 1, 2, 2048, 512, 72),     # full 16-row decode tiles
-    (40, 2, 3, 512, 2048, 73),     # gate/up K=512 (tiled), down K=2048 with 4 row blocks
-    (5, 2, 3, 64, 32, 60),
-    (1, 8, 12, 256, 96, 61),
-    (200, 2, 4, 128, 64, 62),      # 100 rows per expert: prefill tiles
-    (64, 8, 20, 256, 160, 63),
-    (300, 4, 6, 512, 256, 74),     # prefill tiles in the fp16 form, 2 tiles per expert (full + ragged)
-    (150, 8, 40, 256, 512, 75),    # prefill fp16 form, 30 rows per expert on average (1-row-block tiles)
-    (600, 2, 8, 512, 256, 76),     # two activation rows per prep workgroup (ragged last one)
-    (600, 8, 16, 256, 256, 77),    # 4800 slots: the route's three windows, prep rows in pairs
+# Every case names the kernels it reaches (nvfp4_moe_plan, checked before the run):
+# gate/up kernel, down kernel and the down kernel's width (64-row blocks per wave
+# stream of the resident-H decode kernel; 32-row weight blocks per wave of the
+# prefill kernel). Widths of the decode down kernel follow the compute-unit count
+# (256 on MI355X).
+KS, DEC, RES, PRE, FB = "decode_ksplit", "decode", "decode_resident", "prefill", "fallback"
+
+
+@pytest.mark.parametrize("T,k,E,H,I,seed,layout,kern", [
+    # grouped decode MoE workload: 16 experts, top-4, 8 tokens (32 slots: 4-row tiles)
+    (8, 4, 16, 2048, 512, 2, 0, (KS, RES, 1)),
+    (6, 2, 4, 2048, 1536, 70, 0, (KS, RES, 1)),      # K-split gate/up K=2048, resident down K=1536
+    (3, 2, 2, 4096, 512, 71, 0, (KS, RES, 1)),       # K-split gate/up K=4096 (two stages per wave)
+    (32, 1, 2, 2048, 512, 72, 0, (KS, RES, 1)),      # 32 slots, 16 per expert: K-split on 4-row tiles
+    (40, 2, 3, 512, 2048, 73, 0, (PRE, PRE, 1)),     # 80 slots over 3 experts: prefill tiles
+    # decode tiles (more than 32 slots, at most 16 rows per local expert on average)
+    (16, 4, 16, 4096, 1536, 120, 1, (DEC, RES, 1)),  # gate/up decode kernel K=4096, down K=1536 one block per wave
+    (16, 4, 16, 2048, 1536, 121, 1, (DEC, RES, 1)),  # gate/up decode kernel K=2048
+    (64, 4, 32, 4096, 512, 122, 1, (DEC, RES, 2)),   # 48-tile bound x 4096 rows: two 64-row blocks per wave
+    (128, 4, 32, 4096, 512, 123, 1, (DEC, RES, 4)),  # 64-tile bound: four 64-row blocks per wave
+    (64, 4, 32, 4096, 512, 124, 0, (DEC, RES, 2)),   # the same on row-major weights
+    (12, 4, 16, 4096, 2560, 125, 1, (DEC, DEC, 0)),  # down K=2560 > 2048: the streaming decode kernel
+    (5, 2, 3, 64, 32, 60, 0, (FB, FB, 0)),           # shapes only the fallback covers
+    (1, 8, 12, 256, 96, 61, 0, (FB, FB, 0)),
+    (200, 2, 4, 128, 64, 62, 0, (FB, FB, 0)),        # 100 rows per expert, shapes only the fallback covers
+    (64, 8, 20, 256, 160, 63, 0, (PRE, FB, 0)),      # prefill gate/up (bf16 form), fallback down
+    # prefill tiles
+    (300, 4, 6, 512, 256, 74, 0, (PRE, PRE, 1)),     # fp16 gate/up, 2 tiles per expert (full + ragged)
+    (150, 8, 40, 256, 512, 75, 0, (PRE, PRE, 1)),    # ~30 rows per expert (1-row-block tiles, two stages ahead)
+    (600, 2, 8, 512, 256, 76, 0, (PRE, PRE, 1)),     # two activation rows per prep workgroup (ragged last one)
+    (600, 8, 16, 256, 256, 77, 0, (PRE, PRE, 1)),    # 4800 slots: the route's three windows
+    (300, 4, 6, 768, 1280, 126, 1, (PRE, PRE, 1)),   # odd stage counts: gate/up 3, down 5 (3- and 4-block tiles)
+    (150, 8, 40, 768, 1280, 127, 1, (PRE, PRE, 1)),  # odd stage counts on 1- and 2-block tiles (two ahead)
+    (2048, 8, 16, 2048, 768, 128, 1, (PRE, PRE, 2)), # down 3 stages on full-width (512-row) workgroups
 ])
-def test_moe_vs_oracle(T, k, E, H, I, seed):
-    note(f"moe T={T} k={k} E={E} H={H} I={I}")
+def test_moe_vs_oracle(T, k, E, H, I, seed, layout, kern):
+    plan = nv.moe_plan(T, k, E, H, I, layout, layout)
+    note(f"moe T={T} k={k} E={E} H={H} I={I} layout={layout}: {plan}")
+    assert (plan["gate_up"], plan["down"], plan["down_width"]) == kern
     x, ids, w, gate, up, down = _moe_problem(T, k, E, H, I, seed, sigma=0.05)
-    y = _run_moe(x, ids, w, gate, up, down)
+    y = _run_moe(x, ids, w, gate, up, down, layout=layout)
     torch.cuda.synchronize()
     assert_close(bf16_host_f64(y), OM.moe(x, ids, w, gate, up, down), "moe")
+
+
+@pytest.mark.parametrize("cls,T,k,E,H,I,cuts", [
+    (nv.CLASS_PREFILL, 600, 8, 16, 512, 256, [1, 100, 340]),   # chunks of 1, 99, 240 and 260 tokens
+    (nv.CLASS_DECODE, 96, 4, 32, 512, 512, [1, 9, 40]),        # a one-token chunk would take the K-split
+])
+def test_moe_pinned_class_chunks_bitwise(cls, T, k, E, H, I, cuts):
+    # a pinned kernel class gives every token the same bits whatever the chunking
+    # (TensorFold #308, "Questions", item 4), and stays within the oracle's bar
+    note(f"moe class {cls} T={T} chunks at {cuts}")
+    x, ids, w, gate, up, down = _moe_problem(T, k, E, H, I, 129 + cls, sigma=0.05)
+    whole = bf16_host_bits(_run_moe(x, ids, w, gate, up, down, layout=1, kernel_class=cls))
+    parts = [bf16_host_bits(_run_moe(x[a:b], ids[a:b], w[a:b], gate, up, down, layout=1, kernel_class=cls))
+             for a, b in zip([0] + cuts, cuts + [T])]
+    assert np.array_equal(np.concatenate(parts), whole)
+    yf = bf16_host_f64(torch.from_numpy(whole.view(np.int16)).view(torch.bfloat16))
+    assert_close(yf, OM.moe(x, ids, w, gate, up, down), "moe pinned class")
 
 
 def test_moe_expert_parallel_slice_and_duplicates():
@@ -584,7 +636,7 @@ def _calibrated_scales(x, ids, gate, up, k):
 
 
 @pytest.mark.parametrize("T,k,E,H,I,seed,layout", [
-    (8, 4, 16, 2048, 512, 94, 0),      # decode tiles
+    (8, 4, 16, 2048, 512, 94, 0),      # 32 slots: K-split gate/up on 4-row tiles
     (64, 8, 32, 512, 1536, 95, 1),     # decode tiles, resident-H down (K = 1536), tiled weights
     (300, 4, 6, 512, 256, 96, 0),      # prefill tiles, full and ragged
     (150, 8, 40, 256, 512, 97, 1),     # prefill tiles, ~30 rows per expert, tiled weights
@@ -635,11 +687,18 @@ def test_router_topk_vs_oracle(T, E, H, k, seed):
     assert clear.mean() > 0.9
     assert np.array_equal(ids[clear], oid[clear])
     assert np.allclose(w[clear], ow[clear], rtol=2e-5, atol=1e-6)
-    # elsewhere: k distinct experts whose logits are within the error of the oracle's top k
+    # elsewhere: k distinct experts whose logits are within the error of the oracle's top
+    # k, listed in decreasing logit order (up to that error), with the softmax of their
+    # logits as weights
     for t in np.nonzero(~clear)[0]:
+        tol = 1e-4 * np.max(np.abs(lg[t]))
         assert len(set(ids[t].tolist())) == k
         kth = np.sort(lg[t])[-k]
-        assert np.all(lg[t, ids[t]] >= kth - 1e-4 * np.max(np.abs(lg[t])))
+        chosen = lg[t, ids[t]]
+        assert np.all(chosen >= kth - tol)
+        assert np.all(chosen[:-1] >= chosen[1:] - tol), f"row {t}: ids not in decreasing logit order"
+        sm = np.exp(chosen - chosen.max())
+        assert np.allclose(w[t], sm / sm.sum(), rtol=1e-3, atol=1e-6), f"row {t}: weights not the softmax"
 
 
 @pytest.mark.parametrize("M,H,Is,seed", [(1, 4096, 1536, 103), (64, 4096, 1536, 104), (300, 2048, 512, 105),
