@@ -22,6 +22,7 @@ it runs on); and the CPU oracle timed on a bounded sample.
 from __future__ import annotations
 
 import argparse
+import concurrent.futures as cf
 import json
 import os
 import sys
@@ -469,6 +470,8 @@ def main():
     # ------------------------------------------------------------ CPU oracle
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(raw, torch, synth)
+        if not args.no_extras:
+            result["cpu_baseline_configs"] = cpu_baseline_configs(raw, torch, synth)
 
     print(json.dumps(result), flush=True)
 
@@ -533,6 +536,133 @@ def cpu_baseline(raw, torch, synth):
             "sample": f"1 token of the decode-shaped layer ({len(experts)} experts x 3 projections), "
                       f"float64 numpy routed MLP, {reps} repetitions, {sec:.2f} s each",
             "host_cpus": len(os.sched_getaffinity(0))}
+
+
+def _blas():
+    """(library, threads) of numpy's BLAS as threadpoolctl reports it."""
+    try:
+        from threadpoolctl import threadpool_info
+        info = [d for d in threadpool_info() if d.get("user_api") == "blas"]
+        if info:
+            return info[0].get("internal_api", "?"), int(info[0].get("num_threads", 1))
+    except Exception:  # pragma: no cover
+        pass
+    return "unknown", 1
+
+
+def _timed(fn, min_s):
+    """Seconds per call of fn(), repeated until min_s seconds have passed (at least once)."""
+    t0 = time.perf_counter()
+    reps = 0
+    while True:
+        fn()
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= min_s:
+            return el / reps, reps
+
+
+def cpu_baseline_configs(raw, torch, synth):
+    """The CPU oracle timed on a bounded sample of each workload (float64 numpy
+    contractions, float32 pack), with the BLAS thread count set to the host's CPUs
+    for the run and restored afterwards. Figures use the same algorithmic bytes and
+    flops as the GPU lines; each entry says what its sample was."""
+    from oracle import mlp as OM
+    from oracle import nvfp4 as ONV
+    try:
+        from threadpoolctl import threadpool_limits
+    except Exception:  # pragma: no cover
+        threadpool_limits = None
+    cores = len(os.sched_getaffinity(0))
+    host = lambda t: t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    out = {}
+    ctx = threadpool_limits(limits=cores) if threadpool_limits else None
+    try:
+        lib, nthreads = _blas()
+        out["host"] = {"cores": cores, "blas": lib, "blas_threads": nthreads}
+        log("CPU oracle per workload")
+        # single NVFP4 linear X[4,512] . W[256,512]^T: pack then linear
+        w1 = synth.bf16_normal((256, 512), 0.02, 1, synth.S_W)
+        x1 = synth.bf16_normal((4, 512), 1.0, 1, synth.S_X)
+        sp, rp = _timed(lambda: ONV.pack(w1), 0.5)
+        p1 = ONV.pack(w1)
+        sl, rl = _timed(lambda: OM.linear(x1, p1), 0.5)
+        out["single_linear_4x512x256"] = {
+            "pack_ms": round(sp * 1e3, 3), "pack_GB/s": round((256 * 512 * (2 + W_BYTES)) / sp / 1e9, 4),
+            "linear_ms": round(sl * 1e3, 3), "linear_GFLOP/s": round(2 * 4 * 512 * 256 / sl / 1e9, 4),
+            "sample": "the whole workload"}
+        # grouped decode MoE: 16 experts, top-4, 8 tokens, 2048 -> 512
+        E2, k2, T2, H2, I2 = 16, 4, 8, 2048, 512
+        x2 = synth.bf16_normal((T2, H2), 1.0, 2, synth.S_X)
+        ids2, w2 = synth.topk_softmax_routing(T2, E2, k2, 2, synth.S_ROUTE)
+        wg = synth.expert_weights(E2, I2, H2, 0.02, 2, synth.S_GATE)
+        t0 = time.perf_counter()
+        packs2 = [ONV.pack_batch(wg), ONV.pack_batch(synth.expert_weights(E2, I2, H2, 0.02, 2, synth.S_UP)),
+                  ONV.pack_batch(synth.expert_weights(E2, H2, I2, 0.02, 2, synth.S_DOWN))]
+        sp2 = time.perf_counter() - t0
+        sm2, _ = _timed(lambda: OM.moe(x2, ids2, w2, *packs2), 2.0)
+        U2 = len(np.unique(ids2))
+        b2 = U2 * 3 * I2 * H2 * W_BYTES + 2 * T2 * H2 * 2
+        out["grouped_decode_moe_E16_T8"] = {
+            "pack_s": round(sp2, 3), "pack_GB/s": round(3 * E2 * I2 * H2 * (2 + W_BYTES) / sp2 / 1e9, 4),
+            "moe_ms": round(sm2 * 1e3, 2), "moe_GB/s": round(b2 / sm2 / 1e9, 4), "experts_touched": U2,
+            "sample": "the whole workload (16 experts packed, all 8 tokens)"}
+        # the 288-expert layer: oracle packs of the experts a sample touches
+        packs = {}
+
+        def layer_packs(experts):
+            # the oracle packs the touched experts (not timed; threads: numpy releases the GIL)
+            todo = [(e, p) for e in experts if e not in packs for p in ("gate", "up", "down")]
+            with cf.ThreadPoolExecutor(max_workers=cores) as ex:
+                res = list(ex.map(lambda j: ONV.pack(host(raw[j[1]][j[0]])), todo))
+            for i in range(0, len(todo), 3):
+                packs[todo[i][0]] = res[i:i + 3]
+            st = lambda j: (np.stack([packs[e][j][0] for e in experts]), np.stack([packs[e][j][1] for e in experts]),
+                            np.array([packs[e][j][2] for e in experts], np.float32))
+            return st(0), st(1), st(2)
+
+        def sample_moe(x, ids, w):
+            experts = sorted(set(ids.ravel().tolist()))
+            loc = {e: i for i, e in enumerate(experts)}
+            lids = np.vectorize(lambda v: loc[int(v)])(ids).astype(np.int32)
+            g, u, d = layer_packs(experts)
+            sec, reps = _timed(lambda: OM.moe(x, lids, w, g, u, d), 2.0)
+            return sec, reps, len(experts)
+
+        for T in (1, 16, 64):
+            x3 = synth.bf16_normal((T, H), 1.0, 3, synth.S_X, T)
+            ids3, w3 = synth.topk_softmax_routing(T, E, K_TOP, 3, synth.S_ROUTE, T)
+            sec, reps, U = sample_moe(x3[:1], ids3[:1], w3[:1])
+            out[f"decode_layer_T{T}"] = {
+                "ms_per_token": round(sec * 1e3, 1), "GB/s": round((U * EXPERT_BYTES + 2 * H * 2) / sec / 1e9, 4),
+                "sample": f"token 0 of the {T}-token batch ({U} experts), {reps} repetitions"}
+        xp = synth.bf16_normal((4096, H), 1.0, 4, synth.S_X)
+        idp, wp = synth.zipf_routing(4096, E, K_TOP, 1.1, 4, synth.S_ROUTE)
+        sel = np.arange(0, 4096, 1024)
+        sec, reps, U = sample_moe(xp[sel], idp[sel], wp[sel])
+        fl = 6.0 * len(sel) * K_TOP * H * I
+        out["prefill_layer_T4096_zipf"] = {
+            "s_per_sample": round(sec, 3), "TFLOP/s": round(fl / sec / 1e12, 6),
+            "sample": f"{len(sel)} of the 4096 tokens (every 1024th, {U} experts), {reps} repetitions; "
+                      f"the whole layer would take about {round(sec * 4096 / len(sel))} s"}
+        # dense MLP rows and one projection's pack
+        g5 = host(raw["gate"][0])
+        sp5, _ = _timed(lambda: ONV.pack(g5), 2.0)
+        out["pack_one_projection_1536x4096"] = {
+            "s": round(sp5, 3), "GB/s": round(I * H * (2 + W_BYTES) / sp5 / 1e9, 4),
+            "sample": "expert 0's gate projection; 288 x 3 would take about " + f"{round(sp5 * 864)} s"}
+        M5, F5 = 2048, 12288
+        wd5 = {k_: ONV.pack(synth.bf16_normal(shp, sig, 5, synth.S_W, j)) for j, (k_, shp, sig) in
+               enumerate((("gate", (F5, H), 0.02), ("up", (F5, H), 0.025), ("down", (H, F5), 0.02)))}
+        x5 = synth.bf16_normal((8, H), 1.0, 5, synth.S_X)
+        sm5, reps5 = _timed(lambda: OM.dense_mlp(x5, wd5["gate"], wd5["up"], wd5["down"]), 3.0)
+        out["dense_mlp_2048x4096x12288"] = {
+            "s_per_sample": round(sm5, 3), "TFLOP/s": round(6.0 * 8 * H * F5 / sm5 / 1e12, 6),
+            "sample": f"8 of the {M5} rows, {reps5} repetitions (weights dequantized per call, as the oracle does)"}
+    finally:
+        if ctx is not None:
+            ctx.restore_original_limits()
+    return out
 
 
 if __name__ == "__main__":

@@ -1,8 +1,9 @@
 // Grouped NVFP4 x bf16 GEMM on gfx950 matrix cores, with the expert-MLP epilogues.
 //
 // Passage: TensorFold issue #308, "What the branch does" - routed experts run in
-// a grouped NVFP4 kernel on bf16 rows with weight_scale_2 as the per-expert
-// multiplier; the dense MLP runs on Fp4Linear with gate and up apart.
+// a grouped NVFP4 kernel on bf16 activations, each expert's weight_scale_2
+// applied to its product; the dense MLP runs on Fp4Linear with separate gate
+// and up projections (each keeps its own tensor scale).
 //
 // Work decomposition. A workgroup (4 waves) owns one tile of rows (up to
 // 16*NCB activation rows of one expert) and 64 consecutive weight rows n

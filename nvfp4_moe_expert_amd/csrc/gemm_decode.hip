@@ -1,8 +1,8 @@
 // Decode-shaped grouped NVFP4 GEMM (tiles of at most 16 rows): a weight stream.
 //
-// Passage: TensorFold issue #308, "What the branch does" - routed experts in a
-// grouped NVFP4 kernel, bf16 rows only, weight_scale_2 as the per-expert
-// multiplier. In decode an expert sees one or two rows, so every weight byte is
+// Passage: TensorFold issue #308, "What the branch does" - the routed experts
+// run in one grouped NVFP4 kernel that accepts bf16 activations and nothing
+// else, with each expert's weight_scale_2 applied to its product. In decode an expert sees one or two rows, so every weight byte is
 // used for one 16x16 MFMA tile and the kernel is bound by HBM bandwidth.
 //
 // Layout of the work (measured on MI355X):

@@ -13,10 +13,10 @@ What it computes, and from which passage:
 * ``nvfp4``    - the load-time BF16 -> NVFP4 pack and the dequantization of
   stored weights (TensorFold issue #308, section "The checkpoint": e2m1 codes,
   one e4m3 scale per 16 inputs, one fp32 weight_scale_2 per tensor; section
-  "What the branch does": the MTP layer's BF16 experts are packed by ModelOpt's
-  recipe, a projection at a time).
-* ``mlp``      - the dense Fp4Linear (gate and up apart, each with its own tensor
-  scale), the expert permutation, and the routed expert MLP
+  "What the branch does": at load, ModelOpt's recipe quantizes the MTP layer's
+  BF16 experts one projection after another).
+* ``mlp``      - the dense Fp4Linear (separate gate and up projections, each with
+  its own tensor scale), the expert permutation, and the routed expert MLP
   (grouped gate/up, SiLU(gate)*up, grouped down, routing-weighted sum).
 * ``block``    - the steps either side of the routed experts: the BF16 router
   with top-k softmax selection, the shared-expert BF16 MLP, and the MoE block

@@ -5,8 +5,8 @@ block (routed + shared).
 TEST INFRASTRUCTURE ONLY (see the package docstring).
 
 Passages (TensorFold issue #308, section "What the branch does"): the routed
-experts take bf16 rows; the shared expert runs as a BF16 MLP; the dense MLP keeps
-gate and up apart. The model card "GLM-5.3-Flash-NVFP4-W4A4-Experts" (section
+experts take bf16 activations; the shared expert is a plain BF16 MLP; the dense
+MLP has separate gate and up projections. The model card "GLM-5.3-Flash-NVFP4-W4A4-Experts" (section
 "Quantization boundary") lists routers and shared experts among the parts that
 stay BF16.
 

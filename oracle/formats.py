@@ -3,8 +3,9 @@
 TEST INFRASTRUCTURE ONLY (see the package docstring).
 
 The pages name the formats but print neither table nor rounding rule
-(TensorFold issue #308, section "The checkpoint": "e2m1 codes, an e4m3 scale
-per 16 inputs, an fp32 weight_scale_2 per tensor"). Readings taken here:
+(TensorFold issue #308, section "The checkpoint": each weight is a 4-bit e2m1
+code, scaled by one e4m3 byte per 16 inputs and one fp32 weight_scale_2 per
+tensor). Readings taken here:
 
 * e2m1 is the OCP FP4 element: sign, 2 exponent bits (bias 1), 1 mantissa bit,
   no Inf or NaN; magnitudes {0, 0.5, 1, 1.5, 2, 3, 4, 6}.

@@ -7,13 +7,15 @@ inputs, so it stands for the real-number result; the GPU's bf16 outputs are
 compared against it within a tolerance.
 
 Passages:
-* Dense MLP on Fp4Linear with gate and up kept apart "since their tensor
-  scales differ" (TensorFold issue #308, section "What the branch does").
-* Routed experts in a grouped NVFP4 kernel, bf16 rows only (W4A16), with
-  weight_scale_2 as the per-expert multiplier (same section).
-* A prompt-shaped kernel whose sums are "the same for any chunking" (same
-  issue, "Questions", item 4) and deterministic batch execution (model card
-  "GLM-5.3-Flash-NVFP4-W4A4-Experts", opening section).
+* Dense MLP on Fp4Linear with separate gate and up projections, because each
+  has its own tensor scale (TensorFold issue #308, section "What the branch
+  does").
+* Routed experts in one grouped NVFP4 kernel on bf16 activations (W4A16), each
+  expert's weight_scale_2 applied to its product (same section).
+* A prompt-shaped kernel whose sums do not change with how the prompt is
+  chunked (same issue, "Questions", item 4), and batches executed
+  deterministically (model card "GLM-5.3-Flash-NVFP4-W4A4-Experts", opening
+  section).
 
 Readings: scale_2 multiplies the contraction (it is a per-tensor scalar, so it
 factors out of the sum); SiLU(z) = z / (1 + exp(-z)); the routing weight

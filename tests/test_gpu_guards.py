@@ -124,7 +124,8 @@ def test_moe_grouped_output_and_workspace_stay_inside(T, k, E, H, I, cls, layout
     note(f"guards: moe T={T} k={k} E={E} H={H} I={I} class={cls} layout={layout}")
     x, ids, w, packs = _moe_inputs(T, k, E, H, I, 142 + T)
     xd, idd, wd = bf16_dev(x), torch.from_numpy(ids).to(DEV), torch.from_numpy(w).to(DEV)
-    g, u, d = (weight_dev(p, layout)._struct() for p in packs)
+    dev_w = [weight_dev(p, layout) for p in packs]      # kept alive: the structs hold raw pointers
+    g, u, d = (dw._struct() for dw in dev_w)
     wsb = lib.nvfp4_moe_workspace_size(T, k, E, H, I)
     ws = Fenced(wsb)
     y = Fenced(2 * T * H, fill=0)
@@ -184,7 +185,8 @@ def test_bf16_mlp_block_and_bf16_experts_stay_inside(T):
     wr = bf16_dev(synth.bf16_normal((E, H), 0.02, 144, 20))
     packs = [ONV.pack_batch(synth.expert_weights(E, n, kk, 0.05, 144, st))
              for n, kk, st in ((I, H, synth.S_GATE), (I, H, synth.S_UP), (H, I, synth.S_DOWN))]
-    g, u, d = (weight_dev(p)._struct() for p in packs)
+    dev_w = [weight_dev(p) for p in packs]              # kept alive: the structs hold raw pointers
+    g, u, d = (dw._struct() for dw in dev_w)
     bwsb = lib.nvfp4_moe_block_workspace_size(T, k, E, H, I, Is)
     bws, by = Fenced(bwsb), Fenced(2 * T * H)
     _ok(lib.nvfp4_moe_block(xp, T, H, P(wr), k, ctypes.byref(g), ctypes.byref(u), ctypes.byref(d), P(sg), P(su), P(sd),
