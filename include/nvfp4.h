@@ -94,7 +94,8 @@ typedef enum nvfp4_status {
   NVFP4_ERR_ALIGN = 3,       /* a pointer is not 16-byte aligned */
   NVFP4_ERR_WORKSPACE = 4,   /* workspace missing or smaller than the *_workspace_size() figure */
   NVFP4_ERR_UNSUPPORTED = 5, /* a request the kernels do not cover (e.g. W4A4 on fallback shapes) */
-  NVFP4_ERR_HIP = 6          /* the HIP runtime reported an error when enqueueing */
+  NVFP4_ERR_HIP = 6,         /* the HIP runtime reported an error when enqueueing */
+  NVFP4_ERR_SCRATCH = 7      /* more scratch than nvfp4_moe_grouped_noalloc's fixed buffer holds */
 } nvfp4_status;
 
 typedef struct nvfp4_weight_t {
@@ -316,6 +317,31 @@ nvfp4_status nvfp4_moe_grouped_timed(const uint16_t* x, int64_t T, int64_t H,
                                      const nvfp4_weight_t* up, const nvfp4_weight_t* down,
                                      void* ws, size_t ws_bytes, uint16_t* y, void* stream,
                                      void* const* events);
+
+/*
+ * nvfp4_moe_grouped_noalloc - nvfp4_moe_grouped for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc. It takes no workspace: the call's scratch
+ * (the permutation, tile list, H, the fp32 partials and the scaled activations)
+ * lives in a fixed device array of NVFP4_NOALLOC_SCRATCH_BYTES inside the
+ * library, one per GPU, held until the process ends. The first call on a
+ * device looks up that device's copy (with the device current); no call
+ * allocates or frees anything.
+ * Same arguments (minus the workspace), results (bit for bit: the same
+ * kernels), ownership and errors as nvfp4_moe_grouped, plus NVFP4_ERR_SCRATCH
+ * when nvfp4_moe_workspace_size(T, k, E, H, I) exceeds the fixed size (about
+ * 19.5 KB per routed slot at H = 4096, I = 1536: up to about 390 tokens of a
+ * top-8 layer). NVFP4_ERR_HIP if the array's address cannot be looked up.
+ * Every call on one GPU uses the same array: calls that can overlap on one GPU
+ * (other streams, other host threads) race and must be serialized by the
+ * caller; calls on one stream are ordered and safe. The array keeps the last
+ * call's contents; nothing in it needs clearing between calls.
+ */
+#define NVFP4_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+nvfp4_status nvfp4_moe_grouped_noalloc(const uint16_t* x, int64_t T, int64_t H, const int32_t* topk_ids,
+                                       const float* topk_w, int32_t k, int32_t expert_begin,
+                                       const nvfp4_weight_t* gate, const nvfp4_weight_t* up,
+                                       const nvfp4_weight_t* down, uint16_t* y, void* stream);
 
 /*
  * nvfp4_quantize_act - static NVFP4 quantization of bf16 activations, the W4A4

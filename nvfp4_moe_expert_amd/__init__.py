@@ -25,7 +25,7 @@ __all__ = [
     "Nvfp4Error", "NVFP4Weight", "load_library", "library_path", "abi_version", "ABI_VERSION",
     "pack", "relayout", "dequant", "selftest_fp4_convert", "linear", "linear_gated", "moe_route", "moe_grouped",
     "moe_workspace_size", "pack_workspace_size", "moe_plan", "LAYOUT_ROWS", "LAYOUT_TILED32",
-    "CLASS_AUTO", "CLASS_DECODE", "CLASS_PREFILL", "KERNEL_NAMES",
+    "CLASS_AUTO", "CLASS_DECODE", "CLASS_PREFILL", "KERNEL_NAMES", "moe_grouped_noalloc", "NOALLOC_SCRATCH_BYTES",
 ]
 
 # interface version this binding was written against (NVFP4_ABI_VERSION in include/nvfp4.h)
@@ -82,6 +82,7 @@ _SIGNATURES = {
     "nvfp4_moe_grouped_class": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _I32, _I32, _WP, _WP, _WP, _I32, _P, _SZ,
                                                _P, _P]),
     "nvfp4_moe_plan": (ctypes.c_int, [_I64, _I32, _I32, _I64, _I64, _I32, _I32, _I32, ctypes.POINTER(_I32)]),
+    "nvfp4_moe_grouped_noalloc": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _I32, _I32, _WP, _WP, _WP, _P, _P]),
     "nvfp4_moe_grouped_timed": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _I32, _I32, _WP, _WP, _WP, _P, _SZ, _P,
                                                _P, ctypes.POINTER(_P)]),
     "nvfp4_moe_grouped_w4a4": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _I32, _I32, _WP, _WP, _WP, _P, _P, _P, _SZ,
@@ -370,6 +371,31 @@ def moe_grouped(x: torch.Tensor, topk_ids: torch.Tensor, topk_w: torch.Tensor, g
         arr = (_P * 5)(*[ctypes.c_void_p(ev.cuda_event) for ev in events])
         st = lib.nvfp4_moe_grouped_timed(*args, arr)
     _check(st, "nvfp4_moe_grouped")
+    return out
+
+
+# fixed scratch of nvfp4_moe_grouped_noalloc (NVFP4_NOALLOC_SCRATCH_BYTES)
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def moe_grouped_noalloc(x: torch.Tensor, topk_ids: torch.Tensor, topk_w: torch.Tensor, gate: NVFP4Weight,
+                        up: NVFP4Weight, down: NVFP4Weight, out: torch.Tensor, expert_begin: int = 0) -> torch.Tensor:
+    """The routed expert MLP without a workspace (nvfp4_moe_grouped_noalloc): the
+    library's fixed per-GPU scratch serves the call, so nothing is allocated;
+    the caller passes the output y [T, H] bf16."""
+    lib = load_library()
+    _need(x, torch.bfloat16, "x", 2)
+    _need(topk_ids, torch.int32, "topk_ids", 2)
+    _need(topk_w, torch.float32, "topk_w", 2)
+    _need(out, torch.bfloat16, "out", 2)
+    T, H = x.shape
+    k = topk_ids.shape[1]
+    if topk_ids.shape != (T, k) or topk_w.shape != (T, k) or out.shape != (T, H):
+        raise ValueError("topk_ids / topk_w must be [T, k] and out [T, H]")
+    g, u, d = gate._struct(), up._struct(), down._struct()
+    _check(lib.nvfp4_moe_grouped_noalloc(_ptr(x), T, H, _ptr(topk_ids), _ptr(topk_w), k, expert_begin, ctypes.byref(g),
+                                         ctypes.byref(u), ctypes.byref(d), _ptr(out), _stream()),
+           "nvfp4_moe_grouped_noalloc")
     return out
 
 

@@ -7,13 +7,44 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "../../include/nvfp4.h"
 #include "launch.hpp"
 
 using namespace nvfp4;
 
+// Scratch of nvfp4_moe_grouped_noalloc: one fixed array in device memory. Every
+// GPU that runs this library holds its own copy, at its own address, until the
+// process ends. On the host the name is only a stand-in: its device address is
+// looked up once per device and kept (noalloc_scratch below), and only that
+// address is handed to kernels.
+static __device__ __align__(256) unsigned char scratch[NVFP4_NOALLOC_SCRATCH_BYTES];
+
 namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's copy of `scratch`, looked up on the
+// first call on that device (with it current) and kept.
+hipError_t noalloc_scratch(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
 
 constexpr int64_t kMaxExperts = 4096;
 constexpr int kMaxTopk = 64;
@@ -142,7 +173,8 @@ nvfp4_status moe_shape_plan(int64_t T, int64_t H, int32_t k, int64_t E, int64_t 
 // Every argument check of a routed call, before anything is enqueued.
 nvfp4_status moe_check(const uint16_t* x, int64_t T, int64_t H, const int32_t* ids, const float* tw, int32_t k,
                        const nvfp4_weight_t* gate, const nvfp4_weight_t* up, const nvfp4_weight_t* down,
-                       const uint16_t* y, const void* ws, size_t ws_bytes, bool w4a4, int cls, MoePlan& P) {
+                       const uint16_t* y, const void* ws, size_t ws_bytes, bool w4a4, int cls, MoePlan& P,
+                       bool fixed_scratch = false) {
   nvfp4_status st;
   if ((st = check_weight(gate)) != NVFP4_OK) return st;
   if ((st = check_weight(up)) != NVFP4_OK) return st;
@@ -154,7 +186,10 @@ nvfp4_status moe_check(const uint16_t* x, int64_t T, int64_t H, const int32_t* i
   if (T < 0 || k < 1 || k > kMaxTopk || E > kMaxExperts || T * (int64_t)k > kMaxSlots) return NVFP4_ERR_SHAPE;
   if (T > 0 && (!x || !ids || !tw || !y)) return NVFP4_ERR_NULL;
   if (T > 0 && (!aligned16(x) || !aligned16(y))) return NVFP4_ERR_ALIGN;
-  if (T > 0) {
+  if (T > 0 && fixed_scratch) {
+    // the no-allocation entry point: its fixed scratch must hold the workspace
+    if (moe_layout(T, k, E, H, I).total > ws_bytes) return NVFP4_ERR_SCRATCH;
+  } else if (T > 0) {
     if (!ws) return NVFP4_ERR_WORKSPACE;
     if (!aligned16(ws)) return NVFP4_ERR_ALIGN;
     if (ws_bytes < moe_layout(T, k, E, H, I).total) return NVFP4_ERR_WORKSPACE;
@@ -359,6 +394,8 @@ const char* nvfp4_status_string(int status) {
     case NVFP4_ERR_WORKSPACE: return "workspace missing or too small";
     case NVFP4_ERR_UNSUPPORTED: return "unsupported request (a kernel class, or a W4A4 call on shapes only the fallback GEMM covers)";
     case NVFP4_ERR_HIP: return "HIP runtime error while enqueueing";
+    case NVFP4_ERR_SCRATCH:
+      return "the call needs more scratch than the no-allocation entry point's fixed buffer holds";
   }
   return "unknown status";
 }
@@ -517,6 +554,23 @@ nvfp4_status nvfp4_moe_grouped_w4a4(const uint16_t* x, int64_t T, int64_t H, con
   return moe_impl(x, T, H, topk_ids, topk_w, k, expert_begin, gate, up, down, ws, ws_bytes, y,
                   static_cast<hipStream_t>(stream), nullptr, input_scale_gate_up, input_scale_down,
                   NVFP4_CLASS_AUTO);
+}
+
+nvfp4_status nvfp4_moe_grouped_noalloc(const uint16_t* x, int64_t T, int64_t H, const int32_t* topk_ids,
+                                       const float* topk_w, int32_t k, int32_t expert_begin,
+                                       const nvfp4_weight_t* gate, const nvfp4_weight_t* up,
+                                       const nvfp4_weight_t* down, uint16_t* y, void* stream) {
+  MoePlan P{};
+  const nvfp4_status st = moe_check(x, T, H, topk_ids, topk_w, k, gate, up, down, y, nullptr,
+                                    NVFP4_NOALLOC_SCRATCH_BYTES, false, NVFP4_CLASS_AUTO, P, true);
+  if (st != NVFP4_OK) return st;
+  if (T == 0) return NVFP4_OK;
+  void* ws = nullptr;
+  if (noalloc_scratch(&ws) != hipSuccess) return NVFP4_ERR_HIP;
+  // every byte of the routed call's workspace is written before it is read within
+  // the call, so the previous call's contents need no clearing
+  return moe_run(P, x, T, H, topk_ids, topk_w, k, expert_begin, gate, up, down, ws, y,
+                 static_cast<hipStream_t>(stream), nullptr);
 }
 
 nvfp4_status nvfp4_quantize_act(const uint16_t* x, int64_t rows, int64_t k, const float* input_scale,

@@ -16,7 +16,7 @@ import nvfp4_moe_expert_amd as nv
 HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "nvfp4.h")
 A = 0x100000          # 16-byte aligned dummy device address
 B = 0x200000
-OK, ENULL, ESHAPE, EALIGN, EWS, EUNSUP = 0, 1, 2, 3, 4, 5
+OK, ENULL, ESHAPE, EALIGN, EWS, EUNSUP, ESCRATCH = 0, 1, 2, 3, 4, 5, 7
 
 
 def declared_symbols():
@@ -47,7 +47,7 @@ def test_version_and_status_strings():
     assert nv.abi_version() == nv.ABI_VERSION
     with open(HEADER) as f:
         assert f"#define NVFP4_ABI_VERSION {nv.ABI_VERSION}\n" in f.read()
-    for code in range(7):
+    for code in range(8):
         assert lib.nvfp4_status_string(code)
     assert b"unknown" in lib.nvfp4_status_string(99)
 
@@ -363,3 +363,25 @@ def test_moe_grouped_bf16_validation():
     assert f(x=0) == ENULL
     assert f(x=A + 2) == EALIGN
     assert f(wsb=64) == EWS
+
+
+def _noalloc(lib, T=8, H=256, k=4, E=16, I=128, x=A, y=B, **wo):
+    g = _w(n=wo.get("gn", I), k=H, groups=E)
+    u = _w(n=I, k=H, groups=E)
+    d = _w(n=H, k=I, groups=E)
+    return lib.nvfp4_moe_grouped_noalloc(P(x), T, H, P(A), P(A), k, 0, ctypes.byref(g), ctypes.byref(u),
+                                         ctypes.byref(d), P(y), None)
+
+
+def test_moe_noalloc_validation_and_scratch_limit():
+    # every check runs on the host before the scratch is looked up or anything is enqueued
+    lib = nv.load_library()
+    assert _noalloc(lib, gn=64) == ESHAPE
+    assert _noalloc(lib, x=0) == ENULL
+    assert _noalloc(lib, y=B + 2) == EALIGN
+    assert _noalloc(lib, T=0, x=0, y=0) == OK
+    # the fixed scratch holds a 256-token top-8 step of the 288-expert layer, not a 4096-token one
+    layer = dict(H=4096, I=1536, E=288, k=8)
+    assert lib.nvfp4_moe_workspace_size(256, 8, 288, 4096, 1536) <= nv.NOALLOC_SCRATCH_BYTES
+    assert lib.nvfp4_moe_workspace_size(4096, 8, 288, 4096, 1536) > nv.NOALLOC_SCRATCH_BYTES
+    assert _noalloc(lib, T=4096, **layer) == ESCRATCH
