@@ -7,12 +7,12 @@
  * stored, W4A16":
  *   - section "The checkpoint": weights are e2m1 codes with one e4m3 scale per
  *     16 inputs and one fp32 weight_scale_2 per tensor;
- *   - section "What the branch does": routed experts run in a grouped NVFP4
- *     kernel with weight_scale_2 as the per-expert multiplier; the dense MLP
- *     runs on Fp4Linear with gate and up apart (their tensor scales differ);
- *     activations stay bf16 and the grouped kernel takes bf16 rows only; the
- *     MTP layer's BF16 experts are packed to NVFP4 at load, a projection at a
- *     time.
+ *   - section "What the branch does": the routed experts run in one grouped
+ *     NVFP4 kernel, each expert's weight_scale_2 applied to its product; the
+ *     dense MLP runs on Fp4Linear with separate gate and up projections, each
+ *     keeping its own tensor scale; activations stay bf16, the only type the
+ *     grouped kernel accepts; at load the MTP layer's BF16 experts are
+ *     quantized to NVFP4, one projection after another.
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -217,7 +217,8 @@ nvfp4_status nvfp4_moe_route(const int32_t* topk_ids, int64_t T, int32_t k, int3
 /*
  * nvfp4_moe_grouped - the routed expert MLP of one MoE layer.
  * Passage: issue #308 "What the branch does" (routed experts in the grouped
- * NVFP4 kernel, weight_scale_2 as the per-expert multiplier, bf16 rows only).
+ * NVFP4 kernel on bf16 activations, each expert's weight_scale_2 applied to its
+ * product).
  * For every local slot (t, j) with expert e = topk_ids[t, j] - expert_begin:
  *   g = s2g[e] * x_t . Wg_e^T,  u = s2u[e] * x_t . Wu_e^T   (fp32 accumulators)
  *   h = bf16(SiLU(g) * u)                                     [I]
