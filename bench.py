@@ -56,7 +56,7 @@ def parse():
     p.add_argument("--tokens", type=int, default=64, help="decode batch of the headline step")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-extras", action="store_true", help="only the headline decode step")
-    p.add_argument("--only", choices=["decode", "prefill", "dense", "pack", "w4a4", "block", "bf16"], default=None,
+    p.add_argument("--only", choices=["decode", "prefill", "dense", "pack", "w4a4", "block", "bf16", "shards"], default=None,
                    help="run one workload only (profiling runs); prints its figures")
     p.add_argument("--layout", choices=["tiled", "rows"], default="tiled",
                    help="weight layout in HBM: blocks of 32 rows (tiled) or row-major")
@@ -298,6 +298,75 @@ def main():
                 "prefill_T4096_zipf": {"TFLOP/s": round(flops / pms / 1e9, 2), "ms_per_call": round(pms, 4),
                                        "frac_mfma_bf16": round(flops / pms / 1e9 / MFMA_BF16_PEAK_TFLOPS, 4)}}
 
+    def run_shards(steps, warmup):
+        """One GPU's share of the sharded layer at its real shape: expert parallel
+        over 8 GPUs (36 local experts of the 288 ids, expert_begin = 36, so the
+        other ids are skipped) and tensor parallel over I (I/4 = 384 and I/8 = 192,
+        gate/up rows and down columns split, whole 16-input groups kept), each at
+        the 64-token decode batch (rotating routings) and the 4096-token Zipf
+        layer. Expert-parallel calls run with the class picked automatically and
+        pinned; tensor-parallel down weights stay row-major (the tiled layout needs
+        inputs in multiples of 256)."""
+        out = {}
+        Tp = 4096
+        ids_p, w_p = synth.zipf_routing(Tp, E, K_TOP, 1.1, 4, synth.S_ROUTE)
+        xp = torch.from_numpy(synth.bf16_normal((Tp, H), 1.0, 4, synth.S_X).view(np.int16)).view(torch.bfloat16).to(dev)
+        idp, wpt = torch.from_numpy(ids_p).to(dev), torch.from_numpy(w_p).to(dev)
+
+        def timed(call, n):
+            for i in range(warmup):
+                call(i)
+            torch.cuda.synchronize()
+            t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            t0.record()
+            for i in range(n):
+                call(warmup + i)
+            t1.record()
+            torch.cuda.synchronize()
+            return t0.elapsed_time(t1) / n
+
+        def leg(name, gate, up, down, Esh, Ish, eb, cls):
+            x, ids, w, _ = decode_inputs(64, 3)
+            ws = torch.empty((nv.moe_workspace_size(64, K_TOP, Esh, H, Ish),), dtype=torch.uint8, device=dev)
+            y = torch.empty((64, H), dtype=torch.bfloat16, device=dev)
+            call = lambda i: nv.moe_grouped(x[i % ROTATE], ids[i % ROTATE], w[i % ROTATE], gate, up, down,
+                                            expert_begin=eb, workspace=ws, out=y, kernel_class=cls)
+            ms = timed(call, steps)
+            ids_h = [ids[(warmup + i) % ROTATE].cpu().numpy() for i in range(steps)]
+            touched = np.mean([len(np.unique(a[(a >= eb) & (a < eb + Esh)])) for a in ids_h])
+            bpe = 3 * Ish * H * W_BYTES
+            dec = {"GB/s": round(touched * bpe / (ms * 1e-3) / 1e9, 1), "ms_per_step": round(ms, 5),
+                   "local_experts_touched_mean": round(float(touched), 2)}
+            dec["frac_hbm"] = round(dec["GB/s"] / HBM_PEAK_GBS, 4)
+            wsp = torch.empty((nv.moe_workspace_size(Tp, K_TOP, Esh, H, Ish),), dtype=torch.uint8, device=dev)
+            yp = torch.empty((Tp, H), dtype=torch.bfloat16, device=dev)
+            pms = timed(lambda i: nv.moe_grouped(xp, idp, wpt, gate, up, down, expert_begin=eb, workspace=wsp,
+                                                 out=yp, kernel_class=cls), max(3, min(steps, 10)))
+            local = int(((ids_p >= eb) & (ids_p < eb + Esh)).sum())
+            fl = 6.0 * local * H * Ish
+            pre = {"TFLOP/s": round(fl / pms / 1e9, 2), "ms_per_call": round(pms, 4), "local_rows": local,
+                   "frac_mfma_bf16": round(fl / pms / 1e9 / MFMA_BF16_PEAK_TFLOPS, 4)}
+            plans = {T: nv.moe_plan(T, K_TOP, Esh, H, Ish, gate.layout, down.layout,
+                                    nv.CLASS_AUTO if cls is None else cls) for T in (64, Tp)}
+            out[name] = {"decode_T64": dec, "prefill_T4096_zipf": pre,
+                         "kernels": {str(T): f"{p['gate_up']} + {p['down']}" for T, p in plans.items()}}
+
+        # expert parallel: GPU 1 of 8 holds experts 36..71 (its slice of the packed layer)
+        ep = {k_: nv.NVFP4Weight(v.codes[36:72], v.scales[36:72], v.scale_2[36:72], v.layout) for k_, v in layer.items()}
+        log("shards: expert parallel 36 of 288 experts")
+        leg("ep8_36_experts_auto", ep["gate"], ep["up"], ep["down"], 36, I, 36, None)
+        leg("ep8_36_experts_decode_class", ep["gate"], ep["up"], ep["down"], 36, I, 36, nv.CLASS_DECODE)
+        del ep
+        for G in (4, 8):
+            Ish = I // G
+            log(f"shards: tensor parallel I/{G} = {Ish}")
+            tg = nv.pack(raw["gate"][:, :Ish, :].contiguous(), layout=lay)
+            tu = nv.pack(raw["up"][:, :Ish, :].contiguous(), layout=lay)
+            td = nv.pack(raw["down"][:, :, :Ish].contiguous(), layout=nv.LAYOUT_ROWS)
+            leg(f"tp{G}_I{Ish}", tg, tu, td, E, Ish, 0, None)
+            del tg, tu, td
+        return out
+
     def run_prefill():
         log("prefill T=4096 Zipf(1.1)")
         Tp = 4096
@@ -386,7 +455,8 @@ def main():
                "dense": run_dense, "pack": run_pack,
                "w4a4": lambda: run_w4a4(args.tokens, args.steps, args.warmup),
                "block": lambda: run_block(args.tokens, args.steps, args.warmup),
-               "bf16": lambda: run_bf16_experts(args.tokens, args.steps, args.warmup)}[args.only]()
+               "bf16": lambda: run_bf16_experts(args.tokens, args.steps, args.warmup),
+               "shards": lambda: run_shards(args.steps, args.warmup)}[args.only]()
         print(json.dumps({"only": args.only, **fig}), flush=True)
         return
 

@@ -63,15 +63,19 @@ struct Stage {
 // kb/16 bytes per kb inputs with 16-byte code chunks side by side; in the tiled
 // layout (blocks of 32 rows) a 32-input chunk is 512 bytes on, and 256 inputs of
 // scales are 512 bytes on (2*kb bytes per kb inputs).
+// ok == false (only with U == 1: the lane's 32 inputs lie past K in the last stage
+// of a K that is an odd multiple of 64): no load is issued and the codes and scale
+// bytes read as zero, so the lane's products are exact zeros.
 template <int U, bool TL>
-__device__ __forceinline__ void load_codes(Stage<U>& st, const uint8_t* codes, int64_t kb) {
+__device__ __forceinline__ void load_codes(Stage<U>& st, const uint8_t* codes, int64_t kb, bool ok = true) {
 #pragma unroll
-  for (int i = 0; i < U; ++i) st.c[i] = ld16(codes + (TL ? 16 * kb : kb / 2) + (TL ? 512 : 16) * i);
+  for (int i = 0; i < U; ++i) st.c[i] = ok ? ld16(codes + (TL ? 16 * kb : kb / 2) + (TL ? 512 : 16) * i) : u32x4{0, 0, 0, 0};
 }
 
 template <int U, bool TL>
-__device__ __forceinline__ void load_stage(Stage<U>& st, const uint8_t* codes, const uint8_t* scales, int64_t kb) {
-  load_codes<U, TL>(st, codes, kb);
+__device__ __forceinline__ void load_stage(Stage<U>& st, const uint8_t* codes, const uint8_t* scales, int64_t kb,
+                                           bool ok = true) {
+  load_codes<U, TL>(st, codes, kb, ok);
   const uint8_t* sp = scales + (TL ? 2 * kb : kb / 16);
   if constexpr (U == 4) {
     const u32x2 v = *reinterpret_cast<const u32x2*>(sp);
@@ -80,7 +84,7 @@ __device__ __forceinline__ void load_stage(Stage<U>& st, const uint8_t* codes, c
   } else if constexpr (U == 2) {
     st.s[0] = *reinterpret_cast<const uint32_t*>(sp);
   } else {
-    st.s[0] = *reinterpret_cast<const uint16_t*>(sp);
+    st.s[0] = ok ? *reinterpret_cast<const uint16_t*>(sp) : 0u;
   }
 }
 
@@ -132,6 +136,9 @@ __device__ __forceinline__ void decode_item(const GemmArgs& a, const F16Args& d,
   const uint8_t* c1 = kTwo ? a.w1.codes + coff : nullptr;
   const uint8_t* s1 = kTwo ? a.w1.scales + soff : nullptr;
   constexpr int64_t SSTEP = TL ? 2 * KC : KC / 16;   // scale bytes from one stage to the next
+  // U == 1 takes K in multiples of 64: when K % 128 == 64 the lanes q = 2, 3 of the
+  // last stage hold no inputs (their weights and activations are zeros)
+  auto kok = [&](int64_t kb) { return U != 1 || kb + 32 * U * q < K; };
 
   // activation chunks of this thread: U per stage, chunk i = row xr[i], 8 k at 8*xc[i]
   const uint16_t* xsrc[U];
@@ -161,7 +168,8 @@ __device__ __forceinline__ void decode_item(const GemmArgs& a, const F16Args& d,
   }
   auto ldx = [&](u32x4 (&v)[U], int64_t kb) {
 #pragma unroll
-    for (int i = 0; i < U; ++i) v[i] = xsrc[i] ? ld16(xsrc[i] + kb) : u32x4{0, 0, 0, 0};
+    for (int i = 0; i < U; ++i)
+      v[i] = (xsrc[i] && (U != 1 || kb + 8 * xc[i] < K)) ? ld16(xsrc[i] + kb) : u32x4{0, 0, 0, 0};
   };
   auto stx = [&](u32x4 (&v)[U], int b) {
 #pragma unroll
@@ -228,7 +236,7 @@ __device__ __forceinline__ void decode_item(const GemmArgs& a, const F16Args& d,
     compute_s(g, u, gsw, usw, b);
   };
 
-  const int nst = (int)(K / KC);
+  const int nst = (int)((K + KC - 1) / KC);
   if constexpr (NS > 0) {
     // all stage scales up front (scale bytes of stage st at s + st*KC/16), then the
     // stages fully unrolled so every register index is static
@@ -245,9 +253,13 @@ __device__ __forceinline__ void decode_item(const GemmArgs& a, const F16Args& d,
             us_all[st][0] = w[0];
             us_all[st][1] = w[1];
           }
-        } else {
+        } else if constexpr (U == 2) {
           gs_all[st][0] = *reinterpret_cast<const uint32_t*>(s0 + st * SSTEP);
           if constexpr (kTwo) us_all[st][0] = *reinterpret_cast<const uint32_t*>(s1 + st * SSTEP);
+        } else {   // U == 1: two scale bytes per lane and stage
+          const bool ok = kok((int64_t)st * KC);
+          gs_all[st][0] = ok ? *reinterpret_cast<const uint16_t*>(s0 + st * SSTEP) : 0u;
+          if constexpr (kTwo) us_all[st][0] = ok ? *reinterpret_cast<const uint16_t*>(s1 + st * SSTEP) : 0u;
         }
       }
       if constexpr (!kTwo) {
@@ -257,8 +269,8 @@ __device__ __forceinline__ void decode_item(const GemmArgs& a, const F16Args& d,
     }
     Stage<U> Cg[2], Cu[2];
     u32x4 xv[U];
-    load_codes<U, TL>(Cg[0], c0, 0);
-    if constexpr (kTwo) load_codes<U, TL>(Cu[0], c1, 0);
+    load_codes<U, TL>(Cg[0], c0, 0, kok(0));
+    if constexpr (kTwo) load_codes<U, TL>(Cu[0], c1, 0, kok(0));
     ldx(xv, 0);
     stx(xv, 0);
     __syncthreads();
@@ -268,8 +280,9 @@ __device__ __forceinline__ void decode_item(const GemmArgs& a, const F16Args& d,
       const int b = st & 1;
       const bool more = st + 1 < nst;
       if (more) {
-        load_codes<U, TL>(Cg[b ^ 1], c0, (int64_t)(st + 1) * KC);
-        if constexpr (kTwo) load_codes<U, TL>(Cu[b ^ 1], c1, (int64_t)(st + 1) * KC);
+        const bool ok = kok((int64_t)(st + 1) * KC);
+        load_codes<U, TL>(Cg[b ^ 1], c0, (int64_t)(st + 1) * KC, ok);
+        if constexpr (kTwo) load_codes<U, TL>(Cu[b ^ 1], c1, (int64_t)(st + 1) * KC, ok);
         ldx(xv, (int64_t)(st + 1) * KC);
       }
       compute_s(Cg[b], Cu[b], gs_all[st], us_all[st], b);
@@ -279,24 +292,24 @@ __device__ __forceinline__ void decode_item(const GemmArgs& a, const F16Args& d,
   } else {
   Stage<U> Ag, Au, Bg, Bu;
   u32x4 xv[U];
-  load_stage<U, TL>(Ag, c0, s0, 0);
-  if constexpr (kTwo) load_stage<U, TL>(Au, c1, s1, 0);
+  load_stage<U, TL>(Ag, c0, s0, 0, kok(0));
+  if constexpr (kTwo) load_stage<U, TL>(Au, c1, s1, 0, kok(0));
   ldx(xv, 0);
   stx(xv, 0);
   __syncthreads();
   int st = 0;
   for (; st + 2 <= nst; st += 2) {
     const int64_t k1 = (int64_t)(st + 1) * KC, k2 = (int64_t)(st + 2) * KC;
-    load_stage<U, TL>(Bg, c0, s0, k1);
-    if constexpr (kTwo) load_stage<U, TL>(Bu, c1, s1, k1);
+    load_stage<U, TL>(Bg, c0, s0, k1, kok(k1));
+    if constexpr (kTwo) load_stage<U, TL>(Bu, c1, s1, k1, kok(k1));
     ldx(xv, k1);
     compute(Ag, Au, 0);
     stx(xv, 1);
     __syncthreads();
     const bool more = st + 2 < nst;
     if (more) {
-      load_stage<U, TL>(Ag, c0, s0, k2);
-      if constexpr (kTwo) load_stage<U, TL>(Au, c1, s1, k2);
+      load_stage<U, TL>(Ag, c0, s0, k2, kok(k2));
+      if constexpr (kTwo) load_stage<U, TL>(Au, c1, s1, k2, kok(k2));
       ldx(xv, k2);
     }
     compute(Bg, Bu, 1);
@@ -735,9 +748,13 @@ hipError_t launch_decode_small(GemmMode mode, const GemmArgs& a, const F16Args& 
   return hipGetLastError();
 }
 
+// K in multiples of 512 (U = 4) or 256 (U = 2) in either layout; other multiples of 64
+// (U = 1, 128-input stages, the last one half masked when K % 128 == 64) are
+// row-major only: the tiled layout needs K % 256 == 0. Those are the
+// tensor-parallel shards of the intermediate size (1536 / 4 = 384, 1536 / 8 = 192).
 bool decode_supported(GemmMode mode, int64_t K, int64_t N) {
   (void)mode;
-  return N % kBlockN == 0 && K % 256 == 0 && K >= 256;
+  return N % kBlockN == 0 && K % 64 == 0 && K >= 128;
 }
 
 // Workgroups of `kern` resident on the current device at once (cached).
@@ -813,9 +830,16 @@ static hipError_t launch_dec(const GemmArgs& a, const F16Args& d, int64_t grid_t
   if (a.K % 512 == 0) {
     if (a.K / 512 <= NS) NVFP4_DEC(4, NS);
     else NVFP4_DEC(4, 0);
-  } else {
+  } else if (a.K % 256 == 0) {
     if (a.K / 256 <= NS) NVFP4_DEC(2, NS);
     else NVFP4_DEC(2, 0);
+  } else {
+    if constexpr (TL) {
+      return hipErrorInvalidValue;   // the tiled layout has K % 256 == 0
+    } else {
+      if ((a.K + 127) / 128 <= NS) NVFP4_DEC(1, NS);
+      else NVFP4_DEC(1, 0);
+    }
   }
 #undef NVFP4_DEC
   return hipGetLastError();

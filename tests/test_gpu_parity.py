@@ -209,6 +209,7 @@ def test_route_empty_batch():
     (1, 64, 32, 40), (16, 128, 256, 41), (17, 100, 96, 42), (130, 48, 160, 43),
     (300, 256, 1024, 44), (129, 200, 544, 45),
     (4000, 8192, 256, 46),   # prefill tiles, full-width workgroups (grid of 32 x 16), ragged last tile
+    (12, 128, 192, 133), (5, 64, 384, 134),   # at most 16 rows, K % 256 != 0: 128-input decode stages
 ])
 def test_linear_vs_oracle(M, N, K, seed):
     note(f"linear M={M} N={N} K={K}")
@@ -302,6 +303,10 @@ KS, DEC, RES, PRE, FB = "decode_ksplit", "decode", "decode_resident", "prefill",
     (128, 4, 32, 4096, 512, 123, 1, (DEC, RES, 4)),  # 64-tile bound: four 64-row blocks per wave
     (64, 4, 32, 4096, 512, 124, 0, (DEC, RES, 2)),   # the same on row-major weights
     (12, 4, 16, 4096, 2560, 125, 1, (DEC, DEC, 0)),  # down K=2560 > 2048: the streaming decode kernel
+    # tensor-parallel shards of the intermediate size (row-major: K % 256 != 0)
+    (16, 4, 16, 4096, 384, 130, 0, (DEC, DEC, 0)),   # I/4 = 384: down K=384 in 128-input stages
+    (16, 4, 16, 4096, 192, 131, 0, (DEC, DEC, 0)),   # I/8 = 192: the last stage half masked
+    (3, 2, 4, 4096, 192, 132, 0, (KS, DEC, 0)),      # 6 slots: K-split gate/up, down K=192
     (5, 2, 3, 64, 32, 60, 0, (FB, FB, 0)),           # shapes only the fallback covers
     (1, 8, 12, 256, 96, 61, 0, (FB, FB, 0)),
     (200, 2, 4, 128, 64, 62, 0, (FB, FB, 0)),        # 100 rows per expert, shapes only the fallback covers
@@ -640,6 +645,7 @@ def _calibrated_scales(x, ids, gate, up, k):
     (64, 8, 32, 512, 1536, 95, 1),     # decode tiles, resident-H down (K = 1536), tiled weights
     (300, 4, 6, 512, 256, 96, 0),      # prefill tiles, full and ragged
     (150, 8, 40, 256, 512, 97, 1),     # prefill tiles, ~30 rows per expert, tiled weights
+    (16, 4, 16, 4096, 192, 98, 0),     # tensor-parallel shard I/8 = 192: down K=192 on the decode kernel
 ])
 def test_moe_w4a4_vs_oracle(T, k, E, H, I, seed, layout):
     note(f"moe w4a4 T={T} k={k} E={E} H={H} I={I} layout={layout}")
