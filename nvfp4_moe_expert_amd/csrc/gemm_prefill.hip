@@ -144,12 +144,27 @@ __device__ __forceinline__ void prefill_body(const GemmArgs& a, const F16Args& d
   // loads i in [i0, i1) of this wave's XPW; only the loads that fill the NB
   // 32-row blocks the MFMAs read are issued
   constexpr int XN = (32 * NB * RSU + 63) / 64;
+  // Row-major weights may have K % 256 != 0 (any multiple of 64: the shards of a
+  // tensor-parallel split); then the last stage runs past K. Its activation chunks
+  // past K are read through an offset beyond the descriptor's range (zeros, no
+  // memory access), so the weights read there (the next row's finite bytes, or
+  // zeros past the tensor) multiply zeros. Chunk of load i: (64 (wave + 8i) + lane)
+  // mod RSU, the pad chunk read as chunk 0.
+  const int cbase = (64 * wave + lane) % RSU;
   auto issue_x = [&](int kb, int buf, int i0, int i1) {
+    const bool rag = kb + KC > K;   // uniform
 #pragma unroll
     for (int i = 0; i < XPW; ++i) {
       if (i < i0 || i >= i1 || wave + kWaves * i >= XN) continue;
+      uint32_t off = xo[i];
+      if (rag) {
+        int c = cbase + (64 * kWaves * i) % RSU;
+        if (c >= RSU) c -= RSU;
+        if (c == RSU - 1) c = 0;
+        if (kb + 8 * c >= K) off = 0x80000000u;
+      }
       auto* dst = (__attribute__((address_space(3))) void*)(xs + buf * XBUF + 1024 * (wave + kWaves * i));
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(xrs, dst, 16, xo[i], 2 * kb, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(xrs, dst, 16, off, 2 * kb, 0, 0);
     }
   };
 
@@ -201,7 +216,7 @@ __device__ __forceinline__ void prefill_body(const GemmArgs& a, const F16Args& d
   // loads of stage st + 1 (only the code loads issued after the last activation
   // load may still be in flight: 2W of them, 5W with DEEP), barrier (tile st + 1
   // complete everywhere, buffer st % 2 free), and prepare step 0 of stage st + 1.
-  const int nst = (int)(K / KC);
+  const int nst = (int)((K + KC - 1) / KC);
   issue_x(0, 0, 0, XPW);
   load_scales(0, 0);
 #pragma unroll
@@ -370,11 +385,15 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_prefill_kernel(GemmArgs a, F
   }
 }
 
+// K: a multiple of 64 (the tiled layout, which these kernels also read, has
+// K % 256 == 0 by its definition; row-major weights may end on a partial stage).
+// A lane's 8 scale bytes are one 8-byte load, which needs the row pitch of the
+// row-major scales, K/16 bytes, to be a multiple of 4.
 bool prefill_supported(GemmMode mode, int64_t x_rows, int64_t K, int64_t N) {
   (void)mode;
   // 32-bit buffer ranges: x, and one expert's codes (its scales are smaller)
   const int64_t lim = (int64_t)1 << 31;
-  return K % KC == 0 && K >= KC && N % 32 == 0 && x_rows * K * 2 < lim && N * (K / 2) < lim;
+  return K % 64 == 0 && K >= 64 && N % 32 == 0 && x_rows * K * 2 < lim && N * (K / 2) < lim;
 }
 
 int cu_count() {

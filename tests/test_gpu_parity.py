@@ -210,6 +210,8 @@ def test_route_empty_batch():
     (300, 256, 1024, 44), (129, 200, 544, 45),
     (4000, 8192, 256, 46),   # prefill tiles, full-width workgroups (grid of 32 x 16), ragged last tile
     (12, 128, 192, 133), (5, 64, 384, 134),   # at most 16 rows, K % 256 != 0: 128-input decode stages
+    (40, 96, 192, 135), (300, 64, 1088, 136),  # more rows, K % 256 != 0: prefill tiles, last stage partial
+    (40, 96, 160, 141),                        # K % 64 == 32: the fallback
 ])
 def test_linear_vs_oracle(M, N, K, seed):
     note(f"linear M={M} N={N} K={K}")
@@ -309,8 +311,8 @@ KS, DEC, RES, PRE, FB = "decode_ksplit", "decode", "decode_resident", "prefill",
     (3, 2, 4, 4096, 192, 132, 0, (KS, DEC, 0)),      # 6 slots: K-split gate/up, down K=192
     (5, 2, 3, 64, 32, 60, 0, (FB, FB, 0)),           # shapes only the fallback covers
     (1, 8, 12, 256, 96, 61, 0, (FB, FB, 0)),
-    (200, 2, 4, 128, 64, 62, 0, (FB, FB, 0)),        # 100 rows per expert, shapes only the fallback covers
-    (64, 8, 20, 256, 160, 63, 0, (PRE, FB, 0)),      # prefill gate/up (bf16 form), fallback down
+    (200, 2, 4, 128, 64, 62, 0, (PRE, PRE, 1)),      # 100 rows per expert; K = 128 and 64: one partial stage each
+    (64, 8, 20, 256, 160, 63, 0, (PRE, FB, 0)),      # prefill gate/up (bf16 form), down K = 160 on the fallback
     # prefill tiles
     (300, 4, 6, 512, 256, 74, 0, (PRE, PRE, 1)),     # fp16 gate/up, 2 tiles per expert (full + ragged)
     (150, 8, 40, 256, 512, 75, 0, (PRE, PRE, 1)),    # ~30 rows per expert (1-row-block tiles, two stages ahead)
@@ -319,6 +321,11 @@ KS, DEC, RES, PRE, FB = "decode_ksplit", "decode", "decode_resident", "prefill",
     (300, 4, 6, 768, 1280, 126, 1, (PRE, PRE, 1)),   # odd stage counts: gate/up 3, down 5 (3- and 4-block tiles)
     (150, 8, 40, 768, 1280, 127, 1, (PRE, PRE, 1)),  # odd stage counts on 1- and 2-block tiles (two ahead)
     (2048, 8, 16, 2048, 768, 128, 1, (PRE, PRE, 2)), # down 3 stages on full-width (512-row) workgroups
+    # prefill tiles on row-major weights whose K ends on a partial 256-input stage
+    (200, 4, 8, 1088, 320, 137, 0, (PRE, PRE, 1)),   # gate/up K = 4 stages + 64, down K = 256 + 64
+    (200, 4, 8, 1056, 288, 140, 0, (FB, FB, 0)),     # K % 64 == 32 (odd scale row pitch): the fallback
+    (300, 4, 6, 4096, 384, 138, 0, (PRE, PRE, 1)),   # tensor-parallel shard I/4: down K = 384
+    (300, 4, 6, 512, 192, 139, 0, (PRE, PRE, 1)),    # tensor-parallel shard I/8: down K = 192
 ])
 def test_moe_vs_oracle(T, k, E, H, I, seed, layout, kern):
     plan = nv.moe_plan(T, k, E, H, I, layout, layout)
@@ -646,6 +653,7 @@ def _calibrated_scales(x, ids, gate, up, k):
     (300, 4, 6, 512, 256, 96, 0),      # prefill tiles, full and ragged
     (150, 8, 40, 256, 512, 97, 1),     # prefill tiles, ~30 rows per expert, tiled weights
     (16, 4, 16, 4096, 192, 98, 0),     # tensor-parallel shard I/8 = 192: down K=192 on the decode kernel
+    (300, 4, 6, 512, 192, 99, 0),      # the same shard on prefill tiles (partial last stage)
 ])
 def test_moe_w4a4_vs_oracle(T, k, E, H, I, seed, layout):
     note(f"moe w4a4 T={T} k={k} E={E} H={H} I={I} layout={layout}")
