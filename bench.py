@@ -60,8 +60,10 @@ def parse():
                    help="run one workload only (profiling runs); prints its figures")
     p.add_argument("--layout", choices=["tiled", "rows"], default="tiled",
                    help="weight layout in HBM: blocks of 32 rows (tiled) or row-major")
-    p.add_argument("--calibrate-copy-mib", type=int, default=256,
-                   help="size of the plain device copy run once (counter calibration)")
+    p.add_argument("--calibrate-copy-mib", default="64,256",
+                   help="comma-separated sizes of plain device copies run once each after the "
+                        "workload, then one elementwise negation of the largest (counter "
+                        "calibration); 0 for none")
     return p.parse_args()
 
 
@@ -449,6 +451,31 @@ def main():
                 "GB/s": round(pbytes / (ms * 1e-3) / 1e9, 1), "ms_per_call": round(ms, 3),
                 "frac_hbm": round(pbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
 
+    def calibrate():
+        """Kernels of known traffic, in dispatch order, for scaling the FETCH_SIZE and
+        WRITE_SIZE counters: per size a fill (writes n x 4 bytes) and a blit copy
+        (reads and writes n x 4), then a torch elementwise negation of the largest
+        (reads and writes n x 4)."""
+        sizes = [int(v) for v in str(args.calibrate_copy_mib).split(",") if v.strip()]
+        sizes = [v for v in sizes if v > 0]
+        out = []
+        a = b = None
+        for mib in sizes:
+            del a, b
+            n = mib * (1 << 20) // 4
+            a = torch.ones(n, dtype=torch.float32, device=dev)
+            b = torch.empty_like(a)
+            b.copy_(a)
+            torch.cuda.synchronize()
+            out.append({"kind": "fill", "read": 0, "write": n * 4})
+            out.append({"kind": "copy", "read": n * 4, "write": n * 4})
+        if sizes:
+            torch.neg(a, out=b)
+            torch.cuda.synchronize()
+            out.append({"kind": "neg", "read": a.numel() * 4, "write": a.numel() * 4})
+        del a, b
+        return out
+
     if args.only is not None:
         # one workload alone (profiling runs): its figures only, no headline line
         fig = {"decode": lambda: run_decode(args.tokens, args.steps, args.warmup), "prefill": run_prefill,
@@ -457,6 +484,9 @@ def main():
                "block": lambda: run_block(args.tokens, args.steps, args.warmup),
                "bf16": lambda: run_bf16_experts(args.tokens, args.steps, args.warmup),
                "shards": lambda: run_shards(args.steps, args.warmup)}[args.only]()
+        cal = calibrate()
+        if cal:
+            fig["calibration"] = cal
         print(json.dumps({"only": args.only, **fig}), flush=True)
         return
 
@@ -527,15 +557,10 @@ def main():
         layer.update(kept)
         del kept
 
-    # --------------------------------------------- counter calibration copy
-    if args.calibrate_copy_mib > 0:
-        n = args.calibrate_copy_mib * (1 << 20) // 4
-        a = torch.ones(n, dtype=torch.float32, device=dev)
-        b = torch.empty_like(a)
-        b.copy_(a)
-        torch.cuda.synchronize()
-        result["calibration_copy_bytes"] = {"read": n * 4, "write": n * 4}
-        del a, b
+    # --------------------------------------------- counter calibration copies
+    cal = calibrate()
+    if cal:
+        result["calibration"] = cal
 
     # ------------------------------------------------------------ CPU oracle
     if not args.no_cpu_baseline:

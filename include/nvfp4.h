@@ -82,7 +82,7 @@
 extern "C" {
 #endif
 
-#define NVFP4_ABI_VERSION 7
+#define NVFP4_ABI_VERSION 8
 
 #define NVFP4_LAYOUT_ROWS 0
 #define NVFP4_LAYOUT_TILED32 1
@@ -252,7 +252,12 @@ nvfp4_status nvfp4_moe_grouped(const uint16_t* x, int64_t T, int64_t H, const in
  *                         kernel (prompt-shaped calls);
  *   NVFP4_CLASS_AUTO    - what nvfp4_moe_grouped runs: at most 32 slots take
  *                         4-row tiles whose gate/up splits K over four waves
- *                         (partials added in wave order); otherwise DECODE when
+ *                         (partials added in wave order); with at most 4 tokens
+ *                         and 24 slots (W4A16, H and I multiples of 512,
+ *                         H <= 4096, I <= 2048) these run as two launches with no route
+ *                         kernel, the combine inside the down launch (same
+ *                         sums: each slot's products in k order, the slots of a
+ *                         token in j order); otherwise DECODE when
  *                         the average local expert gets at most 16 rows
  *                         (T*k <= 16 * min(T*k, n_experts)), else PREFILL. The
  *                         class, and so the bits, can change with the batch size.
@@ -286,6 +291,7 @@ nvfp4_status nvfp4_moe_grouped_class(const uint16_t* x, int64_t T, int64_t H, co
 #define NVFP4_KERNEL_DECODE_RESIDENT 3 /* down on decode tiles: whole H tile in LDS, 1/2/4 weight blocks per wave */
 #define NVFP4_KERNEL_PREFILL 4         /* prefill tiles, 32x32 matrix-core kernel */
 #define NVFP4_KERNEL_FALLBACK 5        /* tiled fallback GEMM (row-major weights of other shapes) */
+#define NVFP4_KERNEL_TINY 6            /* at most 4 tokens, 24 slots: gate/up routing itself, down with the combine */
 
 /*
  * nvfp4_moe_plan - which kernels a routed call of these shapes runs (host only:
@@ -301,7 +307,8 @@ nvfp4_status nvfp4_moe_grouped_class(const uint16_t* x, int64_t T, int64_t H, co
  *           NVFP4_KERNEL_PREFILL, else 0;
  *   plan[4] 1 if the routed GEMMs run on fp16 operands (see Numerics), else 0.
  * The W4A16 and W4A4 entry points run the same kernels (W4A4 refuses plans
- * with the fallback GEMM). Errors: NVFP4_ERR_NULL, NVFP4_ERR_SHAPE, and those
+ * with the fallback GEMM), except that W4A4 runs NVFP4_KERNEL_DECODE_KSPLIT
+ * gate/up and its decode down kernel where the plan names NVFP4_KERNEL_TINY. Errors: NVFP4_ERR_NULL, NVFP4_ERR_SHAPE, and those
  * of nvfp4_moe_grouped_class for the shapes and class.
  */
 nvfp4_status nvfp4_moe_plan(int64_t T, int32_t k, int32_t n_experts, int64_t H, int64_t I, int32_t gate_layout,

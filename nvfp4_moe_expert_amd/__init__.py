@@ -29,7 +29,7 @@ __all__ = [
 ]
 
 # interface version this binding was written against (NVFP4_ABI_VERSION in include/nvfp4.h)
-ABI_VERSION = 7
+ABI_VERSION = 8
 
 LAYOUT_ROWS = 0       # the checkpoint's row-major codes and scales
 LAYOUT_TILED32 = 1    # blocks of 32 rows (n % 32 == 0, k % 256 == 0)
@@ -39,7 +39,7 @@ CLASS_AUTO = 0
 CLASS_DECODE = 1
 CLASS_PREFILL = 2
 # kernels named by moe_plan (NVFP4_KERNEL_*)
-KERNEL_NAMES = {0: "none", 1: "decode_ksplit", 2: "decode", 3: "decode_resident", 4: "prefill", 5: "fallback"}
+KERNEL_NAMES = {0: "none", 1: "decode_ksplit", 2: "decode", 3: "decode_resident", 4: "prefill", 5: "fallback", 6: "tiny"}
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libnvfp4.so")

@@ -74,7 +74,7 @@ WeightDev dev_weight(const nvfp4_weight_t* w) {
 // prefill-tile matrix-core kernel, or the tiled fallback (row-major weights
 // only). Tiled weights take the prefill kernel wherever the decode kernel does
 // not apply; kNone if no kernel covers the call.
-enum Kern { kKDec, kKPre, kKV1, kKNone, kKDecS };
+enum Kern { kKDec, kKPre, kKV1, kKNone, kKDecS, kKTiny };
 Kern pick(GemmMode mode, GemmVariant v, bool tiled, int64_t x_rows, int64_t K, int64_t N) {
   // tiny batches: gate/up splits K over the waves (its 8 stages of 512 inputs are the
   // long pole); down (few stages) keeps the decode kernels, on the same 4-row tiles
@@ -155,6 +155,13 @@ nvfp4_status moe_shape_plan(int64_t T, int64_t H, int32_t k, int64_t E, int64_t 
   P.v = moe_variant(P.S, E, H, I, cls);
   P.kg = pick(kGateUp, P.v, gate_tiled, T, H, I);
   P.kd = pick(kDown, P.v, down_tiled, P.S, I, H);
+  // at most 24 slots (automatic class, W4A16): the two-launch path without a route
+  // kernel. Its gate/up workgroups each derive the tile list and stage their
+  // activation slices, a fixed cost per workgroup that outweighs the route kernel
+  // it saves once the grid takes about three rounds of the device (32 slots of
+  // 4096 x 1536 experts: 78 against 74 us a step).
+  if (cls == NVFP4_CLASS_AUTO && !w4a4 && P.v == kDecodeSmall && P.S <= 24 && tiny_supported(T, k, H, I))
+    P.kg = P.kd = kKTiny;
   if (T > 0 && (P.kg == kKNone || P.kd == kKNone)) return NVFP4_ERR_SHAPE;
   // a prefill-tile gate/up records no row maxima of H, which a decode-tile down
   // (fp16 form) needs; the class rules never pair the two (their shape conditions exclude it)
@@ -218,6 +225,18 @@ nvfp4_status moe_run(const MoePlan& P, const uint16_t* x, int64_t T, int64_t H, 
   hipError_t e = mark(0);
   if (T == 0) {
     for (int i = 1; i < 5 && e == hipSuccess; ++i) e = mark(i);
+    return from_hip(e);
+  }
+  if (kg == kKTiny) {
+    // no route stage; the combine runs inside the down launch
+    TinyArgs ta{x, ids, tw, T, k, (int)E, eb, H, I, dev_weight(gate), dev_weight(up), dev_weight(down),
+                at<uint16_t>(ws, L.h), at<uint32_t>(ws, L.ypart), extra, extra_splits, y};
+    if (e == hipSuccess) e = mark(1);
+    if (e == hipSuccess) e = launch_tiny(ta, false, s);
+    if (e == hipSuccess) e = mark(2);
+    if (e == hipSuccess) e = launch_tiny(ta, true, s);
+    if (e == hipSuccess) e = mark(3);
+    if (e == hipSuccess) e = mark(4);
     return from_hip(e);
   }
   int32_t* offsets = at<int32_t>(ws, L.offsets);
@@ -304,6 +323,7 @@ int32_t kernel_id(Kern kn, bool down, const MoePlan& P, int64_t H, int32_t* deta
   *detail = 0;
   switch (kn) {
     case kKDecS: return NVFP4_KERNEL_DECODE_KSPLIT;
+    case kKTiny: return NVFP4_KERNEL_TINY;
     case kKDec:
       if (down) {
         if (const int nb = decode_down_streams(P.f16, P.S, P.I, H, P.grid_tiles)) {

@@ -65,6 +65,29 @@ bool decode_small_supported(int64_t K, int64_t N);
 hipError_t launch_decode_small(GemmMode mode, const GemmArgs& a, const F16Args& d, int64_t grid_tiles,
                                hipStream_t s);
 
+// Routed experts of at most 4 tokens in two launches (gate/up; down with the
+// combine), no route kernel: each gate/up workgroup derives its tile from the ids.
+// H is written in slot order ([T*k][I] bf16) with the largest |H| of each block of
+// 16 values in hpart ([T*k][I/16], fp32 bits). fp16 form, W4A16 only.
+struct TinyArgs {
+  const uint16_t* x;       // [T][H] bf16
+  const int32_t* ids;      // [T][k]
+  const float* tw;         // [T][k]
+  int64_t T;
+  int k, E, eb;            // top-k, local experts, first local expert id
+  int64_t H, I;
+  WeightDev gate, up, down;
+  uint16_t* h;             // workspace: [T*k][I] bf16
+  uint32_t* hpart;         // workspace: [T*k][I/16]
+  const float* extra;      // null, or [extra_splits][T][H] fp32 added after the routed sum
+  int extra_splits;
+  uint16_t* y;             // [T][H] bf16
+};
+// T <= 4, T*k <= 32, H % 512 == 0 and H <= 4096, I % 512 == 0 and I <= 2048.
+bool tiny_supported(int64_t T, int64_t k, int64_t H, int64_t I);
+// down = false launches gate/up, true the down projection with the combine.
+hipError_t launch_tiny(const TinyArgs& a, bool down, hipStream_t s);
+
 // Prefill-tile (<= 128 rows) matrix-core GEMM; the tiled kernel covers other shapes.
 bool prefill_supported(GemmMode mode, int64_t x_rows, int64_t K, int64_t N);
 // The fp16 form (routed gate/up only; down takes bf16 H) reads the prep kernel's

@@ -327,14 +327,21 @@ def _plan(lib, T, k, E, H, I, gl=1, dl=1, cls=0):
     return st, tuple(out)
 
 
-DEC_K, DEC, RES, PRE, FB = 1, 2, 3, 4, 5
+DEC_K, DEC, RES, PRE, FB, TINY = 1, 2, 3, 4, 5, 6
 
 
 def test_moe_plan_names_the_kernels():
     # without a GPU the library takes 256 compute units, the MI355X's count
     lib = nv.load_library()
     layer = (8, 288, 4096, 1536)
-    assert _plan(lib, 1, *layer) == (OK, (4, DEC_K, RES, 1, 1))
+    assert _plan(lib, 1, *layer) == (OK, (4, TINY, TINY, 0, 1))
+    assert _plan(lib, 3, *layer) == (OK, (4, TINY, TINY, 0, 1))
+    assert _plan(lib, 4, *layer) == (OK, (4, DEC_K, RES, 2, 1))
+    # 5 tokens (40 slots) leave the 4-row tiles; 4 tokens of top-16 (64 slots) too
+    assert _plan(lib, 5, *layer) == (OK, (16, DEC, RES, 2, 1))
+    assert _plan(lib, 4, 16, 288, 4096, 1536) == (OK, (16, DEC, RES, 4, 1))
+    # 3 tokens of top-8 with I = 192 (a tensor-parallel shard): K-split gate/up, decode down
+    assert _plan(lib, 3, 8, 288, 4096, 192, 0, 0) == (OK, (4, DEC_K, DEC, 0, 1))
     assert _plan(lib, 16, *layer) == (OK, (16, DEC, RES, 4, 1))
     assert _plan(lib, 64, *layer) == (OK, (16, DEC, RES, 4, 1))
     assert _plan(lib, 4096, *layer) == (OK, (128, PRE, PRE, 2, 1))

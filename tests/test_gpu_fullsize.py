@@ -134,7 +134,9 @@ def test_pack_of_288_expert_projections_bit_exact(layer):
 
 
 @pytest.mark.parametrize("T,kernels", [
-    (1, ("decode_ksplit", "decode_resident")),    # 8 slots: 4-row tiles, gate/up K split over 4 waves
+    (1, ("tiny", "tiny")),                        # 8 slots: gate/up routing itself, down with the combine
+    (3, ("tiny", "tiny")),                        # 24 slots
+    (4, ("decode_ksplit", "decode_resident")),    # 32 slots: 4-row tiles, gate/up K split over 4 waves
     (16, ("decode", "decode_resident")),          # 128 slots: 16-row tiles, H resident in LDS for down
     (64, ("decode", "decode_resident")),          # the benchmark's step
 ])

@@ -288,14 +288,23 @@ def _run_moe(x, ids, w, gate, up, down, eb=0, layout=nv.LAYOUT_ROWS, kernel_clas
 # stream of the resident-H decode kernel; 32-row weight blocks per wave of the
 # prefill kernel). Widths of the decode down kernel follow the compute-unit count
 # (256 on MI355X).
-KS, DEC, RES, PRE, FB = "decode_ksplit", "decode", "decode_resident", "prefill", "fallback"
+KS, DEC, RES, PRE, FB, TY = "decode_ksplit", "decode", "decode_resident", "prefill", "fallback", "tiny"
 
 
 @pytest.mark.parametrize("T,k,E,H,I,seed,layout,kern", [
     # grouped decode MoE workload: 16 experts, top-4, 8 tokens (32 slots: 4-row tiles)
     (8, 4, 16, 2048, 512, 2, 0, (KS, RES, 1)),
     (6, 2, 4, 2048, 1536, 70, 0, (KS, RES, 1)),      # K-split gate/up K=2048, resident down K=1536
-    (3, 2, 2, 4096, 512, 71, 0, (KS, RES, 1)),       # K-split gate/up K=4096 (two stages per wave)
+    (3, 2, 2, 4096, 512, 71, 0, (TY, TY, 0)),        # 3 tokens: the two-launch path, K=4096 (two stages per wave)
+    # at most 4 tokens: gate/up routing itself on 4-row tiles, down with the combine
+    (1, 8, 16, 4096, 1536, 141, 1, (TY, TY, 0)),     # the model's shapes, one token
+    (2, 8, 16, 4096, 1536, 142, 0, (TY, TY, 0)),     # 16 slots: four per down wave
+    (3, 8, 12, 2048, 2048, 143, 1, (TY, TY, 0)),     # 24 slots over 12 experts (multi-row tiles), down 4 stages
+    (4, 8, 12, 2048, 2048, 148, 1, (KS, RES, 1)),    # 32 slots: the K-split gate/up
+    (3, 4, 6, 512, 512, 144, 0, (TY, TY, 0)),        # one stage each: waves 1..3 of gate/up idle
+    (3, 8, 8, 2560, 1024, 145, 0, (TY, TY, 0)),      # gate/up 5 stages (waves with one and two), down 2
+    (1, 24, 40, 1024, 512, 149, 1, (TY, TY, 0)),     # top-24: eight slots per down wave
+    (1, 16, 300, 1024, 512, 146, 1, (TY, TY, 0)),    # top-16 over 300 experts: four slots per down wave
     (32, 1, 2, 2048, 512, 72, 0, (KS, RES, 1)),      # 32 slots, 16 per expert: K-split on 4-row tiles
     (40, 2, 3, 512, 2048, 73, 0, (PRE, PRE, 1)),     # 80 slots over 3 experts: prefill tiles
     # decode tiles (more than 32 slots, at most 16 rows per local expert on average)
@@ -369,6 +378,37 @@ def test_moe_expert_parallel_slice_and_duplicates():
     assert np.all(bf16_host_f64(y)[none_local] == 0)
 
 
+@pytest.mark.parametrize("case", ["ep_slice", "one_expert", "no_local_token"])
+def test_moe_tiny_routing_edges(case):
+    # the two-launch path derives its tiles from the ids in every workgroup:
+    # ids outside this GPU's experts, duplicates within a token, all 24 slots on
+    # one expert (tiles of 16 and 8 slots of one expert), and a token with no local slot
+    T, k, E, H, I = 3, 8, 16, 1024, 512
+    g = np.random.default_rng(147)
+    if case == "ep_slice":
+        ids = g.integers(0, 48, (T, k)).astype(np.int32)
+        ids[:, 1] = ids[:, 0]
+        eb = 16
+    elif case == "one_expert":
+        ids = np.full((T, k), 21, np.int32)
+        eb = 16
+    else:
+        ids = g.integers(16, 32, (T, k)).astype(np.int32)
+        ids[2] = g.integers(40, 60, k)
+        eb = 16
+    w = g.uniform(0.1, 1.0, (T, k)).astype(np.float32)
+    plan = nv.moe_plan(T, k, E, H, I, 0, 0)
+    assert (plan["gate_up"], plan["down"]) == (TY, TY)
+    x, _, _, gate, up, down = _moe_problem(T, k, E, H, I, 147, sigma=0.05, ids=ids, weights=w)
+    note(f"moe tiny edges {case}: ids {ids.tolist()}")
+    y = _run_moe(x, ids, w, gate, up, down, eb=eb)
+    torch.cuda.synchronize()
+    ref = OM.moe(x, ids, w, gate, up, down, expert_begin=eb)
+    assert_close(bf16_host_f64(y), ref, f"moe tiny {case}")
+    none_local = ~np.any((ids >= eb) & (ids < eb + E), axis=1)
+    assert np.all(bf16_host_f64(y)[none_local] == 0)
+
+
 def test_moe_all_slots_skipped_gives_zero():
     x, ids, w, gate, up, down = _moe_problem(9, 4, 4, 64, 32, 65)
     y = _run_moe(x, ids, w, gate, up, down, eb=100)
@@ -385,7 +425,7 @@ def test_moe_empty_batch():
     assert y.shape == (0, 64)
 
 
-@pytest.mark.parametrize("T,k,E,H,I", [(8, 4, 16, 2048, 512), (200, 2, 4, 128, 64)])
+@pytest.mark.parametrize("T,k,E,H,I", [(8, 4, 16, 2048, 512), (200, 2, 4, 128, 64), (3, 8, 16, 4096, 1536)])
 def test_moe_token_permutation_and_repeat_bitwise(T, k, E, H, I):
     x, ids, w, gate, up, down = _moe_problem(T, k, E, H, I, 67, sigma=0.05)
     y1 = bf16_host_bits(_run_moe(x, ids, w, gate, up, down))
@@ -396,7 +436,7 @@ def test_moe_token_permutation_and_repeat_bitwise(T, k, E, H, I):
     assert np.array_equal(yp, y1[p])
 
 
-@pytest.mark.parametrize("T,k,E,H,I", [(1, 8, 12, 4096, 512),     # one token: K-split gate/up
+@pytest.mark.parametrize("T,k,E,H,I", [(1, 8, 12, 4096, 512),     # one token: the two-launch path
                                        (8, 4, 16, 2048, 512),     # decode tiles
                                        (300, 4, 6, 512, 256),     # prefill tiles, fp16 form
                                        (600, 8, 16, 256, 256)])   # 4800 slots: three-launch route
@@ -494,8 +534,9 @@ def test_moe_k1_matches_dense_mlp_path(T, I):
     assert_close(bf16_host_f64(y), bf16_host_f64(y2), "moe k=1 vs dense path")
 
 
-def test_moe_timed_events_same_result():
-    x, ids, w, gate, up, down = _moe_problem(8, 4, 16, 256, 128, 69, sigma=0.05)
+@pytest.mark.parametrize("T,k,E,H,I", [(8, 4, 16, 256, 128), (2, 8, 16, 1024, 512)])
+def test_moe_timed_events_same_result(T, k, E, H, I):
+    x, ids, w, gate, up, down = _moe_problem(T, k, E, H, I, 69, sigma=0.05)
     y1 = bf16_host_bits(_run_moe(x, ids, w, gate, up, down))
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
     y2 = nv.moe_grouped(bf16_dev(x), torch.from_numpy(ids).to(DEV), torch.from_numpy(w).to(DEV),
@@ -796,8 +837,9 @@ def test_router_small_and_all_experts(T, E, k):
     assert np.allclose(w.cpu().numpy(), ow, rtol=2e-5, atol=1e-6)
 
 
-def test_moe_block_single_token():
-    T, k, E, H, I, Is, seed = 1, 4, 16, 512, 256, 256, 113
+@pytest.mark.parametrize("T,k,E,H,I,Is,seed", [(1, 4, 16, 512, 256, 256, 113),    # K-split gate/up, decode down
+                                                (2, 4, 16, 512, 512, 256, 114)])   # the two-launch path
+def test_moe_block_single_token(T, k, E, H, I, Is, seed):
     x, wr = _router_case(T, E, H, seed)
     gate = ONV.pack_batch(synth.expert_weights(E, I, H, 0.05, seed, synth.S_GATE))
     up = ONV.pack_batch(synth.expert_weights(E, I, H, 0.05, seed, synth.S_UP))
@@ -808,7 +850,7 @@ def test_moe_block_single_token():
     y = nv.moe_block(bf16_dev(x), bf16_dev(wr), k, weight_dev(gate), weight_dev(up), weight_dev(down),
                      bf16_dev(sg), bf16_dev(su), bf16_dev(sd))
     torch.cuda.synchronize()
-    assert_close(bf16_host_f64(y), y_ref, "moe block T=1")
+    assert_close(bf16_host_f64(y), y_ref, f"moe block T={T}")
 
 
 # ------------------------------------------------------------------ BF16 routed experts
