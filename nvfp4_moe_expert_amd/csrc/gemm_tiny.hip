@@ -23,8 +23,8 @@
 // s2u * u) in slot order, and the largest |H| of each (slot, nb) block of 16
 // values into hpart[slot][nb].
 //
-// tiny_down: workgroup (nb, t) = 16 output rows of token t. Wave w takes the
-// token's slots w, w + 4, ...: the H row and the weights of its next slot are in flight while it
+// tiny_down: workgroup (nb, t) = 16 output rows of token t. Wave w (of 8) takes
+// the token's slots w, w + 8, ...: the H row and the weights of its next slot are in flight while it
 // multiplies the current one (H loads before weight loads, so waiting for a row
 // never waits for weights that are not needed yet). The H row is scaled to fp16
 // by 2^p, p from the largest of the slot's hpart entries, and staged in the
@@ -44,6 +44,7 @@ namespace nvfp4 {
 namespace tiny_detail {
 
 constexpr int kThreads = 256;
+constexpr int kDownWaves = 8;     // down: waves per workgroup (two per SIMD)
 constexpr int kMaxT = 4;          // tokens
 constexpr int kMaxSlots = 32;     // T * k: the ids of a call fit the lanes of one wave
 constexpr int kRows = 16;         // slots per gate/up tile: the columns of one MFMA
@@ -283,12 +284,13 @@ __global__ __launch_bounds__(kThreads) void tiny_gateup_kernel(TinyArgs a) {
   if (q == 0) a.hpart[(int64_t)sl * (N / 16) + nb] = __builtin_bit_cast(uint32_t, mv);
 }
 
-// NST = I / 512 stages per slot (1..4); JW = slots per wave at most (2, 4 or 8).
-// Workgroup (nb, t): 16 output rows of token t, its k slots.
+// NST = I / 512 stages per slot (1..4); JW = slots per wave at most (1, 2 or 4).
+// Workgroup (nb, t): 16 output rows of token t, its k slots over 8 waves.
 template <bool TL, int NST, int JW>
-__global__ __launch_bounds__(kThreads) void tiny_down_kernel(TinyArgs a) {
+__global__ __launch_bounds__(64 * kDownWaves) void tiny_down_kernel(TinyArgs a) {
   constexpr int K = NST * KC;
-  __shared__ __attribute__((aligned(16))) uint16_t hs[4][2][kMaxI + 8];
+  constexpr int NB = JW > 1 ? 2 : 1;   // slots in flight per wave
+  __shared__ __attribute__((aligned(16))) uint16_t hs[kDownWaves][NB][kMaxI + 8];
   __shared__ float part[kMaxSlots][16];
 
   const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, q = lane >> 4;
@@ -309,7 +311,7 @@ __global__ __launch_bounds__(kThreads) void tiny_down_kernel(TinyArgs a) {
     uint32_t hp[2];
     Stage w[NST];
   };
-  Job J[2];
+  Job J[NB];
   // slot s0 + j's loads into set b: H row and its block maxima first, then the
   // weights. Never behind a branch: a slot past the token's last is loaded as the
   // last one again, and an id outside this GPU's experts loads expert 0's rows
@@ -367,16 +369,19 @@ __global__ __launch_bounds__(kThreads) void tiny_down_kernel(TinyArgs a) {
       for (int r = 0; r < 4; ++r) part[j][4 * q + r] = s2 * acc[r];
     }
   };
-  // this wave's slots wave, wave + 4, ... of the token: two in flight
+  // this wave's slots wave, wave + 8, ... of the token: up to two in flight
+  constexpr int W = kDownWaves;
   issue(J[0], wave);
-  issue(J[1], wave + 4);
+  if constexpr (NB > 1) issue(J[NB - 1], wave + W);
 #pragma unroll
   for (int i = 0; i < JW; i += 2) {
-    const int j0 = wave + 4 * i, j1 = j0 + 4;
+    const int j0 = wave + W * i, j1 = j0 + W;
     if (j0 < kk) run(J[0], 0, j0);
-    if (i + 2 < JW) issue(J[0], j0 + 8);
-    if (j1 < kk) run(J[1], 1, j1);
-    if (i + 2 < JW) issue(J[1], j1 + 8);
+    if (i + 2 < JW) issue(J[0], j0 + 2 * W);
+    if constexpr (NB > 1) {
+      if (j1 < kk) run(J[NB - 1], NB - 1, j1);
+      if (i + 2 < JW) issue(J[NB - 1], j1 + 2 * W);
+    }
   }
   __syncthreads();
 
@@ -414,16 +419,16 @@ __global__ __launch_bounds__(kThreads) void tiny_down_kernel(TinyArgs a) {
 
 static hipError_t launch_tiny_down(const TinyArgs& a, hipStream_t s) {
   const dim3 gd((unsigned)(a.H / 16), (unsigned)a.T);
-  // slots per wave: 2 (top-k <= 8), 4 (<= 16) or 8
+  // slots per wave: 1 (top-k <= 8), 2 (<= 16) or 4
   const int jw = a.k <= 8 ? 0 : a.k <= 16 ? 1 : 2;
   switch ((int)(a.I / KC) * 6 + (a.down.tiled ? 3 : 0) + jw) {
 #define NVFP4_TD(NST_)                                                                                             \
-  case NST_ * 6: hipLaunchKernelGGL((tiny_down_kernel<false, NST_, 2>), gd, dim3(kThreads), 0, s, a); break;    \
-  case NST_ * 6 + 1: hipLaunchKernelGGL((tiny_down_kernel<false, NST_, 4>), gd, dim3(kThreads), 0, s, a); break; \
-  case NST_ * 6 + 2: hipLaunchKernelGGL((tiny_down_kernel<false, NST_, 8>), gd, dim3(kThreads), 0, s, a); break; \
-  case NST_ * 6 + 3: hipLaunchKernelGGL((tiny_down_kernel<true, NST_, 2>), gd, dim3(kThreads), 0, s, a); break;  \
-  case NST_ * 6 + 4: hipLaunchKernelGGL((tiny_down_kernel<true, NST_, 4>), gd, dim3(kThreads), 0, s, a); break;  \
-  case NST_ * 6 + 5: hipLaunchKernelGGL((tiny_down_kernel<true, NST_, 8>), gd, dim3(kThreads), 0, s, a); break;
+  case NST_ * 6: hipLaunchKernelGGL((tiny_down_kernel<false, NST_, 1>), gd, dim3(64 * kDownWaves), 0, s, a); break;    \
+  case NST_ * 6 + 1: hipLaunchKernelGGL((tiny_down_kernel<false, NST_, 2>), gd, dim3(64 * kDownWaves), 0, s, a); break; \
+  case NST_ * 6 + 2: hipLaunchKernelGGL((tiny_down_kernel<false, NST_, 4>), gd, dim3(64 * kDownWaves), 0, s, a); break; \
+  case NST_ * 6 + 3: hipLaunchKernelGGL((tiny_down_kernel<true, NST_, 1>), gd, dim3(64 * kDownWaves), 0, s, a); break;  \
+  case NST_ * 6 + 4: hipLaunchKernelGGL((tiny_down_kernel<true, NST_, 2>), gd, dim3(64 * kDownWaves), 0, s, a); break;  \
+  case NST_ * 6 + 5: hipLaunchKernelGGL((tiny_down_kernel<true, NST_, 4>), gd, dim3(64 * kDownWaves), 0, s, a); break;
     NVFP4_TD(1) NVFP4_TD(2) NVFP4_TD(3) NVFP4_TD(4)
 #undef NVFP4_TD
     default: return hipErrorInvalidValue;
