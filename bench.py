@@ -528,6 +528,8 @@ def main():
         "roofline": {"bound": "hbm", "kernel": "gemm_decode_kernel<gate_up, fp16 dequant>",
                      "achieved": round(head["gateup_gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(head["gateup_gbs"] / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     # frac is the gate/up kernel's; the whole step (route, gate/up, down, combine):
+                     "step_frac": round(head["gbs"] / HBM_PEAK_GBS, 4),
                      "traffic_over_algorithmic": (round(traffic / head["gateup_bytes_per_launch"], 3)
                                                   if traffic else None),
                      "algorithmic_bytes_per_launch": round(head["gateup_bytes_per_launch"]),
