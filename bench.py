@@ -542,7 +542,7 @@ def main():
 
     if not args.no_extras:
         sweep = {}
-        for T in (1, 16, 64):
+        for T in (1, 2, 3, 4, 8, 16, 64):
             if T == args.tokens:
                 continue
             log(f"decode T={T}")

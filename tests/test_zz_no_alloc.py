@@ -4,7 +4,8 @@ entry point with a caller workspace (nvfp4_moe_grouped), through the C ABI.
 Both run the same kernels, so their outputs must be equal bit for bit; each
 must also meet the oracle's bar. Two calls in a row share the library's fixed
 scratch, the second on a smaller batch (and a different kernel class) than the
-first; a third call repeats the first over the second's leftovers."""
+first; a third call repeats the first over the second's leftovers, and a fourth
+takes two tokens through the two-launch path for tiny batches."""
 import ctypes
 
 import numpy as np
@@ -50,7 +51,7 @@ def _noalloc_c(xd, idd, wd, dev_w, y):
 def test_noalloc_equals_workspace_entry_point_on_consecutive_calls(weights):
     packs, dev_w = weights
     results = []
-    for T, seed in ((96, 151), (5, 152), (96, 151)):
+    for T, seed in ((96, 151), (5, 152), (96, 151), (2, 154)):
         plan = nv.moe_plan(T, K_TOP, E, H, I, nv.LAYOUT_TILED32, nv.LAYOUT_TILED32)
         note(f"noalloc T={T}: {plan}")
         x, ids, w = _inputs(T, seed)
