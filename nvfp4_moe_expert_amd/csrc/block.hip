@@ -241,6 +241,34 @@ __global__ __launch_bounds__(256) void bf16_reduce_kernel(const float* __restric
   }
 }
 
+// Largest 64-bit key (hi, lo) over the wave, returned from lane 63: DPP shifts
+// within rows of 16 and row broadcasts (lanes a shift reaches past a row's edge
+// keep their own key).
+template <int CTRL, int ROWS>
+__device__ __forceinline__ void dpp_max_step(uint32_t& hi, uint32_t& lo) {
+  const uint32_t h = (uint32_t)__builtin_amdgcn_update_dpp((int)hi, (int)hi, CTRL, ROWS, 0xF, false);
+  const uint32_t l = (uint32_t)__builtin_amdgcn_update_dpp((int)lo, (int)lo, CTRL, ROWS, 0xF, false);
+  const bool gt = h > hi || (h == hi && l > lo);
+  hi = gt ? h : hi;
+  lo = gt ? l : lo;
+}
+__device__ __forceinline__ void wave_max_key(uint32_t& hi, uint32_t& lo) {
+  dpp_max_step<0x111, 0xF>(hi, lo);   // row_shr:1
+  dpp_max_step<0x112, 0xF>(hi, lo);   // row_shr:2
+  dpp_max_step<0x114, 0xF>(hi, lo);   // row_shr:4
+  dpp_max_step<0x118, 0xF>(hi, lo);   // row_shr:8
+  dpp_max_step<0x142, 0xA>(hi, lo);   // row_bcast:15
+  dpp_max_step<0x143, 0xC>(hi, lo);   // row_bcast:31
+  hi = (uint32_t)__builtin_amdgcn_readlane((int)hi, 63);
+  lo = (uint32_t)__builtin_amdgcn_readlane((int)lo, 63);
+}
+
+// fp32 bits -> unsigned key of the same order (negatives below positives)
+__device__ __forceinline__ uint32_t ordered_bits(float v) {
+  const uint32_t b = __builtin_bit_cast(uint32_t, v);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
 // Top-k of each row of fp32 logits (the sum of `splits` partial rows
 // [splits][T][E], in split order), ties to the lower index, and the softmax over
 // the selected. One wave per row: the row is summed once into LDS, then k rounds
@@ -272,24 +300,20 @@ __global__ __launch_bounds__(256) void topk_softmax_kernel(const float* __restri
   float sel_v = 0.0f, top = 0.0f, sum = 0.0f;
   int sel_e = 0;
   for (int r = 0; r < k; ++r) {
-    float bv = -INFINITY;
-    int be = 0x7FFFFFFF;
+    // this lane's best remaining expert as a key (value order, then the lower
+    // index), 0 if it has none; the wave's largest key is the round's pick
+    uint32_t khi = 0, klo = 0;
     for (int i = 0, e = lane; e < E; ++i, e += 64) {
       if ((taken >> i) & 1) continue;
-      const float v = row[e];
-      if (v > bv || (v == bv && e < be)) {
-        bv = v;
-        be = e;
+      const uint32_t h = ordered_bits(row[e]), l = ~(uint32_t)e;
+      if (h > khi || (h == khi && l > klo)) {
+        khi = h;
+        klo = l;
       }
     }
-    for (int off = 32; off >= 1; off >>= 1) {
-      const float ov = __shfl_xor(bv, off);
-      const int oe = __shfl_xor(be, off);
-      if (ov > bv || (ov == bv && oe < be)) {
-        bv = ov;
-        be = oe;
-      }
-    }
+    wave_max_key(khi, klo);
+    const int be = (int)~klo;
+    const float bv = __builtin_bit_cast(float, (khi & 0x80000000u) ? (khi & 0x7FFFFFFFu) : ~khi);
     if ((be & 63) == lane) taken |= 1ull << (be >> 6);
     if (r == 0) top = bv;
     const float p = expf(bv - top);
