@@ -6,9 +6,10 @@
 // do not depend on the chunking).
 //
 // Work decomposition. A workgroup (8 waves, two per SIMD) takes one tile of
-// <= 128 rows of one expert and 512 weight rows: each wave owns 64 weight rows
-// (for gate/up: the same 32 output columns of both weights, so SiLU(gate)*up is
-// formed in registers) against all rows of the tile. v_mfma_f32_32x32x16 with
+// <= 128 rows of one expert and 256 or 512 weight rows; each wave owns W 32-row
+// weight blocks (gate/up: one block of gate and the same 32 columns of up, so
+// SiLU(gate)*up is formed in registers) against all rows of the tile.
+// v_mfma_f32_32x32x16 with
 //   A = weights, dequantized straight from HBM into registers: lane (r, h) of a
 //       32-row block owns row r and the contiguous k range [kb + 128h, +128) of
 //       every 256-k stage: four 128-bit code loads (pieces c of 32 k) and one
@@ -17,17 +18,20 @@
 //       in with direct-to-LDS buffer loads (no registers held while in flight),
 //       double-buffered, one barrier per stage.
 // MFMA step s (0..15) of a stage pairs k = kb + 8s (h = 0) with kb + 128 + 8s
-// (h = 1). The number of 32-row blocks multiplied follows the
-// tile's real row count (1..4, picked per tile), so small experts do not pay for
-// padding rows. Eight waves share each activation tile, so a stage moves 64 KB of
-// activations per 512 weight rows; the two waves of a SIMD hide each other's
-// latencies.
+// (h = 1). The number of 32-row tile blocks multiplied follows the tile's real
+// row count (1..4, picked per tile), so small experts do not pay for padding rows.
+// The two waves of a SIMD cover each other's waits (one wave per SIMD with twice
+// the weight rows and the accumulators in the accumulation registers reads half
+// the LDS operands per MFMA but ran slower).
 //
-// Schedule per wave: step s issues its LDS reads and MFMAs interleaved with the
-// dequant of step s + 1 (sched_group_barrier). The loads of stage st + 1 go out
-// during stage st: one activation load per step, the scales at step 0 (their
-// registers are double-buffered), and code piece c at step 4c + 3, right after
-// its last use (the code registers are single-buffered).
+// Schedule per wave, software-pipelined one MFMA step ahead: while the MFMAs of
+// step s issue, the wave dequantizes the A operands of step s + 1 and, as soon as
+// the last MFMA reading a B register has issued, reads that register's operand of
+// step s + 1 from LDS. The loads of stage st + 1 go out during stage st: the
+// activation loads in steps 0..8, the scales at step 0 (double-buffered), code
+// piece c at step 4c + 3, after the dequant of step 4c + 3 read it (the code
+// registers are single-buffered). Tiles of <= 64 rows keep two code sets and load
+// weights two stages ahead.
 //
 // Summation order of an output element: stages in increasing k, within a stage
 // MFMA steps s = 0..15, each over its 16 k. It depends only on K.
@@ -40,8 +44,6 @@ namespace nvfp4 {
 
 namespace prefill_detail {
 
-constexpr int kWaves = 8;
-constexpr int kThreads = 64 * kWaves;
 constexpr int KC = 256;             // k per stage
 constexpr int SPS = KC / 16;        // MFMA steps per stage
 constexpr int MT = 128;             // max rows per tile
@@ -51,49 +53,59 @@ constexpr int MT = 128;             // max rows per tile
 // compile-time offset.
 constexpr int RSU = KC / 8 + 1;     // 16-byte units per tile row (data + pad)
 constexpr int RSB = 16 * RSU;       // tile row stride in bytes
-constexpr int XI = ((MT * RSU + 63) / 64 + kWaves - 1) / kWaves * kWaves;  // 1 KB direct-to-LDS loads per stage
-constexpr int XPW = XI / kWaves;    // of them per wave
+constexpr int NW = 8;               // waves per workgroup
+constexpr int kThreads = 64 * NW;
+constexpr int XI = ((MT * RSU + 63) / 64 + NW - 1) / NW * NW;  // 1 KB direct-to-LDS loads per stage
+constexpr int XPW = XI / NW;        // of them per wave, one per step in steps 0..8
 constexpr int XBUF = XI * 1024;     // bytes per buffer
+static_assert(XPW <= 9, "activation loads per wave");
+
 template <int SEL>
 __device__ __forceinline__ float sc(uint32_t w) {
   return __builtin_amdgcn_cvt_f32_fp8(w, SEL);
 }
 
-
 // MFMA operand type of the bf16 and fp16 forms
 template <bool F16> struct Op { typedef bf16x8 T; };
 template <> struct Op<true> { typedef f16x8 T; };
 
-
+// s_waitcnt with vmcnt <= VM, lgkmcnt(0), expcnt not waited for (gfx9 encoding:
+// vmcnt[3:0] in bits 3:0 and vmcnt[5:4] in bits 15:14, expcnt bits 6:4, lgkmcnt 11:8)
+template <int VM>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+  static_assert(VM >= 0 && VM < 64, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt((VM & 15) | ((VM >> 4) << 14) | 0x0070);
+}
 
 }  // namespace prefill_detail
 
 using namespace prefill_detail;
 
-template <int MODE, int NB, bool F16, int WB, bool TL>
+template <int MODE, int NB, bool F16, int WB, bool TL, bool RAG>
 __device__ __forceinline__ void prefill_body(const GemmArgs& a, const F16Args& d, char* xs, int e, int rb,
                                              int rows, int nblk) {
   typedef typename Op<F16>::T AT;
   constexpr bool kTwo = (MODE == kGateUp || MODE == kGated);
-  constexpr int W = kTwo ? 2 : WB;     // 32-row weight blocks per wave
+  constexpr int W = kTwo ? 2 : WB;                // 32-row weight blocks per wave
+  constexpr int CW = 32 * (kTwo ? W / 2 : W);     // output columns per wave
   const int tid = threadIdx.x, lane = tid & 63, r32 = lane & 31, h = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t N = a.N, K = a.K;
 
-  // ---- weight rows of this lane: W 32-row blocks
-  // two-weight modes: block 0 = gate rows n0 + r32, block 1 = up rows n0 + r32 (n0 = 256*by + 32*wave)
-  // one-weight modes: block b = rows n0 + 32b + r32 (n0 = 32*WB*(8*by + wave))
+  // ---- weight rows of this lane: W 32-row blocks. The wave's output columns are
+  // nbase .. nbase + CW; two-weight modes: block b < W/2 = gate rows nbase + 32b + r32,
+  // block W/2 + b = the same up rows; one-weight modes: block b = rows nbase + 32b + r32.
   // Every load is a buffer load: a descriptor over one expert's codes / scales
   // (or over x) plus a 32-bit per-lane offset and a uniform stage offset.
-  const int64_t nbase = kTwo ? (int64_t)nblk * (32 * kWaves) + 32 * wave
-                             : (int64_t)nblk * (32 * WB * kWaves) + 32 * WB * wave;
+  const int64_t nbase = (int64_t)nblk * (CW * NW) + CW * wave;
   __amdgpu_buffer_rsrc_t crs[W], srs[W];
   uint32_t co[W], so[W];
 #pragma unroll
   for (int b = 0; b < W; ++b) {
-    int64_t n = kTwo ? nbase + r32 : nbase + 32 * b + r32;
+    const int bc = kTwo ? b % (W / 2) : b;
+    int64_t n = nbase + 32 * bc + r32;
     if (n > N - 1) n = N - 1;                 // rows past N: computed, never stored
-    const WeightDev& w = (kTwo && b == 1) ? a.w1 : a.w0;
+    const WeightDev& w = (kTwo && b >= W / 2) ? a.w1 : a.w0;
     crs[b] = rsrc(w.codes + (int64_t)e * N * (K / 2), N * (K / 2));
     srs[b] = rsrc(w.scales + (int64_t)e * N * (K / 16), N * (K / 16));
     if constexpr (TL) {   // blocks of 32 rows: 512-byte runs per 32-input chunk / 256-input scale chunk
@@ -126,12 +138,12 @@ __device__ __forceinline__ void prefill_body(const GemmArgs& a, const F16Args& d
   // Load J (of XI) lane l fills 16-byte unit u = 64J + l of the buffer: tile row
   // u / RSU, k chunk u % RSU. The pad unit of each row and the units past the
   // last row load the row's first chunk (never read). Rows past the tile load the
-  // tile's last row: their results are never stored. Wave w issues loads J = w + 8i.
+  // tile's last row: their results are never stored. Wave w issues loads J = w + NW*i.
   const __amdgpu_buffer_rsrc_t xrs = rsrc(a.x, a.x_rows * K * 2);
   uint32_t xo[XPW];
 #pragma unroll
   for (int i = 0; i < XPW; ++i) {
-    const int u = 64 * (wave + kWaves * i) + lane;
+    const int u = 64 * (wave + NW * i) + lane;
     int r = u / RSU;
     int c = u % RSU;
     if (c == RSU - 1) c = 0;
@@ -141,29 +153,28 @@ __device__ __forceinline__ void prefill_body(const GemmArgs& a, const F16Args& d
     else src = rb + r;
     xo[i] = (uint32_t)(2 * (src * K + 8 * c));
   }
-  // loads i in [i0, i1) of this wave's XPW; only the loads that fill the NB
-  // 32-row blocks the MFMAs read are issued
+  // Only the loads that fill the NB 32-row blocks the MFMAs read fetch anything;
+  // the others are issued with an offset beyond the descriptor's range (no memory
+  // access) into units of the buffer no MFMA reads, which keeps the steps free of
+  // branches. Row-major weights may have K % 256 != 0 (any multiple of 64: the
+  // shards of a tensor-parallel split); then the last stage runs past K (RAG), and
+  // its activation chunks past K are read the same way as zeros, so the weights
+  // read there (the next row's finite bytes, or zeros past the tensor) multiply
+  // zeros. Chunk of load i: (64 (wave + NW i) + lane) mod RSU, the pad read as 0.
   constexpr int XN = (32 * NB * RSU + 63) / 64;
-  // Row-major weights may have K % 256 != 0 (any multiple of 64: the shards of a
-  // tensor-parallel split); then the last stage runs past K. Its activation chunks
-  // past K are read through an offset beyond the descriptor's range (zeros, no
-  // memory access), so the weights read there (the next row's finite bytes, or
-  // zeros past the tensor) multiply zeros. Chunk of load i: (64 (wave + 8i) + lane)
-  // mod RSU, the pad chunk read as chunk 0.
   const int cbase = (64 * wave + lane) % RSU;
   auto issue_x = [&](int kb, int buf, int i0, int i1) {
-    const bool rag = kb + KC > K;   // uniform
 #pragma unroll
     for (int i = 0; i < XPW; ++i) {
-      if (i < i0 || i >= i1 || wave + kWaves * i >= XN) continue;
-      uint32_t off = xo[i];
-      if (rag) {
-        int c = cbase + (64 * kWaves * i) % RSU;
+      if (i < i0 || i >= i1) continue;
+      uint32_t off = (wave + NW * i < XN) ? xo[i] : 0x80000000u;
+      if constexpr (RAG) {
+        int c = cbase + (64 * NW * i) % RSU;
         if (c >= RSU) c -= RSU;
         if (c == RSU - 1) c = 0;
         if (kb + 8 * c >= K) off = 0x80000000u;
       }
-      auto* dst = (__attribute__((address_space(3))) void*)(xs + buf * XBUF + 1024 * (wave + kWaves * i));
+      auto* dst = (__attribute__((address_space(3))) void*)(xs + buf * XBUF + 1024 * (wave + NW * i));
       __builtin_amdgcn_raw_ptr_buffer_load_lds(xrs, dst, 16, off, 2 * kb, 0, 0);
     }
   };
@@ -191,31 +202,18 @@ __device__ __forceinline__ void prefill_body(const GemmArgs& a, const F16Args& d
       }
     }
   };
-  // B operands of MFMA step s: tile row 32t + r32, 16-byte unit 16h + s
+  // B operand of MFMA step s for tile block t: tile row 32t + r32, 16-byte unit 16h + s
   const char* const xrd = xs + r32 * RSB + 256 * h;
-  auto prep_b = [&](int buf, int s, AT (&B)[NB]) {
-#pragma unroll
-    for (int t = 0; t < NB; ++t)
-      B[t] = *reinterpret_cast<const AT*>(xrd + buf * XBUF + t * 32 * RSB + 16 * s);
-  };
-  // MFMAs i in [i0, i1) of one step, i = W*t + b
-  auto mma = [&](const AT (&A)[W], const AT (&B)[NB], int i0, int i1) {
-#pragma unroll
-    for (int i = 0; i < W * NB; ++i) {
-      if (i < i0 || i >= i1) continue;
-      const int t = i / W, b = i % W;
-      if constexpr (F16) acc[b][t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[b], B[t], acc[b][t], 0, 0, 0);
-      else acc[b][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[b], B[t], acc[b][t], 0, 0, 0);
-    }
+  auto read_b = [&](int buf, int s, int t) {
+    return *reinterpret_cast<const AT*>(xrd + buf * XBUF + t * 32 * RSB + 16 * s);
   };
 
-  // ---- pipeline. Stage st reads LDS buffer st % 2 and scale set st % 2; the loads
-  // of stage st + 1 are spread over its steps (see the header). The last stage
-  // reloads itself there instead (never read), which keeps the steps free of
-  // branches. The last step hands over: wait for this wave's activation and scale
-  // loads of stage st + 1 (only the code loads issued after the last activation
-  // load may still be in flight: 2W of them, 5W with DEEP), barrier (tile st + 1
-  // complete everywhere, buffer st % 2 free), and prepare step 0 of stage st + 1.
+  // ---- pipeline. Stage st reads LDS buffer st % 2 and scale set st % 2 (DEEP:
+  // code set st % 2). At its last step the wave waits for its activation loads of
+  // stage st + 1 (only the code and scale loads issued after the last activation
+  // load may still be in flight: 2W of them, 5W with DEEP), then a barrier makes
+  // tile st + 1 complete everywhere and frees buffer st % 2. The last stage
+  // reloads itself (never read), which keeps the steps free of branches.
   const int nst = (int)((K + KC - 1) / KC);
   issue_x(0, 0, 0, XPW);
   load_scales(0, 0);
@@ -230,51 +228,57 @@ __device__ __forceinline__ void prefill_body(const GemmArgs& a, const F16Args& d
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   AT A[W], B[NB];
+  prep_a(0, 0, A);
 
-  // Stage st uses LDS buffer st % 2, scale set st % 2 and (DEEP) code set st % 2.
-  // Activation loads of stage st + 1 go out one per step in steps 0..8.
-  //   normal: scales of st + 1 at step 0 into the other set, code piece c of st + 1
-  //           at step 4c + 3 (its last use); at the hand-over the 2W code loads of
-  //           steps 11 and 15 may still be in flight;
-  //   DEEP:   code piece c of st + 2 at step 9 + c (c < 3) and 15, scales of st + 2
-  //           at step 15, all into this stage's sets; the 5W loads after the last
-  //           activation load may be in flight at the hand-over.
-  // (A wave whose activation loads end before step 8 waits for more: still safe.)
+  // VALU instructions of the next step's dequant placed after each tile block's MFMAs
+  constexpr int PV = (W * (F16 ? 9 : 19) + NB - 1) / NB;
   auto stage = [&](int set, int buf, int st) {
     const int kn = (st + 1 < nst ? st + 1 : st) * KC;
     const int kn2 = (st + 2 < nst ? st + 2 : nst - 1) * KC;
 #pragma unroll
+    for (int t = 0; t < NB; ++t) B[t] = read_b(buf, 0, t);
+#pragma unroll
     for (int s = 0; s < SPS; ++s) {
-      issue_x(kn, buf ^ 1, s, s + 1);
+      if (s <= 8) issue_x(kn, buf ^ 1, s, s + 1);
       if (!DEEP && s == 0) load_scales(set ^ 1, kn);
-      prep_b(buf, s, B);
-      prep_a(set, s, A);
       if constexpr (DEEP) {
         if (s >= 9 && s <= 11) load_codes(set, s - 9, kn2);
         if (s == 15) {
           load_codes(set, 3, kn2);
           load_scales(set, kn2);
         }
-      } else {
-        if (s % 4 == 3) load_codes(0, s / 4, kn);   // piece s/4 was last used just above
       }
-      // the wave issuing its MFMAs takes the SIMD's issue priority while it does, so
-      // the other wave's dequant and loads fill the gaps instead of delaying them
-      // (dense MLP 958 -> 1036 TFLOP/s)
-      __builtin_amdgcn_s_setprio(3);
-      mma(A, B, 0, W * NB);
-      __builtin_amdgcn_s_setprio(0);
-      // LDS reads and dequant first, then the MFMAs (the other wave of the SIMD
-      // fills the gaps)
-#pragma unroll
-      for (int i = 0; i < NB; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       __builtin_amdgcn_sched_barrier(0);
+      // the wave issuing its MFMAs takes the SIMD's issue priority while it does
+      __builtin_amdgcn_s_setprio(3);
+      AT An[W];
+      if (s + 1 < SPS) prep_a(set, s + 1, An);
+      else prep_a(set ^ 1, 0, An);      // the next stage's first step: its scale set (DEEP: its code set)
+#pragma unroll
+      for (int t = 0; t < NB; ++t) {
+#pragma unroll
+        for (int b = 0; b < W; ++b) {
+          if constexpr (F16) acc[b][t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[b], B[t], acc[b][t], 0, 0, 0);
+          else acc[b][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[b], B[t], acc[b][t], 0, 0, 0);
+        }
+        if (s + 1 < SPS) B[t] = read_b(buf, s + 1, t);
+      }
+      if constexpr (!DEEP) {
+        if (s % 4 == 3) load_codes(0, s / 4, kn);   // piece s/4: its last reader was the dequant of step s
+      }
+      // per tile block: its W MFMAs, the LDS read of its next operand, a share of the dequant
+#pragma unroll
+      for (int t = 0; t < NB; ++t) {
+        __builtin_amdgcn_sched_group_barrier(0x008, W, 0);
+        if (s + 1 < SPS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, PV, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_setprio(0);
+#pragma unroll
+      for (int b = 0; b < W; ++b) A[b] = An[b];
       if (s + 1 == SPS) {
-        // vmcnt(5W) or vmcnt(2W); gfx9 encoding: vmcnt[3:0] (<= 10 here),
-        // expcnt[6:4] = 7 (no wait), lgkmcnt[11:8] = 0
-        constexpr int kVm = DEEP ? 5 * W : 2 * W;
-        static_assert(kVm <= 15, "vmcnt field");
-        __builtin_amdgcn_s_waitcnt(0x0070 | kVm);
+        wait_vm_lgkm0<DEEP ? 5 * W : 2 * W>();
         __syncthreads();
       }
     }
@@ -307,19 +311,15 @@ __device__ __forceinline__ void prefill_body(const GemmArgs& a, const F16Args& d
     const float s2a = s2a0 * unscale, s2b = s2b0 * unscale;
 #pragma unroll
     for (int g = 0; g < 4; ++g) {               // 4 groups of 4 consecutive weight rows
-      float v0[4], v1[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        v0[j] = acc[0][t][4 * g + j];
-        v1[j] = acc[W - 1][t][4 * g + j];
-      }
       const int off = 8 * g + 4 * h;            // weight row within the 32-row block
       if constexpr (kTwo) {
-        const int64_t n = nbase + off;
-        float v[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) v[j] = silu(s2a * v0[j]) * (s2b * v1[j]);
-        if (n < N) {
+        for (int j = 0; j < W / 2; ++j) {
+          const int64_t n = nbase + 32 * j + off;
+          if (n >= N) continue;
+          float v[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) v[q] = silu(s2a * acc[j][t][4 * g + q]) * (s2b * acc[W / 2 + j][t][4 * g + q]);
           uint16_t* dst = reinterpret_cast<uint16_t*>(a.out) + p * N + n;
           u32x2 o;
           o[0] = pack_bf16x2(v[0], v[1]);
@@ -331,15 +331,16 @@ __device__ __forceinline__ void prefill_body(const GemmArgs& a, const F16Args& d
         for (int b = 0; b < W; ++b) {
           const int64_t n = nbase + 32 * b + off;
           if (n >= N) continue;
-          const float* vv = b == 0 ? v0 : v1;
+          const f32x16& vv = acc[b][t];
           if constexpr (MODE == kDown) {
             float* dst = reinterpret_cast<float*>(a.out) + (int64_t)a.perm[p] * N + n;
-            *reinterpret_cast<f32x4*>(dst) = f32x4{s2a * vv[0], s2a * vv[1], s2a * vv[2], s2a * vv[3]};
+            *reinterpret_cast<f32x4*>(dst) =
+                f32x4{s2a * vv[4 * g], s2a * vv[4 * g + 1], s2a * vv[4 * g + 2], s2a * vv[4 * g + 3]};
           } else {
             uint16_t* dst = reinterpret_cast<uint16_t*>(a.out) + p * N + n;
             u32x2 o;
-            o[0] = pack_bf16x2(s2a * vv[0], s2a * vv[1]);
-            o[1] = pack_bf16x2(s2a * vv[2], s2a * vv[3]);
+            o[0] = pack_bf16x2(s2a * vv[4 * g], s2a * vv[4 * g + 1]);
+            o[1] = pack_bf16x2(s2a * vv[4 * g + 2], s2a * vv[4 * g + 3]);
             *reinterpret_cast<u32x2*>(dst) = o;
           }
         }
@@ -350,7 +351,8 @@ __device__ __forceinline__ void prefill_body(const GemmArgs& a, const F16Args& d
 
 // WB (one-weight modes): 32-row weight blocks per wave, 2 (512 weight rows per
 // workgroup) or 1 (256, for grids that would not fill the chip otherwise).
-template <int MODE, bool F16, int WB, bool TL>
+// Two-weight modes: 256 columns of each weight per workgroup.
+template <int MODE, bool F16, int WB, bool TL, bool RAG>
 __global__ __launch_bounds__(kThreads, 1) void gemm_prefill_kernel(GemmArgs a, F16Args d) {
   constexpr bool kMoe = (MODE == kGateUp || MODE == kDown);
   __shared__ __attribute__((aligned(16))) char xs[2 * XBUF];
@@ -378,10 +380,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_prefill_kernel(GemmArgs a, F
   }
   const int nb = (rows + 31) / 32;
   switch (nb) {
-    case 1: prefill_body<MODE, 1, F16, WB, TL>(a, d, xs, e, rb, rows, nblk); break;
-    case 2: prefill_body<MODE, 2, F16, WB, TL>(a, d, xs, e, rb, rows, nblk); break;
-    case 3: prefill_body<MODE, 3, F16, WB, TL>(a, d, xs, e, rb, rows, nblk); break;
-    default: prefill_body<MODE, 4, F16, WB, TL>(a, d, xs, e, rb, rows, nblk); break;
+    case 1: prefill_body<MODE, 1, F16, WB, TL, RAG>(a, d, xs, e, rb, rows, nblk); break;
+    case 2: prefill_body<MODE, 2, F16, WB, TL, RAG>(a, d, xs, e, rb, rows, nblk); break;
+    case 3: prefill_body<MODE, 3, F16, WB, TL, RAG>(a, d, xs, e, rb, rows, nblk); break;
+    default: prefill_body<MODE, 4, F16, WB, TL, RAG>(a, d, xs, e, rb, rows, nblk); break;
   }
 }
 
@@ -413,19 +415,22 @@ template <int MODE, bool F16, int WB>
 static void launch_pf(const GemmArgs& a, const F16Args& d, int64_t grid_tiles, hipStream_t s) {
   static_assert(WB == 1 || WB == 2, "weight blocks per wave");
   const bool two = (MODE == kGateUp || MODE == kGated);
-  const int64_t nw = two ? 32 * kWaves : 32 * WB * kWaves;     // output columns per workgroup
+  const int64_t nw = two ? 256 : 256 * WB;     // output columns per workgroup
   // routed modes: the grid holds ceil(tiles/8)*8 tiles' worth of workgroups (the
   // kernel maps them XCD by XCD); x * y is all that matters there
   const int64_t gt = (MODE == kGateUp || MODE == kDown) ? (grid_tiles + 7) / 8 * 8 : grid_tiles;
   const dim3 grid((unsigned)gt, (unsigned)((a.N + nw - 1) / nw));
-  if (a.w0.tiled) hipLaunchKernelGGL((gemm_prefill_kernel<MODE, F16, WB, true>), grid, dim3(kThreads), 0, s, a, d);
-  else hipLaunchKernelGGL((gemm_prefill_kernel<MODE, F16, WB, false>), grid, dim3(kThreads), 0, s, a, d);
+  const dim3 blk(kThreads);
+  const bool rag = a.K % KC != 0;
+  if (a.w0.tiled) hipLaunchKernelGGL((gemm_prefill_kernel<MODE, F16, WB, true, false>), grid, blk, 0, s, a, d);
+  else if (!rag) hipLaunchKernelGGL((gemm_prefill_kernel<MODE, F16, WB, false, false>), grid, blk, 0, s, a, d);
+  else hipLaunchKernelGGL((gemm_prefill_kernel<MODE, F16, WB, false, true>), grid, blk, 0, s, a, d);
 }
 
 int prefill_weight_blocks(GemmMode mode, int64_t N, int64_t grid_tiles) {
-  if (mode == kGateUp || mode == kGated) return 2;   // 32 rows of each of the two weights per wave
+  if (mode == kGateUp || mode == kGated) return 2;   // 256 columns of each of the two weights per workgroup
   // one-weight modes: half-width workgroups when full-width ones would leave CUs idle
-  return grid_tiles * ((N + 32 * 2 * kWaves - 1) / (32 * 2 * kWaves)) < 2 * (int64_t)cu_count() ? 1 : 2;
+  return grid_tiles * ((N + 511) / 512) < 2 * (int64_t)cu_count() ? 1 : 2;
 }
 
 hipError_t launch_prefill(GemmMode mode, bool f16, const GemmArgs& a, const F16Args& d, int64_t grid_tiles,
