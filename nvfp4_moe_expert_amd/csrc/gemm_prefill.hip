@@ -230,8 +230,10 @@ __device__ __forceinline__ void prefill_body(const GemmArgs& a, const F16Args& d
   AT A[W], B[NB];
   prep_a(0, 0, A);
 
-  // VALU instructions of the next step's dequant placed after each tile block's MFMAs
-  constexpr int PV = (W * (F16 ? 9 : 19) + NB - 1) / NB;
+  // VALU instructions of the next step's dequant placed after each tile block's
+  // MFMAs (about 9 per A operand in fp16, 19 in bf16; the bf16 groups are kept
+  // a little smaller, which measured 2% faster on the dense gated GEMM)
+  constexpr int PV = (W * (F16 ? 9 : 15) + NB - 1) / NB;
   auto stage = [&](int set, int buf, int st) {
     const int kn = (st + 1 < nst ? st + 1 : st) * KC;
     const int kn2 = (st + 2 < nst ? st + 2 : nst - 1) * KC;
