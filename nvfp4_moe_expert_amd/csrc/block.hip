@@ -11,9 +11,10 @@
 //   multiplied by the same wave, so SiLU(gate) * up is formed in registers);
 // * wave (t, w) multiplies activation rows 32t.. against weight rows 32w.. with
 //   A = weights and B = activations, both read from LDS; the K loop runs in
-//   stages of 64 inputs, double-buffered in LDS, the next stage's tiles loaded
-//   into registers while the current one is multiplied (small batches are
-//   bound by how many weight bytes are in flight, hence the deep stage);
+//   stages of 64 inputs, double-buffered in LDS, each stage loaded into
+//   registers one stage ahead of its LDS write (two register sets) when the
+//   loop is long, else while the stage before it is multiplied (the weight
+//   stream is bound by how many bytes are in flight);
 // * small batches split K over up to 16 workgroups per tile; every split writes
 //   its fp32 partial tile and a second kernel sums the splits in split order,
 //   so the result does not depend on scheduling.
@@ -32,10 +33,6 @@ constexpr int BN = 64;        // weight rows per workgroup (per weight matrix)
 constexpr int BK = 64;        // inputs per stage
 constexpr int LPR = BK / 8 / 4;   // 16-byte loads per thread per 64-row tile and stage
 constexpr int LDW = BK + 8;   // LDS row pitch in bf16 (16-byte pad: conflict-free 16-byte reads)
-
-__device__ __forceinline__ u32x4 ld16_guard(const uint16_t* p, bool ok) {
-  return ok ? ld16(p) : u32x4{0, 0, 0, 0};
-}
 
 }  // namespace block_detail
 
@@ -65,7 +62,7 @@ struct Bf16Group {
 // tiles, for grouped calls whose experts average at least 64 rows: every weight
 // row loaded then serves twice the activation rows, and a tile of a large expert
 // re-reads its weights half as often).
-template <int MODE, bool GROUPED, int TM>
+template <int MODE, bool GROUPED, int TM, int R>
 __global__ __launch_bounds__(kThreads) void bf16_gemm_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w0,
                                                              const uint16_t* __restrict__ w1, int64_t M, int64_t N,
                                                              int64_t K, int64_t k_per_split, void* __restrict__ out,
@@ -128,23 +125,31 @@ __global__ __launch_bounds__(kThreads) void bf16_gemm_kernel(const uint16_t* __r
     wok[j] = n0 + lr < N;
     wp[j] = (j == 0 ? w0 : w1) + (wok[j] ? (n0 + lr) * K : 0) + lc;
   }
-  u32x4 rx[TM][LPR], rw[NW][LPR];
-  auto load = [&](int64_t kb) {
+  // Register ring of R sets: stage s is loaded into set s % R, R - 1 stages
+  // before its registers are written to LDS, so each stage's loads have R - 1
+  // stages of MFMAs to land. Rows past M or N read row 0 of their operand (their
+  // results are never stored), so no load sits behind a branch and every wait
+  // counts exactly the loads it needs; loads for stages past the last re-read it.
+  // R == 1 (short K loops, where R stages of such re-reads would cost more than the
+  // lead gains): the next stage is loaded while the current one is multiplied.
+  u32x4 rx[R][TM][LPR], rw[R][NW][LPR];
+  auto load = [&](int set, int s) {
+    const int64_t kb = kb0 + (int64_t)std::min(s, nst - 1) * BK;
 #pragma unroll
     for (int i = 0; i < LPR; ++i) {
 #pragma unroll
-      for (int u = 0; u < TM; ++u) rx[u][i] = ld16_guard(xp[u] + kb + 32 * i, xok[u]);
+      for (int u = 0; u < TM; ++u) rx[set][u][i] = ld16(xp[u] + kb + 32 * i);
 #pragma unroll
-      for (int j = 0; j < NW; ++j) rw[j][i] = ld16_guard(wp[j] + kb + 32 * i, wok[j]);
+      for (int j = 0; j < NW; ++j) rw[set][j][i] = ld16(wp[j] + kb + 32 * i);
     }
   };
-  auto store = [&](int b) {
+  auto store = [&](int set, int b) {
 #pragma unroll
     for (int i = 0; i < LPR; ++i) {
 #pragma unroll
-      for (int u = 0; u < TM; ++u) st16(&xs[b][lr + BM * u][lc + 32 * i], rx[u][i]);
+      for (int u = 0; u < TM; ++u) st16(&xs[b][lr + BM * u][lc + 32 * i], rx[set][u][i]);
 #pragma unroll
-      for (int j = 0; j < NW; ++j) st16(&ws[b][j * BN + lr][lc + 32 * i], rw[j][i]);
+      for (int j = 0; j < NW; ++j) st16(&ws[b][j * BN + lr][lc + 32 * i], rw[set][j][i]);
     }
   };
 
@@ -153,15 +158,8 @@ __global__ __launch_bounds__(kThreads) void bf16_gemm_kernel(const uint16_t* __r
   for (int j = 0; j < NW; ++j)
 #pragma unroll
     for (int t = 0; t < TM; ++t) acc[j][t] = f32x16{};
-
-  if (nst > 0) {
-    load(kb0);
-    store(0);
-  }
-  __syncthreads();
-  for (int st = 0; st < nst; ++st) {
-    const int b = st & 1;
-    if (st + 1 < nst) load(kb0 + (int64_t)(st + 1) * BK);
+  // the MFMAs of one stage, from LDS buffer b
+  auto multiply = [&](int b) {
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
       const int kk = 16 * ks + 8 * (lane >> 5);
@@ -176,7 +174,41 @@ __global__ __launch_bounds__(kThreads) void bf16_gemm_kernel(const uint16_t* __r
         for (int t = 0; t < TM; ++t) acc[j][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, B[t], acc[j][t], 0, 0, 0);
       }
     }
-    if (st + 1 < nst) store(b ^ 1);
+  };
+
+  if (nst > 0) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) load(r, r);
+    store(0, 0);
+    __syncthreads();
+    if constexpr (R == 1) {
+      for (int s = 0; s < nst; ++s) {
+        if (s + 1 < nst) load(0, s + 1);
+        multiply(s & 1);
+        if (s + 1 < nst) store(0, (s & 1) ^ 1);
+        __syncthreads();
+      }
+    } else {
+      // step s: refill set s % R (stage s is in LDS) with stage s + R, multiply
+      // stage s from LDS buffer s % 2, then write stage s + 1 into the other buffer
+      // (read by every wave in step s - 1, before the barrier that ended it). Steps
+      // past the last stage only load and meet the barrier: every step issues the
+      // same loads, so the waits stay exact across the loop's back edge.
+      for (int st = 0; st < nst; st += R) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          const int s = st + r;
+          load(r, s + R);
+          if (s < nst) {
+            multiply(s & 1);
+            if (s + 1 < nst) store((r + 1) % R, (s & 1) ^ 1);
+          }
+          __syncthreads();
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(0);   // the loads past the last stage
+    }
+  } else {
     __syncthreads();
   }
 
@@ -330,6 +362,13 @@ __global__ __launch_bounds__(256) void topk_softmax_kernel(const float* __restri
 }
 
 // ------------------------------------------------------------------ launchers
+// Register sets of the K loop (see bf16_gemm_kernel): two for long loops (routed
+// BF16 experts at 4096 tokens 3.96 -> 3.61 ms; three or four sets measured 3.68 and
+// 3.65), one where a workgroup's K loop is short (the split-K products of small
+// batches), which the re-reads past the last stage would cost more than they gain.
+constexpr int kRing = 2;
+static bool deep_ring(int64_t k_per_workgroup) { return k_per_workgroup / BK >= 12; }
+
 static int splits_for(int64_t tiles, int64_t K) {
   // about two workgroups per CU in all; each split keeps >= 256 inputs
   if (tiles < 1) return 1;
@@ -359,15 +398,16 @@ hipError_t launch_bf16_grouped(bool gated, const uint16_t* x, const uint16_t* w0
   // 128-row tiles: ceil(tiles / 8) * 8 tiles' worth of workgroups (the kernel maps them XCD by XCD)
   const int64_t gt = tile_rows == 2 * BM ? (max_tiles + 7) / 8 * 8 : max_tiles;
   const dim3 grid((unsigned)gt, (unsigned)((N + BN - 1) / BN), 1u);
-#define NVFP4_BF16G(MODE_, TM_)                                                                                   \
-  hipLaunchKernelGGL((bf16_gemm_kernel<MODE_, true, TM_>), grid, dim3(kThreads), 0, s, x, w0, w1, (int64_t)0, N, K, \
-                     K, out, nullptr, grp)
+#define NVFP4_BF16G(MODE_, TM_, R_)                                                                                \
+  hipLaunchKernelGGL((bf16_gemm_kernel<MODE_, true, TM_, R_>), grid, dim3(kThreads), 0, s, x, w0, w1, (int64_t)0, N, \
+                     K, K, out, nullptr, grp)
+  const bool deep = deep_ring(K);
   if (tile_rows == 2 * BM) {
-    if (gated) NVFP4_BF16G(kBf16Gated, 2);
-    else NVFP4_BF16G(kBf16F32, 2);
+    if (gated) { if (deep) NVFP4_BF16G(kBf16Gated, 2, kRing); else NVFP4_BF16G(kBf16Gated, 2, 1); }
+    else { if (deep) NVFP4_BF16G(kBf16F32, 2, kRing); else NVFP4_BF16G(kBf16F32, 2, 1); }
   } else {
-    if (gated) NVFP4_BF16G(kBf16Gated, 1);
-    else NVFP4_BF16G(kBf16F32, 1);
+    if (gated) { if (deep) NVFP4_BF16G(kBf16Gated, 1, kRing); else NVFP4_BF16G(kBf16Gated, 1, 1); }
+    else { if (deep) NVFP4_BF16G(kBf16F32, 1, kRing); else NVFP4_BF16G(kBf16F32, 1, 1); }
   }
 #undef NVFP4_BF16G
   return hipGetLastError();
@@ -383,12 +423,13 @@ hipError_t launch_bf16_gemm(bool gated, const uint16_t* x, const uint16_t* w0, c
   if (M >= 4 * BM && splits_for(gm2 * gn, K) == 1) {
     const dim3 grid2((unsigned)gm2, (unsigned)gn, 1u);
     const Bf16Group none{};
-    if (gated)
-      hipLaunchKernelGGL((bf16_gemm_kernel<kBf16Gated, false, 2>), grid2, dim3(kThreads), 0, s, x, w0, w1, M, N, K, K,
-                         out, nullptr, none);
-    else
-      hipLaunchKernelGGL((bf16_gemm_kernel<kBf16F32, false, 2>), grid2, dim3(kThreads), 0, s, x, w0, w1, M, N, K, K,
-                         out, nullptr, none);
+#define NVFP4_BF16P(MODE_, R_)                                                                                     \
+  hipLaunchKernelGGL((bf16_gemm_kernel<MODE_, false, 2, R_>), grid2, dim3(kThreads), 0, s, x, w0, w1, M, N, K, K, out, \
+                     nullptr, none)
+    const bool deep = deep_ring(K);
+    if (gated) { if (deep) NVFP4_BF16P(kBf16Gated, kRing); else NVFP4_BF16P(kBf16Gated, 1); }
+    else { if (deep) NVFP4_BF16P(kBf16F32, kRing); else NVFP4_BF16P(kBf16F32, 1); }
+#undef NVFP4_BF16P
     return hipGetLastError();
   }
   const int64_t gm = (M + BM - 1) / BM;
@@ -398,12 +439,13 @@ hipError_t launch_bf16_gemm(bool gated, const uint16_t* x, const uint16_t* w0, c
   float* part = gz > 1 ? partial : nullptr;
   const dim3 grid((unsigned)gm, (unsigned)gn, (unsigned)gz);
   const Bf16Group none{};
-  if (gated)
-    hipLaunchKernelGGL((bf16_gemm_kernel<kBf16Gated, false, 1>), grid, dim3(kThreads), 0, s, x, w0, w1, M, N, K, kps, out,
-                       part, none);
-  else
-    hipLaunchKernelGGL((bf16_gemm_kernel<kBf16F32, false, 1>), grid, dim3(kThreads), 0, s, x, w0, w1, M, N, K, kps, out,
-                       part, none);
+#define NVFP4_BF16S(MODE_, R_)                                                                                       \
+  hipLaunchKernelGGL((bf16_gemm_kernel<MODE_, false, 1, R_>), grid, dim3(kThreads), 0, s, x, w0, w1, M, N, K, kps, out, \
+                     part, none)
+  const bool deep = deep_ring(kps);
+  if (gated) { if (deep) NVFP4_BF16S(kBf16Gated, kRing); else NVFP4_BF16S(kBf16Gated, 1); }
+  else { if (deep) NVFP4_BF16S(kBf16F32, kRing); else NVFP4_BF16S(kBf16F32, 1); }
+#undef NVFP4_BF16S
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || gz == 1) return e;
   if (splits_left && !gated) {   // the consumer sums the fp32 splits itself
