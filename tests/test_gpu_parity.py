@@ -758,7 +758,10 @@ def test_router_topk_vs_oracle(T, E, H, k, seed):
 
 @pytest.mark.parametrize("M,H,Is,seed", [(1, 4096, 1536, 103), (64, 4096, 1536, 104), (300, 2048, 512, 105),
                                          (1024, 1024, 2048, 106),
-                                         (4096, 2048, 2048, 109)])   # both products on 128-row tiles
+                                         (4096, 2048, 2048, 109),    # both products on 128-row tiles
+                                         # no K split, two-set register ring with odd stage counts: the gated
+                                         # product on 64-row tiles (19 stages), down on 128-row tiles (13)
+                                         (4096, 1216, 832, 121)])
 def test_bf16_mlp_vs_oracle(M, H, Is, seed):
     note(f"bf16 mlp M={M} H={H} Is={Is}")
     x = synth.bf16_normal((M, H), 1.0, seed, synth.S_X)
@@ -861,6 +864,7 @@ def test_moe_block_single_token(T, k, E, H, I, Is, seed):
     (40, 4, 16, 256, 128, 119, 0),      # 10 rows per expert: 64-row tiles
     (1, 8, 12, 256, 128, 116, 0),       # one token
     (30, 4, 4, 256, 128, 117, 4),       # expert-parallel slice (ids 0..11, local 4..7), duplicates
+    (300, 4, 6, 1216, 832, 120, 0),     # 128-row tiles with K loops of 19 and 13 stages (two-set register ring)
 ])
 def test_moe_grouped_bf16_vs_oracle(T, k, E, H, I, seed, eb):
     note(f"moe bf16 T={T} k={k} E={E} H={H} I={I} eb={eb}")
