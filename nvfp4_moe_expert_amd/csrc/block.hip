@@ -14,7 +14,9 @@
 //   stages of 64 inputs, double-buffered in LDS, each stage loaded into
 //   registers one stage ahead of its LDS write (two register sets) when the
 //   loop is long, else while the stage before it is multiplied (the weight
-//   stream is bound by how many bytes are in flight);
+//   stream is bound by how many bytes are in flight); the tiles move in 16-byte
+//   units, eight threads to each 128-byte row segment of a stage, and a wave
+//   skips the MFMAs of its 32-row blocks that lie past the tile's rows;
 // * small batches split K over up to 16 workgroups per tile; every split writes
 //   its fp32 partial tile and a second kernel sums the splits in split order,
 //   so the result does not depend on scheduling.
@@ -31,7 +33,6 @@ constexpr int kThreads = 256;
 constexpr int BM = 64;        // activation rows per workgroup
 constexpr int BN = 64;        // weight rows per workgroup (per weight matrix)
 constexpr int BK = 64;        // inputs per stage
-constexpr int LPR = BK / 8 / 4;   // 16-byte loads per thread per 64-row tile and stage
 constexpr int LDW = BK + 8;   // LDS row pitch in bf16 (16-byte pad: conflict-free 16-byte reads)
 
 }  // namespace block_detail
@@ -68,6 +69,7 @@ __global__ __launch_bounds__(kThreads) void bf16_gemm_kernel(const uint16_t* __r
                                                              int64_t K, int64_t k_per_split, void* __restrict__ out,
                                                              float* __restrict__ partial, Bf16Group grp) {
   constexpr int NW = MODE == kBf16Gated ? 2 : 1;
+  constexpr int NT = kThreads;
   constexpr int TBM = BM * TM;   // activation rows per workgroup
   __shared__ __attribute__((aligned(16))) uint16_t xs[2][TBM][LDW];
   __shared__ __attribute__((aligned(16))) uint16_t ws[2][NW * BN][LDW];
@@ -103,27 +105,32 @@ __global__ __launch_bounds__(kThreads) void bf16_gemm_kernel(const uint16_t* __r
   const int64_t kb1 = std::min(K, kb0 + k_per_split);
   const int nst = (int)((kb1 - kb0) / BK);
 
-  // global -> LDS: load i of thread tid moves 16 bytes (8 inputs) of row tid / 4,
-  // inputs 8 * (tid % 4) + 32 * i of the stage
-  const int lr = tid >> 2, lc = (tid & 3) * 8;
-  bool xok[TM];
-  const uint16_t* xp[TM];
+  // global -> LDS in 16-byte units (8 inputs): unit u of a stage is row u / 8,
+  // inputs 8 (u % 8) ..; thread tid moves units tid, tid + NT, ... of the
+  // activation tile (TBM rows) and of the weight tile (NW x BN rows)
+  constexpr int XU = TBM * (BK / 8) / NT, WU = NW * BN * (BK / 8) / NT;
+  static_assert(XU * NT == TBM * (BK / 8) && WU * NT == NW * BN * (BK / 8), "loader units");
+  const uint16_t* xp[XU];
+  int xl[XU];   // LDS row * LDW + column of each unit
 #pragma unroll
-  for (int u = 0; u < TM; ++u) {   // activation rows lr and, with TM = 2, lr + 64
-    const int r = lr + BM * u;
-    xok[u] = m0 + r < M;
+  for (int i = 0; i < XU; ++i) {
+    const int u = tid + NT * i, r = u >> 3, c = (u & 7) * 8;
+    const bool ok = m0 + r < M;
     int64_t xrow = m0 + r;
     if constexpr (GROUPED) {
-      if (xok[u]) xrow = grp.topk > 0 ? grp.perm[rb + r] / grp.topk : rb + r;
+      if (ok) xrow = grp.topk > 0 ? grp.perm[rb + r] / grp.topk : rb + r;
     }
-    xp[u] = x + (xok[u] ? xrow * K : 0) + lc;
+    xp[i] = x + (ok ? xrow * K : 0) + c;
+    xl[i] = r * LDW + c;
   }
-  const uint16_t* wp[NW];
-  bool wok[NW];
+  const uint16_t* wp[WU];
+  int wl[WU];
 #pragma unroll
-  for (int j = 0; j < NW; ++j) {
-    wok[j] = n0 + lr < N;
-    wp[j] = (j == 0 ? w0 : w1) + (wok[j] ? (n0 + lr) * K : 0) + lc;
+  for (int i = 0; i < WU; ++i) {
+    const int u = tid + NT * i, j = u / (BN * (BK / 8)), r = (u % (BN * (BK / 8))) >> 3, c = (u & 7) * 8;
+    const bool ok = n0 + r < N;
+    wp[i] = (j == 0 ? w0 : w1) + (ok ? (n0 + r) * K : 0) + c;
+    wl[i] = (j * BN + r) * LDW + c;
   }
   // Register ring of R sets: stage s is loaded into set s % R, R - 1 stages
   // before its registers are written to LDS, so each stage's loads have R - 1
@@ -132,25 +139,19 @@ __global__ __launch_bounds__(kThreads) void bf16_gemm_kernel(const uint16_t* __r
   // counts exactly the loads it needs; loads for stages past the last re-read it.
   // R == 1 (short K loops, where R stages of such re-reads would cost more than the
   // lead gains): the next stage is loaded while the current one is multiplied.
-  u32x4 rx[R][TM][LPR], rw[R][NW][LPR];
+  u32x4 rx[R][XU], rw[R][WU];
   auto load = [&](int set, int s) {
     const int64_t kb = kb0 + (int64_t)std::min(s, nst - 1) * BK;
 #pragma unroll
-    for (int i = 0; i < LPR; ++i) {
+    for (int i = 0; i < XU; ++i) rx[set][i] = ld16(xp[i] + kb);
 #pragma unroll
-      for (int u = 0; u < TM; ++u) rx[set][u][i] = ld16(xp[u] + kb + 32 * i);
-#pragma unroll
-      for (int j = 0; j < NW; ++j) rw[set][j][i] = ld16(wp[j] + kb + 32 * i);
-    }
+    for (int i = 0; i < WU; ++i) rw[set][i] = ld16(wp[i] + kb);
   };
   auto store = [&](int set, int b) {
 #pragma unroll
-    for (int i = 0; i < LPR; ++i) {
+    for (int i = 0; i < XU; ++i) st16(&xs[b][0][0] + xl[i], rx[set][i]);
 #pragma unroll
-      for (int u = 0; u < TM; ++u) st16(&xs[b][lr + BM * u][lc + 32 * i], rx[set][u][i]);
-#pragma unroll
-      for (int j = 0; j < NW; ++j) st16(&ws[b][j * BN + lr][lc + 32 * i], rw[set][j][i]);
-    }
+    for (int i = 0; i < WU; ++i) st16(&ws[b][0][0] + wl[i], rw[set][i]);
   };
 
   f32x16 acc[NW][TM];
@@ -158,22 +159,30 @@ __global__ __launch_bounds__(kThreads) void bf16_gemm_kernel(const uint16_t* __r
   for (int j = 0; j < NW; ++j)
 #pragma unroll
     for (int t = 0; t < TM; ++t) acc[j][t] = f32x16{};
-  // the MFMAs of one stage, from LDS buffer b
-  auto multiply = [&](int b) {
+  // the MFMAs of one stage, from LDS buffer b, for the wave's first NA 32-row
+  // blocks (those past the tile's rows are never stored, so they are skipped)
+  auto multiply_n = [&](int b, auto na_c) {
+    constexpr int NA = decltype(na_c)::value;
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
       const int kk = 16 * ks + 8 * (lane >> 5);
       bf16x8 B[TM];
 #pragma unroll
-      for (int t = 0; t < TM; ++t)
+      for (int t = 0; t < NA; ++t)
         B[t] = *reinterpret_cast<const bf16x8*>(&xs[b][32 * (TM * wt + t) + (lane & 31)][kk]);
 #pragma unroll
       for (int j = 0; j < NW; ++j) {
         const bf16x8 A = *reinterpret_cast<const bf16x8*>(&ws[b][j * BN + 32 * wn + (lane & 31)][kk]);
 #pragma unroll
-        for (int t = 0; t < TM; ++t) acc[j][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, B[t], acc[j][t], 0, 0, 0);
+        for (int t = 0; t < NA; ++t) acc[j][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, B[t], acc[j][t], 0, 0, 0);
       }
     }
+  };
+  const int64_t wrow0 = m0 + 32 * TM * wt;   // first activation row of this wave
+  const int na = wrow0 >= M ? 0 : (int)std::min<int64_t>(TM, (M - wrow0 + 31) / 32);
+  auto multiply = [&](int b) {
+    if (na == TM) multiply_n(b, std::integral_constant<int, TM>{});
+    else if (TM > 1 && na == 1) multiply_n(b, std::integral_constant<int, 1>{});
   };
 
   if (nst > 0) {
