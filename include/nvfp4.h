@@ -23,7 +23,8 @@
  *           change the current device. Between calls it keeps only per-device
  *           caches of device properties (compute-unit count, resident
  *           workgroups per kernel), filled on first use and safe to fill from
- *           several threads.
+ *           several threads; nvfp4_moe_grouped_noalloc alone also uses one
+ *           fixed scratch array per GPU, held until the process ends.
  * bf16.     bf16 tensors are passed as uint16_t bit patterns.
  * Weights.  A weight [n, k] (out x in) is described by nvfp4_weight_t:
  *             codes   [groups, n, k/2]  uint8: element 2j of a row in the LOW
