@@ -42,8 +42,12 @@ using namespace block_detail;
 // NW weight matrices (1: plain, 2: gate and up). Output per MODE:
 //   kBf16F32  - C fp32 [M, N] (splits == 1) or the split's partial;
 //   kBf16Gated- H bf16 [M, N] = bf16(SiLU(C_gate) * C_up) (splits == 1), or the
-//               split's partials of C_gate and C_up ([2][M][N]).
-enum Bf16Mode : int { kBf16F32 = 0, kBf16Gated = 1 };
+//               split's partials of C_gate and C_up ([2][M][N]);
+//   kBf16F32W - as kBf16F32 (grouped calls only, no split) with two adjacent
+//               64-row blocks of the one weight per workgroup: each activation
+//               tile loaded serves 128 weight rows, so the routed down projection
+//               (one weight, N = 4096) reads its H tiles half as often.
+enum Bf16Mode : int { kBf16F32 = 0, kBf16Gated = 1, kBf16F32W = 2 };
 
 // Grouped form (routed experts with bf16 weights): workgroup x takes tile x of
 // the route's tile list (expert e, rows rb .. rb+rows of the permuted order, at
@@ -68,7 +72,9 @@ __global__ __launch_bounds__(kThreads) void bf16_gemm_kernel(const uint16_t* __r
                                                              const uint16_t* __restrict__ w1, int64_t M, int64_t N,
                                                              int64_t K, int64_t k_per_split, void* __restrict__ out,
                                                              float* __restrict__ partial, Bf16Group grp) {
-  constexpr int NW = MODE == kBf16Gated ? 2 : 1;
+  constexpr int NW = MODE == kBf16F32 ? 1 : 2;
+  constexpr bool kWide = MODE == kBf16F32W;   // the NW blocks are rows n0 and n0 + BN of w0
+  static_assert(!kWide || GROUPED, "the wide form is for grouped calls");
   constexpr int NT = kThreads;
   constexpr int TBM = BM * TM;   // activation rows per workgroup
   __shared__ __attribute__((aligned(16))) uint16_t xs[2][TBM][LDW];
@@ -95,12 +101,12 @@ __global__ __launch_bounds__(kThreads) void bf16_gemm_kernel(const uint16_t* __r
     if (tile >= *grp.n_tiles) return;
     const int32_t* t = grp.tiles + 4 * (int64_t)tile;
     w0 += (int64_t)t[0] * grp.w_stride;
-    if (NW == 2) w1 += (int64_t)t[0] * grp.w_stride;
+    if (MODE == kBf16Gated) w1 += (int64_t)t[0] * grp.w_stride;
     rb = t[1];
     M = t[2];   // rows of this tile
     m0 = 0;
   }
-  const int64_t n0 = nb * BN;
+  const int64_t n0 = nb * BN * (kWide ? 2 : 1);
   const int64_t kb0 = (int64_t)blockIdx.z * k_per_split;
   const int64_t kb1 = std::min(K, kb0 + k_per_split);
   const int nst = (int)((kb1 - kb0) / BK);
@@ -128,8 +134,9 @@ __global__ __launch_bounds__(kThreads) void bf16_gemm_kernel(const uint16_t* __r
 #pragma unroll
   for (int i = 0; i < WU; ++i) {
     const int u = tid + NT * i, j = u / (BN * (BK / 8)), r = (u % (BN * (BK / 8))) >> 3, c = (u & 7) * 8;
-    const bool ok = n0 + r < N;
-    wp[i] = (j == 0 ? w0 : w1) + (ok ? (n0 + r) * K : 0) + c;
+    const int64_t row = n0 + (kWide ? j * BN : 0) + r;
+    const bool ok = row < N;
+    wp[i] = (kWide || j == 0 ? w0 : w1) + (ok ? row * K : 0) + c;
     wl[i] = (j * BN + r) * LDW + c;
   }
   // Register ring of R sets: stage s is loaded into set s % R, R - 1 stages
@@ -227,7 +234,7 @@ __global__ __launch_bounds__(kThreads) void bf16_gemm_kernel(const uint16_t* __r
   for (int t = 0; t < TM; ++t) {
     int64_t m = m0 + 32 * (TM * wt + t) + (lane & 31);
     if (m >= M) continue;
-    if constexpr (GROUPED) m = (MODE == kBf16F32) ? grp.perm[rb + m] : rb + m;   // output row
+    if constexpr (GROUPED) m = (MODE != kBf16Gated) ? grp.perm[rb + m] : rb + m;   // output row
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const int64_t n = n0 + 32 * wn + 8 * g + 4 * (lane >> 5);
@@ -242,6 +249,13 @@ __global__ __launch_bounds__(kThreads) void bf16_gemm_kernel(const uint16_t* __r
       } else if constexpr (MODE == kBf16F32) {
         *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) + m * N + n) =
             f32x4{acc[0][t][4 * g], acc[0][t][4 * g + 1], acc[0][t][4 * g + 2], acc[0][t][4 * g + 3]};
+      } else if constexpr (kWide) {
+#pragma unroll
+        for (int j = 0; j < NW; ++j) {
+          if (n + j * BN >= N) continue;
+          *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) + m * N + n + j * BN) =
+              f32x4{acc[j][t][4 * g], acc[j][t][4 * g + 1], acc[j][t][4 * g + 2], acc[j][t][4 * g + 3]};
+        }
       } else {
         float h[4];
 #pragma unroll
@@ -406,14 +420,16 @@ hipError_t launch_bf16_grouped(bool gated, const uint16_t* x, const uint16_t* w0
   const Bf16Group grp{tiles, n_tiles, perm, topk, N * K};
   // 128-row tiles: ceil(tiles / 8) * 8 tiles' worth of workgroups (the kernel maps them XCD by XCD)
   const int64_t gt = tile_rows == 2 * BM ? (max_tiles + 7) / 8 * 8 : max_tiles;
-  const dim3 grid((unsigned)gt, (unsigned)((N + BN - 1) / BN), 1u);
+  // one-weight calls on 128-row tiles take 128 weight rows per workgroup (the wide form)
+  const bool wide = !gated && tile_rows == 2 * BM;
+  const dim3 grid((unsigned)gt, (unsigned)((N + (wide ? 2 : 1) * BN - 1) / ((wide ? 2 : 1) * BN)), 1u);
 #define NVFP4_BF16G(MODE_, TM_, R_)                                                                                \
   hipLaunchKernelGGL((bf16_gemm_kernel<MODE_, true, TM_, R_>), grid, dim3(kThreads), 0, s, x, w0, w1, (int64_t)0, N, \
                      K, K, out, nullptr, grp)
   const bool deep = deep_ring(K);
   if (tile_rows == 2 * BM) {
     if (gated) { if (deep) NVFP4_BF16G(kBf16Gated, 2, kRing); else NVFP4_BF16G(kBf16Gated, 2, 1); }
-    else { if (deep) NVFP4_BF16G(kBf16F32, 2, kRing); else NVFP4_BF16G(kBf16F32, 2, 1); }
+    else { if (deep) NVFP4_BF16G(kBf16F32W, 2, kRing); else NVFP4_BF16G(kBf16F32W, 2, 1); }
   } else {
     if (gated) { if (deep) NVFP4_BF16G(kBf16Gated, 1, kRing); else NVFP4_BF16G(kBf16Gated, 1, 1); }
     else { if (deep) NVFP4_BF16G(kBf16F32, 1, kRing); else NVFP4_BF16G(kBf16F32, 1, 1); }
