@@ -8,7 +8,9 @@
 // K-contiguous), on v_mfma_f32_32x32x16_bf16 with fp32 accumulation:
 // * a workgroup of 4 waves takes 64 activation rows x 64 weight rows (of each of
 //   NW weight matrices: 2 for the gated form, whose gate and up rows n are
-//   multiplied by the same wave, so SiLU(gate) * up is formed in registers);
+//   multiplied by the same wave, so SiLU(gate) * up is formed in registers; the
+//   routed down projection on 128-row tiles takes two adjacent 64-row blocks of
+//   its one weight the same way);
 // * wave (t, w) multiplies activation rows 32t.. against weight rows 32w.. with
 //   A = weights and B = activations, both read from LDS; the K loop runs in
 //   stages of 64 inputs, double-buffered in LDS, each stage loaded into
