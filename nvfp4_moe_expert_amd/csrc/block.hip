@@ -9,8 +9,8 @@
 // * a workgroup of 4 waves takes 64 activation rows x 64 weight rows (of each of
 //   NW weight matrices: 2 for the gated form, whose gate and up rows n are
 //   multiplied by the same wave, so SiLU(gate) * up is formed in registers; the
-//   routed down projection on 128-row tiles takes two adjacent 64-row blocks of
-//   its one weight the same way);
+//   one-weight products on 128-row tiles take two adjacent 64-row blocks of
+//   their weight the same way);
 // * wave (t, w) multiplies activation rows 32t.. against weight rows 32w.. with
 //   A = weights and B = activations, both read from LDS; the K loop runs in
 //   stages of 64 inputs, double-buffered in LDS, each stage loaded into
@@ -45,10 +45,10 @@ using namespace block_detail;
 //   kBf16F32  - C fp32 [M, N] (splits == 1) or the split's partial;
 //   kBf16Gated- H bf16 [M, N] = bf16(SiLU(C_gate) * C_up) (splits == 1), or the
 //               split's partials of C_gate and C_up ([2][M][N]);
-//   kBf16F32W - as kBf16F32 (grouped calls only, no split) with two adjacent
-//               64-row blocks of the one weight per workgroup: each activation
-//               tile loaded serves 128 weight rows, so the routed down projection
-//               (one weight, N = 4096) reads its H tiles half as often.
+//   kBf16F32W - as kBf16F32 (no split) with two adjacent 64-row blocks of the
+//               one weight per workgroup: each activation tile loaded serves 128
+//               weight rows, so a down projection (one weight, N = 4096) reads its
+//               activation tiles half as often.
 enum Bf16Mode : int { kBf16F32 = 0, kBf16Gated = 1, kBf16F32W = 2 };
 
 // Grouped form (routed experts with bf16 weights): workgroup x takes tile x of
@@ -76,7 +76,6 @@ __global__ __launch_bounds__(kThreads) void bf16_gemm_kernel(const uint16_t* __r
                                                              float* __restrict__ partial, Bf16Group grp) {
   constexpr int NW = MODE == kBf16F32 ? 1 : 2;
   constexpr bool kWide = MODE == kBf16F32W;   // the NW blocks are rows n0 and n0 + BN of w0
-  static_assert(!kWide || GROUPED, "the wide form is for grouped calls");
   constexpr int NT = kThreads;
   constexpr int TBM = BM * TM;   // activation rows per workgroup
   __shared__ __attribute__((aligned(16))) uint16_t xs[2][TBM][LDW];
@@ -231,7 +230,7 @@ __global__ __launch_bounds__(kThreads) void bf16_gemm_kernel(const uint16_t* __r
   }
 
   // lane holds C[token m0 + 32(TM wt + t) + lane%32][weight row n0 + 32wn + 8(r/4) + 4(lane/32) + r%4]
-  const bool split = !GROUPED && partial != nullptr;
+  const bool split = !GROUPED && !kWide && partial != nullptr;   // the wide form is never split
 #pragma unroll
   for (int t = 0; t < TM; ++t) {
     int64_t m = m0 + 32 * (TM * wt + t) + (lane & 31);
@@ -448,14 +447,15 @@ hipError_t launch_bf16_gemm(bool gated, const uint16_t* x, const uint16_t* w0, c
   // 128-row tiles where they still give one K split (at least two workgroups per CU)
   const int64_t gm2 = (M + 2 * BM - 1) / (2 * BM);
   if (M >= 4 * BM && splits_for(gm2 * gn, K) == 1) {
-    const dim3 grid2((unsigned)gm2, (unsigned)gn, 1u);
+    // one-weight products take 128 weight rows per workgroup (the wide form)
+    const dim3 grid2((unsigned)gm2, (unsigned)(gated ? gn : (N + 2 * BN - 1) / (2 * BN)), 1u);
     const Bf16Group none{};
 #define NVFP4_BF16P(MODE_, R_)                                                                                     \
   hipLaunchKernelGGL((bf16_gemm_kernel<MODE_, false, 2, R_>), grid2, dim3(kThreads), 0, s, x, w0, w1, M, N, K, K, out, \
                      nullptr, none)
     const bool deep = deep_ring(K);
     if (gated) { if (deep) NVFP4_BF16P(kBf16Gated, kRing); else NVFP4_BF16P(kBf16Gated, 1); }
-    else { if (deep) NVFP4_BF16P(kBf16F32, kRing); else NVFP4_BF16P(kBf16F32, 1); }
+    else { if (deep) NVFP4_BF16P(kBf16F32W, kRing); else NVFP4_BF16P(kBf16F32W, 1); }
 #undef NVFP4_BF16P
     return hipGetLastError();
   }
