@@ -314,6 +314,7 @@ KS, DEC, RES, PRE, FB, TY = "decode_ksplit", "decode", "decode_resident", "prefi
     (128, 4, 32, 4096, 512, 123, 1, (DEC, RES, 4)),  # 64-tile bound: four 64-row blocks per wave
     (64, 4, 32, 4096, 512, 124, 0, (DEC, RES, 2)),   # the same on row-major weights
     (12, 4, 16, 4096, 2560, 125, 1, (DEC, DEC, 0)),  # down K=2560 > 2048: the streaming decode kernel
+    (600, 8, 320, 512, 512, 151, 1, (DEC, RES, 4)),  # 4800 slots: the windowed route feeding decode tiles
     # tensor-parallel shards of the intermediate size (row-major: K % 256 != 0)
     (16, 4, 16, 4096, 384, 130, 0, (DEC, DEC, 0)),   # I/4 = 384: down K=384 in 128-input stages
     (16, 4, 16, 4096, 192, 131, 0, (DEC, DEC, 0)),   # I/8 = 192: the last stage half masked
@@ -349,6 +350,7 @@ def test_moe_vs_oracle(T, k, E, H, I, seed, layout, kern):
 @pytest.mark.parametrize("cls,T,k,E,H,I,cuts", [
     (nv.CLASS_PREFILL, 600, 8, 16, 512, 256, [1, 100, 340]),   # chunks of 1, 99, 240 and 260 tokens
     (nv.CLASS_DECODE, 96, 4, 32, 512, 512, [1, 9, 40]),        # a one-token chunk would take the K-split
+    (nv.CLASS_DECODE, 600, 8, 16, 512, 512, [1, 100, 340]),    # ~300 rows per expert in 16-row tiles, 4800 slots
 ])
 def test_moe_pinned_class_chunks_bitwise(cls, T, k, E, H, I, cuts):
     # a pinned kernel class gives every token the same bits whatever the chunking
