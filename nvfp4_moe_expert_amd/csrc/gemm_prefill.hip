@@ -33,6 +33,9 @@
 // registers are single-buffered). Tiles of <= 64 rows keep two code sets and load
 // weights two stages ahead.
 //
+// Epilogue: the routed down projection's fp32 partials and the two-weight modes'
+// H go through LDS, so that every global store writes whole 128-byte lines.
+//
 // Summation order of an output element: stages in increasing k, within a stage
 // MFMA steps s = 0..15, each over its 16 k. It depends only on K.
 #include <atomic>
@@ -303,49 +306,102 @@ __device__ __forceinline__ void prefill_body(const GemmArgs& a, const F16Args& d
   const float act = a.act_scale ? *a.act_scale : 1.0f;   // W4A4: the activations' input_scale
   const float s2a0 = a.w0.scale_2[e] * act;
   const float s2b0 = kTwo ? a.w1.scale_2[e] * act : 0.0f;
+  // Routed down and the two-weight modes: the results go through LDS (the stage
+  // buffers are free once every wave has passed the barrier below), so that each
+  // global store instruction writes whole 128-byte lines instead of 16- or 32-byte
+  // pieces of 32 rows. Same values, same bits.
+  if constexpr (MODE == kDown) {
+    __syncthreads();
+    constexpr int CWv = 32 * W;                 // output columns of this wave
+    constexpr int PITCH = CWv + 4;              // floats per LDS row
+    static_assert(NW * 64 * PITCH * 4 <= 2 * XBUF, "partials tile");
+    float* lds = reinterpret_cast<float*>(xs) + wave * (64 * PITCH);
+    constexpr int LPR = CWv / 4, RPI = 64 / LPR;   // lanes per row, rows per store instruction
+#pragma unroll
+    for (int half = 0; half < (NB + 1) / 2; ++half) {   // 64 tile rows at a time
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        const int t = 2 * half + tt;
+        if (t >= NB) break;
+#pragma unroll
+        for (int b = 0; b < W; ++b)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const f32x16& vv = acc[b][t];
+            *reinterpret_cast<f32x4*>(lds + (32 * tt + r32) * PITCH + 32 * b + 8 * g + 4 * h) =
+                f32x4{s2a0 * vv[4 * g], s2a0 * vv[4 * g + 1], s2a0 * vv[4 * g + 2], s2a0 * vv[4 * g + 3]};
+          }
+      }
+      wait_vm_lgkm0<63>();   // this wave's LDS writes are done (its own area: no barrier)
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int i = 0; i < 64 / RPI; ++i) {
+        const int rl = i * RPI + lane / LPR, ch = lane % LPR;
+        const int tok = 64 * half + rl;
+        const f32x4 v = *reinterpret_cast<const f32x4*>(lds + rl * PITCH + 4 * ch);
+        const int64_t n = nbase + 4 * ch;
+        if (tok < rows && n < N)   // the partials are read once, by the combine: stream them past the caches
+          __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.out) +
+                                                                 (int64_t)a.perm[rb + tok] * N + n));
+      }
+      wait_vm_lgkm0<63>();
+      __builtin_amdgcn_wave_barrier();
+    }
+    return;
+  }
+  if constexpr (kTwo) {
+    constexpr int HP = CW * NW + 8;   // LDS row pitch (bf16) of the workgroup's [MT][CW * NW] H tile
+    static_assert(MT * HP * 2 <= 2 * XBUF, "H tile");
+    __syncthreads();
+    uint16_t* ht = reinterpret_cast<uint16_t*>(xs);
+#pragma unroll
+    for (int t = 0; t < NB; ++t) {
+      const int tok = 32 * t + r32;
+      float unscale = 1.0f;
+      if constexpr (F16 && MODE == kGateUp) unscale = ldexpf(1.0f, -d.xexp[a.perm[rb + min(tok, rows - 1)] / a.topk]);
+      const float s2a = s2a0 * unscale, s2b = s2b0 * unscale;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int off = 8 * g + 4 * h;
+        float v[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[q] = silu(s2a * acc[0][t][4 * g + q]) * (s2b * acc[1][t][4 * g + q]);
+        u32x2 o;
+        o[0] = pack_bf16x2(v[0], v[1]);
+        o[1] = pack_bf16x2(v[2], v[3]);
+        *reinterpret_cast<u32x2*>(ht + tok * HP + CW * wave + off) = o;
+      }
+    }
+    __syncthreads();
+    const int64_t ncol0 = (int64_t)nblk * (CW * NW);
+    constexpr int RPW = MT / NW;   // tile rows stored by each wave, two per instruction
+#pragma unroll
+    for (int i = 0; i < RPW / 2; ++i) {
+      const int row = RPW * wave + 2 * i + (lane >> 5), ch = lane & 31;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(ht + row * HP + 8 * ch);
+      if (row < rows && ncol0 + 8 * ch < N)
+        *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(a.out) + (rb + row) * N + ncol0 + 8 * ch) = v;
+    }
+    return;
+  }
+  // the dense one-weight product: bf16 rows straight from the accumulators
 #pragma unroll
   for (int t = 0; t < NB; ++t) {
     const int tok = 32 * t + r32;
     if (tok >= rows) continue;
     const int64_t p = rb + tok;
-    float unscale = 1.0f;
-    if constexpr (F16 && MODE == kGateUp) unscale = ldexpf(1.0f, -d.xexp[a.perm[p] / a.topk]);
-    const float s2a = s2a0 * unscale, s2b = s2b0 * unscale;
 #pragma unroll
     for (int g = 0; g < 4; ++g) {               // 4 groups of 4 consecutive weight rows
       const int off = 8 * g + 4 * h;            // weight row within the 32-row block
-      if constexpr (kTwo) {
 #pragma unroll
-        for (int j = 0; j < W / 2; ++j) {
-          const int64_t n = nbase + 32 * j + off;
-          if (n >= N) continue;
-          float v[4];
-#pragma unroll
-          for (int q = 0; q < 4; ++q) v[q] = silu(s2a * acc[j][t][4 * g + q]) * (s2b * acc[W / 2 + j][t][4 * g + q]);
-          uint16_t* dst = reinterpret_cast<uint16_t*>(a.out) + p * N + n;
-          u32x2 o;
-          o[0] = pack_bf16x2(v[0], v[1]);
-          o[1] = pack_bf16x2(v[2], v[3]);
-          *reinterpret_cast<u32x2*>(dst) = o;
-        }
-      } else {
-#pragma unroll
-        for (int b = 0; b < W; ++b) {
-          const int64_t n = nbase + 32 * b + off;
-          if (n >= N) continue;
-          const f32x16& vv = acc[b][t];
-          if constexpr (MODE == kDown) {
-            float* dst = reinterpret_cast<float*>(a.out) + (int64_t)a.perm[p] * N + n;
-            *reinterpret_cast<f32x4*>(dst) =
-                f32x4{s2a * vv[4 * g], s2a * vv[4 * g + 1], s2a * vv[4 * g + 2], s2a * vv[4 * g + 3]};
-          } else {
-            uint16_t* dst = reinterpret_cast<uint16_t*>(a.out) + p * N + n;
-            u32x2 o;
-            o[0] = pack_bf16x2(s2a * vv[4 * g], s2a * vv[4 * g + 1]);
-            o[1] = pack_bf16x2(s2a * vv[4 * g + 2], s2a * vv[4 * g + 3]);
-            *reinterpret_cast<u32x2*>(dst) = o;
-          }
-        }
+      for (int b = 0; b < W; ++b) {
+        const int64_t n = nbase + 32 * b + off;
+        if (n >= N) continue;
+        const f32x16& vv = acc[b][t];
+        u32x2 o;
+        o[0] = pack_bf16x2(s2a0 * vv[4 * g], s2a0 * vv[4 * g + 1]);
+        o[1] = pack_bf16x2(s2a0 * vv[4 * g + 2], s2a0 * vv[4 * g + 3]);
+        *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(a.out) + p * N + n) = o;
       }
     }
   }
