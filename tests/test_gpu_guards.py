@@ -116,6 +116,7 @@ def _moe_inputs(T, k, E, H, I, seed):
     (7, 3, 16, 512, 512, nv.CLASS_AUTO, 1),       # 21 slots: K-split gate/up, resident down
     (37, 3, 8, 512, 512, nv.CLASS_DECODE, 1),     # decode tiles with ragged ends
     (37, 3, 8, 512, 512, nv.CLASS_PREFILL, 1),    # prefill tiles with ragged ends
+    (37, 3, 8, 320, 320, nv.CLASS_PREFILL, 0),    # prefill tiles, partial last column block, K ending mid-stage
     (130, 4, 6, 256, 256, nv.CLASS_AUTO, 0),      # prefill, row-major
     (9, 2, 3, 96, 64, nv.CLASS_AUTO, 0),          # the fallback GEMM
 ])
