@@ -70,7 +70,7 @@ struct Bf16Group {
 // row loaded then serves twice the activation rows, and a tile of a large expert
 // re-reads its weights half as often).
 template <int MODE, bool GROUPED, int TM, int R>
-__global__ __launch_bounds__(kThreads) void bf16_gemm_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w0,
+__global__ __launch_bounds__(kThreads, 2) void bf16_gemm_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w0,
                                                              const uint16_t* __restrict__ w1, int64_t M, int64_t N,
                                                              int64_t K, int64_t k_per_split, void* __restrict__ out,
                                                              float* __restrict__ partial, Bf16Group grp) {
