@@ -76,6 +76,10 @@ __global__ __launch_bounds__(kThreads, 2) void bf16_gemm_kernel(const uint16_t* 
                                                              float* __restrict__ partial, Bf16Group grp) {
   constexpr int NW = MODE == kBf16F32 ? 1 : 2;
   constexpr bool kWide = MODE == kBf16F32W;   // the NW blocks are rows n0 and n0 + BN of w0
+  // 64-row routed tiles (decode-shaped batches) read each weight byte once per call:
+  // non-temporal loads stream them faster. Larger tiles re-read an expert's weights
+  // from the caches, which such loads would lose.
+  constexpr bool kStreamW = GROUPED && TM == 1;
   constexpr int NT = kThreads;
   constexpr int TBM = BM * TM;   // activation rows per workgroup
   __shared__ __attribute__((aligned(16))) uint16_t xs[2][TBM][LDW];
@@ -153,7 +157,7 @@ __global__ __launch_bounds__(kThreads, 2) void bf16_gemm_kernel(const uint16_t* 
 #pragma unroll
     for (int i = 0; i < XU; ++i) rx[set][i] = ld16(xp[i] + kb);
 #pragma unroll
-    for (int i = 0; i < WU; ++i) rw[set][i] = ld16(wp[i] + kb);
+    for (int i = 0; i < WU; ++i) rw[set][i] = kStreamW ? ld16_nt(wp[i] + kb) : ld16(wp[i] + kb);
   };
   auto store = [&](int set, int b) {
 #pragma unroll

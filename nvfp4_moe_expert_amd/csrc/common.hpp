@@ -207,6 +207,12 @@ __device__ __forceinline__ u32x4 ld16(const void* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }
 __device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+// Non-temporal 16-byte load, for bytes that one call reads exactly once (a weight
+// stream): measured on MI355X, a plain read stream of a 4 GiB buffer reaches
+// 6.2-6.4 TB/s with ordinary loads and 7.0-7.1 TB/s with these.
+__device__ __forceinline__ u32x4 ld16_nt(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
 
 // Buffer descriptor over `bytes` bytes from `base` for raw (untyped) buffer
 // access on gfx9-family parts (word 3 below); loads at offsets past the end

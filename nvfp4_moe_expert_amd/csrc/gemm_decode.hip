@@ -69,7 +69,7 @@ struct Stage {
 template <int U, bool TL>
 __device__ __forceinline__ void load_codes(Stage<U>& st, const uint8_t* codes, int64_t kb, bool ok = true) {
 #pragma unroll
-  for (int i = 0; i < U; ++i) st.c[i] = ok ? ld16(codes + (TL ? 16 * kb : kb / 2) + (TL ? 512 : 16) * i) : u32x4{0, 0, 0, 0};
+  for (int i = 0; i < U; ++i) st.c[i] = ok ? ld16_nt(codes + (TL ? 16 * kb : kb / 2) + (TL ? 512 : 16) * i) : u32x4{0, 0, 0, 0};
 }
 
 template <int U, bool TL>

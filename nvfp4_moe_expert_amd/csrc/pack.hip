@@ -25,7 +25,7 @@ __global__ __launch_bounds__(kPackThreads) void pack_amax_kernel(const uint16_t*
   uint32_t m = 0;
   const int64_t stride = (int64_t)nblk * kPackThreads * 8;
   for (int64_t i = ((int64_t)blockIdx.x * kPackThreads + threadIdx.x) * 8; i < per_tensor; i += stride)
-    m = max(m, absmax8(ld16(base + i)));
+    m = max(m, absmax8(ld16_nt(base + i)));   // streamed once (non-temporal loads read faster)
   // wave reduction then across the 4 waves
   for (int off = 32; off >= 1; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
   __shared__ uint32_t red[kPackThreads / 64];
