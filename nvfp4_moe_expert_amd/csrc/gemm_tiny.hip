@@ -292,6 +292,8 @@ __global__ __launch_bounds__(64 * kDownWaves) void tiny_down_kernel(TinyArgs a) 
   constexpr int NB = JW > 1 ? 2 : 1;   // slots in flight per wave
   __shared__ __attribute__((aligned(16))) uint16_t hs[kDownWaves][NB][kMaxI + 8];
   __shared__ float part[kMaxSlots][16];
+  __shared__ float wslot[kMaxSlots];   // w[t, j] of the token's slots
+  __shared__ int okslot[kMaxSlots];    // slot j's expert is one of this GPU's
 
   const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, q = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -299,9 +301,11 @@ __global__ __launch_bounds__(64 * kDownWaves) void tiny_down_kernel(TinyArgs a) 
   const int T = (int)a.T, kk = a.k, t = (int)blockIdx.y, s0 = t * kk;
   // lane j < k: the local expert of slot s0 + j
   int e = -1;
+  float twv = 0.0f;
   if (lane < kk) {
     const int v = a.ids[s0 + lane] - a.eb;
     e = (v >= 0 && v < a.E) ? v : -1;
+    twv = a.tw[s0 + lane];
   }
   const int64_t nrow = (int64_t)blockIdx.x * 16 + lr;
 
@@ -383,6 +387,12 @@ __global__ __launch_bounds__(64 * kDownWaves) void tiny_down_kernel(TinyArgs a) 
       if (i + 2 < JW) issue(J[NB - 1], j1 + 2 * W);
     }
   }
+  // the slots' weights and flags for the sum below, from the registers loaded at
+  // the start (read back from LDS, so the sum waits on no global load per slot)
+  if (wave == 0 && lane < kk) {
+    wslot[lane] = twv;
+    okslot[lane] = e >= 0;
+  }
   __syncthreads();
 
   // ---- y[t][16 nb + 8 h .. +8] for thread h: the combine's fixed-order sum
@@ -390,9 +400,8 @@ __global__ __launch_bounds__(64 * kDownWaves) void tiny_down_kernel(TinyArgs a) 
   const int h8 = 8 * tid;
   float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   for (int j = 0; j < kk; ++j) {
-    const int v = a.ids[s0 + j] - a.eb;
-    if (v < 0 || v >= a.E) continue;
-    const float wt = a.tw[s0 + j];
+    if (!okslot[j]) continue;
+    const float wt = wslot[j];
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] += wt * part[j][h8 + i];
   }
