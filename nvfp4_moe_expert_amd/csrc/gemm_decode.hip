@@ -63,13 +63,20 @@ struct Stage {
 // kb/16 bytes per kb inputs with 16-byte code chunks side by side; in the tiled
 // layout (blocks of 32 rows) a 32-input chunk is 512 bytes on, and 256 inputs of
 // scales are 512 bytes on (2*kb bytes per kb inputs).
+// Tiled codes are read with non-temporal loads (each 128-byte line is read once,
+// whole, by one instruction); row-major codes with ordinary ones: there a line is
+// split over several instructions, and without the cache's copy each of them
+// fetches it again.
 // ok == false (only with U == 1: the lane's 32 inputs lie past K in the last stage
 // of a K that is an odd multiple of 64): no load is issued and the codes and scale
 // bytes read as zero, so the lane's products are exact zeros.
 template <int U, bool TL>
 __device__ __forceinline__ void load_codes(Stage<U>& st, const uint8_t* codes, int64_t kb, bool ok = true) {
 #pragma unroll
-  for (int i = 0; i < U; ++i) st.c[i] = ok ? ld16_nt(codes + (TL ? 16 * kb : kb / 2) + (TL ? 512 : 16) * i) : u32x4{0, 0, 0, 0};
+  for (int i = 0; i < U; ++i) {
+    const uint8_t* p = codes + (TL ? 16 * kb : kb / 2) + (TL ? 512 : 16) * i;
+    st.c[i] = !ok ? u32x4{0, 0, 0, 0} : TL ? ld16_nt(p) : ld16(p);
+  }
 }
 
 template <int U, bool TL>

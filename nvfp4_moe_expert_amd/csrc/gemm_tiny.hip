@@ -78,7 +78,10 @@ __device__ __forceinline__ void lane_offsets(int64_t e, int64_t N, int64_t K, in
 template <bool TL>
 __device__ __forceinline__ void load_stage(Stage& st, const uint8_t* codes, const uint8_t* scales, int kb) {
 #pragma unroll
-  for (int i = 0; i < U; ++i) st.c[i] = ld16_nt(codes + (TL ? 16 * (int64_t)kb : kb / 2) + (TL ? 512 : 16) * i);
+  for (int i = 0; i < U; ++i) {   // non-temporal for tiled codes only (whole lines per instruction)
+    const uint8_t* p = codes + (TL ? 16 * (int64_t)kb : kb / 2) + (TL ? 512 : 16) * i;
+    st.c[i] = TL ? ld16_nt(p) : ld16(p);
+  }
   st.s = *reinterpret_cast<const u32x2*>(scales + (TL ? 2 * (int64_t)kb : kb / 16));
 }
 
