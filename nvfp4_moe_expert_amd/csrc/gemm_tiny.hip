@@ -13,7 +13,9 @@
 // w + 4 of 512 inputs. Every wave loads the (at most 32) top-k ids and its two
 // stage slices of every token's row, then derives the tile list itself (tiles in
 // order of each local expert's first slot, its slots in slot order, 16 per tile)
-// and loads its weights; nothing waits for the weights before the MFMAs. Row
+// and requests the first stage of its gate and up weights (the second stage of
+// each goes out when its first has arrived); nothing waits for weights before the
+// MFMAs. Row
 // maxima: each wave's over its slices (DPP reductions), combined after one
 // barrier; each row is scaled into fp16 by 2^p (p puts its max |x| in
 // [2^14, 2^15), as in the other kernel classes) and each wave stages its own
@@ -54,6 +56,7 @@ constexpr int U = 4;              // 16-byte code chunks per lane and stage
 constexpr int KC = 128 * U;       // inputs per stage
 
 // codes and scale bytes of one stage for one lane
+constexpr int kChunkLoads = U + 1;   // vector loads per Stage (U code chunks, one scale load)
 struct Stage {
   u32x4 c[U];
   u32x2 s;
@@ -83,6 +86,15 @@ __device__ __forceinline__ void load_stage(Stage& st, const uint8_t* codes, cons
     st.c[i] = TL ? ld16_nt(p) : ld16(p);
   }
   st.s = *reinterpret_cast<const u32x2*>(scales + (TL ? 2 * (int64_t)kb : kb / 16));
+}
+
+// s_waitcnt: at most N vector memory operations of this wave still outstanding
+// (gfx9 encoding: vmcnt[3:0] in bits 3:0, vmcnt[5:4] in bits 15:14; expcnt and
+// lgkmcnt at their maxima, so neither is waited for)
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0070 | 0x0F00);
 }
 
 // the two e4m3 scale bytes of code chunk i (blocks 2i and 2i + 1 of the lane's 8) as fp16
@@ -194,11 +206,10 @@ __global__ __launch_bounds__(kThreads) void tiny_gateup_kernel(TinyArgs a) {
   const int64_t nrow = (int64_t)nb * 16 + lr;
   int64_t coff, soff;
   lane_offsets<TL>(ex, N, K, nrow, q, coff, soff);
+  // (the first stage of each weight now, the second one as each first one arrives)
   Stage G[2], Up[2];
   load_stage<TL>(G[0], a.gate.codes + coff, a.gate.scales + soff, st0 * KC);
   load_stage<TL>(Up[0], a.up.codes + coff, a.up.scales + soff, st0 * KC);
-  load_stage<TL>(G[1], a.gate.codes + coff, a.gate.scales + soff, st1 * KC);
-  load_stage<TL>(Up[1], a.up.codes + coff, a.up.scales + soff, st1 * KC);
   const float s2g = a.gate.scale_2[ex], s2u = a.up.scale_2[ex];
 
   // ---- row maxima: each wave's over its slices (the waves' stages cover the row),
@@ -227,7 +238,8 @@ __global__ __launch_bounds__(kThreads) void tiny_gateup_kernel(TinyArgs a) {
   // an MFMA result depends on its own column of B alone).
   const int trow = lr < rows ? tslot[wave][lr] / a.k : 0;
   f32x4 acc0 = {0, 0, 0, 0}, acc1 = {0, 0, 0, 0};
-  auto step = [&](const Stage& g, const Stage& u, const int h) {
+  // one weight's stage h into acc
+  auto step = [&](const Stage& g, f32x4& acc, const int h) {
     const uint16_t* xrow = &xw[wave][trow][h][128 * q];
     f16x8 B[U][4];   // the stage's activations, read from LDS together
 #pragma unroll
@@ -236,18 +248,33 @@ __global__ __launch_bounds__(kThreads) void tiny_gateup_kernel(TinyArgs a) {
       for (int sst = 0; sst < 4; ++sst) B[i][sst] = *reinterpret_cast<const f16x8*>(xrow + 32 * i + 8 * sst);
 #pragma unroll
     for (int i = 0; i < U; ++i) {
-      const f16x2 gsc = chunk_scales(g.s, i), usc = chunk_scales(u.s, i);
+      const f16x2 gsc = chunk_scales(g.s, i);
 #pragma unroll
       for (int sst = 0; sst < 4; ++sst) {
         const f16x2 gs = sst < 2 ? f16x2{gsc[0], gsc[0]} : f16x2{gsc[1], gsc[1]};
-        const f16x2 us = sst < 2 ? f16x2{usc[0], usc[0]} : f16x2{usc[1], usc[1]};
-        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(dequant8_f16(g.c[i][sst], gs), B[i][sst], acc0, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(dequant8_f16(u.c[i][sst], us), B[i][sst], acc1, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(dequant8_f16(g.c[i][sst], gs), B[i][sst], acc, 0, 0, 0);
       }
     }
   };
-  if (has0) step(G[0], Up[0], 0);
-  if (has1) step(G[1], Up[1], 1);
+  // Weight chunks (one weight, one stage: kChunkLoads loads) stream two at a time:
+  // when a first-stage chunk has arrived, the same weight's second stage is
+  // requested, then the arrived chunk is multiplied. With all four chunks requested
+  // at once, every wave's chunks arrived only towards the end of the stream and all
+  // of the dequantization (eight VALU instructions per MFMA) ran after it; this way
+  // only the last chunk's does. The scheduling barriers keep the loads where they
+  // are written; the waits are the compiler's own plus the two explicit ones.
+  wait_vm<kChunkLoads>();   // G[0] in, Up[0] may still be in flight
+  __builtin_amdgcn_sched_barrier(0);
+  load_stage<TL>(G[1], a.gate.codes + coff, a.gate.scales + soff, st1 * KC);
+  __builtin_amdgcn_sched_barrier(0);
+  if (has0) step(G[0], acc0, 0);
+  wait_vm<kChunkLoads>();   // Up[0] in, G[1] may still be in flight
+  __builtin_amdgcn_sched_barrier(0);
+  load_stage<TL>(Up[1], a.up.codes + coff, a.up.scales + soff, st1 * KC);
+  __builtin_amdgcn_sched_barrier(0);
+  if (has0) step(Up[0], acc1, 0);
+  if (has1) step(G[1], acc0, 1);
+  if (has1) step(Up[1], acc1, 1);
 
   // partial sums of waves 1..3 to wave 0, added in wave order
   if (wave > 0) {
