@@ -453,13 +453,18 @@ hipError_t launch_route(const int32_t* ids, int64_t S, int E, int eb, int tile_r
   return hipGetLastError();
 }
 
-// One thread: 8 consecutive outputs of one token. KM > 0 (k <= KM): the ids,
+// One thread: 8 outputs of one token. KM > 0 (k <= KM): the ids,
 // weights and partial rows of all k slots are loaded before the sum, so the
 // loads overlap; the sum runs over j in order either way.
 // NT: the partials are read with non-temporal loads (large batches, whose partials
 // do not stay in the caches: 4096 tokens 114 -> 108 us; at 64 tokens, where down
 // has just written them into the caches, plain loads are faster, 7.0 against 7.9 us).
-template <int KM, bool NT>
+// WL (H % 512 == 0): the 64 threads of a wave take 512 columns of one token, lane l
+// the 4 columns at 4l and the 4 at 256 + 4l, so that every 16-byte load and 8-byte
+// store instruction of the wave covers whole 128-byte lines (each line once);
+// otherwise a thread takes 8 consecutive columns, and each line is split over two
+// load instructions.
+template <int KM, bool NT, bool WL>
 __global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict__ ids,
                                                       const float* __restrict__ w,
                                                       const float* __restrict__ ypart, int64_t T, int k,
@@ -469,6 +474,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict_
   const int64_t per_tok = H / 8;
   if (u >= T * per_tok) return;
   const int64_t t = u / per_tok, c8 = u % per_tok;
+  const int64_t ca = WL ? (c8 / 64) * 512 + 4 * (c8 % 64) : 8 * c8;   // first and second group of 4
+  const int64_t cb = WL ? ca + 256 : ca + 4;
   float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   if constexpr (KM > 0) {
     // the partial rows are loaded before the ids are known (a skipped slot's row is
@@ -483,13 +490,15 @@ __global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict_
       wt[j] = (j < k) ? w[t * k + j] : 0.0f;
       a[j] = b[j] = f32x4{0, 0, 0, 0};
       if (j < k) {
-        const f32x4* src = reinterpret_cast<const f32x4*>(ypart + (t * k + j) * H + c8 * 8);
+        const float* row = ypart + (t * k + j) * H;
+        const f32x4* pa = reinterpret_cast<const f32x4*>(row + ca);
+        const f32x4* pb = reinterpret_cast<const f32x4*>(row + cb);
         if constexpr (NT) {
-          a[j] = __builtin_nontemporal_load(src);
-          b[j] = __builtin_nontemporal_load(src + 1);
+          a[j] = __builtin_nontemporal_load(pa);
+          b[j] = __builtin_nontemporal_load(pb);
         } else {
-          a[j] = src[0];
-          b[j] = src[1];
+          a[j] = *pa;
+          b[j] = *pb;
         }
       }
     }
@@ -509,8 +518,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict_
       const int e = ids[slot] - eb;
       if (e < 0 || e >= E) continue;
       const float wt = w[slot];
-      const f32x4* src = reinterpret_cast<const f32x4*>(ypart + slot * H + c8 * 8);
-      const f32x4 a = src[0], b = src[1];
+      const f32x4 a = *reinterpret_cast<const f32x4*>(ypart + slot * H + ca);
+      const f32x4 b = *reinterpret_cast<const f32x4*>(ypart + slot * H + cb);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         acc[i] += wt * a[i];
@@ -522,8 +531,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict_
     f32x4 a = {0, 0, 0, 0}, b = {0, 0, 0, 0};
 #pragma unroll 4
     for (int z = 0; z < extra_splits; ++z) {   // its K splits, in split order
-      const f32x4* ex = reinterpret_cast<const f32x4*>(extra + (int64_t)z * T * H + t * H + c8 * 8);
-      const f32x4 p = ex[0], q = ex[1];
+      const float* ex = extra + (int64_t)z * T * H + t * H;
+      const f32x4 p = *reinterpret_cast<const f32x4*>(ex + ca), q = *reinterpret_cast<const f32x4*>(ex + cb);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         a[i] += p[i];
@@ -536,10 +545,17 @@ __global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict_
       acc[4 + i] += b[i];
     }
   }
-  u32x4 o;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(acc[2 * i], acc[2 * i + 1]);
-  st16(y + t * H + c8 * 8, o);
+  u32x2 oa, ob;
+  oa[0] = pack_bf16x2(acc[0], acc[1]);
+  oa[1] = pack_bf16x2(acc[2], acc[3]);
+  ob[0] = pack_bf16x2(acc[4], acc[5]);
+  ob[1] = pack_bf16x2(acc[6], acc[7]);
+  if constexpr (WL) {
+    *reinterpret_cast<u32x2*>(y + t * H + ca) = oa;
+    *reinterpret_cast<u32x2*>(y + t * H + cb) = ob;
+  } else {
+    st16(y + t * H + ca, u32x4{oa[0], oa[1], ob[0], ob[1]});
+  }
 }
 
 hipError_t launch_combine(const int32_t* ids, const float* w, const float* ypart, int64_t T, int k,
@@ -551,15 +567,18 @@ hipError_t launch_combine(const int32_t* ids, const float* w, const float* ypart
   const int bs = n < 256 * 256 ? 64 : 256;
   const int64_t gx = (n + bs - 1) / bs;
   const bool nt = T * k * H * (int64_t)sizeof(float) > ((int64_t)128 << 20);   // partials beyond 128 MB
-  if (k <= 8 && nt)
-    hipLaunchKernelGGL((combine_kernel<8, true>), dim3((unsigned)gx), dim3(bs), 0, s, ids, w, ypart, T, k, H, E, eb,
-                       extra, extra_splits, y);
-  else if (k <= 8)
-    hipLaunchKernelGGL((combine_kernel<8, false>), dim3((unsigned)gx), dim3(bs), 0, s, ids, w, ypart, T, k, H, E, eb,
-                       extra, extra_splits, y);
-  else
-    hipLaunchKernelGGL((combine_kernel<0, false>), dim3((unsigned)gx), dim3(bs), 0, s, ids, w, ypart, T, k, H, E, eb,
-                       extra, extra_splits, y);
+  const bool wl = H % 512 == 0;
+#define NVFP4_CB(KM_, NT_, WL_) \
+  hipLaunchKernelGGL((combine_kernel<KM_, NT_, WL_>), dim3((unsigned)gx), dim3(bs), 0, s, ids, w, ypart, T, k, H, E, \
+                     eb, extra, extra_splits, y)
+  if (k <= 8 && nt) {
+    if (wl) NVFP4_CB(8, true, true); else NVFP4_CB(8, true, false);
+  } else if (k <= 8) {
+    if (wl) NVFP4_CB(8, false, true); else NVFP4_CB(8, false, false);
+  } else {
+    if (wl) NVFP4_CB(0, false, true); else NVFP4_CB(0, false, false);
+  }
+#undef NVFP4_CB
   return hipGetLastError();
 }
 
